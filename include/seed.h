@@ -1,0 +1,154 @@
+/*
+ * seed.h -- C ABI of the MI355X (gfx950) shallow recurrent-state engine.
+ *
+ * A linear-attention / state-space head keeps a d_k x d_v recurrent state S.
+ * SEED stores it as a sink along a fixed per-head direction plus rank-R
+ * factors,  S = a vbar^T + U V^T  (SEED summary on picx.dev, "SEED
+ * Architecture"; SEED figures and tables on thelatestinai.com, Fig. 1 (b)).
+ * Each decode step reads the state out and applies the head's gated update
+ * exactly by rescaling a, decaying U and appending one column to U and V
+ * (picx.dev summary, "Exact Update (Lemma 2)"); every W steps the factors
+ * are compressed back to rank R (Fig. 1 (b) caption).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them.  Base pointers must be 16-byte
+ *    aligned.  Arrays are dense, row-major, in the layouts given below.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; nothing synchronises.  Calls on the
+ *    same state must be serialised by the caller (same stream or events).
+ *  - Every call validates its arguments on the host BEFORE touching the HIP
+ *    runtime and returns a seed_status.  Nothing aborts, throws or prints.
+ *    On failure nothing was launched and seed_last_error() (thread-local)
+ *    describes the problem.  A kernel fault surfaces at the caller's next
+ *    synchronisation, not here.
+ *  - NaN / Inf inputs are not checked; they propagate into the outputs.
+ *  - Supported head shapes (d_k, d_v): (128,128), (128,64), (64,64).
+ *    Factor capacity cap = R + W <= 96 columns.  Larger or other shapes
+ *    return SEED_E_UNSUPPORTED.
+ *
+ * Layouts, for `batch` requests of `heads` heads (unit index b*heads + h):
+ *   a    float [batch][heads][d_k]          sink coefficients
+ *   U    float [batch][heads][cap][d_k]     factor columns; column j of U is
+ *                                           the contiguous U[b][h][j][:]
+ *   V    float [batch][heads][cap][d_v]     factor columns, same scheme
+ *   vbar float [heads][d_v]                 per-head direction, shared by
+ *                                           all requests; any nonzero vector
+ *   S    float [batch][heads][d_k][d_v]     dense state (row i = key i)
+ *   q, k       [batch][heads][d_k]          fp32 or bf16 (see in_dtype)
+ *   v          [batch][heads][d_v]          fp32 or bf16
+ *   g    float [batch][heads]               decay (Gated DeltaNet, Mamba-2)
+ *        float [batch][heads][d_k]          decay per key channel (KDA)
+ *   beta float [batch][heads]               write strength (NULL for Mamba-2)
+ *   o    float [batch][heads][d_v]          read-out (must not alias inputs)
+ *
+ * The factor columns form a ring of fixed capacity: a step writes column r
+ * (never moves data), compression rewrites columns 0..R-1.  The caller keeps
+ * r, the number of columns held, which is the same for the whole batch.
+ */
+#ifndef SEED_H
+#define SEED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SEED_OK = 0,
+  SEED_E_ARG = 1,          /* NULL or misaligned pointer, unknown enum value   */
+  SEED_E_SHAPE = 2,        /* sizes that contradict each other or are <= 0     */
+  SEED_E_UNSUPPORTED = 3,  /* valid, but outside the shapes this build covers  */
+  SEED_E_FULL = 4,         /* decode step asked for with r == cap: compress first */
+  SEED_E_DEVICE = 5        /* the HIP runtime refused the launch               */
+} seed_status;
+
+typedef enum {
+  SEED_RULE_GDN = 0,    /* Gated DeltaNet:        S' = g (I - beta k k^T) S + beta k v^T      */
+  SEED_RULE_KDA = 1,    /* Kimi Delta Attention:  S' = (I - beta k k^T) Diag(g) S + beta k v^T */
+  SEED_RULE_MAMBA2 = 2  /* Mamba-2 (d_k = state dim, d_v = head dim):  S' = g S + k v^T    */
+} seed_rule;
+
+typedef enum { SEED_F32 = 0, SEED_BF16 = 1 } seed_dtype;  /* storage type of q, k, v */
+
+/*
+ * seed_decode_step -- one decode step of every (request, head) unit.
+ *
+ * Defined by Lemma 2 (picx.dev summary, "Exact Update (Lemma 2)"), with
+ * omega = v.vbar/|vbar|^2 and eps = v - omega vbar:
+ *   Gated DeltaNet:  a <- g a + beta (omega - g k.a) k
+ *                    U <- [g U, k],  V <- [V, beta (eps - V (g U)^T k)]
+ *   Kimi Delta Attention: the same with Diag(g) for the scalar g.
+ *   Mamba-2:         a <- g a + omega k,  U <- [g U, k],  V <- [V, eps]
+ * then the read-out of the updated state, o = vbar (a.q) + V (U^T q)
+ * (SEED figures and tables, Table 1: the factors give the read-out and the
+ * exact update).  U is decayed in place.  `r` is the number of columns held
+ * on entry (0 <= r < cap); on return r + 1 columns are held.
+ * Returns SEED_E_FULL if r == cap.  `beta` must be NULL for Mamba-2 and
+ * non-NULL otherwise.  All factor and output arithmetic is fp32; bf16
+ * inputs are widened exactly.
+ */
+seed_status seed_decode_step(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
+                             float *a, float *U, float *V, const float *vbar,
+                             const void *q, const void *k, const void *v, int in_dtype,
+                             const float *g, const float *beta, float *o, void *stream);
+
+/*
+ * seed_compress -- compress the factors of every unit from r to R columns.
+ *
+ * Replaces the content U V^T by its best rank-R approximation (truncated
+ * SVD) and leaves the sink coefficient a untouched: every W steps the
+ * factors are compressed back to rank R (SEED figures and tables, Fig. 1 (b)
+ * caption); the sink is preserved exactly (sungsoo.github.io summary,
+ * method list, "Decode").  On return columns 0..R-1 hold U' with orthonormal
+ * columns and V' = M^T U' (M = the old U V^T), so U' V'^T is the rank-R
+ * truncation; the caller sets r = R.  If r <= R nothing is launched and
+ * SEED_OK is returned.  Computed in fp32 in one workgroup per unit.
+ */
+seed_status seed_compress(int batch, int heads, int d_k, int d_v, int cap, int r, int R,
+                          float *U, float *V, void *stream);
+
+/*
+ * seed_state_from_dense -- convert dense states to the shallow form.
+ *
+ * At the end of the prefill the states are compressed to the sink plus
+ * rank-R factors (SEED figures and tables, Fig. 1 (a) caption, Table 1).
+ * The sink is the state's projection on vbar (Fig. 3 (b), (c)):
+ *   a = S vbar / |vbar|^2,   C = S - a vbar^T,
+ * and U, V (columns 0..R-1) are the rank-R truncation of C, U orthonormal.
+ * S is read only.  The caller sets r = R.  Requires 1 <= R <= min(d_k, d_v)
+ * and R <= cap.
+ */
+seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
+                                  const float *S, const float *vbar,
+                                  float *a, float *U, float *V, void *stream);
+
+/*
+ * dense_decode_step -- the dense-state baseline: one step of the head's own
+ * recurrence on S (updated in place), then o = S'^T q.  The three rules are
+ * the ones listed under seed_rule (the updates named in the picx.dev
+ * summary, "Exact Update (Lemma 2)").  Same input conventions as
+ * seed_decode_step.
+ */
+seed_status dense_decode_step(int rule, int batch, int heads, int d_k, int d_v, float *S,
+                              const void *q, const void *k, const void *v, int in_dtype,
+                              const float *g, const float *beta, float *o, void *stream);
+
+/* Static text for a status code. */
+const char *seed_status_string(int status);
+
+/* Thread-local description of the last failure of a call on this thread
+ * ("" after a successful call). */
+const char *seed_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int seed_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEED_H */

@@ -1,0 +1,211 @@
+"""Python binding of libseed.so: argument marshalling only.
+
+Every function here takes torch tensors that already live in device memory,
+checks that their shapes agree, and passes raw pointers and sizes to the C
+ABI declared in include/seed.h, on torch's current HIP stream.  All
+arithmetic happens in the HIP kernels.  If the library has not been built
+the first call raises; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libseed.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "seed.h")
+
+RULES = {"gdn": 0, "kda": 1, "mamba2": 2}
+STATUS = {0: "SEED_OK", 1: "SEED_E_ARG", 2: "SEED_E_SHAPE", 3: "SEED_E_UNSUPPORTED",
+          4: "SEED_E_FULL", 5: "SEED_E_DEVICE"}
+
+_lib = None
+
+
+class SeedError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}: {detail}")
+        self.fn = fn
+        self.status = status
+        self.detail = detail
+
+
+def header_functions() -> list:
+    """Names of the functions include/seed.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libseed.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sink_rank_recurrent_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    i, p, f = ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+    L.seed_decode_step.argtypes = [i, i, i, i, i, i, i, p, p, p, p, p, p, p, i, p, p, p, p]
+    L.seed_compress.argtypes = [i, i, i, i, i, i, i, p, p, p]
+    L.seed_state_from_dense.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p]
+    L.dense_decode_step.argtypes = [i, i, i, i, i, p, p, p, p, i, p, p, p, p]
+    for fn in ("seed_decode_step", "seed_compress", "seed_state_from_dense", "dense_decode_step",
+               "seed_abi_version"):
+        getattr(L, fn).restype = ctypes.c_int
+    L.seed_status_string.argtypes = [i]
+    L.seed_status_string.restype = ctypes.c_char_p
+    L.seed_last_error.argtypes = []
+    L.seed_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SeedError(fn, status, lib().seed_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape: tuple, dtypes) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be in device memory (got {t.device})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_F32 = (torch.float32,)
+_IN = (torch.float32, torch.bfloat16)
+
+
+def _in_dtype(q, k, v) -> int:
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    return 1 if q.dtype == torch.bfloat16 else 0
+
+
+def seed_decode_step(rule: str, a, U, V, vbar, q, k, v, g, beta, o, r: int, stream=None) -> None:
+    """One decode step on the shallow states (see include/seed.h)."""
+    B, H, cap, d_k = U.shape
+    d_v = V.shape[-1]
+    _need(a, "a", (B, H, d_k), _F32)
+    _need(U, "U", (B, H, cap, d_k), _F32)
+    _need(V, "V", (B, H, cap, d_v), _F32)
+    _need(vbar, "vbar", (H, d_v), _F32)
+    _need(q, "q", (B, H, d_k), _IN)
+    _need(k, "k", (B, H, d_k), _IN)
+    _need(v, "v", (B, H, d_v), _IN)
+    _need(g, "g", (B, H, d_k) if rule == "kda" else (B, H), _F32)
+    if beta is not None:
+        _need(beta, "beta", (B, H), _F32)
+    _need(o, "o", (B, H, d_v), _F32)
+    st = lib().seed_decode_step(RULES[rule], B, H, d_k, d_v, cap, int(r), _ptr(a), _ptr(U),
+                                _ptr(V), _ptr(vbar), _ptr(q), _ptr(k), _ptr(v), _in_dtype(q, k, v),
+                                _ptr(g), _ptr(beta), _ptr(o), _stream(stream))
+    _check("seed_decode_step", st)
+
+
+def seed_compress(U, V, r: int, R: int, stream=None) -> None:
+    """Compress every unit's factors from r to R columns (see include/seed.h)."""
+    B, H, cap, d_k = U.shape
+    d_v = V.shape[-1]
+    _need(U, "U", (B, H, cap, d_k), _F32)
+    _need(V, "V", (B, H, cap, d_v), _F32)
+    st = lib().seed_compress(B, H, d_k, d_v, cap, int(r), int(R), _ptr(U), _ptr(V),
+                             _stream(stream))
+    _check("seed_compress", st)
+
+
+def seed_state_from_dense(S, vbar, a, U, V, R: int, stream=None) -> None:
+    """Convert dense states to sink + rank-R factors (see include/seed.h)."""
+    B, H, cap, d_k = U.shape
+    d_v = V.shape[-1]
+    _need(S, "S", (B, H, d_k, d_v), _F32)
+    _need(vbar, "vbar", (H, d_v), _F32)
+    _need(a, "a", (B, H, d_k), _F32)
+    _need(U, "U", (B, H, cap, d_k), _F32)
+    _need(V, "V", (B, H, cap, d_v), _F32)
+    st = lib().seed_state_from_dense(B, H, d_k, d_v, cap, int(R), _ptr(S), _ptr(vbar), _ptr(a),
+                                     _ptr(U), _ptr(V), _stream(stream))
+    _check("seed_state_from_dense", st)
+
+
+def dense_decode_step(rule: str, S, q, k, v, g, beta, o, stream=None) -> None:
+    """Dense-state baseline step (see include/seed.h)."""
+    B, H, d_k, d_v = S.shape
+    _need(S, "S", (B, H, d_k, d_v), _F32)
+    _need(q, "q", (B, H, d_k), _IN)
+    _need(k, "k", (B, H, d_k), _IN)
+    _need(v, "v", (B, H, d_v), _IN)
+    _need(g, "g", (B, H, d_k) if rule == "kda" else (B, H), _F32)
+    if beta is not None:
+        _need(beta, "beta", (B, H), _F32)
+    _need(o, "o", (B, H, d_v), _F32)
+    st = lib().dense_decode_step(RULES[rule], B, H, d_k, d_v, _ptr(S), _ptr(q), _ptr(k), _ptr(v),
+                                 _in_dtype(q, k, v), _ptr(g), _ptr(beta), _ptr(o), _stream(stream))
+    _check("dense_decode_step", st)
+
+
+class ShallowState:
+    """Device tensors of one layer's shallow states plus the column count r.
+
+    a [B, H, d_k], U [B, H, R+W, d_k], V [B, H, R+W, d_v] (fp32, zeroed) and the
+    shared vbar [H, d_v].  `step` advances r, `compress` resets it to R when
+    all R + W columns are in use.
+    """
+
+    def __init__(self, rule: str, batch: int, heads: int, d_k: int, d_v: int, R: int, W: int,
+                 vbar: torch.Tensor, device="cuda"):
+        self.rule, self.R, self.W = rule, R, W
+        self.batch, self.heads, self.d_k, self.d_v = batch, heads, d_k, d_v
+        f32 = torch.float32
+        self.a = torch.zeros(batch, heads, d_k, device=device, dtype=f32)
+        self.U = torch.zeros(batch, heads, R + W, d_k, device=device, dtype=f32)
+        self.V = torch.zeros(batch, heads, R + W, d_v, device=device, dtype=f32)
+        self.vbar = vbar.to(device=device, dtype=f32).contiguous()
+        self.r = 0
+
+    @property
+    def cap(self) -> int:
+        return self.R + self.W
+
+    def from_dense(self, S: torch.Tensor, stream=None) -> None:
+        seed_state_from_dense(S, self.vbar, self.a, self.U, self.V, self.R, stream)
+        self.r = self.R
+
+    def step(self, q, k, v, g, beta, o, stream=None) -> None:
+        seed_decode_step(self.rule, self.a, self.U, self.V, self.vbar, q, k, v, g, beta, o,
+                         self.r, stream)
+        self.r += 1
+
+    def compress(self, stream=None) -> None:
+        seed_compress(self.U, self.V, self.r, self.R, stream)
+        self.r = min(self.r, self.R)
+
+    def step_and_maybe_compress(self, q, k, v, g, beta, o, stream=None) -> bool:
+        """One decode step; compress afterwards when all R + W columns are held."""
+        self.step(q, k, v, g, beta, o, stream)
+        if self.r >= self.cap:
+            self.compress(stream)
+            return True
+        return False

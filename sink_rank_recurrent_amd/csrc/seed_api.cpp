@@ -1,0 +1,186 @@
+// C ABI of the shallow-state engine (declared in include/seed.h).
+//
+// Every entry point validates its arguments on the host first and returns a
+// status without touching the HIP runtime when they are wrong; only valid
+// calls reach the launchers.  The library keeps no state besides a
+// thread-local error message.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/seed.h"
+#include "seed_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+seed_status fail(seed_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+seed_status ok() {
+  g_err[0] = '\0';
+  return SEED_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define SEED_PTR(p)                                                                     \
+  do {                                                                                  \
+    if ((p) == nullptr) return fail(SEED_E_ARG, "%s: %s is NULL", fn, #p);              \
+    if (!aligned16(p)) return fail(SEED_E_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+bool supported_dims(int d_k, int d_v) {
+  return (d_k == 128 && d_v == 128) || (d_k == 128 && d_v == 64) || (d_k == 64 && d_v == 64);
+}
+
+seed_status check_units(const char* fn, int batch, int heads, int d_k, int d_v) {
+  if (batch <= 0 || heads <= 0 || d_k <= 0 || d_v <= 0)
+    return fail(SEED_E_SHAPE, "%s: batch, heads, d_k, d_v must be positive (got %d, %d, %d, %d)",
+                fn, batch, heads, d_k, d_v);
+  if ((long long)batch * heads > 0x7fffffffLL)
+    return fail(SEED_E_SHAPE, "%s: batch * heads = %lld exceeds the grid limit", fn,
+                (long long)batch * heads);
+  if (!supported_dims(d_k, d_v))
+    return fail(SEED_E_UNSUPPORTED,
+                "%s: head shape d_k=%d d_v=%d not supported (use 128x128, 128x64 or 64x64)", fn,
+                d_k, d_v);
+  return SEED_OK;
+}
+
+seed_status check_step_inputs(const char* fn, int rule, const void* q, const void* k,
+                              const void* v, int in_dtype, const float* g, const float* beta,
+                              float* o) {
+  if (rule != SEED_RULE_GDN && rule != SEED_RULE_KDA && rule != SEED_RULE_MAMBA2)
+    return fail(SEED_E_ARG, "%s: unknown rule %d", fn, rule);
+  if (in_dtype != SEED_F32 && in_dtype != SEED_BF16)
+    return fail(SEED_E_ARG, "%s: unknown input dtype %d", fn, in_dtype);
+  SEED_PTR(q);
+  SEED_PTR(k);
+  SEED_PTR(v);
+  SEED_PTR(g);
+  SEED_PTR(o);
+  if (rule == SEED_RULE_MAMBA2) {
+    if (beta != nullptr) return fail(SEED_E_ARG, "%s: beta must be NULL for Mamba-2", fn);
+  } else {
+    SEED_PTR(beta);
+  }
+  return SEED_OK;
+}
+
+seed_status device_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess)
+    return fail(SEED_E_DEVICE, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+seed_status seed_decode_step(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
+                             float* a, float* U, float* V, const float* vbar, const void* q,
+                             const void* k, const void* v, int in_dtype, const float* g,
+                             const float* beta, float* o, void* stream) {
+  const char* fn = "seed_decode_step";
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (cap <= 0 || r < 0 || r > cap)
+    return fail(SEED_E_SHAPE, "%s: need 0 <= r <= cap, cap > 0 (got r=%d cap=%d)", fn, r, cap);
+  if (cap > seed::kMaxCap)
+    return fail(SEED_E_UNSUPPORTED, "%s: capacity %d above %d", fn, cap, seed::kMaxCap);
+  if (r == cap)
+    return fail(SEED_E_FULL, "%s: all %d columns are in use; compress first", fn, cap);
+  st = check_step_inputs(fn, rule, q, k, v, in_dtype, g, beta, o);
+  if (st != SEED_OK) return st;
+  SEED_PTR(a);
+  SEED_PTR(U);
+  SEED_PTR(V);
+  SEED_PTR(vbar);
+  return device_status(fn, seed::launch_step(rule, in_dtype == SEED_BF16, batch, heads, d_k, d_v,
+                                             cap, r, a, U, V, vbar, q, k, v, g, beta, o,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+seed_status seed_compress(int batch, int heads, int d_k, int d_v, int cap, int r, int R,
+                          float* U, float* V, void* stream) {
+  const char* fn = "seed_compress";
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (cap <= 0 || R <= 0 || r < 0 || r > cap || R > cap)
+    return fail(SEED_E_SHAPE, "%s: need 0 < R <= cap and 0 <= r <= cap (got R=%d r=%d cap=%d)",
+                fn, R, r, cap);
+  if (cap > seed::kMaxCap)
+    return fail(SEED_E_UNSUPPORTED, "%s: capacity %d above %d", fn, cap, seed::kMaxCap);
+  if (R > 32) return fail(SEED_E_UNSUPPORTED, "%s: rank %d above 32", fn, R);
+  SEED_PTR(U);
+  SEED_PTR(V);
+  if (r <= R) return ok();
+  if (seed::compress_lds_bytes(r, R) > seed::kMaxLds)
+    return fail(SEED_E_UNSUPPORTED, "%s: %d columns at rank %d need more LDS than a CU has", fn,
+                r, R);
+  return device_status(fn, seed::launch_compress(batch, heads, d_k, d_v, cap, r, R, U, V,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
+                                  const float* S, const float* vbar, float* a, float* U,
+                                  float* V, void* stream) {
+  const char* fn = "seed_state_from_dense";
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (cap <= 0 || R <= 0 || R > cap || R > d_k || R > d_v)
+    return fail(SEED_E_SHAPE, "%s: need 0 < R <= min(cap, d_k, d_v) (got R=%d cap=%d)", fn, R,
+                cap);
+  if (cap > seed::kMaxCap)
+    return fail(SEED_E_UNSUPPORTED, "%s: capacity %d above %d", fn, cap, seed::kMaxCap);
+  if (R > 32) return fail(SEED_E_UNSUPPORTED, "%s: rank %d above 32", fn, R);
+  SEED_PTR(S);
+  SEED_PTR(vbar);
+  SEED_PTR(a);
+  SEED_PTR(U);
+  SEED_PTR(V);
+  if (seed::from_dense_lds_bytes(d_k, R) > seed::kMaxLds)
+    return fail(SEED_E_UNSUPPORTED, "%s: d_k=%d at rank %d needs more LDS than a CU has", fn, d_k,
+                R);
+  return device_status(fn, seed::launch_from_dense(batch, heads, d_k, d_v, cap, R, S, vbar, a, U,
+                                                   V, static_cast<hipStream_t>(stream)));
+}
+
+seed_status dense_decode_step(int rule, int batch, int heads, int d_k, int d_v, float* S,
+                              const void* q, const void* k, const void* v, int in_dtype,
+                              const float* g, const float* beta, float* o, void* stream) {
+  const char* fn = "dense_decode_step";
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  st = check_step_inputs(fn, rule, q, k, v, in_dtype, g, beta, o);
+  if (st != SEED_OK) return st;
+  SEED_PTR(S);
+  return device_status(fn, seed::launch_dense(rule, in_dtype == SEED_BF16, batch, heads, d_k, d_v,
+                                              S, q, k, v, g, beta, o,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+const char* seed_status_string(int status) {
+  switch (status) {
+    case SEED_OK: return "ok";
+    case SEED_E_ARG: return "invalid argument";
+    case SEED_E_SHAPE: return "inconsistent shape";
+    case SEED_E_UNSUPPORTED: return "unsupported shape";
+    case SEED_E_FULL: return "factor capacity full";
+    case SEED_E_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* seed_last_error(void) { return g_err; }
+
+int seed_abi_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Host-side launchers of the gfx950 kernels.  They assume validated
+// arguments (seed_api.cpp checks everything first) and only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace seed {
+
+// Largest factor capacity (R + W) the kernels are compiled for.
+constexpr int kMaxCap = 96;
+// LDS available to one workgroup on gfx950.
+constexpr size_t kMaxLds = 160 * 1024;
+
+hipError_t launch_step(int rule, bool in_bf16, int batch, int heads, int d_k, int d_v, int cap,
+                       int r, float* a, float* U, float* V, const float* vbar, const void* q,
+                       const void* k, const void* v, const float* g, const float* beta, float* o,
+                       hipStream_t stream);
+
+hipError_t launch_dense(int rule, bool in_bf16, int batch, int heads, int d_k, int d_v, float* S,
+                        const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, float* o, hipStream_t stream);
+
+// Dynamic LDS bytes the compression kernel needs for n columns kept to R.
+size_t compress_lds_bytes(int n, int R);
+// Dynamic LDS bytes the dense-to-shallow kernel needs.
+size_t from_dense_lds_bytes(int d_k, int R);
+
+hipError_t launch_compress(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
+                           float* U, float* V, hipStream_t stream);
+
+hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
+                             const float* S, const float* vbar, float* a, float* U, float* V,
+                             hipStream_t stream);
+
+}  // namespace seed

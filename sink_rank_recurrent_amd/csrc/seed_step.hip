@@ -1,0 +1,282 @@
+// Fused read-out + exact update of the shallow state (one decode step).
+//
+// Lemma 2 (SEED summary on picx.dev, "Exact Update (Lemma 2)"), with the
+// Kimi Delta Attention form taking Diag(g) for the scalar decay and the
+// Mamba-2 form being Lemma 1 with Phi = g I:
+//   omega = v.vbar/|vbar|^2,  eps = v - omega vbar
+//   a+ = G a + beta (omega - k.(G a)) k          (Mamba-2: g a + omega k)
+//   U+ = [G U, k]
+//   V+ = [V, beta (eps - V (G U)^T k)]            (Mamba-2: [V, eps])
+//   o  = vbar (a+.q) + V+ (U+^T q)               (read-out after the update)
+//
+// Mapping on gfx950: one 256-thread workgroup (4 wave64s) per (request,
+// head).  The workgroup is 8 column groups of 32 lanes (half-waves).  Group
+// c owns factor columns j = c, c+8, c+16, ...; inside a column each lane
+// holds d_k/32 consecutive entries of the U column and d_v/32 of the V
+// column, so every load and store is a coalesced 8- or 16-byte access per
+// lane.  All U and V columns are loaded into registers at the start (the
+// state is read exactly once), so the only dependent step is the reduction
+// of c_k = (G U)^T k and c_q = (G U)^T q inside each half-wave, which then
+// feeds that half-wave's own V columns without any exchange.  The 8 partial
+// V-sums are combined through LDS.  Every half-wave recomputes the scalars
+// (omega, k.Ga, k.q, a+.q) from its own copy of the small vectors, which
+// avoids a barrier; only group 0 writes a, the new V column and o.
+#include "seed_device.h"
+#include "seed_launch.h"
+
+namespace seed {
+
+template <int RULE, int DK, int DV, typename IN_T, int SLOTS>
+__global__ __launch_bounds__(256) void seed_step_kernel(
+    float* __restrict__ a, float* __restrict__ U, float* __restrict__ V,
+    const float* __restrict__ vbar, const IN_T* __restrict__ q, const IN_T* __restrict__ k,
+    const IN_T* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    float* __restrict__ o, int heads, int cap, int r) {
+  constexpr int EK = DK / 32;  // key-space entries per lane
+  constexpr int EV = DV / 32;  // value-space entries per lane
+  const int unit = blockIdx.x;
+  const int h = unit % heads;
+  const int tid = threadIdx.x;
+  const int grp = tid >> 5;
+  const int lane = tid & 31;
+  const size_t ub = (size_t)unit;
+  float* Uh = U + ub * cap * DK;
+  float* Vh = V + ub * cap * DV;
+
+  // 1. the factors: every column this half-wave owns, loaded once
+  float u[SLOTS][EK];
+  float w[SLOTS][EV];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int j = grp + 8 * s;
+    if (j < r) {
+      load_vec<EK>(Uh + (size_t)j * DK + lane * EK, u[s]);
+      load_vec<EV>(Vh + (size_t)j * DV + lane * EV, w[s]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EK; ++e) u[s][e] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) w[s][e] = 0.f;
+    }
+  }
+
+  // 2. the step's inputs and the sink coefficient
+  float kk[EK], qq[EK], aa[EK], gk[EK];
+  load_vec<EK>(k + ub * DK + lane * EK, kk);
+  load_vec<EK>(q + ub * DK + lane * EK, qq);
+  load_vec<EK>(a + ub * DK + lane * EK, aa);
+  float gs = 1.f;
+  if constexpr (RULE == kKDA) {
+    load_vec<EK>(g + ub * DK + lane * EK, gk);
+  } else {
+    gs = g[ub];
+#pragma unroll
+    for (int e = 0; e < EK; ++e) gk[e] = gs;
+  }
+  float bt = 1.f;
+  if constexpr (RULE != kMAMBA2) bt = beta[ub];
+  float vv[EV], vb[EV];
+  load_vec<EV>(v + ub * DV + lane * EV, vv);
+  load_vec<EV>(vbar + (size_t)h * DV + lane * EV, vb);
+
+  // 3. value split: omega = v.vbar / |vbar|^2
+  float p_vvb = 0.f, p_nvb = 0.f;
+#pragma unroll
+  for (int e = 0; e < EV; ++e) {
+    p_vvb += vv[e] * vb[e];
+    p_nvb += vb[e] * vb[e];
+  }
+  const float omega = sum32(p_vvb) / sum32(p_nvb);
+
+  // 4. sink coefficient
+  float ga[EK];
+  float p_kga = 0.f, p_kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < EK; ++e) {
+    ga[e] = gk[e] * aa[e];
+    p_kga += kk[e] * ga[e];
+    p_kq += kk[e] * qq[e];
+  }
+  const float kq = sum32(p_kq);
+  float an[EK];
+  if constexpr (RULE == kMAMBA2) {
+#pragma unroll
+    for (int e = 0; e < EK; ++e) an[e] = ga[e] + omega * kk[e];
+  } else {
+    const float coef = bt * (omega - sum32(p_kga));
+#pragma unroll
+    for (int e = 0; e < EK; ++e) an[e] = ga[e] + coef * kk[e];
+  }
+  float p_aq = 0.f;
+#pragma unroll
+  for (int e = 0; e < EK; ++e) p_aq += an[e] * qq[e];
+  const float aq = sum32(p_aq);
+
+  // 5. U pass: decay in place, c_k = (G U)^T k, c_q = (G U)^T q
+  float ck[SLOTS], cq[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    float pk = 0.f, pq = 0.f;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      const float x = gk[e] * u[s][e];
+      u[s][e] = x;
+      pk += x * kk[e];
+      pq += x * qq[e];
+    }
+    ck[s] = pk;
+    cq[s] = pq;
+  }
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    if constexpr (RULE != kMAMBA2) ck[s] = sum32(ck[s]);
+    cq[s] = sum32(cq[s]);
+  }
+  // decayed columns back in place, and the appended column U_r = k
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int j = grp + 8 * s;
+    if (j < r) store_vec<EK>(Uh + (size_t)j * DK + lane * EK, u[s]);
+  }
+  if (grp == (r & 7)) store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kk);
+
+  // 6. V pass: partial V c_k and V c_q over this half-wave's columns
+  float sk[EV], sq[EV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) {
+    sk[e] = 0.f;
+    sq[e] = 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      if constexpr (RULE != kMAMBA2) sk[e] += w[s][e] * ck[s];
+      sq[e] += w[s][e] * cq[s];
+    }
+  }
+
+  // 7. combine the 8 column groups through LDS
+  __shared__ float red[2][8][DV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) {
+    red[0][grp][lane * EV + e] = sk[e];
+    red[1][grp][lane * EV + e] = sq[e];
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float tk[EV], tq[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      tk[e] = 0.f;
+      tq[e] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int e = 0; e < EV; ++e) {
+        tk[e] += red[0][c][lane * EV + e];
+        tq[e] += red[1][c][lane * EV + e];
+      }
+    }
+    float vn[EV], oo[EV];
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      const float eps = vv[e] - omega * vb[e];
+      if constexpr (RULE == kMAMBA2) {
+        vn[e] = eps;
+      } else {
+        vn[e] = bt * (eps - tk[e]);
+      }
+      oo[e] = vb[e] * aq + tq[e] + vn[e] * kq;
+    }
+    store_vec<EV>(Vh + (size_t)r * DV + lane * EV, vn);
+    store_vec<EV>(o + ub * DV + lane * EV, oo);
+    store_vec<EK>(a + ub * DK + lane * EK, an);
+  }
+}
+
+namespace {
+
+template <int RULE, int DK, int DV, typename IN_T, int SLOTS>
+hipError_t step_go(int units, int heads, int cap, int r, float* a, float* U, float* V,
+                   const float* vbar, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, float* o, hipStream_t s) {
+  hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS>), dim3(units), dim3(256), 0, s,
+                     a, U, V, vbar, static_cast<const IN_T*>(q), static_cast<const IN_T*>(k),
+                     static_cast<const IN_T*>(v), g, beta, o, heads, cap, r);
+  return hipGetLastError();
+}
+
+template <int RULE, int DK, int DV, typename IN_T>
+hipError_t step_slots(int units, int heads, int cap, int r, float* a, float* U, float* V,
+                      const float* vbar, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, float* o, hipStream_t s) {
+  const int need = (r + 7) / 8;
+#define SEED_STEP_SLOTS(N)                                                                    \
+  if (need <= N)                                                                              \
+    return step_go<RULE, DK, DV, IN_T, N>(units, heads, cap, r, a, U, V, vbar, q, k, v, g, beta, \
+                                          o, s);
+  SEED_STEP_SLOTS(1)
+  SEED_STEP_SLOTS(2)
+  SEED_STEP_SLOTS(3)
+  SEED_STEP_SLOTS(4)
+  SEED_STEP_SLOTS(5)
+  SEED_STEP_SLOTS(6)
+  SEED_STEP_SLOTS(8)
+  SEED_STEP_SLOTS(10)
+  SEED_STEP_SLOTS(12)
+#undef SEED_STEP_SLOTS
+  return hipErrorInvalidValue;
+}
+
+template <int RULE, typename IN_T>
+hipError_t step_dims(int units, int heads, int d_k, int d_v, int cap, int r, float* a, float* U,
+                     float* V, const float* vbar, const void* q, const void* k, const void* v,
+                     const float* g, const float* beta, float* o, hipStream_t s) {
+  if (d_k == 128 && d_v == 128)
+    return step_slots<RULE, 128, 128, IN_T>(units, heads, cap, r, a, U, V, vbar, q, k, v, g, beta,
+                                            o, s);
+  if (d_k == 128 && d_v == 64)
+    return step_slots<RULE, 128, 64, IN_T>(units, heads, cap, r, a, U, V, vbar, q, k, v, g, beta,
+                                           o, s);
+  if (d_k == 64 && d_v == 64)
+    return step_slots<RULE, 64, 64, IN_T>(units, heads, cap, r, a, U, V, vbar, q, k, v, g, beta,
+                                          o, s);
+  return hipErrorInvalidValue;
+}
+
+template <int RULE>
+hipError_t step_dtype(bool bf16, int units, int heads, int d_k, int d_v, int cap, int r, float* a,
+                      float* U, float* V, const float* vbar, const void* q, const void* k,
+                      const void* v, const float* g, const float* beta, float* o, hipStream_t s) {
+  if (bf16)
+    return step_dims<RULE, bf16_t>(units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v, g, beta,
+                                   o, s);
+  return step_dims<RULE, float>(units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v, g, beta, o,
+                                s);
+}
+
+}  // namespace
+
+hipError_t launch_step(int rule, bool in_bf16, int batch, int heads, int d_k, int d_v, int cap,
+                       int r, float* a, float* U, float* V, const float* vbar, const void* q,
+                       const void* k, const void* v, const float* g, const float* beta, float* o,
+                       hipStream_t stream) {
+  const int units = batch * heads;
+  switch (rule) {
+    case kGDN:
+      return step_dtype<kGDN>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v, g,
+                              beta, o, stream);
+    case kKDA:
+      return step_dtype<kKDA>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v, g,
+                              beta, o, stream);
+    case kMAMBA2:
+      return step_dtype<kMAMBA2>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v,
+                                 g, beta, o, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace seed

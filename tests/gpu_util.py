@@ -1,0 +1,91 @@
+"""Helpers for the GPU parity tests: move device state and inputs into the
+oracle's layout (float64, math orientation) and measure errors the way the
+tolerances are stated (per (request, head) unit)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sink_rank_recurrent_amd import binding
+from sink_rank_recurrent_amd import workloads as wl
+
+requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+# tolerances (relative, per unit)
+TOL_STATE_STEP = 1e-5      # reconstructed state between compressions
+TOL_STATE_COMPRESS = 1e-4  # after a compression
+TOL_READOUT = 1e-4
+TIE_GAP = 1e-4             # (s_R - s_{R+1}) / s_1 below this: the truncation is not unique
+
+
+def f64(x):
+    return x.detach().to("cpu", torch.float64).numpy()
+
+
+def units_of(t: torch.Tensor, lead: int = 2):
+    """Flatten the leading (batch, heads) dims into one unit axis."""
+    return t.reshape((-1,) + tuple(t.shape[lead:]))
+
+
+def state_np(st: binding.ShallowState, units=None, r=None):
+    """(a [n, d_k], U [n, d_k, r], V [n, d_v, r], vbar [n, d_v]) in float64."""
+    r = st.r if r is None else r
+    a = f64(units_of(st.a))
+    U = f64(units_of(st.U))[:, :r].transpose(0, 2, 1)
+    V = f64(units_of(st.V))[:, :r].transpose(0, 2, 1)
+    vb = np.broadcast_to(f64(st.vbar)[None], (st.batch, st.heads, st.d_v)).reshape(-1, st.d_v)
+    if units is not None:
+        a, U, V, vb = a[units], U[units], V[units], vb[units]
+    return a, U, V, vb
+
+
+def inputs_np(inp: dict, units=None) -> dict:
+    out = {}
+    for key in ("q", "k", "v", "g", "beta"):
+        x = inp.get(key)
+        if x is None:
+            out[key] = None
+            continue
+        x = f64(units_of(x))
+        out[key] = x if units is None else x[units]
+    return out
+
+
+def rel_err(x, ref, axes):
+    num = np.sqrt(np.sum((np.asarray(x) - ref) ** 2, axis=axes))
+    den = np.sqrt(np.sum(np.asarray(ref) ** 2, axis=axes))
+    return num / np.maximum(den, 1e-300)
+
+
+def state_rel_err(a, U, V, a_ref, U_ref, V_ref, vb):
+    S = oracle.reconstruct(a, U, V, vb)
+    S_ref = oracle.reconstruct(a_ref, U_ref, V_ref, vb)
+    return rel_err(S, S_ref, (-2, -1))
+
+
+def content_gap(U, V, R):
+    """Relative gap (s_R - s_{R+1}) / s_1 of the content U V^T, per unit."""
+    s = np.linalg.svd(U @ np.swapaxes(V, -1, -2), compute_uv=False)
+    if s.shape[-1] <= R:
+        return np.full(s.shape[:-1], np.inf)
+    return (s[..., R - 1] - s[..., R]) / np.maximum(s[..., 0], 1e-300)
+
+
+def make_state(rule, batch, heads, d_k, d_v, R, W, vbar, device="cuda"):
+    return binding.ShallowState(rule, batch, heads, d_k, d_v, R, W, vbar, device=device)
+
+
+def gpu_inputs(rule, batch, heads, d_k, d_v, vbar, seed, t, in_dtype, layer=0):
+    return wl.make_step(rule, batch, heads, d_k, d_v, vbar, seed, t, layer, in_dtype, "cuda")
+
+
+def dense_prefill(rule, batch, heads, d_k, d_v, vbar, seed, steps, in_dtype, layer=0):
+    """Dense prefill on the GPU (dense_decode_step), returns S [B, H, d_k, d_v]."""
+    S = torch.zeros(batch, heads, d_k, d_v, device="cuda", dtype=torch.float32)
+    o = torch.empty(batch, heads, d_v, device="cuda", dtype=torch.float32)
+    for t in range(-steps, 0):
+        inp = gpu_inputs(rule, batch, heads, d_k, d_v, vbar, seed, t, in_dtype, layer)
+        binding.dense_decode_step(rule, S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o)
+    return S

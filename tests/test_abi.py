@@ -1,0 +1,89 @@
+"""The C ABI without a GPU: libseed.so loads, exports every function that
+include/seed.h declares, and rejects bad arguments on the host before any
+HIP call (so these run on a machine without a GPU)."""
+import ctypes
+
+import pytest
+
+from sink_rank_recurrent_amd import binding
+
+L = binding.lib()
+ALIGNED = ctypes.c_void_p(0x10000)     # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def test_exports_every_declared_function():
+    names = binding.header_functions()
+    assert set(names) == {"seed_decode_step", "seed_compress", "seed_state_from_dense",
+                          "dense_decode_step", "seed_status_string", "seed_last_error",
+                          "seed_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.seed_abi_version() == 100
+
+
+def test_status_strings():
+    assert L.seed_status_string(0) == b"ok"
+    assert L.seed_status_string(4) == b"factor capacity full"
+    assert L.seed_status_string(99) == b"unknown status"
+
+
+def _step(rule=0, batch=2, heads=3, d_k=128, d_v=128, cap=48, r=16, ptr=ALIGNED, beta=ALIGNED,
+          dtype=1):
+    p = ptr
+    return L.seed_decode_step(rule, batch, heads, d_k, d_v, cap, r, p, p, p, p, p, p, p, dtype, p,
+                              beta, p, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(r=48), 4, "compress first"),
+    (dict(r=49), 2, "r <= cap"),
+    (dict(r=-1), 2, "r <= cap"),
+    (dict(batch=0), 2, "positive"),
+    (dict(d_v=100), 3, "not supported"),
+    (dict(d_k=64, d_v=128), 3, "not supported"),
+    (dict(cap=128, r=10), 3, "capacity"),
+    (dict(rule=7), 1, "unknown rule"),
+    (dict(dtype=5), 1, "dtype"),
+    (dict(ptr=None), 1, "NULL"),
+    (dict(ptr=MISALIGNED), 1, "aligned"),
+    (dict(rule=2), 1, "beta must be NULL"),
+    (dict(rule=0, beta=None), 1, "beta is NULL"),
+])
+def test_step_rejects(kwargs, status, needle):
+    assert _step(**kwargs) == status
+    assert needle in L.seed_last_error().decode()
+
+
+def test_compress_validation():
+    p = ALIGNED
+    assert L.seed_compress(1, 1, 128, 128, 48, 48, 0, p, p, None) == 2          # R = 0
+    assert L.seed_compress(1, 1, 128, 128, 48, 48, 33, p, p, None) == 3         # R > 32
+    assert L.seed_compress(1, 1, 128, 128, 48, 50, 16, p, p, None) == 2         # r > cap
+    assert L.seed_compress(1, 1, 128, 128, 48, 48, 16, None, p, None) == 1
+    # r <= R is a no-op that touches nothing (pointers are never dereferenced)
+    assert L.seed_compress(1, 1, 128, 128, 48, 16, 16, p, p, None) == 0
+    assert L.seed_last_error() == b""
+
+
+def test_from_dense_validation():
+    p = ALIGNED
+    assert L.seed_state_from_dense(1, 1, 128, 64, 48, 65, p, p, p, p, p, None) == 2  # R > d_v
+    assert L.seed_state_from_dense(1, 1, 128, 128, 16, 17, p, p, p, p, p, None) == 2  # R > cap
+    assert L.seed_state_from_dense(1, 1, 128, 128, 48, 33, p, p, p, p, p, None) == 3
+    assert L.seed_state_from_dense(1, 1, 128, 128, 48, 16, p, MISALIGNED, p, p, p, None) == 1
+
+
+def test_dense_step_validation():
+    p = ALIGNED
+    assert L.dense_decode_step(0, 1, 1, 128, 96, p, p, p, p, 0, p, p, p, None) == 3
+    assert L.dense_decode_step(2, 1, 1, 128, 64, p, p, p, p, 0, p, p, p, None) == 1  # beta non-NULL
+    assert L.dense_decode_step(1, 1, 1, 128, 128, None, p, p, p, 0, p, p, p, None) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    U = torch.zeros(1, 1, 48, 128)
+    V = torch.zeros(1, 1, 48, 128)
+    with pytest.raises(ValueError, match="device memory"):
+        binding.seed_compress(U, V, 48, 16)

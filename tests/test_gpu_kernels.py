@@ -1,0 +1,197 @@
+"""Per-call parity of every entry point with the CPU oracle, on identical
+inputs (bf16 inputs are compared through their exact fp64 values).
+
+Sizes: 15 (request, head) units (3 x 5, a ragged count of workgroups), every
+head shape the library supports, and column counts r that leave ragged
+tails in the 8 column groups of the step kernel (0, 1, 7, 9, 31, 47) or sit
+at the capacity limit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (TIE_GAP, TOL_READOUT, TOL_STATE_COMPRESS, TOL_STATE_STEP, content_gap, f64,
+                      inputs_np, make_state, rel_err, requires_gpu, state_np, state_rel_err,
+                      units_of)
+from sink_rank_recurrent_amd import binding
+from sink_rank_recurrent_amd import workloads as wl
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+RULES = ["gdn", "kda", "mamba2"]
+DIMS = [(128, 128), (128, 64), (64, 64)]
+DTYPES = [torch.float32, torch.bfloat16]
+B, H = 3, 5
+
+
+def _vbar(d_v, seed):
+    return wl.make_vbar(H, d_v, seed, device="cuda")
+
+
+def _random_factors(st, r, seed):
+    """Fill a, U, V with state-like values: U columns unit-norm-ish and
+    decayed, V columns orthogonal to vbar with spread norms."""
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    cap, d_k, d_v = st.cap, st.d_k, st.d_v
+    st.a.copy_(torch.randn(B, H, d_k, generator=gen, device="cuda"))
+    U = torch.randn(B, H, cap, d_k, generator=gen, device="cuda") / d_k ** 0.5
+    U *= torch.rand(B, H, cap, 1, generator=gen, device="cuda") * 0.9 + 0.1
+    V = torch.randn(B, H, cap, d_v, generator=gen, device="cuda")
+    vb = st.vbar[None, :, None, :]
+    V -= (V * vb).sum(-1, keepdim=True) / (vb * vb).sum(-1, keepdim=True) * vb
+    V *= torch.rand(B, H, cap, 1, generator=gen, device="cuda") * 2.0
+    st.U.copy_(U)
+    st.V.copy_(V)
+    st.r = r
+
+
+@pytest.mark.parametrize("in_dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: f"{d[0]}x{d[1]}")
+@pytest.mark.parametrize("rule", RULES)
+def test_dense_step(rule, dims, in_dtype):
+    d_k, d_v = dims
+    vbar = _vbar(d_v, 11)
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    S = torch.randn(B, H, d_k, d_v, generator=gen, device="cuda")
+    o = torch.empty(B, H, d_v, device="cuda")
+    for t in range(3):
+        inp = wl.make_step(rule, B, H, d_k, d_v, vbar, 13, t, 0, in_dtype, "cuda")
+        S_ref, o_ref = oracle.dense_step(rule, f64(units_of(S)), **inputs_np(inp))
+        binding.dense_decode_step(rule, S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o)
+        torch.cuda.synchronize()
+        assert rel_err(f64(units_of(S)), S_ref, (-2, -1)).max() < TOL_STATE_STEP
+        assert rel_err(f64(units_of(o)), o_ref, -1).max() < TOL_READOUT
+
+
+@pytest.mark.parametrize("in_dtype", DTYPES, ids=["f32", "bf16"])
+@pytest.mark.parametrize("dims", DIMS, ids=lambda d: f"{d[0]}x{d[1]}")
+@pytest.mark.parametrize("rule", RULES)
+def test_decode_step(rule, dims, in_dtype):
+    d_k, d_v = dims
+    R, W = 16, 32
+    st = make_state(rule, B, H, d_k, d_v, R, W, _vbar(d_v, 21))
+    o = torch.empty(B, H, d_v, device="cuda")
+    for i, r in enumerate([0, 1, 7, 9, 16, 31, 47]):
+        _random_factors(st, r, 100 + i)
+        inp = wl.make_step(rule, B, H, d_k, d_v, st.vbar, 22, i, 0, in_dtype, "cuda")
+        a0, U0, V0, vb = state_np(st)
+        U_full_before = f64(st.U)
+        st.step(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o)
+        torch.cuda.synchronize()
+        a_ref, U_ref, V_ref, o_ref = oracle.seed_step(rule, a0, U0, V0, vb, **inputs_np(inp))
+        a1, U1, V1, _ = state_np(st)
+        assert st.r == r + 1
+        # the step is exact arithmetic on the factors: compare them directly
+        assert rel_err(a1, a_ref, -1).max() < TOL_STATE_STEP
+        assert rel_err(U1, U_ref, (-2, -1)).max() < TOL_STATE_STEP
+        assert state_rel_err(a1, U1, V1, a_ref, U_ref, V_ref, vb).max() < TOL_STATE_STEP
+        assert rel_err(f64(units_of(o)), o_ref, -1).max() < TOL_READOUT
+        # columns beyond the appended one are untouched
+        np.testing.assert_array_equal(f64(st.U)[:, :, r + 1:], U_full_before[:, :, r + 1:])
+
+
+def _oracle_precompress_states(rule, d_k, d_v, R, n, seed, units=4):
+    """Realistic factors just before a compression, produced by the oracle:
+    a short dense prefill, conversion, then n - R exact steps."""
+    rng = np.random.default_rng(seed)
+    vbar = rng.standard_normal(d_v)
+
+    def inp():
+        k = rng.standard_normal((units, d_k)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q = rng.standard_normal((units, d_k)); q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        v = vbar + 0.3 * rng.standard_normal((units, d_v))
+        if rule == "kda":
+            g = rng.uniform(0.95, 0.9999, (units, d_k))
+        elif rule == "gdn":
+            g = rng.uniform(0.9, 0.999, units)
+        else:
+            g = np.exp(-np.logaddexp(0, rng.standard_normal(units)) * 0.1)
+        beta = None if rule == "mamba2" else rng.uniform(0, 1, units)
+        return dict(q=q, k=k, v=v, g=g, beta=beta)
+
+    S = np.zeros((units, d_k, d_v))
+    for _ in range(48):
+        S, _ = oracle.dense_step(rule, S, **inp())
+    a, U, V = oracle.state_from_dense(S, vbar, R)
+    for _ in range(n - R):
+        a, U, V, _ = oracle.seed_step(rule, a, U, V, vbar, **inp())
+    return a, U, V, vbar
+
+
+@pytest.mark.parametrize("rule,dims,R,W,n", [
+    ("gdn", (128, 128), 16, 32, 48),
+    ("gdn", (128, 128), 16, 16, 32),
+    ("gdn", (128, 128), 16, 32, 33),     # compress before the ring is full, odd n
+    ("kda", (128, 128), 16, 64, 80),
+    ("kda", (128, 128), 32, 64, 96),     # largest capacity
+    ("mamba2", (128, 64), 16, 32, 48),
+    ("mamba2", (128, 64), 16, 32, 47),
+    ("gdn", (64, 64), 8, 24, 32),
+    ("gdn", (128, 128), 1, 8, 9),
+])
+def test_compress(rule, dims, R, W, n):
+    d_k, d_v = dims
+    units = B * H
+    a, U, V, vbar_np = _oracle_precompress_states(rule, d_k, d_v, R, n, 31 + n, units)
+    st = make_state(rule, B, H, d_k, d_v, R, W, torch.tensor(np.broadcast_to(vbar_np, (H, d_v)).copy(),
+                                                             dtype=torch.float32))
+    U32 = U.astype(np.float32)
+    V32 = V.astype(np.float32)
+    st.a.copy_(torch.tensor(a.reshape(B, H, d_k), dtype=torch.float32))
+    st.U[:, :, :n] = torch.tensor(U32.transpose(0, 2, 1).reshape(B, H, n, d_k), device="cuda")
+    st.V[:, :, :n] = torch.tensor(V32.transpose(0, 2, 1).reshape(B, H, n, d_v), device="cuda")
+    st.r = n
+    a_before = f64(st.a).copy()
+    st.compress()
+    torch.cuda.synchronize()
+    assert st.r == R
+    Ug, Vg = state_np(st)[1:3]
+    Uc, Vc = oracle.compress(U32.astype(np.float64), V32.astype(np.float64), R)
+    gap = content_gap(U32.astype(np.float64), V32.astype(np.float64), R)
+    ok = gap >= TIE_GAP
+    assert ok.sum() >= units - 1, f"too many near-ties: {gap}"
+    prod_g = Ug @ np.swapaxes(Vg, -1, -2)
+    prod_r = Uc @ np.swapaxes(Vc, -1, -2)
+    S_ref = oracle.reconstruct(a.reshape(units, d_k), Uc, Vc, np.broadcast_to(vbar_np, (units, d_v)))
+    err_state = np.sqrt(np.sum((prod_g - prod_r) ** 2, axis=(-2, -1))) / np.sqrt(
+        np.sum(S_ref ** 2, axis=(-2, -1)))
+    err_content = rel_err(prod_g, prod_r, (-2, -1))
+    assert err_state[ok].max() < TOL_STATE_COMPRESS, err_state
+    assert err_content[ok].max() < 1e-3, err_content
+    # U' orthonormal, the sink untouched (bit for bit)
+    gram = np.swapaxes(Ug, -1, -2) @ Ug
+    assert np.abs(gram - np.eye(R)).max() < 1e-4
+    np.testing.assert_array_equal(f64(st.a), a_before)
+
+
+@pytest.mark.parametrize("dims,R", [((128, 128), 16), ((128, 64), 16), ((64, 64), 8),
+                                    ((128, 128), 32)])
+def test_state_from_dense(dims, R):
+    d_k, d_v = dims
+    gen = torch.Generator(device="cuda").manual_seed(41)
+    vbar = wl.make_vbar(H, d_v, 42, device="cuda")
+    # a dense state with a strong sink and a decaying content spectrum
+    a_true = torch.randn(B, H, d_k, 1, generator=gen, device="cuda")
+    L = torch.randn(B, H, d_k, 40, generator=gen, device="cuda")
+    Rm = torch.randn(B, H, 40, d_v, generator=gen, device="cuda") * torch.logspace(
+        0, -3, 40, device="cuda")[:, None]
+    S = (a_true * vbar[None, :, None, :] + L @ Rm * 0.3).contiguous()
+    st = make_state("gdn", B, H, d_k, d_v, R, 16, vbar)
+    st.from_dense(S)
+    torch.cuda.synchronize()
+    assert st.r == R
+    vb = np.broadcast_to(f64(vbar)[None], (B, H, d_v)).reshape(-1, d_v)
+    a_r, U_r, V_r = oracle.state_from_dense(f64(units_of(S)), vb, R)
+    a_g, U_g, V_g, _ = state_np(st)
+    assert rel_err(a_g, a_r, -1).max() < TOL_STATE_STEP
+    C = f64(units_of(S)) - a_r[..., :, None] * vb[..., None, :]
+    gap = content_gap(C, np.broadcast_to(np.eye(d_v), C.shape[:-2] + (d_v, d_v)), R)
+    ok = gap >= TIE_GAP
+    assert ok.sum() >= B * H - 1
+    err = state_rel_err(a_g, U_g, V_g, a_r, U_r, V_r, vb)
+    assert err[ok].max() < TOL_STATE_COMPRESS, err
+    assert np.abs(np.swapaxes(U_g, -1, -2) @ U_g - np.eye(R)).max() < 1e-4
+    # the content stays orthogonal to vbar
+    assert (np.abs(np.swapaxes(V_g, -1, -2) @ vb[..., :, None]).max()
+            < 1e-4 * np.abs(V_g).max() * np.linalg.norm(vb, axis=-1).max())
