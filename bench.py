@@ -1,0 +1,331 @@
+"""Benchmark of the shallow-state decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+
+One benchmark step is one decode step of every (request, head) unit of the
+workload: the fused read-out + exact update kernel, plus the compression of
+all units whenever R + W columns are held (every W steps), exactly as a
+served decode loop would run them.  Inputs for every timed step are drawn
+before timing and are resident in HBM; the state starts from a dense
+prefill converted to the shallow form (both untimed).
+
+The metric is decode head-steps/s (whole job).  Also reported: the step
+kernel's achieved HBM bandwidth from its algorithmic bytes and its average
+launch duration (HIP events on the launch stream), the dense-state baseline
+kernel on the same workload, and the CPU oracle timed on a bounded sample.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+from sink_rank_recurrent_amd import binding  # noqa: E402
+from sink_rank_recurrent_amd import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+DEFAULT_WORKLOAD = 2
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_seed_step_gdn_64x16_r16w32_bf16.json")
+STEP_SOURCE = os.path.join(ROOT, "sink_rank_recurrent_amd", "csrc", "seed_step.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (what the method must move; see the byte account in the
+# design notes): reads a, r columns of U and V, the inputs and vbar; writes a,
+# all r + 1 columns of U (in-place decay plus the new column), one V column
+# and o (fp32).
+# ---------------------------------------------------------------------------
+
+def step_bytes_per_unit(w: wl.Workload, r: int) -> float:
+    s_in = 2 if w.in_dtype == torch.bfloat16 else 4
+    g_bytes = 4 * w.d_k if w.rule == "kda" else 4
+    beta_bytes = 0 if w.rule == "mamba2" else 4
+    read = 4 * w.d_k + 4 * (w.d_k + w.d_v) * r + s_in * (2 * w.d_k + w.d_v) + g_bytes + beta_bytes
+    read += 4 * w.d_v / w.batch          # vbar, shared by the requests of a head
+    write = 4 * w.d_k + 4 * w.d_k * (r + 1) + 4 * w.d_v + 4 * w.d_v
+    return read + write
+
+
+def dense_bytes_per_unit(w: wl.Workload) -> float:
+    s_in = 2 if w.in_dtype == torch.bfloat16 else 4
+    g_bytes = 4 * w.d_k if w.rule == "kda" else 4
+    beta_bytes = 0 if w.rule == "mamba2" else 4
+    return 8 * w.d_k * w.d_v + s_in * (2 * w.d_k + w.d_v) + g_bytes + beta_bytes + 4 * w.d_v
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(w: wl.Workload):
+    """HBM bytes per step-kernel launch from the committed counter summary,
+    or None if there is none or the kernel source changed since."""
+    if w.name != wl.WORKLOADS[DEFAULT_WORKLOAD].name or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != source_hash(STEP_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+def prepare(w: wl.Workload, layer: int, n_steps: int, dev: str):
+    """vbar, a converted shallow state and resident inputs for n_steps steps."""
+    vbar = wl.make_vbar(w.heads, w.d_v, w.seed, layer, dev)
+    S = torch.zeros(w.batch, w.heads, w.d_k, w.d_v, device=dev)
+    o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
+    for t in range(-w.prefill, 0):
+        x = wl.workload_step(w, vbar, t, layer, dev)
+        binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+    st = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar, device=dev)
+    st.from_dense(S)
+    inputs = [wl.workload_step(w, vbar, t, layer, dev) for t in range(n_steps)]
+    torch.cuda.synchronize()
+    return vbar, S, st, inputs
+
+
+def run_shallow(st, inputs, o, warmup: int, steps: int):
+    """Warm up, then time `steps` steps.
+
+    HIP events (on the launch stream) bracket each run of consecutive step
+    launches between two compressions, and each compression, so no event
+    marker sits between two step kernels."""
+    for t in range(warmup):
+        x = inputs[t]
+        st.step_and_maybe_compress(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    windows, comp_ev, step_r = [], [], []
+    t_begin, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record()
+    w0, n_in_window = ev(), 0
+    w0.record()
+    for t in range(warmup, warmup + steps):
+        x = inputs[t]
+        step_r.append(st.r)
+        st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        n_in_window += 1
+        if st.r >= st.cap:
+            w1 = ev()
+            w1.record()
+            windows.append((w0, w1, n_in_window))
+            st.compress()
+            w0, n_in_window = ev(), 0
+            w0.record()
+            comp_ev.append((w1, w0))
+    if n_in_window:
+        w1 = ev()
+        w1.record()
+        windows.append((w0, w1, n_in_window))
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return {
+        "elapsed_s": t_begin.elapsed_time(t_end) / 1e3,
+        "wall_s": wall,
+        "step_window_ms": [(a.elapsed_time(b), n) for a, b, n in windows],
+        "step_r": step_r,
+        "compress_ms": [a.elapsed_time(b) for a, b in comp_ev],
+    }
+
+
+def run_dense(w, S, inputs, o, warmup: int, steps: int):
+    for t in range(warmup):
+        x = inputs[t]
+        binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for t in range(warmup, warmup + steps):
+        x = inputs[t]
+        binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+    t1.record()
+    torch.cuda.synchronize()
+    return {"elapsed_s": t0.elapsed_time(t1) / 1e3}
+
+
+def cpu_baseline(w, st0_np, inputs_np, budget_s: float):
+    """The oracle's factored mode, as it stands, on a bounded sample: the
+    first units of the workload from their converted state, stepping through
+    the same inputs (cycled) until `budget_s` seconds have been spent."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    a, U, V, vb = st0_np
+    n_units = a.shape[0]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - t0 < budget_s:
+            x = inputs_np[done % len(inputs_np)]
+            a, U, V, _ = oracle.seed_step(w.rule, a, U, V, vb, x["q"], x["k"], x["v"], x["g"],
+                                          x["beta"])
+            if U.shape[-1] >= w.R + w.W:
+                U, V = oracle.compress(U, V, w.R)
+            done += 1
+    el = time.perf_counter() - t0
+    return {"value": n_units * done / el, "unit": "head-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_units} units x {done} decode steps (compression every {w.W}) of "
+                      f"{w.name}, from the converted state, fp64 numpy oracle, 1 thread, "
+                      f"{el:.1f} s"}
+
+
+def copy_probe(n_bytes: int = 1 << 30, reps: int = 8) -> None:
+    """A plain device copy of known size (calibration of the HBM byte
+    counters): `reps` launches of dst.copy_(src) over n_bytes each."""
+    src = torch.ones(n_bytes // 4, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    print(json.dumps({"copy_probe_bytes_read_per_launch": n_bytes,
+                      "copy_probe_bytes_written_per_launch": n_bytes, "launches": reps,
+                      "GBs_read_plus_write": 2 * n_bytes * reps / el / 1e9}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--layer", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the shallow-state path has no cross-GPU exchange and "
+              "this build runs on a single MI355X; --gpus must be 1", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    if args.copy_probe:
+        copy_probe()
+        return 0
+
+    w = wl.WORKLOADS[args.workload]
+    steps = args.steps if args.steps is not None else min(w.steps, 1024)
+    warmup = args.warmup
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    binding.lib()
+    units = w.batch * w.heads
+    log(f"workload {w.name}: {units} units, {steps} timed steps after {warmup} warm-up")
+
+    vbar, S_dense, st, inputs = prepare(w, args.layer, warmup + steps, dev)
+    log("prepared state and inputs")
+
+    # snapshot for the CPU baseline (first units, converted state)
+    cpu = None
+    if not args.no_cpu:
+        n_cpu = min(units, 64)
+        f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+        a0 = f64(st.a.reshape(units, w.d_k)[:n_cpu])
+        U0 = f64(st.U.reshape(units, w.cap, w.d_k)[:n_cpu, :st.r]).transpose(0, 2, 1)
+        V0 = f64(st.V.reshape(units, w.cap, w.d_v)[:n_cpu, :st.r]).transpose(0, 2, 1)
+        vb0 = f64(vbar)[[u % w.heads for u in range(n_cpu)]]
+        cpu_inputs = []
+        for x in inputs[: min(len(inputs), 256)]:
+            cpu_inputs.append({k: (None if v is None else f64(v.reshape((units,) + v.shape[2:])[:n_cpu]))
+                               for k, v in x.items()})
+        cpu_state = (a0, U0, V0, vb0)
+
+    S_copy = S_dense.clone() if not args.no_dense else None
+    o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
+    res = run_shallow(st, inputs, o, warmup, steps)
+    log(f"shallow: {res['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
+
+    dense = None
+    if not args.no_dense:
+        dres = run_dense(w, S_copy, inputs, o, warmup, steps)
+        d_bytes = dense_bytes_per_unit(w) * units
+        d_avg = dres["elapsed_s"] / steps
+        dense = {"value": units * steps / dres["elapsed_s"], "unit": "head-steps/s",
+                 "bytes_per_head_step": dense_bytes_per_unit(w),
+                 "kernel_avg_us": d_avg * 1e6,
+                 "achieved_GBs": d_bytes / d_avg / 1e9}
+        log(f"dense: {dres['elapsed_s'] * 1e3:.2f} ms")
+
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, cpu_state, cpu_inputs, args.cpu_budget)
+        log(f"cpu oracle: {cpu['value']:.1f} head-steps/s")
+
+    elapsed = res["elapsed_s"]
+    value = units * steps / elapsed
+    step_total_s = sum(ms for ms, _ in res["step_window_ms"]) / 1e3
+    comp_total_s = sum(res["compress_ms"]) / 1e3
+    step_bytes = sum(step_bytes_per_unit(w, r) * units for r in res["step_r"])
+    n_launch = sum(n for _, n in res["step_window_ms"])
+    assert n_launch == len(res["step_r"])
+    avg_launch_s = step_total_s / n_launch
+    achieved = step_bytes / n_launch / avg_launch_s / 1e9
+    traffic = load_traffic(w)
+    mean_bytes = step_bytes / n_launch / units
+
+    out = {
+        "metric": "decode head-steps/s (sink + rank-R state update, whole job incl. compression)",
+        "value": value,
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": elapsed * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; no trace or checkpoint)",
+        "config": {"workload": w.name, "rule": w.rule, "requests": w.batch, "heads": w.heads,
+                   "layers_per_launch": 1, "d_k": w.d_k, "d_v": w.d_v, "R": w.R, "W": w.W,
+                   "inputs": "bf16 q/k/v, fp32 gates" if w.in_dtype == torch.bfloat16 else "fp32",
+                   "prefill": w.prefill},
+        "roofline": {"bound": "hbm", "kernel": "seed_step_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": step_bytes / n_launch,
+                     "avg_launch_us": avg_launch_s * 1e6},
+        "cpu_baseline": cpu,
+        "breakdown": {"step_kernel_s": step_total_s, "compress_kernel_s": comp_total_s,
+                      "compressions": len(res["compress_ms"]),
+                      "compress_avg_us": (comp_total_s / max(1, len(res["compress_ms"]))) * 1e6,
+                      "step_bytes_per_head_step": mean_bytes,
+                      "step_only_head_steps_per_s": units * n_launch / step_total_s,
+                      "wall_s": res["wall_s"]},
+        "dense_baseline": dense,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -519,7 +519,7 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 template <int DK, int DV>
 hipError_t compress_go(int units, int cap, int n, int R, float* U, float* V, hipStream_t s) {
-  const size_t bytes = compress_lds_bytes(n, R);
+  const size_t bytes = compress_jacobi_lds_bytes(n, R);
   hipError_t err = set_lds(compress_kernel<DK, DV>, bytes);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((compress_kernel<DK, DV>), dim3(units), dim3(kNT), bytes, s, U, V, cap, n, R);
@@ -539,12 +539,17 @@ hipError_t from_dense_go(int units, int heads, int cap, int R, const float* S, c
 
 }  // namespace
 
-size_t compress_lds_bytes(int n, int R) { return 4 * lds_floats(padded(n), R, true); }
+size_t compress_jacobi_lds_bytes(int n, int R) { return 4 * lds_floats(padded(n), R, true); }
+
+size_t compress_lds_bytes(int n, int R) {
+  return n <= kWaveMaxN ? compress_wave_lds_bytes(n, R) : compress_jacobi_lds_bytes(n, R);
+}
 
 size_t from_dense_lds_bytes(int d_k, int R) { return 4 * lds_floats(padded(d_k), R, false); }
 
 hipError_t launch_compress(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
                            float* U, float* V, hipStream_t stream) {
+  if (n <= kWaveMaxN) return launch_compress_wave(batch, heads, d_k, d_v, cap, n, R, U, V, stream);
   const int units = batch * heads;
   if (d_k == 128 && d_v == 128) return compress_go<128, 128>(units, cap, n, R, U, V, stream);
   if (d_k == 128 && d_v == 64) return compress_go<128, 64>(units, cap, n, R, U, V, stream);
