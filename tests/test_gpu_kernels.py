@@ -195,3 +195,123 @@ def test_state_from_dense(dims, R):
     # the content stays orthogonal to vbar
     assert (np.abs(np.swapaxes(V_g, -1, -2) @ vb[..., :, None]).max()
             < 1e-4 * np.abs(V_g).max() * np.linalg.norm(vb, axis=-1).max())
+
+
+# ---------------------------------------------------------------------------
+# edge cases and degenerate inputs
+# ---------------------------------------------------------------------------
+
+def test_step_is_deterministic():
+    """Two runs of the same step from the same state give identical bits
+    (one workgroup owns a unit; no atomics, fixed reduction order)."""
+    st = make_state("gdn", B, H, 128, 128, 16, 32, _vbar(128, 61))
+    _random_factors(st, 29, 62)
+    inp = wl.make_step("gdn", B, H, 128, 128, st.vbar, 63, 0, 0, torch.bfloat16, "cuda")
+    saved = [t.clone() for t in (st.a, st.U, st.V)]
+    outs = []
+    for _ in range(2):
+        st.a.copy_(saved[0]); st.U.copy_(saved[1]); st.V.copy_(saved[2]); st.r = 29
+        o = torch.empty(B, H, 128, device="cuda")
+        st.step(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (st.a, st.U, st.V, o)])
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("rule", ["gdn", "kda"])
+def test_no_write_no_decay_keeps_state(rule):
+    st = make_state(rule, B, H, 128, 128, 16, 32, _vbar(128, 64))
+    _random_factors(st, 20, 65)
+    a0, U0, V0, vb = state_np(st)
+    inp = wl.make_step(rule, B, H, 128, 128, st.vbar, 66, 0, 0, torch.float32, "cuda")
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    inp["g"] = torch.ones_like(inp["g"])
+    o = torch.empty(B, H, 128, device="cuda")
+    st.step(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o)
+    torch.cuda.synchronize()
+    a1, U1, V1, _ = state_np(st)
+    np.testing.assert_array_equal(a1, a0)
+    np.testing.assert_array_equal(U1[..., :20], U0)
+    np.testing.assert_array_equal(V1[..., 20], 0.0)        # the appended V column is zero
+    assert state_rel_err(a1, U1, V1, a0, U0, V0, vb).max() == 0.0
+
+
+def test_mamba2_value_along_vbar():
+    st = make_state("mamba2", B, H, 128, 64, 16, 32, _vbar(64, 67))
+    _random_factors(st, 17, 68)
+    inp = wl.make_step("mamba2", B, H, 128, 64, st.vbar, 69, 0, 0, torch.float32, "cuda")
+    inp["v"] = (2.5 * st.vbar).expand(B, H, 64).contiguous()
+    a0 = f64(st.a)
+    o = torch.empty(B, H, 64, device="cuda")
+    st.step(inp["q"], inp["k"], inp["v"], inp["g"], None, o)
+    torch.cuda.synchronize()
+    newcol = f64(st.V)[:, :, 17]
+    assert np.abs(newcol).max() < 1e-5 * np.abs(f64(st.vbar)).max() * 2.5
+    g = f64(inp["g"])[..., None]
+    np.testing.assert_allclose(f64(st.a), g * a0 + 2.5 * f64(inp["k"]), rtol=1e-5, atol=1e-6)
+
+
+def test_nan_stays_in_its_unit():
+    """NaN inputs are not checked: they propagate into that unit's outputs
+    and nowhere else."""
+    st = make_state("gdn", B, H, 128, 128, 16, 32, _vbar(128, 70))
+    _random_factors(st, 12, 71)
+    inp = wl.make_step("gdn", B, H, 128, 128, st.vbar, 72, 0, 0, torch.float32, "cuda")
+    inp["v"][1, 2, 5] = float("nan")
+    o = torch.empty(B, H, 128, device="cuda")
+    st.step(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o)
+    torch.cuda.synchronize()
+    on = torch.isnan(o).any(dim=-1)
+    assert on[1, 2] and on.sum() == 1
+    assert torch.isnan(st.a[1, 2]).any() and torch.isnan(st.a).any(dim=-1).sum() == 1
+
+
+@pytest.mark.parametrize("case", ["dup_keys", "zero_v_cols", "all_zero_v", "zero_u_cols"])
+def test_compress_degenerate(case):
+    d_k = d_v = 128
+    R, W = 16, 32
+    n = R + W
+    rng = np.random.default_rng(73)
+    units = B * H
+    U = rng.standard_normal((units, d_k, n)) / np.sqrt(d_k)
+    V = rng.standard_normal((units, d_v, n))
+    if case == "dup_keys":
+        U[:, :, 30] = 0.7 * U[:, :, 5]
+        U[:, :, 41] = U[:, :, 40]
+    elif case == "zero_v_cols":
+        V[:, :, 16:] = 0.0
+    elif case == "all_zero_v":
+        V[:] = 0.0
+    else:
+        U[:, :, 20:] = 0.0
+    U = U.astype(np.float32).astype(np.float64)
+    V = V.astype(np.float32).astype(np.float64)
+    st = make_state("gdn", B, H, d_k, d_v, R, W, torch.randn(H, d_v))
+    st.U[:, :, :n] = torch.tensor(U.transpose(0, 2, 1).reshape(B, H, n, d_k), dtype=torch.float32)
+    st.V[:, :, :n] = torch.tensor(V.transpose(0, 2, 1).reshape(B, H, n, d_v), dtype=torch.float32)
+    st.r = n
+    st.compress()
+    torch.cuda.synchronize()
+    Ug, Vg = state_np(st)[1:3]
+    assert np.isfinite(Ug).all() and np.isfinite(Vg).all()
+    Uc, Vc = oracle.compress(U, V, R)
+    P = Uc @ np.swapaxes(Vc, -1, -2)
+    Pg = Ug @ np.swapaxes(Vg, -1, -2)
+    scale = np.maximum(np.sqrt(np.sum((U @ np.swapaxes(V, -1, -2)) ** 2, axis=(-2, -1))), 1e-30)
+    err = np.sqrt(np.sum((Pg - P) ** 2, axis=(-2, -1))) / scale
+    ok = content_gap(U, V, R) >= TIE_GAP if case != "all_zero_v" else np.ones(units, bool)
+    assert err[ok].max() < 1e-4, err
+
+
+def test_from_dense_of_pure_sink():
+    vbar = _vbar(128, 74)
+    a_true = torch.randn(B, H, 128, 1, device="cuda")
+    S = (a_true * vbar[None, :, None, :]).contiguous()
+    st = make_state("gdn", B, H, 128, 128, 16, 16, vbar)
+    st.from_dense(S)
+    torch.cuda.synchronize()
+    a, U, V, vb = state_np(st)
+    np.testing.assert_allclose(a, f64(a_true)[..., 0].reshape(-1, 128), rtol=1e-5, atol=1e-6)
+    prod = U @ np.swapaxes(V, -1, -2)
+    assert np.abs(prod).max() < 1e-5 * np.abs(f64(S)).max()
