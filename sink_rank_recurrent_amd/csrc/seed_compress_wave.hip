@@ -31,8 +31,15 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kEps = 1.1920928955078125e-7f;   // 2^-23
 constexpr float kPivTol = 1e-5f;                   // dependent-column threshold (relative)
-constexpr float kClusterTol = 1e-3f;               // eigenvalue cluster width / |T|
-constexpr int kInvIters = 3;
+// Shifts closer than kClusterTol |T| are re-orthogonalised during inverse
+// iteration (their vectors could otherwise come out nearly parallel); all
+// top-R vectors then go through one modified Gram-Schmidt pass.
+constexpr float kClusterTol = 1e-5f;
+constexpr int kInvIters = 2;
+// T is padded to NMAX rows with this diagonal and zero couplings: the padded
+// eigenvalues are never among the counted ones and the padded entries of
+// every solve are exactly 0, so the loops below need no bounds tests.
+constexpr float kPadDiag = 1.0e30f;
 
 // Sum / min / max over the 64 lanes, returned to every lane.  Inside each
 // row of 16 lanes: DPP butterflies (xor 1, xor 2, mirror within 8, mirror
@@ -97,6 +104,7 @@ struct WaveLds {
   float* lam;   // [36]
   int* rnk;     // [36]
   float* misc;  // [4]
+  float* cb;    // [NMAX] one lane's column, broadcast to the others
 };
 
 __host__ __device__ inline size_t wave_f_floats(int nmax, int R) {
@@ -106,7 +114,7 @@ __host__ __device__ inline size_t wave_f_floats(int nmax, int R) {
 __host__ __device__ inline size_t wave_lds_floats(int nmax, int R) {
   const size_t ldn = nmax + 1;
   return 2 * nmax * ldn + (size_t)nmax * R + wave_f_floats(nmax, R) + 6 * (size_t)nmax + 64 + 64 +
-         36 + 36 + 4;
+         36 + 36 + 4 + (size_t)nmax;
 }
 
 template <int NMAX>
@@ -128,7 +136,8 @@ __device__ inline WaveLds<NMAX> wave_carve(float* base, int R) {
   L.bfl = reinterpret_cast<int*>(p); p += 64;
   L.lam = p; p += 36;
   L.rnk = reinterpret_cast<int*>(p); p += 36;
-  L.misc = p;
+  L.misc = p; p += 4;
+  L.cb = p;
   return L;
 }
 
@@ -234,7 +243,13 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
   __syncthreads();
   gram_mfma<NMAX, DV>(Vh, n, L.G);
   for (int j = 0; j < n; ++j) {
-    const float gj = pick(g, j);
+    // M[j][l] = M[l][j]: lane j publishes its column, every lane reads its entry
+    if (l == j) {
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i) L.cb[i] = g[i];
+    }
+    __syncthreads();
+    const float gj = act ? L.cb[l] : 0.f;
     const float piv = lane_value(gj, j);
     const bool ok = piv > kPivTol;
     const float p = ok ? sqrtf(piv) : 0.f;
@@ -250,39 +265,65 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
     __syncthreads();
   }
 
-  // ---- C: H = R G~ R^T, column l per lane --------------------------------
+  // ---- C: H = R G~ R^T with two MFMA products ---------------------------
+  //   P = G~ R^T  (into the inverse-iteration region, row stride NMAX)
+  //   H = R P     (into G, which G~ no longer needs), then lane l reads
+  //   column l of H.
 #pragma unroll
   for (int i = 0; i < NMAX; ++i)
     if (act) L.G[i * LDN + l] *= L.dv[i] * L.dv[l];
   __syncthreads();
-  float h[NMAX];
   {
-    // z = G~ r_l with r_l = row l of R (read from Rb); z is staged per lane
-    // in the (still unused) inverse-iteration region as [i][64]
-    float* zs = reinterpret_cast<float*>(L.F);
-    float z[NMAX];
+    constexpr int NT = NMAX / 16;
+    const int ci = l & 15, kk = l >> 4;
+    float* P = reinterpret_cast<float*>(L.F);
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) z[i] = 0.f;
-    for (int m = 0; m < n; ++m) {
-      const float rm = act ? L.Rb[m * LDN + l] : 0.f;   // R[l][m]
+    for (int I = 0; I < NT; ++I)
 #pragma unroll
-      for (int i = 0; i < NMAX; ++i) z[i] += L.G[m * LDN + i] * rm;
-    }
+      for (int J = 0; J < NT; ++J) {
+        f4v acc = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) zs[i * 64 + l] = z[i];
+        for (int K = 0; K < NMAX / 4; ++K) {
+          const int m = K * 4 + kk;
+          const float av = L.G[(I * 16 + ci) * LDN + m];   // G~[i][m]
+          const float bv = L.Rb[m * LDN + J * 16 + ci];    // R^T[m][j] = R[j][m]
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+        }
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) h[i] = 0.f;
-    for (int m = 0; m < n; ++m) {
-      const float zm = zs[m * 64 + l];
+        for (int r = 0; r < 4; ++r) P[(I * 16 + 4 * kk + r) * NMAX + J * 16 + ci] = acc[r];
+      }
+    __syncthreads();
 #pragma unroll
-      for (int i = 0; i < NMAX; ++i) h[i] += L.Rb[m * LDN + i] * zm;   // R[i][m] z[m]
-    }
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        f4v acc = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int K = 0; K < NMAX / 4; ++K) {
+          const int m = K * 4 + kk;
+          const float av = L.Rb[m * LDN + I * 16 + ci];    // R[i][m]
+          const float bv = P[m * NMAX + J * 16 + ci];      // P[m][j]
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) L.G[(I * 16 + 4 * kk + r) * LDN + J * 16 + ci] = acc[r];
+      }
+    __syncthreads();
   }
+  float h[NMAX];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) h[i] = act ? L.G[i * LDN + l] : 0.f;
   __syncthreads();
 
   // ---- D: Householder tridiagonalisation ---------------------------------
   for (int k = 0; k + 2 < n; ++k) {
-    const float hk = pick(h, k);                 // lane i: H[k][i]
+    // lane k publishes column k; lane i reads H[i][k] (= H[k][i])
+    if (l == k) {
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i) L.cb[i] = h[i];
+    }
+    __syncthreads();
+    const float hk = act ? L.cb[l] : 0.f;
     const float alpha = lane_value(hk, k + 1);
     const float dkk = lane_value(hk, k);
     const float xn2 = wave_sum(l > k + 1 ? hk * hk : 0.f);
@@ -326,10 +367,21 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
     __syncthreads();
   }
   {
-    const float hn2 = pick(h, n - 2), hn1 = pick(h, n - 1);
-    const float d2 = lane_value(hn2, n - 2);
-    const float e2 = lane_value(hn2, n - 1);
-    const float d1 = lane_value(hn1, n - 1);
+    // the trailing 2 x 2 block, from lane n - 1's column
+    if (l == n - 1) {
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i) L.cb[i] = h[i];
+    }
+    __syncthreads();
+    const float e2 = L.cb[n - 2];     // H[n-2][n-1]
+    const float d1 = L.cb[n - 1];     // H[n-1][n-1]
+    __syncthreads();
+    if (l == n - 2) {
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i) L.cb[i] = h[i];
+    }
+    __syncthreads();
+    const float d2 = L.cb[n - 2];     // H[n-2][n-2]
     if (l == 0) {
       L.td[n - 2] = d2;
       L.te[n - 2] = e2;
@@ -358,10 +410,17 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
     const int grp = l / m, sub = l % m;
     const bool live = grp < T;
     const int target = n - 1 - grp;       // ascending index of the eigenvalue
-    // squared off-diagonal, e2[i] = T[i][i-1]^2 (vb is free after the reduction)
-    float* e2 = L.vb;
-    if (act) e2[l] = (l > 0 && l < n) ? L.te[l - 1] * L.te[l - 1] : 0.f;
+    // pad T to NMAX: diagonal kPadDiag, zero off-diagonal beyond row n - 1
+    if (act && l >= n) L.td[l] = kPadDiag;
+    if (act && l >= n - 1) L.te[l] = 0.f;
     __syncthreads();
+    float dr[NMAX], e2r[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+      dr[i] = L.td[i];
+      const float ei = (i > 0) ? L.te[i - 1] : 0.f;
+      e2r[i] = ei * ei;
+    }
     float lo = lo0, hi = hi0;
     for (int it = 0; it < 64; ++it) {
       const bool done = !live || target < 0 ||
@@ -369,14 +428,14 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
       if (__all(done)) break;
       const float pt = lo + (hi - lo) * ((float)(sub + 1) / (float)(m + 1));
       int cnt = 0;
-      float q = 1.f;
+      float q = dr[0] - pt;
+      q = (fabsf(q) < pivmin) ? -pivmin : q;
+      cnt += (q < 0.f);
 #pragma unroll
-      for (int i = 0; i < NMAX; ++i) {
-        if (i < n) {
-          q = (L.td[i] - pt) - (i > 0 ? e2[i] * __builtin_amdgcn_rcpf(q) : 0.f);
-          q = (fabsf(q) < pivmin) ? -pivmin : q;
-          cnt += (q < 0.f);
-        }
+      for (int i = 1; i < NMAX; ++i) {
+        q = (dr[i] - pt) - e2r[i] * __builtin_amdgcn_rcpf(q);
+        q = (fabsf(q) < pivmin) ? -pivmin : q;
+        cnt += (q < 0.f);
       }
       L.bpt[l] = pt;
       L.bfl[l] = (cnt > target) ? 1 : 0;
@@ -415,11 +474,13 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
   {
     const int maxr = __float_as_int(L.misc[0]);
     const float tiny = kEps * tnorm + 1e-30f;
-    // off-diagonal masked at the end of T (wb is free after the reduction)
-    float* er = L.wb;
-    if (act) er[l] = (l + 1 < n) ? L.te[l] : 0.f;
-    __syncthreads();
-    const float* dr = L.td;
+    // padded T in registers (td / te were padded in phase E)
+    float dr[NMAX], er[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+      dr[i] = L.td[i];
+      er[i] = L.te[i];
+    }
     const int c = l;
     for (int rnd = 0; rnd <= maxr; ++rnd) {
       if (c < R && L.rnk[c] == rnd) {
@@ -428,39 +489,37 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
 #pragma unroll
         for (int i = 0; i < NMAX; ++i) x[i] = (i < n) ? start_entry(i, c) : 0.f;
         for (int it = 0; it < kInvIters; ++it) {
-          // factor T - lc I with partial pivoting while eliminating x
+          // factor T - lc I with partial pivoting while eliminating x; the
+          // reciprocal pivot is stored
           float a = dr[0] - lc, b1 = er[0], b2 = 0.f, rr = x[0];
 #pragma unroll
           for (int i = 0; i + 1 < NMAX; ++i) {
-            if (i + 1 < n) {
-              const float lw = er[i];
-              const float ap = dr[i + 1] - lc;
-              const float b1p = er[i + 1 < NMAX ? i + 1 : i];
-              const float b1q = (i + 2 < n) ? b1p : 0.f;
-              const float rp = x[i + 1];
-              const bool sw = fabsf(lw) > fabsf(a);
-              const float pa = sw ? lw : ((a != 0.f) ? a : tiny);
-              const float f1 = sw ? ap : b1, f2 = sw ? b1q : b2, fr = sw ? rp : rr;
-              L.F[i * R + c] = make_float4(pa, f1, f2, fr);
-              const float mm = sw ? a / lw : lw / pa;
-              const float na = sw ? (b1 - mm * ap) : (ap - mm * b1);
-              const float nb1 = sw ? (b2 - mm * b1q) : (b1q - mm * b2);
-              const float nr = sw ? (rr - mm * rp) : (rp - mm * rr);
-              a = na; b1 = nb1; b2 = 0.f; rr = nr;
-            }
+            const float lw = er[i];
+            const float ap = dr[i + 1] - lc;
+            const float b1p = (i + 2 < NMAX) ? er[i + 1] : 0.f;
+            const float rp = x[i + 1];
+            const bool sw = fabsf(lw) > fabsf(a);
+            const float pa = sw ? lw : ((a != 0.f) ? a : tiny);
+            const float ipa = __builtin_amdgcn_rcpf(pa);
+            const float f1 = sw ? ap : b1, f2 = sw ? b1p : b2, fr = sw ? rp : rr;
+            L.F[i * R + c] = make_float4(ipa, f1, f2, fr);
+            const float mm = sw ? a * ipa : lw * ipa;
+            const float na = sw ? (b1 - mm * ap) : (ap - mm * b1);
+            const float nb1 = sw ? (b2 - mm * b1p) : (b1p - mm * b2);
+            const float nr = sw ? (rr - mm * rp) : (rp - mm * rr);
+            a = na; b1 = nb1; b2 = 0.f; rr = nr;
           }
-          L.F[(n - 1) * R + c] = make_float4((a != 0.f) ? a : tiny, 0.f, 0.f, rr);
+          L.F[(NMAX - 1) * R + c] =
+              make_float4(__builtin_amdgcn_rcpf((a != 0.f) ? a : tiny), 0.f, 0.f, rr);
           float x1 = 0.f, x2 = 0.f, mx = 0.f;
 #pragma unroll
           for (int i = NMAX - 1; i >= 0; --i) {
-            if (i < n) {
-              const float4 f = L.F[i * R + c];
-              const float xi = (f.w - f.y * x1 - f.z * x2) / f.x;
-              x[i] = xi;
-              mx = fmaxf(mx, fabsf(xi));
-              x2 = x1;
-              x1 = xi;
-            }
+            const float4 f = L.F[i * R + c];
+            const float xi = (f.w - f.y * x1 - f.z * x2) * f.x;
+            x[i] = xi;
+            mx = fmaxf(mx, fabsf(xi));
+            x2 = x1;
+            x1 = xi;
           }
           if (!(mx > 0.f) || !(mx < 3.0e38f)) {
 #pragma unroll
@@ -502,6 +561,39 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
     }
   }
 
+  // one modified Gram-Schmidt pass over the R eigenvectors of T (lane c
+  // owns vector c; the current pivot vector is broadcast through cb)
+  {
+    float x[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) x[i] = (l < R && i < n) ? L.XR[i * R + l] : 0.f;
+    for (int c0 = 0; c0 < R; ++c0) {
+      if (l == c0) {
+#pragma unroll
+        for (int i = 0; i < NMAX; ++i) L.cb[i] = x[i];
+      }
+      __syncthreads();
+      float xb[NMAX];
+      float nrm2 = 0.f, dt = 0.f;
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i) {
+        xb[i] = L.cb[i];
+        nrm2 += xb[i] * xb[i];
+        dt += x[i] * xb[i];
+      }
+      const float inv2 = nrm2 > 0.f ? 1.f / nrm2 : 0.f;
+      const float f = (l > c0 && l < R) ? dt * inv2 : 0.f;
+      const float sc = (l == c0) ? (nrm2 > 0.f ? 1.f / sqrtf(nrm2) : 0.f) : 1.f;
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i) x[i] = (x[i] - f * xb[i]) * sc;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i)
+      if (l < R && i < n) L.XR[i * R + l] = x[i];
+  }
+  __syncthreads();
+
   // ---- G + H: X_R = Q Y; P2 = D R^T X_R; T' = D^-1 R^-1 X_R ---------------
   {
     constexpr int CH = NMAX / 2;
@@ -522,113 +614,92 @@ __global__ __launch_bounds__(64) void compress_wave_kernel(float* __restrict__ U
 #pragma unroll
       for (int s = 0; s < CH; ++s) y[s] -= dt * L.G[k * LDN + part * CH + s];
     }
+    // P2 = D R^T X_R (R is exactly upper triangular in Rb)
     float* P2 = reinterpret_cast<float*>(L.F);
     for (int j = 0; j < n; ++j) {
       float pd = 0.f;
 #pragma unroll
-      for (int s = 0; s < CH; ++s) {
-        const int i = part * CH + s;
-        const float rij = L.Rb[j * LDN + i];          // R[i][j], zero below the diagonal
-        pd += (i <= j ? rij : 0.f) * y[s];
-      }
+      for (int s = 0; s < CH; ++s) pd += L.Rb[j * LDN + part * CH + s] * y[s];   // R[i][j]
       pd += __shfl_xor(pd, 32);
       if (colok && part == 0) P2[j * R + c] = L.dv[j] * pd;
     }
-    // back substitution R t = x, column by column
+    // back substitution R t = x, column-oriented; the part owning row i
+    // stores t_i / d_i (the row of T') into XR
     for (int i = n - 1; i >= 0; --i) {
-      const int own = i / CH, si = i % CH;
-      float yi = 0.f;
-#pragma unroll
-      for (int s = 0; s < CH; ++s) yi = (s == si) ? y[s] : yi;
+      const int own = i / CH, si = i - own * CH;
+      float yi = pick(y, si);
       yi = __shfl(yi, c + 32 * own);
       const float rii = L.Rb[i * LDN + i];
       const float ti = rii != 0.f ? yi / rii : 0.f;
-#pragma unroll
-      for (int s = 0; s < CH; ++s) {
-        const int m2 = part * CH + s;
-        const float rmi = L.Rb[i * LDN + m2];         // R[m2][i]
-        const float upd = y[s] - rmi * ti;
-        y[s] = (m2 < i) ? upd : ((m2 == i) ? ti : y[s]);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < CH; ++s) {
-      const int i = part * CH + s;
-      if (colok && i < n) {
+      if (colok && part == own) {
         const float di = L.dv[i];
-        L.XR[i * R + c] = di > 0.f ? y[s] / di : 0.f;
+        L.XR[i * R + c] = di > 0.f ? ti / di : 0.f;
       }
+#pragma unroll
+      for (int s = 0; s < CH; ++s) y[s] -= L.Rb[i * LDN + part * CH + s] * ti;   // R[m][i]
     }
   }
   __syncthreads();
 
-  // ---- I: U' = U T', V' = V P2 -------------------------------------------
-  // Each lane owns rows l + 64 mu of U and V; all n entries of its rows are
-  // loaded in one batch, then combined with T' / P2 (broadcast from LDS).
+  // ---- I: U' = U T', V' = V P2 as MFMA products --------------------------
+  // Tile E covers rows 16 E .. 16 E + 15 of the factor; every read of those
+  // rows happens before they are overwritten, and no tile reads another
+  // tile's rows, so the products can be written in place.
   {
-    constexpr int MU = DK / 64;
-    constexpr int JC = 8;
-    float acc[MU][RMAX];
-#pragma unroll
-    for (int mu = 0; mu < MU; ++mu)
-#pragma unroll
-      for (int cc = 0; cc < RMAX; ++cc) acc[mu][cc] = 0.f;
-    for (int j0 = 0; j0 < n; j0 += JC) {
-      float uj[JC][MU];
-#pragma unroll
-      for (int jj = 0; jj < JC; ++jj)
-#pragma unroll
-        for (int mu = 0; mu < MU; ++mu)
-          uj[jj][mu] = (j0 + jj < n) ? Uh[(size_t)(j0 + jj) * DK + l + 64 * mu] : 0.f;
-#pragma unroll
-      for (int jj = 0; jj < JC; ++jj) {
-        const int j = j0 + jj < n ? j0 + jj : 0;
-#pragma unroll
-        for (int cc = 0; cc < RMAX; ++cc) {
-          const float tj = (cc < R) ? L.XR[j * R + (cc < R ? cc : 0)] : 0.f;
-#pragma unroll
-          for (int mu = 0; mu < MU; ++mu) acc[mu][cc] += uj[jj][mu] * tj;
-        }
-      }
-    }
-#pragma unroll
-    for (int cc = 0; cc < RMAX; ++cc)
-      if (cc < R)
-#pragma unroll
-        for (int mu = 0; mu < MU; ++mu) Uh[(size_t)cc * DK + l + 64 * mu] = acc[mu][cc];
-  }
-  {
-    constexpr int MV = DV / 64;
+    const int ci = l & 15, kk = l >> 4;
+    constexpr int NK = NMAX / 4;
+    constexpr int NC = RMAX / 16;
     const float* P2 = reinterpret_cast<const float*>(L.F);
-    constexpr int JC = 8;
-    float acc[MV][RMAX];
 #pragma unroll
-    for (int mv = 0; mv < MV; ++mv)
+    for (int E = 0; E < DK / 16; ++E) {
+      f4v acc[NC];
 #pragma unroll
-      for (int cc = 0; cc < RMAX; ++cc) acc[mv][cc] = 0.f;
-    for (int j0 = 0; j0 < n; j0 += JC) {
-      float vj[JC][MV];
+      for (int C = 0; C < NC; ++C) acc[C] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jj = 0; jj < JC; ++jj)
+      for (int K = 0; K < NK; ++K) {
+        const int j = K * 4 + kk;
+        const float av = (j < n) ? Uh[(size_t)j * DK + E * 16 + ci] : 0.f;   // U[e][j]
 #pragma unroll
-        for (int mv = 0; mv < MV; ++mv)
-          vj[jj][mv] = (j0 + jj < n) ? Vh[(size_t)(j0 + jj) * DV + l + 64 * mv] : 0.f;
+        for (int C = 0; C < NC; ++C) {
+          const int cc = C * 16 + ci;
+          const float bv = (j < n && cc < R) ? L.XR[j * R + cc] : 0.f;    // T'[j][cc]
+          acc[C] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[C], 0, 0, 0);
+        }
+      }
 #pragma unroll
-      for (int jj = 0; jj < JC; ++jj) {
-        const int j = j0 + jj < n ? j0 + jj : 0;
+      for (int C = 0; C < NC; ++C) {
+        const int cc = C * 16 + ci;
+        if (cc < R) {
 #pragma unroll
-        for (int cc = 0; cc < RMAX; ++cc) {
-          const float pj = (cc < R) ? P2[j * R + (cc < R ? cc : 0)] : 0.f;
-#pragma unroll
-          for (int mv = 0; mv < MV; ++mv) acc[mv][cc] += vj[jj][mv] * pj;
+          for (int r = 0; r < 4; ++r) Uh[(size_t)cc * DK + E * 16 + 4 * kk + r] = acc[C][r];
         }
       }
     }
 #pragma unroll
-    for (int cc = 0; cc < RMAX; ++cc)
-      if (cc < R)
+    for (int E = 0; E < DV / 16; ++E) {
+      f4v acc[NC];
 #pragma unroll
-        for (int mv = 0; mv < MV; ++mv) Vh[(size_t)cc * DV + l + 64 * mv] = acc[mv][cc];
+      for (int C = 0; C < NC; ++C) acc[C] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int K = 0; K < NK; ++K) {
+        const int j = K * 4 + kk;
+        const float av = (j < n) ? Vh[(size_t)j * DV + E * 16 + ci] : 0.f;   // V[e][j]
+#pragma unroll
+        for (int C = 0; C < NC; ++C) {
+          const int cc = C * 16 + ci;
+          const float bv = (j < n && cc < R) ? P2[j * R + cc] : 0.f;       // P2[j][cc]
+          acc[C] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[C], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int C = 0; C < NC; ++C) {
+        const int cc = C * 16 + ci;
+        if (cc < R) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Vh[(size_t)cc * DV + E * 16 + 4 * kk + r] = acc[C][r];
+        }
+      }
+    }
   }
 }
 
