@@ -21,7 +21,8 @@ from collections import defaultdict
 
 GROUPS = {
     "seed_step_kernel": r"seed_step_kernel<",
-    "compress_kernel": r"compress_kernel<",
+    "compress_kernel (one wave per unit)": r"compress_wave_kernel<",
+    "compress_kernel (workgroup Jacobi)": r"::compress_kernel<",
     "from_dense_kernel": r"from_dense_kernel<",
     "dense_step_kernel": r"dense_step_kernel<",
 }
@@ -102,8 +103,8 @@ def main() -> int:
 
     fetch, nf = mean_kib(args.fetch, args.kernel, "FETCH_SIZE")
     write, nw = mean_kib(args.write, args.kernel, "WRITE_SIZE")
-    cf, _ = mean_kib(args.copy_fetch, r"copy|elementwise", "FETCH_SIZE")
-    cw, _ = mean_kib(args.copy_write, r"copy|elementwise", "WRITE_SIZE")
+    cf, _ = mean_kib(args.copy_fetch, r"copyBuffer", "FETCH_SIZE")
+    cw, _ = mean_kib(args.copy_write, r"copyBuffer", "WRITE_SIZE")
     f_scale = args.copy_bytes / (cf * 1024.0)
     w_scale = args.copy_bytes / (cw * 1024.0)
     hbm = fetch * 1024.0 * f_scale + write * 1024.0 * w_scale
