@@ -7,7 +7,10 @@ workload: the fused read-out + exact update kernel, plus the compression of
 all units whenever R + W columns are held (every W steps), exactly as a
 served decode loop would run them.  Inputs for every timed step are drawn
 before timing and are resident in HBM; the state starts from a dense
-prefill converted to the shallow form (both untimed).
+prefill converted to the shallow form (both untimed).  Every kernel is
+launched from Python through the C ABI; --graphs replays HIP graphs
+captured from the same calls instead (one per run of step launches, one
+per compression).
 
 The metric is decode head-steps/s (whole job).  Also reported: the step
 kernel's achieved HBM bandwidth from its algorithmic bytes and its average
@@ -101,64 +104,111 @@ def prepare(w: wl.Workload, layer: int, n_steps: int, dev: str):
     return vbar, S, st, inputs
 
 
-def run_shallow(st, inputs, o, warmup: int, steps: int):
-    """Warm up, then time `steps` steps.
+def _plan(st, warmup: int, steps: int):
+    """The timed loop as a list of actions: ("steps", [(t, r), ...]) for each
+    run of step launches between two compressions, ("compress", r) for each
+    compression."""
+    seq, cur, r = [], [], st.r
+    for t in range(warmup, warmup + steps):
+        cur.append((t, r))
+        r += 1
+        if r >= st.cap:
+            seq.append(("steps", cur))
+            cur = []
+            seq.append(("compress", r))
+            r = st.R
+    if cur:
+        seq.append(("steps", cur))
+    return seq, r
 
-    HIP events (on the launch stream) bracket each run of consecutive step
-    launches between two compressions, and each compression, so no event
-    marker sits between two step kernels."""
+
+def _do(st, inputs, o, action) -> None:
+    if action[0] == "steps":
+        for t, r in action[1]:
+            x = inputs[t]
+            binding.seed_decode_step(st.rule, st.a, st.U, st.V, st.vbar, x["q"], x["k"], x["v"],
+                                     x["g"], x["beta"], o, r)
+    else:
+        binding.seed_compress(st.U, st.V, action[1], st.R)
+
+
+def run_shallow(st, inputs, o, warmup: int, steps: int, graphs: bool):
+    """Warm up eagerly, then time `steps` steps.
+
+    With `graphs`, each run of step launches between two compressions and
+    each compression is captured once as a HIP graph (untimed) and replayed
+    in the timed loop, so host launch cost does not enter the timing.  HIP
+    events on the launch stream bracket every action; no event marker sits
+    between two step kernels."""
     for t in range(warmup):
         x = inputs[t]
         st.step_and_maybe_compress(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
     torch.cuda.synchronize()
+    seq, r_end = _plan(st, warmup, steps)
+    captured = []
+    if graphs:
+        for action in seq:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                _do(st, inputs, o, action)
+            captured.append(g)
+        torch.cuda.synchronize()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    windows, comp_ev, step_r = [], [], []
-    t_begin, t_end = ev(), ev()
+    marks = [ev() for _ in range(len(seq) + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_begin.record()
-    w0, n_in_window = ev(), 0
-    w0.record()
-    for t in range(warmup, warmup + steps):
-        x = inputs[t]
-        step_r.append(st.r)
-        st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-        n_in_window += 1
-        if st.r >= st.cap:
-            w1 = ev()
-            w1.record()
-            windows.append((w0, w1, n_in_window))
-            st.compress()
-            w0, n_in_window = ev(), 0
-            w0.record()
-            comp_ev.append((w1, w0))
-    if n_in_window:
-        w1 = ev()
-        w1.record()
-        windows.append((w0, w1, n_in_window))
-    t_end.record()
+    for i, action in enumerate(seq):
+        marks[i].record()
+        if graphs:
+            captured[i].replay()
+        else:
+            _do(st, inputs, o, action)
+    marks[-1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    st.r = r_end
+    windows, comp, step_r = [], [], []
+    for i, action in enumerate(seq):
+        ms = marks[i].elapsed_time(marks[i + 1])
+        if action[0] == "steps":
+            windows.append((ms, len(action[1])))
+            step_r += [r for _, r in action[1]]
+        else:
+            comp.append(ms)
     return {
-        "elapsed_s": t_begin.elapsed_time(t_end) / 1e3,
+        "elapsed_s": marks[0].elapsed_time(marks[-1]) / 1e3,
         "wall_s": wall,
-        "step_window_ms": [(a.elapsed_time(b), n) for a, b, n in windows],
+        "step_window_ms": windows,
         "step_r": step_r,
-        "compress_ms": [a.elapsed_time(b) for a, b in comp_ev],
+        "compress_ms": comp,
     }
 
 
-def run_dense(w, S, inputs, o, warmup: int, steps: int):
-    for t in range(warmup):
-        x = inputs[t]
-        binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+def run_dense(w, S, inputs, o, warmup: int, steps: int, graphs: bool, chunk: int = 32):
+    def do(ts):
+        for t in ts:
+            x = inputs[t]
+            binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+
+    do(range(warmup))
     torch.cuda.synchronize()
+    chunks = [range(c, min(c + chunk, warmup + steps)) for c in range(warmup, warmup + steps, chunk)]
+    captured = []
+    if graphs:
+        for ts in chunks:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                do(ts)
+            captured.append(g)
+        torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for t in range(warmup, warmup + steps):
-        x = inputs[t]
-        binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+    for i, ts in enumerate(chunks):
+        if graphs:
+            captured[i].replay()
+        else:
+            do(ts)
     t1.record()
     torch.cuda.synchronize()
     return {"elapsed_s": t0.elapsed_time(t1) / 1e3}
@@ -219,6 +269,9 @@ def main() -> int:
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--graphs", action="store_true",
+                    help="replay HIP graphs captured from the same calls instead of launching "
+                         "every kernel from Python")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -262,12 +315,12 @@ def main() -> int:
 
     S_copy = S_dense.clone() if not args.no_dense else None
     o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
-    res = run_shallow(st, inputs, o, warmup, steps)
+    res = run_shallow(st, inputs, o, warmup, steps, graphs=args.graphs)
     log(f"shallow: {res['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
 
     dense = None
     if not args.no_dense:
-        dres = run_dense(w, S_copy, inputs, o, warmup, steps)
+        dres = run_dense(w, S_copy, inputs, o, warmup, steps, graphs=args.graphs)
         d_bytes = dense_bytes_per_unit(w) * units
         d_avg = dres["elapsed_s"] / steps
         dense = {"value": units * steps / dres["elapsed_s"], "unit": "head-steps/s",
@@ -308,7 +361,9 @@ def main() -> int:
         "config": {"workload": w.name, "rule": w.rule, "requests": w.batch, "heads": w.heads,
                    "layers_per_launch": 1, "d_k": w.d_k, "d_v": w.d_v, "R": w.R, "W": w.W,
                    "inputs": "bf16 q/k/v, fp32 gates" if w.in_dtype == torch.bfloat16 else "fp32",
-                   "prefill": w.prefill},
+                   "prefill": w.prefill,
+                   "launch": ("hip graphs (one per run of steps, one per compression)" if args.graphs
+                              else "eager (one launch per kernel)")},
         "roofline": {"bound": "hbm", "kernel": "seed_step_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,

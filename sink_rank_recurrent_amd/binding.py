@@ -72,26 +72,35 @@ def _check(fn: str, status: int) -> None:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device_index: int):
+    """Handle of `stream`, else of torch's current stream on the tensors' device."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device_index)
+    return torch.cuda.current_stream(device_index).cuda_stream
 
 
 def _need(t: torch.Tensor, name: str, shape: tuple, dtypes) -> None:
+    # one combined test on the hot path; the detailed message only on failure
+    if (isinstance(t, torch.Tensor) and t.is_cuda and t.shape == shape and t.dtype in dtypes
+            and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be in device memory (got {t.device})")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    raise ValueError(f"{name} must be contiguous")
 
 
 _F32 = (torch.float32,)
@@ -121,7 +130,7 @@ def seed_decode_step(rule: str, a, U, V, vbar, q, k, v, g, beta, o, r: int, stre
     _need(o, "o", (B, H, d_v), _F32)
     st = lib().seed_decode_step(RULES[rule], B, H, d_k, d_v, cap, int(r), _ptr(a), _ptr(U),
                                 _ptr(V), _ptr(vbar), _ptr(q), _ptr(k), _ptr(v), _in_dtype(q, k, v),
-                                _ptr(g), _ptr(beta), _ptr(o), _stream(stream))
+                                _ptr(g), _ptr(beta), _ptr(o), _stream(stream, U.device.index))
     _check("seed_decode_step", st)
 
 
@@ -132,7 +141,7 @@ def seed_compress(U, V, r: int, R: int, stream=None) -> None:
     _need(U, "U", (B, H, cap, d_k), _F32)
     _need(V, "V", (B, H, cap, d_v), _F32)
     st = lib().seed_compress(B, H, d_k, d_v, cap, int(r), int(R), _ptr(U), _ptr(V),
-                             _stream(stream))
+                             _stream(stream, U.device.index))
     _check("seed_compress", st)
 
 
@@ -146,7 +155,7 @@ def seed_state_from_dense(S, vbar, a, U, V, R: int, stream=None) -> None:
     _need(U, "U", (B, H, cap, d_k), _F32)
     _need(V, "V", (B, H, cap, d_v), _F32)
     st = lib().seed_state_from_dense(B, H, d_k, d_v, cap, int(R), _ptr(S), _ptr(vbar), _ptr(a),
-                                     _ptr(U), _ptr(V), _stream(stream))
+                                     _ptr(U), _ptr(V), _stream(stream, U.device.index))
     _check("seed_state_from_dense", st)
 
 
@@ -162,7 +171,8 @@ def dense_decode_step(rule: str, S, q, k, v, g, beta, o, stream=None) -> None:
         _need(beta, "beta", (B, H), _F32)
     _need(o, "o", (B, H, d_v), _F32)
     st = lib().dense_decode_step(RULES[rule], B, H, d_k, d_v, _ptr(S), _ptr(q), _ptr(k), _ptr(v),
-                                 _in_dtype(q, k, v), _ptr(g), _ptr(beta), _ptr(o), _stream(stream))
+                                 _in_dtype(q, k, v), _ptr(g), _ptr(beta), _ptr(o),
+                                 _stream(stream, S.device.index))
     _check("dense_decode_step", st)
 
 

@@ -1,30 +1,17 @@
-// Compression of the factors to rank R, and conversion of dense states to
-// the shallow form.
+// Conversion of dense states to the shallow form at the end of the prefill.
 //
-// What is computed.  Every W steps the content U V^T is replaced by its best
-// rank-R approximation; the sink is left alone (SEED figures and tables on
-// thelatestinai.com, Fig. 1 (b) caption; sungsoo.github.io summary, method
-// list, "Decode").  At the end of the prefill a dense state S is split into
-// its sink a = S vbar/|vbar|^2 (Fig. 3 (b)) and content C = S - a vbar^T,
-// which is truncated the same way (Fig. 1 (a) caption).
+// What is computed.  A dense state S is split into its sink
+// a = S vbar/|vbar|^2 (SEED figures and tables on thelatestinai.com,
+// Fig. 3 (b)) and content C = S - a vbar^T, which is truncated to its best
+// rank-R approximation (Fig. 1 (a) caption): U = top-R left singular
+// vectors of C, V = C^T U.
 //
 // How (one 256-thread workgroup per unit, everything small lives in LDS):
-//   M = U V^T with U d_k x n, V d_v x n, n = R + W columns.  The top-R left
-//   singular subspace of M is the top-R eigenspace of M M^T restricted to
-//   span(U).  With U = Q_U R_U:
-//     G_U = U^T U = R_U^T R_U        (column-equilibrated Cholesky, fp32)
-//     H   = R_U (V^T V) R_U^T        (n x n, symmetric PSD, eigenvalues s^2)
-//     H   = X diag(s^2) X^T          (cyclic Jacobi, parallel ordering)
-//     U'  = U R_U^{-1} X_R           (orthonormal)
-//     V'  = M^T U' = V R_U^T X_R     (so U' V'^T = P_R M, the truncation)
-//   Only the separation of the top-R eigenvectors from the rest matters for
-//   U' V'^T, so the sweeps stop once every rotation angle coupling the two
-//   sets, |H_ij| / (H_ii - H_jj), is below 1e-5.  U is well conditioned
-//   (orthonormal columns plus unit-norm keys, all decayed), so forming
-//   U^T U in fp32 is safe; V, which may be badly conditioned, never goes
-//   through a factorisation.  Columns of U that are (numerically) in the
-//   span of the previous ones get a zero pivot and drop out exactly.
-//   For the dense conversion U = I (n = d_k) and H = C C^T directly.
+// H = C C^T (d_k x d_k) is diagonalised by cyclic Jacobi with parallel
+// ordering.  Only the separation of the top-R eigenvectors from the rest
+// matters for U V^T, so the sweeps stop once every rotation angle coupling
+// the two sets, |H_ij| / (H_ii - H_jj), is below 1e-5.  This runs once per
+// request; the per-step compression lives in seed_compress_wave.h.
 #include "seed_device.h"
 #include "seed_launch.h"
 
@@ -35,20 +22,15 @@ namespace {
 constexpr int kNT = 256;
 constexpr int kRMax = 32;           // largest rank kept
 constexpr int kChunk = 32;          // rows staged per Gram pass
-constexpr float kPivotTol = 1e-5f;  // relative pivot below which a column is dependent
 constexpr float kRotTol = 1e-6f;    // rotate when |h_pq| > kRotTol sqrt(h_pp h_qq)
 constexpr float kAngleTol = 1e-5f;  // top-R / rest coupling angle at convergence
 constexpr int kMaxSweeps = 15;
 
 struct Lds {
   int np, ld;     // padded order (even) and row stride
-  float* A;       // [np][ld]  G_U, then the Cholesky factor R (upper)
   float* H;       // [np][ld]  G_V, then the core H (Jacobi works here)
   float* X;       // [max(np,kChunk)][ld]  Gram staging, then P, then eigenvectors
   float* T;       // [np][R]   X_R, then R^{-1} X_R scaled
-  float* P2;      // [np][R]   R^T X_R scaled (compression only)
-  float* dvec;    // [np]      column norms of U (equilibration)
-  float* rrow;    // [np]      scaled Cholesky row
   float* cs;      // [np]      (c, s) per pair
   int* pq;        // [np]      (p, q) per pair
   int* rank;      // [np]      descending rank of H_ii
@@ -58,36 +40,28 @@ struct Lds {
 
 __host__ __device__ inline int padded(int n) { return n + (n & 1); }
 
-__host__ __device__ inline size_t lds_floats(int np, int R, bool with_A) {
+__host__ __device__ inline size_t lds_floats(int np, int R) {
   const int ld = np + 1;
   const int xrows = np > kChunk ? np : kChunk;
   size_t f = 0;
-  if (with_A) f += (size_t)np * ld;      // A
   f += (size_t)np * ld;                   // H
   f += (size_t)xrows * ld;                // X
   f += (size_t)np * R;                    // T
-  if (with_A) f += (size_t)np * R;        // P2 (compression only)
-  f += 4 * (size_t)np;                    // dvec, rrow, cs, pq
+  f += 2 * (size_t)np;                    // cs, pq
   f += np;                                // rank
   f += 256 + 4;                           // aux, flag
   return f;
 }
 
-__device__ inline Lds carve(float* base, int n, int R, bool with_A) {
+__device__ inline Lds carve(float* base, int n, int R) {
   Lds L;
   L.np = padded(n);
   L.ld = L.np + 1;
   const int xrows = L.np > kChunk ? L.np : kChunk;
   float* p = base;
-  L.A = nullptr;
-  if (with_A) { L.A = p; p += (size_t)L.np * L.ld; }
   L.H = p; p += (size_t)L.np * L.ld;
   L.X = p; p += (size_t)xrows * L.ld;
   L.T = p; p += (size_t)L.np * R;
-  L.P2 = nullptr;
-  if (with_A) { L.P2 = p; p += (size_t)L.np * R; }
-  L.dvec = p; p += L.np;
-  L.rrow = p; p += L.np;
   L.cs = p; p += L.np;
   L.pq = reinterpret_cast<int*>(p); p += L.np;
   L.rank = reinterpret_cast<int*>(p); p += L.np;
@@ -147,48 +121,6 @@ __device__ __forceinline__ void gram_dispatch(ColFn col, int n, int d, float* ou
   else if (bs <= 4) gram<4>(col, n, d, out, ld, stage);
   else if (bs <= 6) gram<6>(col, n, d, out, ld, stage);
   else gram<8>(col, n, d, out, ld, stage);
-}
-
-// Column-equilibrated Cholesky of the Gram matrix in L.A (n x n):
-// G = D R^T R D with D = diag(dvec); leaves R (upper) in L.A, zero below the
-// diagonal and in the padding.  Pivots below kPivotTol mark dependent
-// columns: their row of R is zero.
-__device__ __forceinline__ void cholesky_equilibrated(const Lds& L, int n) {
-  const int tid = threadIdx.x;
-  float* A = L.A;
-  const int ld = L.ld, np = L.np;
-  for (int i = tid; i < np; i += kNT) {
-    const float dii = i < n ? A[i * ld + i] : 0.f;
-    L.dvec[i] = dii > 0.f ? sqrtf(dii) : 0.f;
-  }
-  __syncthreads();
-  for (int w = tid; w < np * np; w += kNT) {
-    const int i = w / np, j = w % np;
-    const float di = L.dvec[i], dj = L.dvec[j];
-    A[i * ld + j] = (i < n && j < n && di > 0.f && dj > 0.f) ? A[i * ld + j] / (di * dj) : 0.f;
-  }
-  __syncthreads();
-  for (int j = 0; j < n; ++j) {
-    const float piv = A[j * ld + j];
-    const bool ok = piv > kPivotTol;
-    const float p = ok ? sqrtf(piv) : 0.f;
-    const float inv = ok ? 1.f / p : 0.f;
-    for (int i = j + 1 + tid; i < n; i += kNT) L.rrow[i] = A[j * ld + i] * inv;
-    __syncthreads();
-    const int m = n - j - 1;
-    for (int w = tid; w < m * m; w += kNT) {
-      const int i = j + 1 + w / m, l = j + 1 + w % m;
-      if (l >= i) A[i * ld + l] -= L.rrow[i] * L.rrow[l];
-    }
-    for (int i = j + 1 + tid; i < n; i += kNT) A[j * ld + i] = L.rrow[i];
-    if (tid == 0) A[j * ld + j] = p;
-    __syncthreads();
-  }
-  for (int w = tid; w < np * np; w += kNT) {
-    const int i = w / np, j = w % np;
-    if (j < i || i >= n || j >= n) A[i * ld + j] = 0.f;
-  }
-  __syncthreads();
 }
 
 __device__ inline void rr_pair(int t, int i, int np, int& p, int& q) {
@@ -330,113 +262,6 @@ __device__ __forceinline__ void select_top(const Lds& L, int n, int R) {
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void compress_kernel(float* __restrict__ U,
-                                                        float* __restrict__ V, int cap, int n,
-                                                        int R) {
-  extern __shared__ float smem[];
-  const Lds L = carve(smem, n, R, true);
-  const int tid = threadIdx.x;
-  const int np = L.np, ld = L.ld;
-  const size_t ub = blockIdx.x;
-  float* Uh = U + ub * cap * DK;
-  float* Vh = V + ub * cap * DV;
-
-  // Gram matrices
-  gram_dispatch([=](int j, int e) { return Uh[(size_t)j * DK + e]; }, n, DK, L.A, ld, L.X);
-  gram_dispatch([=](int j, int e) { return Vh[(size_t)j * DV + e]; }, n, DV, L.H, ld, L.X);
-  __syncthreads();
-
-  cholesky_equilibrated(L, n);
-
-  // G~_V = D G_V D, then P = G~_V R^T (into X), then H = R P (upper, mirrored)
-  for (int w = tid; w < n * n; w += kNT) {
-    const int i = w / n, j = w % n;
-    L.H[i * ld + j] *= L.dvec[i] * L.dvec[j];
-  }
-  __syncthreads();
-  for (int w = tid; w < n * n; w += kNT) {
-    const int i = w / n, j = w % n;
-    float acc = 0.f;
-    for (int l = j; l < n; ++l) acc += L.H[i * ld + l] * L.A[j * ld + l];
-    L.X[i * ld + j] = acc;
-  }
-  __syncthreads();
-  for (int w = tid; w < np * np; w += kNT) {
-    const int i = w / np, j = w % np;
-    if (i > j) continue;
-    float acc = 0.f;
-    if (j < n)
-      for (int l = i; l < n; ++l) acc += L.A[i * ld + l] * L.X[l * ld + j];
-    L.H[i * ld + j] = acc;
-    L.H[j * ld + i] = acc;
-  }
-  __syncthreads();
-
-  jacobi(L, R);
-  select_top(L, n, R);
-
-  // P2 = D R^T X_R ;  T = D^-1 R^-1 X_R  (back substitution, zero pivots -> 0)
-  for (int w = tid; w < n * R; w += kNT) {
-    const int j = w / R, c = w % R;
-    float acc = 0.f;
-    for (int i = 0; i <= j; ++i) acc += L.A[i * ld + j] * L.T[i * R + c];
-    L.P2[j * R + c] = L.dvec[j] * acc;
-  }
-  __syncthreads();
-  for (int c = tid; c < R; c += kNT) {
-    for (int i = n - 1; i >= 0; --i) {
-      const float rii = L.A[i * ld + i];
-      float acc = L.T[i * R + c];
-      for (int l = i + 1; l < n; ++l) acc -= L.A[i * ld + l] * L.T[l * R + c];
-      L.T[i * R + c] = rii != 0.f ? acc / rii : 0.f;
-    }
-  }
-  __syncthreads();
-  for (int w = tid; w < n * R; w += kNT) {
-    const int i = w / R;
-    const float di = L.dvec[i];
-    L.T[w] = di > 0.f ? L.T[w] / di : 0.f;
-  }
-  __syncthreads();
-
-  // U' = U T, V' = V P2: read everything, then overwrite columns 0..R-1
-  constexpr int NCU = kNT / DK, NCV = kNT / DV;
-  constexpr int CPT_U = kRMax / NCU, CPT_V = kRMax / NCV;
-  const int eu = tid % DK, cu = tid / DK;
-  const int ev = tid % DV, cv = tid / DV;
-  float accu[CPT_U], accv[CPT_V];
-#pragma unroll
-  for (int m = 0; m < CPT_U; ++m) accu[m] = 0.f;
-#pragma unroll
-  for (int m = 0; m < CPT_V; ++m) accv[m] = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float uj = Uh[(size_t)j * DK + eu];
-    const float vj = Vh[(size_t)j * DV + ev];
-#pragma unroll
-    for (int m = 0; m < CPT_U; ++m) {
-      const int c = cu + NCU * m;
-      if (c < R) accu[m] += uj * L.T[j * R + c];
-    }
-#pragma unroll
-    for (int m = 0; m < CPT_V; ++m) {
-      const int c = cv + NCV * m;
-      if (c < R) accv[m] += vj * L.P2[j * R + c];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < CPT_U; ++m) {
-    const int c = cu + NCU * m;
-    if (c < R) Uh[(size_t)c * DK + eu] = accu[m];
-  }
-#pragma unroll
-  for (int m = 0; m < CPT_V; ++m) {
-    const int c = cv + NCV * m;
-    if (c < R) Vh[(size_t)c * DV + ev] = accv[m];
-  }
-}
-
-template <int DK, int DV>
 __global__ __launch_bounds__(256) void from_dense_kernel(const float* __restrict__ S,
                                                           const float* __restrict__ vbar,
                                                           float* __restrict__ a,
@@ -445,7 +270,7 @@ __global__ __launch_bounds__(256) void from_dense_kernel(const float* __restrict
                                                           int cap, int R) {
   extern __shared__ float smem[];
   const int n = DK;
-  const Lds L = carve(smem, n, R, false);
+  const Lds L = carve(smem, n, R);
   const int tid = threadIdx.x;
   const int ld = L.ld;
   const size_t ub = blockIdx.x;
@@ -518,15 +343,6 @@ hipError_t set_lds(K kernel, size_t bytes) {
 }
 
 template <int DK, int DV>
-hipError_t compress_go(int units, int cap, int n, int R, float* U, float* V, hipStream_t s) {
-  const size_t bytes = compress_jacobi_lds_bytes(n, R);
-  hipError_t err = set_lds(compress_kernel<DK, DV>, bytes);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((compress_kernel<DK, DV>), dim3(units), dim3(kNT), bytes, s, U, V, cap, n, R);
-  return hipGetLastError();
-}
-
-template <int DK, int DV>
 hipError_t from_dense_go(int units, int heads, int cap, int R, const float* S, const float* vbar,
                          float* a, float* U, float* V, hipStream_t s) {
   const size_t bytes = from_dense_lds_bytes(DK, R);
@@ -539,22 +355,13 @@ hipError_t from_dense_go(int units, int heads, int cap, int R, const float* S, c
 
 }  // namespace
 
-size_t compress_jacobi_lds_bytes(int n, int R) { return 4 * lds_floats(padded(n), R, true); }
+size_t compress_lds_bytes(int n, int R) { return compress_wave_lds_bytes(n, R); }
 
-size_t compress_lds_bytes(int n, int R) {
-  return n <= kWaveMaxN ? compress_wave_lds_bytes(n, R) : compress_jacobi_lds_bytes(n, R);
-}
-
-size_t from_dense_lds_bytes(int d_k, int R) { return 4 * lds_floats(padded(d_k), R, false); }
+size_t from_dense_lds_bytes(int d_k, int R) { return 4 * lds_floats(padded(d_k), R); }
 
 hipError_t launch_compress(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
                            float* U, float* V, hipStream_t stream) {
-  if (n <= kWaveMaxN) return launch_compress_wave(batch, heads, d_k, d_v, cap, n, R, U, V, stream);
-  const int units = batch * heads;
-  if (d_k == 128 && d_v == 128) return compress_go<128, 128>(units, cap, n, R, U, V, stream);
-  if (d_k == 128 && d_v == 64) return compress_go<128, 64>(units, cap, n, R, U, V, stream);
-  if (d_k == 64 && d_v == 64) return compress_go<64, 64>(units, cap, n, R, U, V, stream);
-  return hipErrorInvalidValue;
+  return launch_compress_wave(batch, heads, d_k, d_v, cap, n, R, U, V, stream);
 }
 
 hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,

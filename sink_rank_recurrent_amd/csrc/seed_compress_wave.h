@@ -1,0 +1,926 @@
+// Compression of the factors to rank R with one or two wave64 per
+// (request, head): the kernel template, instantiated per head shape by
+// seed_compress_wave_<d_k>x<d_v>.hip.
+//
+// Mathematics (SEED figures and tables on thelatestinai.com, Fig. 1 (b)
+// caption: the content U V^T is replaced by its best rank-R approximation,
+// the sink untouched).  With U^T U = R_U^T R_U (n = R + W columns),
+//     H = R_U (V^T V) R_U^T = X diag(s^2) X^T,
+//     U' = U R_U^-1 X_R,   V' = V R_U^T X_R,
+// and U' V'^T is the truncation of U V^T to its R largest singular values.
+// Phases:
+//   A  Gram matrices U^T U and V^T V by v_mfma_f32_16x16x4f32;
+//   B  Cholesky of the column-equilibrated U^T U (D^-1 U^T U D^-1 = R~^T R~,
+//      R_U = R~ D), thread t owning column t;
+//   C  H = R~ (D V^T V D) R~^T by two in-place MFMA products;
+//   D  Householder reduction of H to a tridiagonal T, thread t owning
+//      column t of H in registers; the reflectors go to LDS rows;
+//   E  the R largest eigenvalues of T by multisection on Sturm counts;
+//   F  their eigenvectors by inverse iteration (pivoted tridiagonal solve),
+//      re-orthogonalised inside runs of close eigenvalues, then one modified
+//      Gram-Schmidt pass;
+//   G  back-transform through the reflectors (X_R = Q Y);
+//   H  P2 = D R~^T X_R (MFMA) and T' = D^-1 R~^-1 X_R (back substitution);
+//   I  U' = U T' and V' = V P2 by MFMA, written in place.
+// Every LDS offset is a compile-time constant, so accesses use immediate
+// offsets and 16-byte vector forms.  With one wave the workgroup barriers
+// only order LDS traffic inside the wave.
+#pragma once
+
+#include <atomic>
+
+#include "seed_device.h"
+#include "seed_launch.h"
+
+namespace seed {
+namespace wave {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr float kEps = 1.1920928955078125e-7f;   // 2^-23
+constexpr float kPivTol = 1e-5f;                   // dependent-column threshold (relative)
+// Eigenvalues closer than kClusterTol |T| form a run whose vectors are
+// computed one after another, each re-orthogonalised against the earlier
+// ones of its run.
+constexpr float kClusterTol = 1e-5f;
+constexpr int kInvIters = 2;
+// T is padded to NMAX rows with this diagonal and zero couplings; the padded
+// entries of every solve are exactly 0.
+constexpr float kPadDiag = 1.0e30f;
+
+// ---------------------------------------------------------------------------
+// reductions
+
+// Sum / min / max over the 64 lanes of a wave, returned to every lane: DPP
+// butterflies inside each row of 16 lanes, then one readlane per row.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+struct AddOp { __device__ float operator()(float a, float b) const { return a + b; } };
+struct MinOp { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+struct MaxOp { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+
+// The same over the NW waves of the workgroup; `red` holds one slot of NW
+// partials per call site, and every slot is separated from its next use by
+// a barrier of the surrounding loop.
+template <int NW, typename Op>
+__device__ __forceinline__ float block_reduce(float x, Op op, float* red, int slot) {
+  const float s = wave_reduce(x, op);
+  if constexpr (NW == 1) {
+    return s;
+  } else {
+    if ((threadIdx.x & 63) == 0) red[slot * NW + (threadIdx.x >> 6)] = s;
+    __syncthreads();
+    float r = red[slot * NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) r = op(r, red[slot * NW + w]);
+    return r;
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ bool block_all(bool p, float* red, int slot) {
+  if constexpr (NW == 1) {
+    return __all(p);
+  } else {
+    return block_reduce<NW>(p ? 1.f : 0.f, MinOp(), red, slot) > 0.5f;
+  }
+}
+
+// Sum over groups of P consecutive lanes (P = 2 or 4), returned to the group.
+template <int P>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));
+  if constexpr (P == 4)
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
+  return x;
+}
+
+// Lane `own` of each group of P consecutive lanes, broadcast to the group.
+template <int P, int own>
+__device__ __forceinline__ float group_bcast(float x) {
+  constexpr int ctrl = (P == 4) ? (own | (own << 2) | (own << 4) | (own << 6))
+                                : (own | (own << 2) | ((2 + own) << 4) | ((2 + own) << 6));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float frsq(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float fsqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+// Deterministic start vector of inverse iteration, entries in [0.5, 1.5).
+__device__ __forceinline__ float start_entry(int i, int c) {
+  uint32_t h = (uint32_t)(i + 1) * 2654435761u ^ (uint32_t)(c + 1) * 2246822519u;
+  h ^= h >> 13;
+  h *= 3266489917u;
+  h ^= h >> 16;
+  return (float)(h & 0xFFFFu) * (1.0f / 65536.0f) + 0.5f;
+}
+
+// ---------------------------------------------------------------------------
+// LDS layout (offsets in floats; every region a multiple of 4 floats)
+
+template <int NMAX, int RMAX>
+struct Lay {
+  static constexpr int NW = (NMAX + 63) / 64;     // waves per unit
+  static constexpr int NTH = 64 * NW;
+  static constexpr int LDN = NMAX + 4;             // row stride: 16-byte aligned rows
+  static constexpr int PARTS = NTH / RMAX < 4 ? NTH / RMAX : 4;   // lanes per eigenvector
+  static constexpr int NACT = RMAX * PARTS;        // threads holding eigenvector rows
+  static constexpr int CH = NMAX / PARTS;          // rows per lane
+  static constexpr int G = 0;                      // [NMAX][LDN] Grams, Z, H, then reflectors (row k)
+  static constexpr int RB = G + NMAX * LDN;        // [NMAX][LDN] R~ by columns: RB[m*LDN + i] = R~[i][m]
+  static constexpr int XR = RB + NMAX * LDN;       // [NMAX][RMAX] eigenvectors, Y, then T'
+  static constexpr int FA = XR + NMAX * RMAX;      // [NMAX][RMAX] x 3: solve factors; FA then holds P2
+  static constexpr int FB = FA + NMAX * RMAX;
+  static constexpr int FC = FB + NMAX * RMAX;
+  static constexpr int CB = FC + NMAX * RMAX;      // [NTH] published column
+  static constexpr int VB = CB + NTH;              // [NTH] Householder vector
+  static constexpr int WB = VB + NTH;              // [NTH] rank-2 update vector / Cholesky row
+  static constexpr int CB2 = WB + NTH;             // [2][NMAX] Gram-Schmidt pivot (double buffer)
+  static constexpr int TD = CB2 + 2 * NMAX;        // [NMAX] diagonal of T
+  static constexpr int TE = TD + NMAX;             // [NMAX] off-diagonal of T
+  static constexpr int E2 = TE + NMAX;             // [NMAX] E2[i] = TE[i-1]^2
+  static constexpr int TAU = E2 + NMAX;            // [NMAX]
+  static constexpr int DV = TAU + NMAX;            // [NMAX] column norms d of U
+  static constexpr int IDV = DV + NMAX;            // [NMAX] 1/d
+  static constexpr int IRD = IDV + NMAX;           // [NMAX] 1/R~[i][i]
+  static constexpr int BPT = IRD + NMAX;           // [2 NTH] bisection points
+  static constexpr int BFL = BPT + 2 * NTH;        // [2 NTH] their flags (int)
+  static constexpr int LAM = BFL + 2 * NTH;        // [RMAX] eigenvalues (descending)
+  static constexpr int RNK = LAM + RMAX;           // [RMAX] round of each vector (int)
+  static constexpr int STA = RNK + RMAX;           // [RMAX] first index of its run (int)
+  static constexpr int RED = STA + RMAX;           // [8][NW] cross-wave partials
+  static constexpr int MISC = RED + 8 * NW + (8 * NW) % 4;
+  static constexpr int TOTAL = MISC + 4;
+  static_assert(NMAX % 16 == 0 && NMAX <= 128, "NMAX");
+  static_assert(RMAX == 16 || RMAX == 32, "RMAX");
+};
+
+// ---------------------------------------------------------------------------
+// A: G[i][j] = s_ij sum_e X[e][i] X[e][j] for i, j < NMAX (zero beyond n),
+// s_ij = d_i d_j when SCALE, else 1.  X holds one unit's columns, D entries
+// each.  MFMA 16x16x4: lane l feeds column 16 t + l % 16 of tile t at the
+// k-slot l / 16.  Wave w sums e over [w D / NW, (w + 1) D / NW), slot kk
+// over its quarter of that range; with two waves the partial sums meet in
+// LDS (wave 1 stores, wave 0 adds and stores the total).
+template <int NMAX, int NW, int D, bool SCALE>
+__device__ __forceinline__ void gram(const float* __restrict__ X, int n, float* __restrict__ G,
+                                     const float* __restrict__ dv) {
+  constexpr int LDN = NMAX + 4;
+  constexpr int NT = NMAX / 16;
+  constexpr int NP = NT * (NT + 1) / 2;
+  constexpr int KPL = D / (4 * NW);
+  constexpr int KC = ((NT > 4) ? 8 : 16) < KPL ? ((NT > 4) ? 8 : 16) : KPL;
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ci = l & 15, kk = l >> 4;
+  f4v acc[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) acc[p] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s0 = 0; s0 < KPL; s0 += KC) {
+    float x[NT][KC];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = t * 16 + ci;
+      if (col < n) {
+        const float* src = X + (size_t)col * D + (w * 4 + kk) * KPL + s0;
+#pragma unroll
+        for (int q = 0; q < KC / 4; ++q) {
+          const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * q);
+          x[t][4 * q + 0] = v4.x; x[t][4 * q + 1] = v4.y;
+          x[t][4 * q + 2] = v4.z; x[t][4 * q + 3] = v4.w;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < KC; ++s) x[t][s] = 0.f;
+      }
+    }
+    int p = 0;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = I; J < NT; ++J) {
+#pragma unroll
+        for (int s = 0; s < KC; ++s)
+          acc[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[I][s], x[J][s], acc[p], 0, 0, 0);
+        ++p;
+      }
+  }
+  // lane l holds D[4 (l/16) + r][l % 16] of each 16 x 16 tile
+  if constexpr (NW > 1) {
+    if (w == 1) {
+      int p = 0;
+#pragma unroll
+      for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int J = I; J < NT; ++J) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) G[(I * 16 + 4 * kk + r) * LDN + J * 16 + ci] = acc[p][r];
+          ++p;
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+      // every partial is read before any total is stored (the diagonal
+      // tiles store transposed positions that other lanes still read)
+      int p = 0;
+#pragma unroll
+      for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int J = I; J < NT; ++J) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[p][r] += G[(I * 16 + 4 * kk + r) * LDN + J * 16 + ci];
+          ++p;
+        }
+    }
+  }
+  if (w == 0) {
+    int p = 0;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = I; J < NT; ++J) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = I * 16 + 4 * kk + r, j = J * 16 + ci;
+          float v = acc[p][r];
+          if constexpr (SCALE) v *= dv[i] * dv[j];
+          G[i * LDN + j] = v;
+          G[j * LDN + i] = v;
+        }
+        ++p;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+template <int NMAX, int RMAX, int DK, int DV_>
+__global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
+    float* __restrict__ U, float* __restrict__ V, int cap, int n, int R) {
+  using L = Lay<NMAX, RMAX>;
+  constexpr int NW = L::NW, NTH = L::NTH, LDN = L::LDN;
+  constexpr int PARTS = L::PARTS, CH = L::CH, NACT = L::NACT;
+  extern __shared__ float4 smem4[];
+  float* const sm = reinterpret_cast<float*>(smem4);
+  float* const G = sm + L::G;
+  float* const RB = sm + L::RB;
+  float* const XR = sm + L::XR;
+  float* const FA = sm + L::FA;
+  float* const FB = sm + L::FB;
+  float* const FC = sm + L::FC;
+  float* const CB = sm + L::CB;
+  float* const VB = sm + L::VB;
+  float* const WB = sm + L::WB;
+  float* const CB2 = sm + L::CB2;
+  float* const TD = sm + L::TD;
+  float* const TE = sm + L::TE;
+  float* const E2 = sm + L::E2;
+  float* const TAU = sm + L::TAU;
+  float* const DVs = sm + L::DV;
+  float* const IDV = sm + L::IDV;
+  float* const IRD = sm + L::IRD;
+  float* const BPT = sm + L::BPT;
+  int* const BFL = reinterpret_cast<int*>(sm + L::BFL);
+  float* const LAM = sm + L::LAM;
+  int* const RNK = reinterpret_cast<int*>(sm + L::RNK);
+  int* const STA = reinterpret_cast<int*>(sm + L::STA);
+  float* const RED = sm + L::RED;
+  float* const MISC = sm + L::MISC;
+
+  const int t = threadIdx.x;
+  const bool act = t < NMAX;
+  const size_t ub = blockIdx.x;
+  float* const Uh = U + ub * cap * DK;
+  float* const Vh = V + ub * cap * DV_;
+
+  // R~ (with its zero lower part), the eigenvector block and the published
+  // vectors start at zero
+  for (int i = 4 * t; i < NMAX * LDN; i += 4 * NTH)
+    *reinterpret_cast<float4*>(RB + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 4 * t; i < NMAX * RMAX; i += 4 * NTH)
+    *reinterpret_cast<float4*>(XR + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  CB[t] = 0.f;
+  VB[t] = 0.f;
+  WB[t] = 0.f;
+
+  // @phase A: Gram of U and column norms
+  gram<NMAX, NW, DK, false>(Uh, n, G, nullptr);
+  __syncthreads();
+  if (act) {
+    const float gtt = G[t * LDN + t];
+    const bool pos = t < n && gtt > 0.f;
+    DVs[t] = pos ? fsqrt(gtt) : 0.f;
+    IDV[t] = pos ? frsq(gtt) : 0.f;
+  }
+  __syncthreads();
+  float g[NMAX];
+  {
+    const float it = act ? IDV[t] : 0.f;
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) g[i] = act ? G[i * LDN + t] * it * IDV[i] : 0.f;
+  }
+  __syncthreads();
+  // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
+  gram<NMAX, NW, DV_, true>(Vh, n, G, DVs);
+
+  // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
+  for (int j = 0; j < n; ++j) {
+    if (t == j) {
+#pragma unroll
+      for (int i = 0; i < NMAX; i += 4)
+        *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
+    }
+    __syncthreads();
+    const float gj = CB[t];
+    const float piv = CB[j];
+    const bool ok = piv > kPivTol;
+    const float rp = ok ? frsq(piv) : 0.f;
+    const float r = (t > j) ? gj * rp : 0.f;
+    if (act) {
+      RB[t * LDN + j] = (t == j) ? piv * rp : r;   // R~[j][t]
+      WB[t] = r;
+    }
+    if (t == j) IRD[j] = rp;
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NMAX / 8; ++b) {
+      if (8 * b + 7 > j) {
+        const float4 w0 = *reinterpret_cast<const float4*>(WB + 8 * b);
+        const float4 w1 = *reinterpret_cast<const float4*>(WB + 8 * b + 4);
+        g[8 * b + 0] = fmaf(-w0.x, r, g[8 * b + 0]);
+        g[8 * b + 1] = fmaf(-w0.y, r, g[8 * b + 1]);
+        g[8 * b + 2] = fmaf(-w0.z, r, g[8 * b + 2]);
+        g[8 * b + 3] = fmaf(-w0.w, r, g[8 * b + 3]);
+        g[8 * b + 4] = fmaf(-w1.x, r, g[8 * b + 4]);
+        g[8 * b + 5] = fmaf(-w1.y, r, g[8 * b + 5]);
+        g[8 * b + 6] = fmaf(-w1.z, r, g[8 * b + 6]);
+        g[8 * b + 7] = fmaf(-w1.w, r, g[8 * b + 7]);
+      }
+    }
+  }
+  for (int j = n + t; j < NMAX; j += NTH) IRD[j] = 0.f;
+  __syncthreads();
+
+  // @phase C: Z = R~ G~ in place by column tiles, then H = Z R~^T in place
+  // by row tiles (R~[i][m] = 0 for m < i, so those k-steps are skipped)
+  {
+    constexpr int NT = NMAX / 16;
+    const int l = t & 63, w = t >> 6;
+    const int ci = l & 15, kk = l >> 4;
+#pragma unroll
+    for (int J = 0; J < NT; ++J) {
+      if (J % NW != w) continue;
+      f4v acc[NT];
+#pragma unroll
+      for (int I = 0; I < NT; ++I) acc[I] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int K = 0; K < NMAX / 4; ++K) {
+        const int m = 4 * K + kk;
+        const float bv = G[m * LDN + 16 * J + ci];          // G~[m][j]
+#pragma unroll
+        for (int I = 0; I < NT; ++I) {
+          if (4 * K + 3 < 16 * I) continue;
+          const float av = RB[m * LDN + 16 * I + ci];        // R~[i][m]
+          acc[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[I], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDN + 16 * J + ci] = acc[I][r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int I = 0; I < NT; ++I) {
+      if (I % NW != w) continue;
+      f4v acc[NT];
+#pragma unroll
+      for (int J = 0; J < NT; ++J) acc[J] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int K = 0; K < NMAX / 4; ++K) {
+        const int m = 4 * K + kk;
+        const float av = G[(16 * I + ci) * LDN + m];        // Z[i][m]
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+          if (4 * K + 3 < 16 * J) continue;
+          const float bv = RB[m * LDN + 16 * J + ci];        // R~[j][m]
+          acc[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[J], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int J = 0; J < NT; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDN + 16 * J + ci] = acc[J][r];
+    }
+    __syncthreads();
+  }
+
+  // @phase D: Householder tridiagonalisation, thread t owning column t of H
+  float h[NMAX];
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) h[i] = act ? G[i * LDN + t] : 0.f;
+  __syncthreads();
+  for (int k = 0; k + 2 < n; ++k) {
+    if (t == k) {
+#pragma unroll
+      for (int i = 0; i < NMAX; i += 4)
+        *reinterpret_cast<float4*>(CB + i) = make_float4(h[i], h[i + 1], h[i + 2], h[i + 3]);
+    }
+    __syncthreads();
+    const float hk = CB[t];                    // H[t][k]
+    const float alpha = CB[k + 1];
+    const float dkk = CB[k];
+    const float xn2 = block_reduce<NW>(t > k + 1 ? hk * hk : 0.f, AddOp(), RED, 0);
+    float tau = 0.f, beta = alpha, sc = 0.f;
+    if (xn2 != 0.f) {
+      const float nrm = fsqrt(fmaf(alpha, alpha, xn2));
+      beta = alpha >= 0.f ? -nrm : nrm;
+      tau = (beta - alpha) * frcp(beta);
+      sc = frcp(alpha - beta);
+    }
+    const float vl = (t > k + 1) ? hk * sc : (t == k + 1 ? 1.f : 0.f);
+    if (t == 0) {
+      TD[k] = dkk;
+      TE[k] = beta;
+      TAU[k] = tau;
+    }
+    if (act) {
+      VB[t] = vl;
+      G[k * LDN + t] = vl;                     // reflector k, zero at rows <= k
+    }
+    __syncthreads();
+    float pl = 0.f;
+#pragma unroll
+    for (int b = 0; b < NMAX / 8; ++b) {
+      if (8 * b + 7 > k) {
+        const float4 v0 = *reinterpret_cast<const float4*>(VB + 8 * b);
+        const float4 v1 = *reinterpret_cast<const float4*>(VB + 8 * b + 4);
+        const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) pl = fmaf(h[8 * b + s], vv[s], pl);
+      }
+    }
+    pl *= tau;
+    const float K = -0.5f * tau * block_reduce<NW>(pl * vl, AddOp(), RED, 1);
+    const float wl = fmaf(K, vl, pl);
+    if (act) WB[t] = wl;
+    __syncthreads();
+    // H <- H - v w^T - w v^T on rows > k (rows <= k of this column are never read again)
+#pragma unroll
+    for (int b = 0; b < NMAX / 8; ++b) {
+      if (8 * b + 7 > k) {
+        const float4 v0 = *reinterpret_cast<const float4*>(VB + 8 * b);
+        const float4 v1 = *reinterpret_cast<const float4*>(VB + 8 * b + 4);
+        const float4 w0 = *reinterpret_cast<const float4*>(WB + 8 * b);
+        const float4 w1 = *reinterpret_cast<const float4*>(WB + 8 * b + 4);
+        const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const float wb[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int i = 8 * b + s;
+          h[i] = fmaf(-vv[s], wl, h[i]);
+          h[i] = fmaf(-wb[s], vl, h[i]);
+        }
+      }
+    }
+  }
+  {
+    // the trailing 2 x 2 block, from columns n - 1 and n - 2
+    if (t == n - 1) {
+#pragma unroll
+      for (int i = 0; i < NMAX; i += 4)
+        *reinterpret_cast<float4*>(CB + i) = make_float4(h[i], h[i + 1], h[i + 2], h[i + 3]);
+    }
+    if (t == n - 2) {
+#pragma unroll
+      for (int i = 0; i < NMAX; i += 4)
+        *reinterpret_cast<float4*>(VB + i) = make_float4(h[i], h[i + 1], h[i + 2], h[i + 3]);
+    }
+    __syncthreads();
+    if (t == 0) {
+      TD[n - 2] = VB[n - 2];
+      TE[n - 2] = CB[n - 2];
+      TD[n - 1] = CB[n - 1];
+    }
+    // pad T to NMAX rows
+    if (act && t >= n) TD[t] = kPadDiag;
+    if (act && t >= n - 1) TE[t] = 0.f;
+    __syncthreads();
+    if (act) {
+      const float e = t > 0 ? TE[t - 1] : 0.f;
+      E2[t] = e * e;
+    }
+    __syncthreads();
+  }
+
+  // @phase E: the R largest eigenvalues of T by multisection
+  float tnorm, pivmin;
+  {
+    float lo_i = 3.0e38f, hi_i = -3.0e38f;
+    for (int i = t; i < n; i += NTH) {
+      const float rad = fabsf(TE[i]) + (i > 0 ? fabsf(TE[i - 1]) : 0.f);
+      lo_i = fminf(lo_i, TD[i] - rad);
+      hi_i = fmaxf(hi_i, TD[i] + rad);
+    }
+    float lo0 = block_reduce<NW>(lo_i, MinOp(), RED, 2);
+    float hi0 = block_reduce<NW>(hi_i, MaxOp(), RED, 3);
+    tnorm = fmaxf(fabsf(lo0), fabsf(hi0));
+    pivmin = tnorm * 1e-30f + 1e-35f;
+    lo0 -= 2.f * kEps * tnorm + pivmin;
+    hi0 += 2.f * kEps * tnorm + pivmin;
+    const int m = NTH / R;                     // threads per eigenvalue (>= 2)
+    const int grp = t / m, sub = t - grp * m;
+    const bool live = grp < R;
+    const int target = n - 1 - grp;            // ascending index of the eigenvalue
+    const float frac = 1.f / (float)(2 * m + 1);
+    float lo = lo0, hi = hi0;
+    for (int it = 0; it < 48; ++it) {
+      const bool done = !live || (hi - lo) <= 2.f * kEps * fmaxf(fabsf(lo), fabsf(hi)) + pivmin;
+      if (block_all<NW>(done, RED, 4)) break;
+      const float step = (hi - lo) * frac;
+      const float xa = lo + step * (float)(2 * sub + 1);
+      const float xb = lo + step * (float)(2 * sub + 2);
+      int ca = 0, cb = 0;
+      float qa = 1.f, qb = 1.f;
+      for (int i4 = 0; i4 < n; i4 += 4) {
+        const float4 d4 = *reinterpret_cast<const float4*>(TD + i4);
+        const float4 e4 = *reinterpret_cast<const float4*>(E2 + i4);
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          qa = (dd[s] - xa) - ee[s] * frcp(qa);
+          qb = (dd[s] - xb) - ee[s] * frcp(qb);
+          qa = fabsf(qa) < pivmin ? -pivmin : qa;
+          qb = fabsf(qb) < pivmin ? -pivmin : qb;
+          ca += qa < 0.f;
+          cb += qb < 0.f;
+        }
+      }
+      BPT[2 * t] = xa;
+      BPT[2 * t + 1] = xb;
+      BFL[2 * t] = ca > target;
+      BFL[2 * t + 1] = cb > target;
+      __syncthreads();
+      if (live && !done) {
+        for (int s = 0; s < 2 * m; ++s) {
+          const float ps = BPT[2 * grp * m + s];
+          if (BFL[2 * grp * m + s]) hi = fminf(hi, ps);
+          else lo = fmaxf(lo, ps);
+        }
+      }
+      __syncthreads();
+    }
+    if (live && sub == 0) LAM[grp] = 0.5f * (lo + hi);
+  }
+  __syncthreads();
+
+  // @phase F: eigenvectors of T by inverse iteration
+  if (t < 64) {
+    // separate equal shifts: lam'_c = min_{j <= c} (lam_j - (c - j) sep)
+    const float sep = 10.f * kEps * tnorm;
+    float lc = 3.0e38f;
+    for (int j = 0; j < R; ++j)
+      if (j <= t) lc = fminf(lc, LAM[j] - (float)(t - j) * sep);
+    // runs of close eigenvalues: the vector of c is computed in round
+    // c - (first index of its run)
+    const float prev = __shfl_up(lc, 1);
+    const bool head = t == 0 || !(prev - lc < kClusterTol * tnorm);
+    const unsigned long long heads = __ballot(head && t < R);
+    const unsigned long long upto = heads & ((t >= 63) ? ~0ull : ((2ull << t) - 1ull));
+    const int start = upto ? 63 - __clzll(upto) : 0;
+    const int rk = t - start;
+    const float maxr = wave_reduce(t < R ? (float)rk : 0.f, MaxOp());
+    if (t < R) {
+      LAM[t] = lc;
+      RNK[t] = rk;
+      STA[t] = start;
+    }
+    if (t == 0) MISC[0] = maxr;
+  }
+  __syncthreads();
+  {
+    const int maxr = (int)MISC[0];
+    const float tiny = kEps * tnorm + 1e-30f;
+    const int c = t;
+    for (int rnd = 0; rnd <= maxr; ++rnd) {
+      if (c < R && RNK[c] == rnd) {
+        const float lc = LAM[c];
+        float x[NMAX];
+#pragma unroll
+        for (int i = 0; i < NMAX; ++i) x[i] = (i < n) ? start_entry(i, c) : 0.f;
+        for (int it = 0; it < kInvIters; ++it) {
+          // factor T - lc I with partial pivoting while eliminating x; the
+          // reciprocal pivots and the two superdiagonals of U go to LDS, the
+          // eliminated right-hand side stays in x
+          float a = TD[0] - lc, b1 = TE[0], b2 = 0.f, rr = x[0];
+#pragma unroll
+          for (int i = 0; i + 1 < NMAX; ++i) {
+            const float lw = TE[i];
+            const float ap = TD[i + 1] - lc;
+            const float b1p = (i + 2 < NMAX) ? TE[i + 1] : 0.f;
+            const float rp = x[i + 1];
+            const bool sw = fabsf(lw) > fabsf(a);
+            const float pa = sw ? lw : ((a != 0.f) ? a : tiny);
+            const float ipa = frcp(pa);
+            FA[i * RMAX + c] = ipa;
+            FB[i * RMAX + c] = sw ? ap : b1;
+            FC[i * RMAX + c] = sw ? b1p : b2;
+            x[i] = sw ? rp : rr;
+            const float mm = (sw ? a : lw) * ipa;
+            const float na = fmaf(-mm, sw ? ap : b1, sw ? b1 : ap);
+            const float nb1 = fmaf(-mm, sw ? b1p : b2, sw ? b2 : b1p);
+            const float nr = fmaf(-mm, sw ? rp : rr, sw ? rr : rp);
+            a = na; b1 = nb1; b2 = 0.f; rr = nr;
+          }
+          FA[(NMAX - 1) * RMAX + c] = frcp((a != 0.f) ? a : tiny);
+          FB[(NMAX - 1) * RMAX + c] = 0.f;
+          FC[(NMAX - 1) * RMAX + c] = 0.f;
+          x[NMAX - 1] = rr;
+          float x1 = 0.f, x2 = 0.f, mx = 0.f;
+#pragma unroll
+          for (int i = NMAX - 1; i >= 0; --i) {
+            const float xi = (x[i] - FB[i * RMAX + c] * x1 - FC[i * RMAX + c] * x2) * FA[i * RMAX + c];
+            x[i] = xi;
+            mx = fmaxf(mx, fabsf(xi));
+            x2 = x1;
+            x1 = xi;
+          }
+          if (!(mx > 0.f) || !(mx < 3.0e38f)) {
+#pragma unroll
+            for (int i = 0; i < NMAX; ++i) x[i] = (i < n) ? start_entry(i, c + 7 * it + 1) : 0.f;
+            continue;
+          }
+          const float imx = frcp(mx);
+#pragma unroll
+          for (int i = 0; i < NMAX; ++i) x[i] *= imx;
+          for (int pass = 0; pass < 2; ++pass) {
+            for (int j = STA[c]; j < c; ++j) {
+              float dt = 0.f;
+#pragma unroll
+              for (int i = 0; i < NMAX; ++i) dt = fmaf(x[i], XR[i * RMAX + j], dt);
+#pragma unroll
+              for (int i = 0; i < NMAX; ++i) x[i] = fmaf(-dt, XR[i * RMAX + j], x[i]);
+            }
+          }
+          float nx = 0.f;
+#pragma unroll
+          for (int i = 0; i < NMAX; ++i) nx = fmaf(x[i], x[i], nx);
+          if (nx > 0.f) {
+            const float inx = frsq(nx);
+#pragma unroll
+            for (int i = 0; i < NMAX; ++i) x[i] *= inx;
+          } else {
+#pragma unroll
+            for (int i = 0; i < NMAX; ++i) x[i] = (i < n) ? start_entry(i, c + 7 * it + 3) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NMAX; ++i) XR[i * RMAX + c] = x[i];
+      }
+      __syncthreads();
+    }
+  }
+
+  // one modified Gram-Schmidt pass over the R vectors; thread (c, part)
+  // holds rows part * CH .. part * CH + CH - 1 of vector c
+  const int c = t / PARTS, part = t % PARTS;
+  const bool w0 = t < NACT;
+  float y[CH];
+#pragma unroll
+  for (int s = 0; s < CH; ++s) y[s] = (w0 && c < R) ? XR[(part * CH + s) * RMAX + c] : 0.f;
+  for (int c0 = 0; c0 < R; ++c0) {
+    float* const buf = CB2 + (c0 & 1) * NMAX;
+    if (w0 && c == c0) {
+#pragma unroll
+      for (int s = 0; s < CH; ++s) buf[part * CH + s] = y[s];
+    }
+    __syncthreads();
+    if (w0) {
+      float nrm2 = 0.f, dt = 0.f;
+#pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        const float xb = buf[part * CH + s];
+        nrm2 = fmaf(xb, xb, nrm2);
+        dt = fmaf(y[s], xb, dt);
+      }
+      nrm2 = group_sum<PARTS>(nrm2);
+      dt = group_sum<PARTS>(dt);
+      const float f = (c > c0 && c < R && nrm2 > 0.f) ? dt * frcp(nrm2) : 0.f;
+      const float sc = (c == c0) ? (nrm2 > 0.f ? frsq(nrm2) : 0.f) : 1.f;
+#pragma unroll
+      for (int s = 0; s < CH; ++s) y[s] = fmaf(-f, buf[part * CH + s], y[s]) * sc;
+    }
+  }
+
+  // @phase G: back-transform Y -> Q Y through the reflectors (rows of G)
+  if (w0) {
+    for (int k = n - 3; k >= 0; --k) {
+      const float tk = TAU[k];
+      const float* vk = G + k * LDN + part * CH;
+      float pd = 0.f;
+#pragma unroll
+      for (int s = 0; s < CH; ++s) pd = fmaf(vk[s], y[s], pd);
+      pd = group_sum<PARTS>(pd) * tk;
+#pragma unroll
+      for (int s = 0; s < CH; ++s) y[s] = fmaf(-pd, vk[s], y[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < CH; ++s) XR[(part * CH + s) * RMAX + c] = y[s];
+  }
+  __syncthreads();
+
+  // @phase H: P2 = D R~^T X_R (MFMA, into FA), then T' = D^-1 R~^-1 X_R
+  {
+    constexpr int NT = NMAX / 16;
+    const int l = t & 63, w = t >> 6;
+    const int ci = l & 15, kk = l >> 4;
+#pragma unroll
+    for (int J = 0; J < NT; ++J) {
+      if (J % NW != w) continue;
+#pragma unroll
+      for (int C = 0; C < RMAX / 16; ++C) {
+        f4v acc = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int K = 0; K < NMAX / 4; ++K) {
+          if (4 * K > 16 * J + 15) continue;                 // R~[i][j] = 0 for i > j
+          const float av = RB[(16 * J + ci) * LDN + 4 * K + kk];   // R~[i][j]
+          const float bv = XR[(4 * K + kk) * RMAX + 16 * C + ci];  // X_R[i][c]
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * J + 4 * kk + r;
+          FA[j * RMAX + 16 * C + ci] = DVs[j] * acc[r];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (w0) {
+    // R~ t = y from the last row up; the lane owning row i broadcasts t_i
+    // to its group and stores t_i / d_i as row i of T'
+#pragma unroll
+    for (int i = NMAX - 1; i >= 0; --i) {
+      if (i < n) {
+        const int own = i / CH, si = i - (i / CH) * CH;
+        const float yi = y[si];
+        float ti = (part == own) ? yi * IRD[i] : 0.f;
+        switch (own) {
+          case 0: ti = group_bcast<PARTS, 0>(ti); break;
+          case 1: ti = group_bcast<PARTS, 1>(ti); break;
+          case 2: if constexpr (PARTS > 2) ti = group_bcast<PARTS, 2>(ti); break;
+          default: if constexpr (PARTS > 3) ti = group_bcast<PARTS, 3>(ti); break;
+        }
+        if (part == own && c < R) XR[i * RMAX + c] = ti * IDV[i];
+        const float* ri = RB + i * LDN + part * CH;          // R~[m][i]
+#pragma unroll
+        for (int s = 0; s < CH; ++s) y[s] = fmaf(-ri[s], ti, y[s]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // @phase I: U' = U T' and V' = V P2, MFMA over 16-row tiles, written in
+  // place.  A tile reads and writes only its own rows; the next tile's rows
+  // are loaded before the current tile is computed.
+  {
+    constexpr int NK = NMAX / 4, NC = RMAX / 16;
+    constexpr int TU = DK / 16, TT = DK / 16 + DV_ / 16;
+    static_assert(TU % NW == 0 && TT % NW == 0, "row tiles per wave");
+    const int l = t & 63, w = t >> 6;
+    const int ci = l & 15, kk = l >> 4;
+    float bt[NC][NK], bp[NC][NK];
+#pragma unroll
+    for (int C = 0; C < NC; ++C)
+#pragma unroll
+      for (int K = 0; K < NK; ++K) {
+        const int j = 4 * K + kk, cc = 16 * C + ci;
+        const bool ok = j < n && cc < R;
+        bt[C][K] = ok ? XR[j * RMAX + cc] : 0.f;
+        bp[C][K] = ok ? FA[j * RMAX + cc] : 0.f;
+      }
+    float av[NK], an[NK];
+    // wave w takes tiles E = q NW + w; the U tiles come first and TU is a
+    // multiple of NW, so whether tile q is a U tile does not depend on w
+    auto load_tile = [=](int q, float (&dst)[NK]) {
+      const bool isu = q < TU / NW;
+      const int E = q * NW + w;
+      const float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
+      const int ld = isu ? DK : DV_;
+#pragma unroll
+      for (int K = 0; K < NK; ++K) {
+        const int j = 4 * K + kk;
+        dst[K] = (j < n) ? base[(size_t)j * ld + ci] : 0.f;
+      }
+    };
+    load_tile(0, av);
+#pragma unroll
+    for (int q = 0; q < TT / NW; ++q) {
+      if (q + 1 < TT / NW) load_tile(q + 1, an);
+      const bool isu = q < TU / NW;
+      const int E = q * NW + w;
+      f4v acc[NC];
+#pragma unroll
+      for (int C = 0; C < NC; ++C) acc[C] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int K = 0; K < NK; ++K)
+#pragma unroll
+        for (int C = 0; C < NC; ++C)
+          acc[C] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[K], isu ? bt[C][K] : bp[C][K], acc[C],
+                                                        0, 0, 0);
+      float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
+      const int ld = isu ? DK : DV_;
+#pragma unroll
+      for (int C = 0; C < NC; ++C) {
+        const int cc = 16 * C + ci;
+        if (cc < R)
+          *reinterpret_cast<float4*>(base + (size_t)cc * ld + 4 * kk) =
+              make_float4(acc[C][0], acc[C][1], acc[C][2], acc[C][3]);
+      }
+#pragma unroll
+      for (int K = 0; K < NK; ++K) av[K] = an[K];
+    }
+  }
+}
+
+template <int NMAX, int RMAX>
+constexpr size_t wave_lds_bytes() {
+  return 4 * (size_t)Lay<NMAX, RMAX>::TOTAL;
+}
+
+template <int NMAX, int RMAX, int DK, int DV_>
+hipError_t wave_go(int units, int cap, int n, int R, float* U, float* V, hipStream_t s) {
+  constexpr size_t bytes = wave_lds_bytes<NMAX, RMAX>();
+  // the LDS limit is raised once per device, so that later calls (also
+  // under stream capture) only enqueue the kernel
+  static std::atomic<unsigned long long> lds_set{0};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const unsigned long long bit = 1ull << (dev & 63);
+  if (!(lds_set.load(std::memory_order_acquire) & bit)) {
+    err = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(compress_wave_kernel<NMAX, RMAX, DK, DV_>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (err != hipSuccess) return err;
+    lds_set.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  hipLaunchKernelGGL((compress_wave_kernel<NMAX, RMAX, DK, DV_>), dim3(units),
+                     dim3(Lay<NMAX, RMAX>::NTH), bytes, s, U, V, cap, n, R);
+  return hipGetLastError();
+}
+
+// NMAX: n rounded up to a multiple of 16; RMAX: R rounded up to 16 or 32.
+inline int wave_nmax(int n) { return (n + 15) / 16 * 16; }
+
+inline size_t wave_lds_bytes_for(int n, int R) {
+  const int nm = wave_nmax(n);
+  const bool r16 = R <= 16;
+  switch (nm) {
+    case 16: return wave_lds_bytes<16, 16>();
+    case 32: return r16 ? wave_lds_bytes<32, 16>() : wave_lds_bytes<32, 32>();
+    case 48: return r16 ? wave_lds_bytes<48, 16>() : wave_lds_bytes<48, 32>();
+    case 64: return r16 ? wave_lds_bytes<64, 16>() : wave_lds_bytes<64, 32>();
+    case 80: return r16 ? wave_lds_bytes<80, 16>() : wave_lds_bytes<80, 32>();
+    default: return r16 ? wave_lds_bytes<96, 16>() : wave_lds_bytes<96, 32>();
+  }
+}
+
+template <int DK, int DV_>
+hipError_t wave_dispatch(int units, int cap, int n, int R, float* U, float* V, hipStream_t s) {
+  const int nm = wave_nmax(n);
+  if (R <= 16) {
+    switch (nm) {
+      case 16: return wave_go<16, 16, DK, DV_>(units, cap, n, R, U, V, s);
+      case 32: return wave_go<32, 16, DK, DV_>(units, cap, n, R, U, V, s);
+      case 48: return wave_go<48, 16, DK, DV_>(units, cap, n, R, U, V, s);
+      case 64: return wave_go<64, 16, DK, DV_>(units, cap, n, R, U, V, s);
+      case 80: return wave_go<80, 16, DK, DV_>(units, cap, n, R, U, V, s);
+      case 96: return wave_go<96, 16, DK, DV_>(units, cap, n, R, U, V, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (nm) {
+    case 32: return wave_go<32, 32, DK, DV_>(units, cap, n, R, U, V, s);
+    case 48: return wave_go<48, 32, DK, DV_>(units, cap, n, R, U, V, s);
+    case 64: return wave_go<64, 32, DK, DV_>(units, cap, n, R, U, V, s);
+    case 80: return wave_go<80, 32, DK, DV_>(units, cap, n, R, U, V, s);
+    case 96: return wave_go<96, 32, DK, DV_>(units, cap, n, R, U, V, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace wave
+}  // namespace seed

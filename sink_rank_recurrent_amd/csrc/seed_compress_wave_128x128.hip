@@ -1,0 +1,11 @@
+// Compression kernels for 128 x 128 heads (kernel template in seed_compress_wave.h).
+#include "seed_compress_wave.h"
+
+namespace seed {
+
+hipError_t compress_wave_128x128(int units, int cap, int n, int R, float* U, float* V,
+                              hipStream_t stream) {
+  return wave::wave_dispatch<128, 128>(units, cap, n, R, U, V, stream);
+}
+
+}  // namespace seed

@@ -55,15 +55,24 @@ __device__ __forceinline__ void store_vec(float* __restrict__ p, const float (&x
   }
 }
 
-// Sum over the 32 lanes of a half-wave (lanes 0-31 or 32-63 of a wave64).
-// Butterfly: every lane ends with the same, order-independent bit pattern.
+// Sum over the 32 lanes of a half-wave (lanes 0-31 or 32-63 of a wave64),
+// returned to all of them with one bit pattern.  Inside each row of 16
+// lanes: DPP butterflies (xor 1, xor 2, mirror within 8, mirror within 16);
+// then row_bcast:15 adds row 0's sum into row 1 (and row 2's into row 3),
+// and lanes 31 and 63, which now hold the half-wave sums, are read back.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float sum32(float x) {
-  x += __shfl_xor(x, 16, 32);
-  x += __shfl_xor(x, 8, 32);
-  x += __shfl_xor(x, 4, 32);
-  x += __shfl_xor(x, 2, 32);
-  x += __shfl_xor(x, 1, 32);
-  return x;
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  x += dpp_mov<0x140>(x);   // row_mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));
+  const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+  return (__lane_id() & 32) ? hi : lo;
 }
 
 }  // namespace seed

@@ -21,24 +21,27 @@ hipError_t launch_dense(int rule, bool in_bf16, int batch, int heads, int d_k, i
                         const void* q, const void* k, const void* v, const float* g,
                         const float* beta, float* o, hipStream_t stream);
 
-// Largest column count the one-wave compression kernel handles.
-constexpr int kWaveMaxN = 64;
+// Largest column count the wave compression kernel handles (one wave per
+// unit up to 64 columns, two above).
+constexpr int kWaveMaxN = 96;
 
-// Dynamic LDS bytes the compression of n columns to rank R needs (whichever
-// kernel launch_compress picks).
+// Dynamic LDS bytes the compression of n columns to rank R needs.
 size_t compress_lds_bytes(int n, int R);
-// LDS bytes of the workgroup (Jacobi) and one-wave (tridiagonal) kernels.
-size_t compress_jacobi_lds_bytes(int n, int R);
 size_t compress_wave_lds_bytes(int n, int R);
 // Dynamic LDS bytes the dense-to-shallow kernel needs.
 size_t from_dense_lds_bytes(int d_k, int R);
 
-// Compression of n columns to rank R: the one-wave kernel for n <= kWaveMaxN,
-// the workgroup Jacobi kernel above that.
+// Compression of n <= kWaveMaxN columns to rank R (seed_compress_wave.h).
 hipError_t launch_compress(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
                            float* U, float* V, hipStream_t stream);
 hipError_t launch_compress_wave(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
                                 float* U, float* V, hipStream_t stream);
+hipError_t compress_wave_128x128(int units, int cap, int n, int R, float* U, float* V,
+                                 hipStream_t stream);
+hipError_t compress_wave_128x64(int units, int cap, int n, int R, float* U, float* V,
+                                hipStream_t stream);
+hipError_t compress_wave_64x64(int units, int cap, int n, int R, float* U, float* V,
+                               hipStream_t stream);
 
 hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                              const float* S, const float* vbar, float* a, float* U, float* V,

@@ -112,7 +112,9 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
   for (int e = 0; e < EK; ++e) p_aq += an[e] * qq[e];
   const float aq = sum32(p_aq);
 
-  // 5. U pass: decay in place, c_k = (G U)^T k, c_q = (G U)^T q
+  // 5. U pass: decay in place (each decayed column is stored as soon as it
+  // is formed, and the appended column U_r = k with them), then
+  // c_k = (G U)^T k and c_q = (G U)^T q
   float ck[SLOTS], cq[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
@@ -124,21 +126,17 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
       pk += x * kk[e];
       pq += x * qq[e];
     }
+    const int j = grp + 8 * s;
+    if (j < r) store_vec<EK>(Uh + (size_t)j * DK + lane * EK, u[s]);
     ck[s] = pk;
     cq[s] = pq;
   }
+  if (grp == (r & 7)) store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kk);
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     if constexpr (RULE != kMAMBA2) ck[s] = sum32(ck[s]);
     cq[s] = sum32(cq[s]);
   }
-  // decayed columns back in place, and the appended column U_r = k
-#pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    const int j = grp + 8 * s;
-    if (j < r) store_vec<EK>(Uh + (size_t)j * DK + lane * EK, u[s]);
-  }
-  if (grp == (r & 7)) store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kk);
 
   // 6. V pass: partial V c_k and V c_q over this half-wave's columns
   float sk[EV], sq[EV];
