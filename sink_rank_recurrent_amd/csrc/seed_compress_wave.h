@@ -113,6 +113,16 @@ __device__ __forceinline__ float group_bcast(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, false));
 }
 
+// x[0..N) = p[0..N), p 16-byte aligned, read with 16-byte loads.
+template <int N>
+__device__ __forceinline__ void load_row(const float* __restrict__ p, float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(p + i);
+    x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+  }
+}
+
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float frsq(float x) { return __builtin_amdgcn_rsqf(x); }
 __device__ __forceinline__ float fsqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
@@ -154,15 +164,16 @@ struct Lay {
   static constexpr int DV = TAU + NMAX;            // [NMAX] column norms d of U
   static constexpr int IDV = DV + NMAX;            // [NMAX] 1/d
   static constexpr int IRD = IDV + NMAX;           // [NMAX] 1/R~[i][i]
-  static constexpr int BPT = IRD + NMAX;           // [2 NTH] bisection points
-  static constexpr int BFL = BPT + 2 * NTH;        // [2 NTH] their flags (int)
-  static constexpr int LAM = BFL + 2 * NTH;        // [RMAX] eigenvalues (descending)
+  static constexpr int BPT = FA;                   // [4 NTH] bisection points (FA is free then)
+  static constexpr int BFL = FA + 4 * NTH;         // [4 NTH] their flags (int)
+  static constexpr int LAM = IRD + NMAX;           // [RMAX] eigenvalues (descending)
   static constexpr int RNK = LAM + RMAX;           // [RMAX] round of each vector (int)
   static constexpr int STA = RNK + RMAX;           // [RMAX] first index of its run (int)
   static constexpr int RED = STA + RMAX;           // [8][NW] cross-wave partials
   static constexpr int MISC = RED + 8 * NW + (8 * NW) % 4;
   static constexpr int TOTAL = MISC + 4;
   static_assert(NMAX % 16 == 0 && NMAX <= 128, "NMAX");
+  static_assert(8 * NTH <= 3 * NMAX * RMAX, "bisection points fit in the solve factors");
   static_assert(RMAX == 16 || RMAX == 32, "RMAX");
 };
 
@@ -263,6 +274,130 @@ __device__ __forceinline__ void gram(const float* __restrict__ X, int n, float* 
   }
 }
 
+// Rows i updated by a step at index j: whole aligned groups of 4 rows when
+// j is a compile-time constant (fully unrolled loops), so that the 16-byte
+// LDS reads stay whole; whole 8-row blocks (one uniform branch each)
+// otherwise.  Rows <= j of a group are updated harmlessly.
+template <bool STATIC>
+__device__ __forceinline__ bool live_row(int i, int j) {
+  if constexpr (STATIC) return (i | 3) > j;
+  else return (i | 7) > j;
+}
+
+// B, one column: thread t owns column t of the Schur complement in g, gj is
+// its entry j (= G~[j][t]) and piv the pivot G~[j][j].  Writes row j of R~
+// (RB[t LDN + j] = R~[j][t]) and 1/R~[j][j], then removes the rank-one term.
+template <int NMAX, bool STATIC>
+__device__ __forceinline__ void chol_step(float (&g)[NMAX], int j, float gj, float piv, int t,
+                                          bool act, float* RB, float* WB, float* IRD) {
+  constexpr int LDN = NMAX + 4;
+  const bool ok = piv > kPivTol;
+  const float rp = ok ? frsq(piv) : 0.f;
+  const float r = (t > j) ? gj * rp : 0.f;
+  if (act) {
+    RB[t * LDN + j] = (t == j) ? piv * rp : r;
+    WB[t] = r;
+  }
+  if (t == j) IRD[j] = rp;
+  __syncthreads();
+  // every read is issued before the first use
+  float wr[NMAX];
+  load_row<NMAX>(WB, wr);
+#pragma unroll
+  for (int b = 0; b < NMAX / 8; ++b) {
+    if (live_row<STATIC>(8 * b + 7, j)) {
+#pragma unroll
+      for (int i = 8 * b; i < 8 * b + 8; ++i)
+        if (live_row<STATIC>(i, j)) g[i] = fmaf(-wr[i], r, g[i]);
+    }
+  }
+}
+
+// D, one Householder step k: thread t owns column t of H in h, hk is
+// H[t][k], alpha = H[k+1][k], dkk = H[k][k].  Records T's row k and the
+// reflector (row k of G), then H <- H - v w^T - w v^T on the rows > k (rows
+// <= k of a column are never read again).
+template <int NMAX, int NW, bool STATIC>
+__device__ __forceinline__ void tri_step(float (&h)[NMAX], int k, float hk, float alpha, float dkk,
+                                         int t, bool act, float* VB, float* WB, float* G,
+                                         float* TD, float* TE, float* TAU, float* RED) {
+  constexpr int LDN = NMAX + 4;
+  const float xn2 = block_reduce<NW>(t > k + 1 ? hk * hk : 0.f, AddOp(), RED, 0);
+  float tau = 0.f, beta = alpha, sc = 0.f;
+  if (xn2 != 0.f) {
+    const float nrm = fsqrt(fmaf(alpha, alpha, xn2));
+    beta = alpha >= 0.f ? -nrm : nrm;
+    tau = (beta - alpha) * frcp(beta);
+    sc = frcp(alpha - beta);
+  }
+  const float vl = (t > k + 1) ? hk * sc : (t == k + 1 ? 1.f : 0.f);
+  if (t == 0) {
+    TD[k] = dkk;
+    TE[k] = beta;
+    TAU[k] = tau;
+  }
+  if (act) {
+    VB[t] = vl;
+    G[k * LDN + t] = vl;                     // reflector k, zero at rows <= k
+  }
+  __syncthreads();
+  // v is read whole before the first use (it stays live for the update)
+  float vv[NMAX];
+  load_row<NMAX>(VB, vv);
+  float pa = 0.f, pb = 0.f;
+#pragma unroll
+  for (int b = 0; b < NMAX / 8; ++b) {
+    if (live_row<STATIC>(8 * b + 7, k)) {
+#pragma unroll
+      for (int i = 8 * b; i < 8 * b + 8; ++i) {
+        if (live_row<STATIC>(i, k)) {
+          if (i & 1) pb = fmaf(h[i], vv[i], pb);
+          else pa = fmaf(h[i], vv[i], pa);
+        }
+      }
+    }
+  }
+  const float pl = (pa + pb) * tau;
+  const float K = -0.5f * tau * block_reduce<NW>(pl * vl, AddOp(), RED, 1);
+  const float wl = fmaf(K, vl, pl);
+  if (act) WB[t] = wl;
+  __syncthreads();
+  if constexpr (NMAX <= 64) {
+    float wr[NMAX];
+    load_row<NMAX>(WB, wr);
+#pragma unroll
+    for (int b = 0; b < NMAX / 8; ++b) {
+      if (live_row<STATIC>(8 * b + 7, k)) {
+#pragma unroll
+        for (int i = 8 * b; i < 8 * b + 8; ++i) {
+          if (live_row<STATIC>(i, k)) {
+            h[i] = fmaf(-vv[i], wl, h[i]);
+            h[i] = fmaf(-wr[i], vl, h[i]);
+          }
+        }
+      }
+    }
+  } else {
+    // registers are short here: w is read per block, one block ahead
+    float wc[8], wn[8];
+    load_row<8>(WB, wc);
+#pragma unroll
+    for (int b = 0; b < NMAX / 8; ++b) {
+      if (b + 1 < NMAX / 8) load_row<8>(WB + 8 * b + 8, wn);
+      if (live_row<STATIC>(8 * b + 7, k)) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int i = 8 * b + s;
+          h[i] = fmaf(-vv[i], wl, h[i]);
+          h[i] = fmaf(-wc[s], vl, h[i]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) wc[s] = wn[s];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 
 template <int NMAX, int RMAX, int DK, int DV_>
@@ -327,46 +462,36 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   float g[NMAX];
   {
     const float it = act ? IDV[t] : 0.f;
+    // the scale d_t^-1 d_i^-1 is one product for both (i, t) and (t, i), so
+    // the columns stay exactly symmetric through the Cholesky
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) g[i] = act ? G[i * LDN + t] * it * IDV[i] : 0.f;
+    for (int i = 0; i < NMAX; ++i) g[i] = act ? G[i * LDN + t] * (it * IDV[i]) : 0.f;
   }
   __syncthreads();
   // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
   gram<NMAX, NW, DV_, true>(Vh, n, G, DVs);
 
   // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
-  for (int j = 0; j < n; ++j) {
-    if (t == j) {
-#pragma unroll
-      for (int i = 0; i < NMAX; i += 4)
-        *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
-    }
-    __syncthreads();
-    const float gj = CB[t];
-    const float piv = CB[j];
-    const bool ok = piv > kPivTol;
-    const float rp = ok ? frsq(piv) : 0.f;
-    const float r = (t > j) ? gj * rp : 0.f;
-    if (act) {
-      RB[t * LDN + j] = (t == j) ? piv * rp : r;   // R~[j][t]
-      WB[t] = r;
-    }
-    if (t == j) IRD[j] = rp;
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < NMAX / 8; ++b) {
-      if (8 * b + 7 > j) {
-        const float4 w0 = *reinterpret_cast<const float4*>(WB + 8 * b);
-        const float4 w1 = *reinterpret_cast<const float4*>(WB + 8 * b + 4);
-        g[8 * b + 0] = fmaf(-w0.x, r, g[8 * b + 0]);
-        g[8 * b + 1] = fmaf(-w0.y, r, g[8 * b + 1]);
-        g[8 * b + 2] = fmaf(-w0.z, r, g[8 * b + 2]);
-        g[8 * b + 3] = fmaf(-w0.w, r, g[8 * b + 3]);
-        g[8 * b + 4] = fmaf(-w1.x, r, g[8 * b + 4]);
-        g[8 * b + 5] = fmaf(-w1.y, r, g[8 * b + 5]);
-        g[8 * b + 6] = fmaf(-w1.z, r, g[8 * b + 6]);
-        g[8 * b + 7] = fmaf(-w1.w, r, g[8 * b + 7]);
+  if constexpr (NW == 1) {
+    // one wave: fully unrolled, so g[j] is a fixed register; the Schur
+    // complement is symmetric, so it is this column's copy of G~[j][t]
+#pragma clang loop unroll(full)
+    for (int j = 0; j < NMAX; ++j) {
+      if (j < n) {
+        const float gj = g[j];
+        const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gj), j));
+        chol_step<NMAX, true>(g, j, gj, piv, t, act, RB, WB, IRD);
       }
+    }
+  } else {
+    for (int j = 0; j < n; ++j) {
+      if (t == j) {
+#pragma unroll
+        for (int i = 0; i < NMAX; i += 4)
+          *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
+      }
+      __syncthreads();
+      chol_step<NMAX, false>(g, j, CB[t], CB[j], t, act, RB, WB, IRD);
     }
   }
   for (int j = n + t; j < NMAX; j += NTH) IRD[j] = 0.f;
@@ -431,68 +556,28 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
 #pragma unroll
   for (int i = 0; i < NMAX; ++i) h[i] = act ? G[i * LDN + t] : 0.f;
   __syncthreads();
-  for (int k = 0; k + 2 < n; ++k) {
-    if (t == k) {
-#pragma unroll
-      for (int i = 0; i < NMAX; i += 4)
-        *reinterpret_cast<float4*>(CB + i) = make_float4(h[i], h[i + 1], h[i + 2], h[i + 3]);
-    }
-    __syncthreads();
-    const float hk = CB[t];                    // H[t][k]
-    const float alpha = CB[k + 1];
-    const float dkk = CB[k];
-    const float xn2 = block_reduce<NW>(t > k + 1 ? hk * hk : 0.f, AddOp(), RED, 0);
-    float tau = 0.f, beta = alpha, sc = 0.f;
-    if (xn2 != 0.f) {
-      const float nrm = fsqrt(fmaf(alpha, alpha, xn2));
-      beta = alpha >= 0.f ? -nrm : nrm;
-      tau = (beta - alpha) * frcp(beta);
-      sc = frcp(alpha - beta);
-    }
-    const float vl = (t > k + 1) ? hk * sc : (t == k + 1 ? 1.f : 0.f);
-    if (t == 0) {
-      TD[k] = dkk;
-      TE[k] = beta;
-      TAU[k] = tau;
-    }
-    if (act) {
-      VB[t] = vl;
-      G[k * LDN + t] = vl;                     // reflector k, zero at rows <= k
-    }
-    __syncthreads();
-    float pl = 0.f;
-#pragma unroll
-    for (int b = 0; b < NMAX / 8; ++b) {
-      if (8 * b + 7 > k) {
-        const float4 v0 = *reinterpret_cast<const float4*>(VB + 8 * b);
-        const float4 v1 = *reinterpret_cast<const float4*>(VB + 8 * b + 4);
-        const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) pl = fmaf(h[8 * b + s], vv[s], pl);
+  if constexpr (NW == 1) {
+    // one wave: fully unrolled, so h[k] is a fixed register; H is
+    // symmetric, so entry k of this thread's column stands for H[t][k]
+#pragma clang loop unroll(full)
+    for (int k = 0; k < NMAX - 2; ++k) {
+      if (k + 2 < n) {
+        const float hk = h[k];
+        const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hk), k + 1));
+        const float dkk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hk), k));
+        tri_step<NMAX, NW, true>(h, k, hk, alpha, dkk, t, act, VB, WB, G, TD, TE, TAU, RED);
       }
     }
-    pl *= tau;
-    const float K = -0.5f * tau * block_reduce<NW>(pl * vl, AddOp(), RED, 1);
-    const float wl = fmaf(K, vl, pl);
-    if (act) WB[t] = wl;
-    __syncthreads();
-    // H <- H - v w^T - w v^T on rows > k (rows <= k of this column are never read again)
+  } else {
+    for (int k = 0; k + 2 < n; ++k) {
+      if (t == k) {
 #pragma unroll
-    for (int b = 0; b < NMAX / 8; ++b) {
-      if (8 * b + 7 > k) {
-        const float4 v0 = *reinterpret_cast<const float4*>(VB + 8 * b);
-        const float4 v1 = *reinterpret_cast<const float4*>(VB + 8 * b + 4);
-        const float4 w0 = *reinterpret_cast<const float4*>(WB + 8 * b);
-        const float4 w1 = *reinterpret_cast<const float4*>(WB + 8 * b + 4);
-        const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const float wb[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int i = 8 * b + s;
-          h[i] = fmaf(-vv[s], wl, h[i]);
-          h[i] = fmaf(-wb[s], vl, h[i]);
-        }
+        for (int i = 0; i < NMAX; i += 4)
+          *reinterpret_cast<float4*>(CB + i) = make_float4(h[i], h[i + 1], h[i + 2], h[i + 3]);
       }
+      __syncthreads();
+      tri_step<NMAX, NW, false>(h, k, CB[t], CB[k + 1], CB[k], t, act, VB, WB, G, TD, TE, TAU,
+                                RED);
     }
   }
   {
@@ -543,40 +628,71 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     const int grp = t / m, sub = t - grp * m;
     const bool live = grp < R;
     const int target = n - 1 - grp;            // ascending index of the eigenvalue
-    const float frac = 1.f / (float)(2 * m + 1);
+    // NP points per thread, NP m per eigenvalue: each pass shrinks the
+    // interval NP m + 1 times.  Two points keep the reciprocal (a
+    // quarter-rate instruction) chains busy without adding passes' work.  The shifts only need absolute accuracy
+    // against |T| (they seed inverse iteration), so the stop is absolute.
+    constexpr int NP = 2;
+    const float frac = 1.f / (float)(NP * m + 1);
+    const float tol = 4.f * kEps * tnorm + pivmin;
+    // up to 64 rows, T sits in registers (padded rows never count)
+    constexpr bool TREG = NMAX <= 64;
+    float dr[TREG ? NMAX : 4], er[TREG ? NMAX : 4];
+    if constexpr (TREG) {
+      load_row<NMAX>(TD, dr);
+      load_row<NMAX>(E2, er);
+    }
     float lo = lo0, hi = hi0;
     for (int it = 0; it < 48; ++it) {
-      const bool done = !live || (hi - lo) <= 2.f * kEps * fmaxf(fabsf(lo), fabsf(hi)) + pivmin;
+      const bool done = !live || (hi - lo) <= tol;
       if (block_all<NW>(done, RED, 4)) break;
       const float step = (hi - lo) * frac;
-      const float xa = lo + step * (float)(2 * sub + 1);
-      const float xb = lo + step * (float)(2 * sub + 2);
-      int ca = 0, cb = 0;
-      float qa = 1.f, qb = 1.f;
-      for (int i4 = 0; i4 < n; i4 += 4) {
-        const float4 d4 = *reinterpret_cast<const float4*>(TD + i4);
-        const float4 e4 = *reinterpret_cast<const float4*>(E2 + i4);
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-        const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
+      float x[NP], qv[NP];
+      int cnt[NP];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          qa = (dd[s] - xa) - ee[s] * frcp(qa);
-          qb = (dd[s] - xb) - ee[s] * frcp(qb);
-          qa = fabsf(qa) < pivmin ? -pivmin : qa;
-          qb = fabsf(qb) < pivmin ? -pivmin : qb;
-          ca += qa < 0.f;
-          cb += qb < 0.f;
+      for (int p = 0; p < NP; ++p) {
+        x[p] = lo + step * (float)(NP * sub + p + 1);
+        qv[p] = 1.f;
+        cnt[p] = 0;
+      }
+      if constexpr (TREG) {
+#pragma unroll
+        for (int i = 0; i < NMAX; ++i) {
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            float q = (dr[i] - x[p]) - er[i] * frcp(qv[p]);
+            q = fabsf(q) < pivmin ? -pivmin : q;
+            cnt[p] += q < 0.f;
+            qv[p] = q;
+          }
+        }
+      } else {
+        for (int i4 = 0; i4 < n; i4 += 4) {
+          float dd[4], ee[4];
+          load_row<4>(TD + i4, dd);
+          load_row<4>(E2 + i4, ee);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+              float q = (dd[s] - x[p]) - ee[s] * frcp(qv[p]);
+              q = fabsf(q) < pivmin ? -pivmin : q;
+              cnt[p] += q < 0.f;
+              qv[p] = q;
+            }
+          }
         }
       }
-      BPT[2 * t] = xa;
-      BPT[2 * t + 1] = xb;
-      BFL[2 * t] = ca > target;
-      BFL[2 * t + 1] = cb > target;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        BPT[NP * t + p] = x[p];
+        BFL[NP * t + p] = cnt[p] > target;
+      }
       __syncthreads();
       if (live && !done) {
-        for (int s = 0; s < 2 * m; ++s) {
-          const float ps = BPT[2 * grp * m + s];
-          if (BFL[2 * grp * m + s]) hi = fminf(hi, ps);
+        for (int s2 = 0; s2 < NP * m; ++s2) {
+          const float ps = BPT[NP * grp * m + s2];
+          if (BFL[NP * grp * m + s2]) hi = fminf(hi, ps);
           else lo = fmaxf(lo, ps);
         }
       }
@@ -614,6 +730,16 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     const int maxr = (int)MISC[0];
     const float tiny = kEps * tnorm + 1e-30f;
     const int c = t;
+    // up to 64 rows, T sits in registers: the factor stores below would
+    // otherwise hold back every read of T on the serial chain
+    constexpr bool TREG = NMAX <= 64;
+    float tdr[TREG ? NMAX : 4], ter[TREG ? NMAX : 4];
+    if constexpr (TREG) {
+      load_row<NMAX>(TD, tdr);
+      load_row<NMAX>(TE, ter);
+    }
+    auto tdv = [&](int i) { if constexpr (TREG) return tdr[i]; else return TD[i]; };
+    auto tev = [&](int i) { if constexpr (TREG) return ter[i]; else return TE[i]; };
     for (int rnd = 0; rnd <= maxr; ++rnd) {
       if (c < R && RNK[c] == rnd) {
         const float lc = LAM[c];
@@ -624,12 +750,12 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           // factor T - lc I with partial pivoting while eliminating x; the
           // reciprocal pivots and the two superdiagonals of U go to LDS, the
           // eliminated right-hand side stays in x
-          float a = TD[0] - lc, b1 = TE[0], b2 = 0.f, rr = x[0];
+          float a = tdv(0) - lc, b1 = tev(0), b2 = 0.f, rr = x[0];
 #pragma unroll
           for (int i = 0; i + 1 < NMAX; ++i) {
-            const float lw = TE[i];
-            const float ap = TD[i + 1] - lc;
-            const float b1p = (i + 2 < NMAX) ? TE[i + 1] : 0.f;
+            const float lw = tev(i);
+            const float ap = tdv(i + 1) - lc;
+            const float b1p = (i + 2 < NMAX) ? tev(i + 1) : 0.f;
             const float rp = x[i + 1];
             const bool sw = fabsf(lw) > fabsf(a);
             const float pa = sw ? lw : ((a != 0.f) ? a : tiny);
@@ -726,15 +852,32 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
 
   // @phase G: back-transform Y -> Q Y through the reflectors (rows of G)
   if (w0) {
-    for (int k = n - 3; k >= 0; --k) {
-      const float tk = TAU[k];
-      const float* vk = G + k * LDN + part * CH;
-      float pd = 0.f;
+    // reflector k (this lane's rows) and tau_k are read one step ahead; the
+    // loop runs over every k < NMAX - 2 so that it unrolls, and skips
+    // k > n - 3
+    float vk[CH], vn[CH];
+    load_row<CH>(G + (NMAX - 3) * LDN + part * CH, vk);
+    float tk = TAU[NMAX - 3], tn = 0.f;
 #pragma unroll
-      for (int s = 0; s < CH; ++s) pd = fmaf(vk[s], y[s], pd);
-      pd = group_sum<PARTS>(pd) * tk;
+    for (int k = NMAX - 3; k >= 0; --k) {
+      if (k > 0) {
+        load_row<CH>(G + (k - 1) * LDN + part * CH, vn);
+        tn = TAU[k - 1];
+      }
+      if (k <= n - 3) {
+        float pd0 = 0.f, pd1 = 0.f;
 #pragma unroll
-      for (int s = 0; s < CH; ++s) y[s] = fmaf(-pd, vk[s], y[s]);
+        for (int s = 0; s < CH; s += 2) {
+          pd0 = fmaf(vk[s], y[s], pd0);
+          pd1 = fmaf(vk[s + 1], y[s + 1], pd1);
+        }
+        const float pd = group_sum<PARTS>(pd0 + pd1) * tk;
+#pragma unroll
+        for (int s = 0; s < CH; ++s) y[s] = fmaf(-pd, vk[s], y[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < CH; ++s) vk[s] = vn[s];
+      tk = tn;
     }
 #pragma unroll
     for (int s = 0; s < CH; ++s) XR[(part * CH + s) * RMAX + c] = y[s];
@@ -770,24 +913,40 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   __syncthreads();
   if (w0) {
     // R~ t = y from the last row up; the lane owning row i broadcasts t_i
-    // to its group and stores t_i / d_i as row i of T'
+    // to its group and stores t_i / d_i as row i of T'.  The reciprocal
+    // pivots of the lane's own rows are read before the serial chain.
+    float ird[CH], idv[CH];
+#pragma unroll
+    for (int s = 0; s < CH; ++s) {
+      ird[s] = IRD[part * CH + s];
+      idv[s] = IDV[part * CH + s];
+    }
+    // column i of R~ (this lane's rows) is read one step ahead
+    float rc[CH], rn[CH];
+#pragma unroll
+    for (int s = 0; s < CH; ++s) rc[s] = RB[(NMAX - 1) * LDN + part * CH + s];
 #pragma unroll
     for (int i = NMAX - 1; i >= 0; --i) {
+      if (i > 0) {
+#pragma unroll
+        for (int s = 0; s < CH; ++s) rn[s] = RB[(i - 1) * LDN + part * CH + s];   // R~[m][i-1]
+      }
       if (i < n) {
         const int own = i / CH, si = i - (i / CH) * CH;
-        const float yi = y[si];
-        float ti = (part == own) ? yi * IRD[i] : 0.f;
+        const float yi = y[si] * ird[si];
+        float ti = (part == own) ? yi : 0.f;
         switch (own) {
           case 0: ti = group_bcast<PARTS, 0>(ti); break;
           case 1: ti = group_bcast<PARTS, 1>(ti); break;
           case 2: if constexpr (PARTS > 2) ti = group_bcast<PARTS, 2>(ti); break;
           default: if constexpr (PARTS > 3) ti = group_bcast<PARTS, 3>(ti); break;
         }
-        if (part == own && c < R) XR[i * RMAX + c] = ti * IDV[i];
-        const float* ri = RB + i * LDN + part * CH;          // R~[m][i]
+        if (part == own && c < R) XR[i * RMAX + c] = ti * idv[si];
 #pragma unroll
-        for (int s = 0; s < CH; ++s) y[s] = fmaf(-ri[s], ti, y[s]);
+        for (int s = 0; s < CH; ++s) y[s] = fmaf(-rc[s], ti, y[s]);
       }
+#pragma unroll
+      for (int s = 0; s < CH; ++s) rc[s] = rn[s];
     }
   }
   __syncthreads();

@@ -154,43 +154,35 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
     }
   }
 
-  // 7. combine the 8 column groups through LDS
+  // 7. combine the 8 column groups through LDS: thread e < d_v finishes
+  // value entry e (a short tail: 16 partial sums per thread)
   __shared__ float red[2][8][DV];
+  __shared__ float eps_s[DV], sink_s[DV];
 #pragma unroll
   for (int e = 0; e < EV; ++e) {
     red[0][grp][lane * EV + e] = sk[e];
     red[1][grp][lane * EV + e] = sq[e];
   }
-  __syncthreads();
   if (grp == 0) {
-    float tk[EV], tq[EV];
 #pragma unroll
     for (int e = 0; e < EV; ++e) {
-      tk[e] = 0.f;
-      tq[e] = 0.f;
+      eps_s[lane * EV + e] = vv[e] - omega * vb[e];
+      sink_s[lane * EV + e] = vb[e] * aq;
     }
+    store_vec<EK>(a + ub * DK + lane * EK, an);
+  }
+  __syncthreads();
+  if (tid < DV) {
+    float tk = 0.f, tq = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int e = 0; e < EV; ++e) {
-        tk[e] += red[0][c][lane * EV + e];
-        tq[e] += red[1][c][lane * EV + e];
-      }
+      tk += red[0][c][tid];
+      tq += red[1][c][tid];
     }
-    float vn[EV], oo[EV];
-#pragma unroll
-    for (int e = 0; e < EV; ++e) {
-      const float eps = vv[e] - omega * vb[e];
-      if constexpr (RULE == kMAMBA2) {
-        vn[e] = eps;
-      } else {
-        vn[e] = bt * (eps - tk[e]);
-      }
-      oo[e] = vb[e] * aq + tq[e] + vn[e] * kq;
-    }
-    store_vec<EV>(Vh + (size_t)r * DV + lane * EV, vn);
-    store_vec<EV>(o + ub * DV + lane * EV, oo);
-    store_vec<EK>(a + ub * DK + lane * EK, an);
+    const float eps = eps_s[tid];
+    const float vn = (RULE == kMAMBA2) ? eps : bt * (eps - tk);
+    Vh[(size_t)r * DV + tid] = vn;
+    o[ub * DV + tid] = sink_s[tid] + tq + vn * kq;
   }
 }
 

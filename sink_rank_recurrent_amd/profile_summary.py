@@ -21,15 +21,15 @@ from collections import defaultdict
 
 GROUPS = {
     "seed_step_kernel": r"seed_step_kernel<",
-    "compress_kernel (one wave per unit)": r"compress_wave_kernel<",
-    "compress_kernel (workgroup Jacobi)": r"::compress_kernel<",
+    "compress_wave_kernel": r"compress_wave_kernel<",
     "from_dense_kernel": r"from_dense_kernel<",
     "dense_step_kernel": r"dense_step_kernel<",
 }
 
 
 def short(name: str) -> str:
-    name = re.sub(r"\(.*$", "", name.replace("void ", ""))
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    name = re.sub(r"\(.*$", "", name)
     return name[:110]
 
 
