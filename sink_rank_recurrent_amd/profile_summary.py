@@ -4,6 +4,8 @@
         --command "<the rocprofv3 command>" --out profiles/<name>.md
     python -m sink_rank_recurrent_amd.profile_summary counters <counter_collection.csv> \
         --kernel seed_step_kernel --out <file.json> ...
+    python -m sink_rank_recurrent_amd.profile_summary pmc <a.csv> [<b.csv> ...] \
+        --kernel compress_wave_kernel --units 1024 --command "..." --out profiles/<name>.md
 
 The step kernel is compiled once per column-slot count, so its dispatches
 appear under several template names; `trace` also reports them merged.
@@ -87,7 +89,34 @@ def main() -> int:
                    help="algorithmic bytes per launch of the profiled runs")
     c.add_argument("--commands", required=True)
     c.add_argument("--out", required=True)
+    m = sub.add_parser("pmc")
+    m.add_argument("csvs", nargs="+", help="counter_collection.csv files (one per pass)")
+    m.add_argument("--kernel", required=True, help="regex of the kernel name")
+    m.add_argument("--units", type=int, required=True, help="workgroups (units) per dispatch")
+    m.add_argument("--waves-per-unit", type=int, default=1)
+    m.add_argument("--command", required=True)
+    m.add_argument("--title", default="rocprofv3 counters")
+    m.add_argument("--out", required=True)
     args = ap.parse_args()
+
+    if args.cmd == "pmc":
+        means = {}
+        for path in args.csvs:
+            per = counter_totals(path, args.kernel)
+            names = sorted({k for d in per.values() for k in d})
+            for name in names:
+                vals = [d[name] for d in per.values() if name in d]
+                means[name] = (sum(vals) / len(vals), len(vals))
+        lines = [f"# {args.title}", "", "Commands:", "", "```", args.command, "```", "",
+                 f"Kernel: `{args.kernel}`, {args.units} units per dispatch.", "",
+                 "| counter | dispatches | mean per dispatch | per unit |", "|---|---|---|---|"]
+        for name, (v, nd) in sorted(means.items()):
+            lines.append(f"| {name} | {nd} | {v:.4g} | {v / args.units:.4g} |")
+        lines.append("")
+        with open(args.out, "w") as f:
+            f.write("\n".join(lines))
+        print("\n".join(lines))
+        return 0
 
     if args.cmd == "trace":
         text, merged = trace_summary(args.stats, args.trace, args.command, args.title)
