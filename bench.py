@@ -15,8 +15,9 @@ per compression).
 The metric is decode head-steps/s (whole job).  Also reported: the step
 kernel's achieved HBM bandwidth from its algorithmic bytes and its average
 launch duration (HIP events on the launch stream), the dense-state baseline
-kernel on the same workload, and the CPU oracle timed on a bounded sample.
-Prints one JSON line.
+kernel on the same workload, the lazily decayed form (U's decay kept as a
+running product, seed_decode_step_lazy) timed on the same state and
+inputs, and the CPU oracle timed on a bounded sample.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -53,13 +54,21 @@ def log(msg: str) -> None:
 # and o (fp32).
 # ---------------------------------------------------------------------------
 
-def step_bytes_per_unit(w: wl.Workload, r: int) -> float:
+def step_bytes_per_unit(w: wl.Workload, r: int, lazy: bool = False) -> float:
+    """In place: U is read and written whole.  Lazy decay: U is only read,
+    one new column is written, and the decay product (one float, or d_k for
+    KDA) is read and written."""
     s_in = 2 if w.in_dtype == torch.bfloat16 else 4
     g_bytes = 4 * w.d_k if w.rule == "kda" else 4
     beta_bytes = 0 if w.rule == "mamba2" else 4
     read = 4 * w.d_k + 4 * (w.d_k + w.d_v) * r + s_in * (2 * w.d_k + w.d_v) + g_bytes + beta_bytes
     read += 4 * w.d_v / w.batch          # vbar, shared by the requests of a head
-    write = 4 * w.d_k + 4 * w.d_k * (r + 1) + 4 * w.d_v + 4 * w.d_v
+    if lazy:
+        gam_bytes = 4 * w.d_k if w.rule == "kda" else 4
+        read += gam_bytes
+        write = 4 * w.d_k + 4 * w.d_k + 4 * w.d_v + 4 * w.d_v + gam_bytes
+    else:
+        write = 4 * w.d_k + 4 * w.d_k * (r + 1) + 4 * w.d_v + 4 * w.d_v
     return read + write
 
 
@@ -89,7 +98,7 @@ def load_traffic(w: wl.Workload):
 
 # ---------------------------------------------------------------------------
 
-def prepare(w: wl.Workload, layer: int, n_steps: int, dev: str):
+def prepare(w: wl.Workload, layer: int, n_steps: int, dev: str, lazy: bool = False):
     """vbar, a converted shallow state and resident inputs for n_steps steps."""
     vbar = wl.make_vbar(w.heads, w.d_v, w.seed, layer, dev)
     S = torch.zeros(w.batch, w.heads, w.d_k, w.d_v, device=dev)
@@ -97,7 +106,8 @@ def prepare(w: wl.Workload, layer: int, n_steps: int, dev: str):
     for t in range(-w.prefill, 0):
         x = wl.workload_step(w, vbar, t, layer, dev)
         binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-    st = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar, device=dev)
+    st = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar, device=dev,
+                              lazy=lazy)
     st.from_dense(S)
     inputs = [wl.workload_step(w, vbar, t, layer, dev) for t in range(n_steps)]
     torch.cuda.synchronize()
@@ -126,8 +136,14 @@ def _do(st, inputs, o, action) -> None:
     if action[0] == "steps":
         for t, r in action[1]:
             x = inputs[t]
-            binding.seed_decode_step(st.rule, st.a, st.U, st.V, st.vbar, x["q"], x["k"], x["v"],
-                                     x["g"], x["beta"], o, r)
+            if st.lazy:
+                binding.seed_decode_step_lazy(st.rule, st.a, st.U, st.V, st.gam, st.vbar, x["q"],
+                                              x["k"], x["v"], x["g"], x["beta"], o, r)
+            else:
+                binding.seed_decode_step(st.rule, st.a, st.U, st.V, st.vbar, x["q"], x["k"],
+                                         x["v"], x["g"], x["beta"], o, r)
+    elif st.lazy:
+        binding.seed_compress_lazy(st.rule, st.U, st.V, st.gam, action[1], st.R)
     else:
         binding.seed_compress(st.U, st.V, action[1], st.R)
 
@@ -269,6 +285,11 @@ def main() -> int:
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--lazy", action="store_true",
+                    help="keep U's decay as a running product (seed_decode_step_lazy) instead of "
+                         "rewriting U every step")
+    ap.add_argument("--no-variant", action="store_true",
+                    help="skip the lazily decayed form that is otherwise timed as well")
     ap.add_argument("--graphs", action="store_true",
                     help="replay HIP graphs captured from the same calls instead of launching "
                          "every kernel from Python")
@@ -295,7 +316,7 @@ def main() -> int:
     units = w.batch * w.heads
     log(f"workload {w.name}: {units} units, {steps} timed steps after {warmup} warm-up")
 
-    vbar, S_dense, st, inputs = prepare(w, args.layer, warmup + steps, dev)
+    vbar, S_dense, st, inputs = prepare(w, args.layer, warmup + steps, dev, lazy=args.lazy)
     log("prepared state and inputs")
 
     # snapshot for the CPU baseline (first units, converted state)
@@ -304,7 +325,7 @@ def main() -> int:
         n_cpu = min(units, 64)
         f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
         a0 = f64(st.a.reshape(units, w.d_k)[:n_cpu])
-        U0 = f64(st.U.reshape(units, w.cap, w.d_k)[:n_cpu, :st.r]).transpose(0, 2, 1)
+        U0 = f64(st.true_U().reshape(units, w.cap, w.d_k)[:n_cpu, :st.r]).transpose(0, 2, 1)
         V0 = f64(st.V.reshape(units, w.cap, w.d_v)[:n_cpu, :st.r]).transpose(0, 2, 1)
         vb0 = f64(vbar)[[u % w.heads for u in range(n_cpu)]]
         cpu_inputs = []
@@ -314,9 +335,31 @@ def main() -> int:
         cpu_state = (a0, U0, V0, vb0)
 
     S_copy = S_dense.clone() if not args.no_dense else None
+    S_var = S_dense.clone() if not (args.lazy or args.no_variant) else None
     o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
     res = run_shallow(st, inputs, o, warmup, steps, graphs=args.graphs)
     log(f"shallow: {res['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
+
+    # the lazily decayed form on the same converted state and inputs
+    variant = None
+    if S_var is not None:
+        st2 = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
+                                   device=dev, lazy=True)
+        st2.from_dense(S_var)
+        del S_var
+        r2 = run_shallow(st2, inputs, o, warmup, steps, graphs=args.graphs)
+        s2 = sum(ms for ms, _ in r2["step_window_ms"]) / 1e3
+        n2 = sum(n for _, n in r2["step_window_ms"])
+        b2 = sum(step_bytes_per_unit(w, r, True) * units for r in r2["step_r"])
+        variant = {"value": units * steps / r2["elapsed_s"], "unit": "head-steps/s",
+                   "ms_per_step": r2["elapsed_s"] * 1e3 / steps,
+                   "step_bytes_per_head_step": b2 / n2 / units,
+                   "step_avg_launch_us": s2 / n2 * 1e6,
+                   "step_achieved_GBs": b2 / s2 / 1e9,
+                   "step_frac_of_peak": b2 / s2 / 1e9 / HBM_PEAK_GBS,
+                   "compress_avg_us": sum(r2["compress_ms"]) / max(1, len(r2["compress_ms"])) * 1e3}
+        del st2
+        log(f"lazy decay: {r2['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
 
     dense = None
     if not args.no_dense:
@@ -337,12 +380,12 @@ def main() -> int:
     value = units * steps / elapsed
     step_total_s = sum(ms for ms, _ in res["step_window_ms"]) / 1e3
     comp_total_s = sum(res["compress_ms"]) / 1e3
-    step_bytes = sum(step_bytes_per_unit(w, r) * units for r in res["step_r"])
+    step_bytes = sum(step_bytes_per_unit(w, r, args.lazy) * units for r in res["step_r"])
     n_launch = sum(n for _, n in res["step_window_ms"])
     assert n_launch == len(res["step_r"])
     avg_launch_s = step_total_s / n_launch
     achieved = step_bytes / n_launch / avg_launch_s / 1e9
-    traffic = load_traffic(w)
+    traffic = None if args.lazy else load_traffic(w)
     mean_bytes = step_bytes / n_launch / units
 
     out = {
@@ -362,6 +405,7 @@ def main() -> int:
                    "layers_per_launch": 1, "d_k": w.d_k, "d_v": w.d_v, "R": w.R, "W": w.W,
                    "inputs": "bf16 q/k/v, fp32 gates" if w.in_dtype == torch.bfloat16 else "fp32",
                    "prefill": w.prefill,
+                   "decay_of_U": "running product (lazy)" if args.lazy else "in place",
                    "launch": ("hip graphs (one per run of steps, one per compression)" if args.graphs
                               else "eager (one launch per kernel)")},
         "roofline": {"bound": "hbm", "kernel": "seed_step_kernel", "achieved": achieved,
@@ -377,6 +421,7 @@ def main() -> int:
                       "step_only_head_steps_per_s": units * n_launch / step_total_s,
                       "wall_s": res["wall_s"]},
         "dense_baseline": dense,
+        "lazy_decay_variant": variant,
     }
     print(json.dumps(out), flush=True)
     return 0

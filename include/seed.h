@@ -112,6 +112,40 @@ seed_status seed_compress(int batch, int heads, int d_k, int d_v, int cap, int r
                           float *U, float *V, void *stream);
 
 /*
+ * seed_decode_step_lazy -- the step of seed_decode_step with the decay of U
+ * kept as a running product instead of being applied in place.
+ *
+ *   gam  float [batch][heads][d_k]   decay product per key channel (KDA)
+ *        float [batch][heads]        one decay product per unit (GDN, Mamba-2)
+ *
+ * The stored columns are U~ with U = Diag(gam) U~ (GDN and Mamba-2:
+ * U = gam U~).  A step sets gam <- g gam (per channel for KDA), appends
+ * U~_r = k / gam and leaves every other column of U~ as it is: only the
+ * write-back of the decayed U disappears.  The update and read-out are
+ * those of seed_decode_step (Lemma 2, picx.dev summary, "Exact Update
+ * (Lemma 2)"; the caption of Table 2 of the SEED figures and tables has U
+ * rescaled at every step, which gam does implicitly), so a, V and o agree
+ * with it up to fp32 rounding.  A state from seed_state_from_dense or
+ * seed_compress is in this form with gam = 1.  Valid while every product
+ * in gam stays a normal fp32 number (above about 1e-37); compress with
+ * seed_compress_lazy, which resets gam to 1.  gam is read and written.
+ */
+seed_status seed_decode_step_lazy(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
+                                  float *a, float *U, float *V, float *gam, const float *vbar,
+                                  const void *q, const void *k, const void *v, int in_dtype,
+                                  const float *g, const float *beta, float *o, void *stream);
+
+/*
+ * seed_compress_lazy -- seed_compress for the form of seed_decode_step_lazy:
+ * the content Diag(gam) U~ V^T is replaced by its rank-R truncation,
+ * stored as U' (orthonormal, true scale) and V' in columns 0..R-1, and gam
+ * is set to 1.  `rule` selects the layout of gam (per key channel for
+ * KDA).  If r <= R nothing is launched and gam is left as it is.
+ */
+seed_status seed_compress_lazy(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
+                               int R, float *U, float *V, float *gam, void *stream);
+
+/*
  * seed_state_from_dense -- convert dense states to the shallow form.
  *
  * At the end of the prefill the states are compressed to the sink plus

@@ -52,11 +52,13 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     i, p, f = ctypes.c_int, ctypes.c_void_p, ctypes.c_float
     L.seed_decode_step.argtypes = [i, i, i, i, i, i, i, p, p, p, p, p, p, p, i, p, p, p, p]
+    L.seed_decode_step_lazy.argtypes = [i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, i, p, p, p, p]
     L.seed_compress.argtypes = [i, i, i, i, i, i, i, p, p, p]
+    L.seed_compress_lazy.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p]
     L.seed_state_from_dense.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p]
     L.dense_decode_step.argtypes = [i, i, i, i, i, p, p, p, p, i, p, p, p, p]
-    for fn in ("seed_decode_step", "seed_compress", "seed_state_from_dense", "dense_decode_step",
-               "seed_abi_version"):
+    for fn in ("seed_decode_step", "seed_decode_step_lazy", "seed_compress", "seed_compress_lazy",
+               "seed_state_from_dense", "dense_decode_step", "seed_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
     L.seed_status_string.argtypes = [i]
     L.seed_status_string.restype = ctypes.c_char_p
@@ -134,6 +136,46 @@ def seed_decode_step(rule: str, a, U, V, vbar, q, k, v, g, beta, o, r: int, stre
     _check("seed_decode_step", st)
 
 
+def _gam_shape(rule: str, B: int, H: int, d_k: int) -> tuple:
+    return (B, H, d_k) if rule == "kda" else (B, H)
+
+
+def seed_decode_step_lazy(rule: str, a, U, V, gam, vbar, q, k, v, g, beta, o, r: int,
+                          stream=None) -> None:
+    """One decode step on lazily decayed shallow states (see include/seed.h)."""
+    B, H, cap, d_k = U.shape
+    d_v = V.shape[-1]
+    _need(a, "a", (B, H, d_k), _F32)
+    _need(U, "U", (B, H, cap, d_k), _F32)
+    _need(V, "V", (B, H, cap, d_v), _F32)
+    _need(gam, "gam", _gam_shape(rule, B, H, d_k), _F32)
+    _need(vbar, "vbar", (H, d_v), _F32)
+    _need(q, "q", (B, H, d_k), _IN)
+    _need(k, "k", (B, H, d_k), _IN)
+    _need(v, "v", (B, H, d_v), _IN)
+    _need(g, "g", (B, H, d_k) if rule == "kda" else (B, H), _F32)
+    if beta is not None:
+        _need(beta, "beta", (B, H), _F32)
+    _need(o, "o", (B, H, d_v), _F32)
+    st = lib().seed_decode_step_lazy(RULES[rule], B, H, d_k, d_v, cap, int(r), _ptr(a), _ptr(U),
+                                     _ptr(V), _ptr(gam), _ptr(vbar), _ptr(q), _ptr(k), _ptr(v),
+                                     _in_dtype(q, k, v), _ptr(g), _ptr(beta), _ptr(o),
+                                     _stream(stream, U.device.index))
+    _check("seed_decode_step_lazy", st)
+
+
+def seed_compress_lazy(rule: str, U, V, gam, r: int, R: int, stream=None) -> None:
+    """Compress lazily decayed factors from r to R columns (see include/seed.h)."""
+    B, H, cap, d_k = U.shape
+    d_v = V.shape[-1]
+    _need(U, "U", (B, H, cap, d_k), _F32)
+    _need(V, "V", (B, H, cap, d_v), _F32)
+    _need(gam, "gam", _gam_shape(rule, B, H, d_k), _F32)
+    st = lib().seed_compress_lazy(RULES[rule], B, H, d_k, d_v, cap, int(r), int(R), _ptr(U),
+                                  _ptr(V), _ptr(gam), _stream(stream, U.device.index))
+    _check("seed_compress_lazy", st)
+
+
 def seed_compress(U, V, r: int, R: int, stream=None) -> None:
     """Compress every unit's factors from r to R columns (see include/seed.h)."""
     B, H, cap, d_k = U.shape
@@ -185,14 +227,17 @@ class ShallowState:
     """
 
     def __init__(self, rule: str, batch: int, heads: int, d_k: int, d_v: int, R: int, W: int,
-                 vbar: torch.Tensor, device="cuda"):
-        self.rule, self.R, self.W = rule, R, W
+                 vbar: torch.Tensor, device="cuda", lazy: bool = False):
+        self.rule, self.R, self.W, self.lazy = rule, R, W, lazy
         self.batch, self.heads, self.d_k, self.d_v = batch, heads, d_k, d_v
         f32 = torch.float32
         self.a = torch.zeros(batch, heads, d_k, device=device, dtype=f32)
         self.U = torch.zeros(batch, heads, R + W, d_k, device=device, dtype=f32)
         self.V = torch.zeros(batch, heads, R + W, d_v, device=device, dtype=f32)
         self.vbar = vbar.to(device=device, dtype=f32).contiguous()
+        # lazy form: U = Diag(gam) U~, gam the decay product since the last compression
+        self.gam = (torch.ones(_gam_shape(rule, batch, heads, d_k), device=device, dtype=f32)
+                    if lazy else None)
         self.r = 0
 
     @property
@@ -201,16 +246,32 @@ class ShallowState:
 
     def from_dense(self, S: torch.Tensor, stream=None) -> None:
         seed_state_from_dense(S, self.vbar, self.a, self.U, self.V, self.R, stream)
+        if self.lazy:
+            self.gam.fill_(1.0)
         self.r = self.R
 
     def step(self, q, k, v, g, beta, o, stream=None) -> None:
-        seed_decode_step(self.rule, self.a, self.U, self.V, self.vbar, q, k, v, g, beta, o,
-                         self.r, stream)
+        if self.lazy:
+            seed_decode_step_lazy(self.rule, self.a, self.U, self.V, self.gam, self.vbar, q, k, v,
+                                  g, beta, o, self.r, stream)
+        else:
+            seed_decode_step(self.rule, self.a, self.U, self.V, self.vbar, q, k, v, g, beta, o,
+                             self.r, stream)
         self.r += 1
 
     def compress(self, stream=None) -> None:
-        seed_compress(self.U, self.V, self.r, self.R, stream)
+        if self.lazy:
+            seed_compress_lazy(self.rule, self.U, self.V, self.gam, self.r, self.R, stream)
+        else:
+            seed_compress(self.U, self.V, self.r, self.R, stream)
         self.r = min(self.r, self.R)
+
+    def true_U(self) -> torch.Tensor:
+        """U at true scale (Diag(gam) U~ in the lazy form); a new tensor when lazy."""
+        if not self.lazy:
+            return self.U
+        gs = self.gam if self.rule == "kda" else self.gam[..., None]
+        return self.U * gs[:, :, None, :]
 
     def step_and_maybe_compress(self, q, k, v, g, beta, o, stream=None) -> bool:
         """One decode step; compress afterwards when all R + W columns are held."""

@@ -82,13 +82,12 @@ seed_status device_status(const char* fn, hipError_t e) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-seed_status seed_decode_step(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
-                             float* a, float* U, float* V, const float* vbar, const void* q,
-                             const void* k, const void* v, int in_dtype, const float* g,
-                             const float* beta, float* o, void* stream) {
-  const char* fn = "seed_decode_step";
+seed_status decode_step(const char* fn, int rule, int batch, int heads, int d_k, int d_v, int cap,
+                        int r, float* a, float* U, float* V, float* gam, bool lazy,
+                        const float* vbar, const void* q, const void* k, const void* v,
+                        int in_dtype, const float* g, const float* beta, float* o, void* stream) {
   seed_status st = check_units(fn, batch, heads, d_k, d_v);
   if (st != SEED_OK) return st;
   if (cap <= 0 || r < 0 || r > cap)
@@ -103,16 +102,18 @@ seed_status seed_decode_step(int rule, int batch, int heads, int d_k, int d_v, i
   SEED_PTR(U);
   SEED_PTR(V);
   SEED_PTR(vbar);
+  if (lazy) SEED_PTR(gam);
   return device_status(fn, seed::launch_step(rule, in_dtype == SEED_BF16, batch, heads, d_k, d_v,
-                                             cap, r, a, U, V, vbar, q, k, v, g, beta, o,
-                                             static_cast<hipStream_t>(stream)));
+                                             cap, r, a, U, V, lazy ? gam : nullptr, vbar, q, k, v,
+                                             g, beta, o, static_cast<hipStream_t>(stream)));
 }
 
-seed_status seed_compress(int batch, int heads, int d_k, int d_v, int cap, int r, int R,
-                          float* U, float* V, void* stream) {
-  const char* fn = "seed_compress";
+seed_status compress(const char* fn, int rule, int batch, int heads, int d_k, int d_v, int cap,
+                     int r, int R, float* U, float* V, float* gam, bool lazy, void* stream) {
   seed_status st = check_units(fn, batch, heads, d_k, d_v);
   if (st != SEED_OK) return st;
+  if (lazy && rule != SEED_RULE_GDN && rule != SEED_RULE_KDA && rule != SEED_RULE_MAMBA2)
+    return fail(SEED_E_ARG, "%s: unknown rule %d", fn, rule);
   if (cap <= 0 || R <= 0 || r < 0 || r > cap || R > cap)
     return fail(SEED_E_SHAPE, "%s: need 0 < R <= cap and 0 <= r <= cap (got R=%d r=%d cap=%d)",
                 fn, R, r, cap);
@@ -121,12 +122,47 @@ seed_status seed_compress(int batch, int heads, int d_k, int d_v, int cap, int r
   if (R > 32) return fail(SEED_E_UNSUPPORTED, "%s: rank %d above 32", fn, R);
   SEED_PTR(U);
   SEED_PTR(V);
+  if (lazy) SEED_PTR(gam);
   if (r <= R) return ok();
   if (seed::compress_lds_bytes(r, R) > seed::kMaxLds)
     return fail(SEED_E_UNSUPPORTED, "%s: %d columns at rank %d need more LDS than a CU has", fn,
                 r, R);
   return device_status(fn, seed::launch_compress(batch, heads, d_k, d_v, cap, r, R, U, V,
+                                                 lazy ? gam : nullptr, rule == SEED_RULE_KDA,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+seed_status seed_decode_step(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
+                             float* a, float* U, float* V, const float* vbar, const void* q,
+                             const void* k, const void* v, int in_dtype, const float* g,
+                             const float* beta, float* o, void* stream) {
+  return decode_step("seed_decode_step", rule, batch, heads, d_k, d_v, cap, r, a, U, V, nullptr,
+                     false, vbar, q, k, v, in_dtype, g, beta, o, stream);
+}
+
+seed_status seed_decode_step_lazy(int rule, int batch, int heads, int d_k, int d_v, int cap,
+                                  int r, float* a, float* U, float* V, float* gam,
+                                  const float* vbar, const void* q, const void* k, const void* v,
+                                  int in_dtype, const float* g, const float* beta, float* o,
+                                  void* stream) {
+  return decode_step("seed_decode_step_lazy", rule, batch, heads, d_k, d_v, cap, r, a, U, V, gam,
+                     true, vbar, q, k, v, in_dtype, g, beta, o, stream);
+}
+
+seed_status seed_compress(int batch, int heads, int d_k, int d_v, int cap, int r, int R,
+                          float* U, float* V, void* stream) {
+  return compress("seed_compress", SEED_RULE_GDN, batch, heads, d_k, d_v, cap, r, R, U, V,
+                  nullptr, false, stream);
+}
+
+seed_status seed_compress_lazy(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
+                               int R, float* U, float* V, float* gam, void* stream) {
+  return compress("seed_compress_lazy", rule, batch, heads, d_k, d_v, cap, r, R, U, V, gam, true,
+                  stream);
 }
 
 seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
@@ -181,6 +217,6 @@ const char* seed_status_string(int status) {
 
 const char* seed_last_error(void) { return g_err; }
 
-int seed_abi_version(void) { return 100; }
+int seed_abi_version(void) { return 101; }
 
 }  // extern "C"

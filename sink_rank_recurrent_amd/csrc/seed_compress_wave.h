@@ -169,7 +169,12 @@ struct Lay {
   static constexpr int LAM = IRD + NMAX;           // [RMAX] eigenvalues (descending)
   static constexpr int RNK = LAM + RMAX;           // [RMAX] round of each vector (int)
   static constexpr int STA = RNK + RMAX;           // [RMAX] first index of its run (int)
-  static constexpr int RED = STA + RMAX;           // [8][NW] cross-wave partials
+  // decay product per key row (lazy form), 128 entries: in the 4 padding
+  // columns of the rows of RB (never read or written otherwise) when they
+  // hold 128 entries, else in a region of its own
+  static constexpr bool GS_PAD = 4 * NMAX >= 128;
+  static constexpr int GS = STA + RMAX;
+  static constexpr int RED = GS + (GS_PAD ? 0 : 128);   // [8][NW] cross-wave partials
   static constexpr int MISC = RED + 8 * NW + (8 * NW) % 4;
   static constexpr int TOTAL = MISC + 4;
   static_assert(NMAX % 16 == 0 && NMAX <= 128, "NMAX");
@@ -183,10 +188,12 @@ struct Lay {
 // each.  MFMA 16x16x4: lane l feeds column 16 t + l % 16 of tile t at the
 // k-slot l / 16.  Wave w sums e over [w D / NW, (w + 1) D / NW), slot kk
 // over its quarter of that range; with two waves the partial sums meet in
-// LDS (wave 1 stores, wave 0 adds and stores the total).
+// LDS (wave 1 stores, wave 0 adds and stores the total).  If rs is not
+// NULL, row e of X is first multiplied by rs[e] (rs_per_row) or by rs[0].
 template <int NMAX, int NW, int D, bool SCALE>
 __device__ __forceinline__ void gram(const float* __restrict__ X, int n, float* __restrict__ G,
-                                     const float* __restrict__ dv) {
+                                     const float* __restrict__ dv, const float* __restrict__ rs,
+                                     bool rs_per_row) {
   constexpr int LDN = NMAX + 4;
   constexpr int NT = NMAX / 16;
   constexpr int NP = NT * (NT + 1) / 2;
@@ -215,6 +222,25 @@ __device__ __forceinline__ void gram(const float* __restrict__ X, int n, float* 
 #pragma unroll
         for (int s = 0; s < KC; ++s) x[t][s] = 0.f;
       }
+    }
+    if (rs != nullptr) {
+      float sc[KC];
+      if (rs_per_row) {
+        const float* src = rs + (w * 4 + kk) * KPL + s0;
+#pragma unroll
+        for (int q = 0; q < KC / 4; ++q) {
+          const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * q);
+          sc[4 * q + 0] = v4.x; sc[4 * q + 1] = v4.y; sc[4 * q + 2] = v4.z; sc[4 * q + 3] = v4.w;
+        }
+      } else {
+        const float r0 = rs[0];
+#pragma unroll
+        for (int s = 0; s < KC; ++s) sc[s] = r0;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int s = 0; s < KC; ++s) x[t][s] *= sc[s];
     }
     int p = 0;
 #pragma unroll
@@ -402,7 +428,8 @@ __device__ __forceinline__ void tri_step(float (&h)[NMAX], int k, float hk, floa
 
 template <int NMAX, int RMAX, int DK, int DV_>
 __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
-    float* __restrict__ U, float* __restrict__ V, int cap, int n, int R) {
+    float* __restrict__ U, float* __restrict__ V, float* __restrict__ gam, int gam_per_row, int cap,
+    int n, int R) {
   using L = Lay<NMAX, RMAX>;
   constexpr int NW = L::NW, NTH = L::NTH, LDN = L::LDN;
   constexpr int PARTS = L::PARTS, CH = L::CH, NACT = L::NACT;
@@ -431,6 +458,11 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   int* const RNK = reinterpret_cast<int*>(sm + L::RNK);
   int* const STA = reinterpret_cast<int*>(sm + L::STA);
   float* const RED = sm + L::RED;
+  // entry i of the staged decay product
+  auto gs_at = [=](int i) -> float* {
+    if constexpr (L::GS_PAD) return RB + (i >> 2) * LDN + NMAX + (i & 3);
+    else return sm + L::GS + i;
+  };
   float* const MISC = sm + L::MISC;
 
   const int t = threadIdx.x;
@@ -438,6 +470,8 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   const size_t ub = blockIdx.x;
   float* const Uh = U + ub * cap * DK;
   float* const Vh = V + ub * cap * DV_;
+  // lazily decayed form: U = Diag(gam) U~ (gam per key channel, or one scalar)
+  float* const gamh = gam != nullptr ? gam + ub * (gam_per_row ? DK : 1) : nullptr;
 
   // R~ (with its zero lower part), the eigenvector block and the published
   // vectors start at zero
@@ -448,9 +482,15 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   CB[t] = 0.f;
   VB[t] = 0.f;
   WB[t] = 0.f;
+  if (gamh != nullptr) {
+    // the decay product of every key row, staged once
+    __syncthreads();   // after the zeroing of RB
+    for (int i = t; i < DK; i += NTH) *gs_at(i) = gamh[gam_per_row ? i : 0];
+    __syncthreads();
+  }
 
   // @phase A: Gram of U and column norms
-  gram<NMAX, NW, DK, false>(Uh, n, G, nullptr);
+  gram<NMAX, NW, DK, false>(Uh, n, G, nullptr, gamh, gam_per_row);
   __syncthreads();
   if (act) {
     const float gtt = G[t * LDN + t];
@@ -469,7 +509,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
   __syncthreads();
   // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
-  gram<NMAX, NW, DV_, true>(Vh, n, G, DVs);
+  gram<NMAX, NW, DV_, true>(Vh, n, G, DVs, nullptr, false);
 
   // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
   if constexpr (NW == 1) {
@@ -971,9 +1011,18 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
         bp[C][K] = ok ? FA[j * RMAX + cc] : 0.f;
       }
     float av[NK], an[NK];
+    // in the lazy form, row 16 E + ci of U carries its decay factor: one
+    // scale per U tile of this wave, read before the tile pipeline
+    float rsc[TU / NW];
+#pragma unroll
+    for (int q = 0; q < TU / NW; ++q) rsc[q] = 1.f;
+    if (gamh != nullptr) {
+#pragma unroll
+      for (int q = 0; q < TU / NW; ++q) rsc[q] = *gs_at(16 * (q * NW + w) + ci);
+    }
     // wave w takes tiles E = q NW + w; the U tiles come first and TU is a
     // multiple of NW, so whether tile q is a U tile does not depend on w
-    auto load_tile = [=](int q, float (&dst)[NK]) {
+    auto load_tile = [&](int q, float (&dst)[NK]) {
       const bool isu = q < TU / NW;
       const int E = q * NW + w;
       const float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
@@ -982,6 +1031,10 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       for (int K = 0; K < NK; ++K) {
         const int j = 4 * K + kk;
         dst[K] = (j < n) ? base[(size_t)j * ld + ci] : 0.f;
+      }
+      if (isu) {
+#pragma unroll
+        for (int K = 0; K < NK; ++K) dst[K] *= rsc[q < TU / NW ? q : 0];
       }
     };
     load_tile(0, av);
@@ -1012,6 +1065,15 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       for (int K = 0; K < NK; ++K) av[K] = an[K];
     }
   }
+  if (gamh != nullptr) {
+    // U' is stored at true scale: the decay product starts again from 1
+    __syncthreads();
+    if (gam_per_row) {
+      for (int i = t; i < DK; i += NTH) gamh[i] = 1.f;
+    } else if (t == 0) {
+      gamh[0] = 1.f;
+    }
+  }
 }
 
 template <int NMAX, int RMAX>
@@ -1020,7 +1082,8 @@ constexpr size_t wave_lds_bytes() {
 }
 
 template <int NMAX, int RMAX, int DK, int DV_>
-hipError_t wave_go(int units, int cap, int n, int R, float* U, float* V, hipStream_t s) {
+hipError_t wave_go(int units, int cap, int n, int R, float* U, float* V, float* gam,
+                   int gam_per_row, hipStream_t s) {
   constexpr size_t bytes = wave_lds_bytes<NMAX, RMAX>();
   // the LDS limit is raised once per device, so that later calls (also
   // under stream capture) only enqueue the kernel
@@ -1037,7 +1100,7 @@ hipError_t wave_go(int units, int cap, int n, int R, float* U, float* V, hipStre
     lds_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   hipLaunchKernelGGL((compress_wave_kernel<NMAX, RMAX, DK, DV_>), dim3(units),
-                     dim3(Lay<NMAX, RMAX>::NTH), bytes, s, U, V, cap, n, R);
+                     dim3(Lay<NMAX, RMAX>::NTH), bytes, s, U, V, gam, gam_per_row, cap, n, R);
   return hipGetLastError();
 }
 
@@ -1058,25 +1121,26 @@ inline size_t wave_lds_bytes_for(int n, int R) {
 }
 
 template <int DK, int DV_>
-hipError_t wave_dispatch(int units, int cap, int n, int R, float* U, float* V, hipStream_t s) {
+hipError_t wave_dispatch(int units, int cap, int n, int R, float* U, float* V, float* gam,
+                         int gam_per_row, hipStream_t s) {
   const int nm = wave_nmax(n);
   if (R <= 16) {
     switch (nm) {
-      case 16: return wave_go<16, 16, DK, DV_>(units, cap, n, R, U, V, s);
-      case 32: return wave_go<32, 16, DK, DV_>(units, cap, n, R, U, V, s);
-      case 48: return wave_go<48, 16, DK, DV_>(units, cap, n, R, U, V, s);
-      case 64: return wave_go<64, 16, DK, DV_>(units, cap, n, R, U, V, s);
-      case 80: return wave_go<80, 16, DK, DV_>(units, cap, n, R, U, V, s);
-      case 96: return wave_go<96, 16, DK, DV_>(units, cap, n, R, U, V, s);
+      case 16: return wave_go<16, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+      case 32: return wave_go<32, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+      case 48: return wave_go<48, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+      case 64: return wave_go<64, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+      case 80: return wave_go<80, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+      case 96: return wave_go<96, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (nm) {
-    case 32: return wave_go<32, 32, DK, DV_>(units, cap, n, R, U, V, s);
-    case 48: return wave_go<48, 32, DK, DV_>(units, cap, n, R, U, V, s);
-    case 64: return wave_go<64, 32, DK, DV_>(units, cap, n, R, U, V, s);
-    case 80: return wave_go<80, 32, DK, DV_>(units, cap, n, R, U, V, s);
-    case 96: return wave_go<96, 32, DK, DV_>(units, cap, n, R, U, V, s);
+    case 32: return wave_go<32, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+    case 48: return wave_go<48, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+    case 64: return wave_go<64, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+    case 80: return wave_go<80, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+    case 96: return wave_go<96, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
     default: return hipErrorInvalidValue;
   }
 }

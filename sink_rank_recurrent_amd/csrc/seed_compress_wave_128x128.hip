@@ -3,9 +3,9 @@
 
 namespace seed {
 
-hipError_t compress_wave_128x128(int units, int cap, int n, int R, float* U, float* V,
-                              hipStream_t stream) {
-  return wave::wave_dispatch<128, 128>(units, cap, n, R, U, V, stream);
+hipError_t compress_wave_128x128(int units, int cap, int n, int R, float* U, float* V, float* gam,
+                              int gam_per_row, hipStream_t stream) {
+  return wave::wave_dispatch<128, 128>(units, cap, n, R, U, V, gam, gam_per_row, stream);
 }
 
 }  // namespace seed

@@ -21,17 +21,24 @@
 // V-sums are combined through LDS.  Every half-wave recomputes the scalars
 // (omega, k.Ga, k.q, a+.q) from its own copy of the small vectors, which
 // avoids a barrier; only group 0 writes a, the new V column and o.
+//
+// LAZY: the decay of U is kept as a running product gam per unit (per key
+// channel for Kimi Delta Attention) instead of being applied in place: the
+// stored columns are U~ with U = Diag(gam) U~.  A step multiplies gam by g,
+// reads U~ without rewriting it (c_k = U~^T (gam k), c_q = U~^T (gam q))
+// and appends U~_r = k / gam.  The arithmetic is Lemma 2's; only the U
+// write-back disappears.
 #include "seed_device.h"
 #include "seed_launch.h"
 
 namespace seed {
 
-template <int RULE, int DK, int DV, typename IN_T, int SLOTS>
+template <int RULE, int DK, int DV, typename IN_T, int SLOTS, bool LAZY>
 __global__ __launch_bounds__(256) void seed_step_kernel(
     float* __restrict__ a, float* __restrict__ U, float* __restrict__ V,
-    const float* __restrict__ vbar, const IN_T* __restrict__ q, const IN_T* __restrict__ k,
-    const IN_T* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
-    float* __restrict__ o, int heads, int cap, int r) {
+    float* __restrict__ gam, const float* __restrict__ vbar, const IN_T* __restrict__ q,
+    const IN_T* __restrict__ k, const IN_T* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, float* __restrict__ o, int heads, int cap, int r) {
   constexpr int EK = DK / 32;  // key-space entries per lane
   constexpr int EV = DV / 32;  // value-space entries per lane
   const int unit = blockIdx.x;
@@ -72,6 +79,30 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
     gs = g[ub];
 #pragma unroll
     for (int e = 0; e < EK; ++e) gk[e] = gs;
+  }
+  // LAZY: the running decay product after this step, and k, q scaled by it
+  float gn[EK];
+  float kx[EK], qx[EK];
+#pragma unroll
+  for (int e = 0; e < EK; ++e) {
+    gn[e] = 1.f;
+    kx[e] = kk[e];
+    qx[e] = qq[e];
+  }
+  if constexpr (LAZY) {
+    if constexpr (RULE == kKDA) {
+      load_vec<EK>(gam + ub * DK + lane * EK, gn);
+    } else {
+      const float g0 = gam[ub];
+#pragma unroll
+      for (int e = 0; e < EK; ++e) gn[e] = g0;
+    }
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      gn[e] *= gk[e];
+      kx[e] = gn[e] * kk[e];
+      qx[e] = gn[e] * qq[e];
+    }
   }
   float bt = 1.f;
   if constexpr (RULE != kMAMBA2) bt = beta[ub];
@@ -119,19 +150,36 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     float pk = 0.f, pq = 0.f;
+    if constexpr (LAZY) {
 #pragma unroll
-    for (int e = 0; e < EK; ++e) {
-      const float x = gk[e] * u[s][e];
-      u[s][e] = x;
-      pk += x * kk[e];
-      pq += x * qq[e];
+      for (int e = 0; e < EK; ++e) {
+        pk += u[s][e] * kx[e];
+        pq += u[s][e] * qx[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EK; ++e) {
+        const float x = gk[e] * u[s][e];
+        u[s][e] = x;
+        pk += x * kk[e];
+        pq += x * qq[e];
+      }
+      const int j = grp + 8 * s;
+      if (j < r) store_vec<EK>(Uh + (size_t)j * DK + lane * EK, u[s]);
     }
-    const int j = grp + 8 * s;
-    if (j < r) store_vec<EK>(Uh + (size_t)j * DK + lane * EK, u[s]);
     ck[s] = pk;
     cq[s] = pq;
   }
-  if (grp == (r & 7)) store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kk);
+  if (grp == (r & 7)) {
+    if constexpr (LAZY) {
+      float kd[EK];
+#pragma unroll
+      for (int e = 0; e < EK; ++e) kd[e] = kk[e] / gn[e];
+      store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kd);
+    } else {
+      store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kk);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     if constexpr (RULE != kMAMBA2) ck[s] = sum32(ck[s]);
@@ -170,6 +218,10 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
       sink_s[lane * EV + e] = vb[e] * aq;
     }
     store_vec<EK>(a + ub * DK + lane * EK, an);
+    if constexpr (LAZY) {
+      if constexpr (RULE == kKDA) store_vec<EK>(gam + ub * DK + lane * EK, gn);
+      else if (lane == 0) gam[ub] = gn[0];
+    }
   }
   __syncthreads();
   if (tid < DV) {
@@ -189,24 +241,32 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
 namespace {
 
 template <int RULE, int DK, int DV, typename IN_T, int SLOTS>
-hipError_t step_go(int units, int heads, int cap, int r, float* a, float* U, float* V,
+hipError_t step_go(int units, int heads, int cap, int r, float* a, float* U, float* V, float* gam,
                    const float* vbar, const void* q, const void* k, const void* v, const float* g,
                    const float* beta, float* o, hipStream_t s) {
-  hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS>), dim3(units), dim3(256), 0, s,
-                     a, U, V, vbar, static_cast<const IN_T*>(q), static_cast<const IN_T*>(k),
-                     static_cast<const IN_T*>(v), g, beta, o, heads, cap, r);
+  if (gam != nullptr) {
+    hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS, true>), dim3(units), dim3(256),
+                       0, s, a, U, V, gam, vbar, static_cast<const IN_T*>(q),
+                       static_cast<const IN_T*>(k), static_cast<const IN_T*>(v), g, beta, o,
+                       heads, cap, r);
+  } else {
+    hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS, false>), dim3(units),
+                       dim3(256), 0, s, a, U, V, gam, vbar, static_cast<const IN_T*>(q),
+                       static_cast<const IN_T*>(k), static_cast<const IN_T*>(v), g, beta, o,
+                       heads, cap, r);
+  }
   return hipGetLastError();
 }
 
 template <int RULE, int DK, int DV, typename IN_T>
 hipError_t step_slots(int units, int heads, int cap, int r, float* a, float* U, float* V,
-                      const float* vbar, const void* q, const void* k, const void* v,
+                      float* gam, const float* vbar, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, float* o, hipStream_t s) {
   const int need = (r + 7) / 8;
 #define SEED_STEP_SLOTS(N)                                                                    \
   if (need <= N)                                                                              \
-    return step_go<RULE, DK, DV, IN_T, N>(units, heads, cap, r, a, U, V, vbar, q, k, v, g, beta, \
-                                          o, s);
+    return step_go<RULE, DK, DV, IN_T, N>(units, heads, cap, r, a, U, V, gam, vbar, q, k, v, g, \
+                                          beta, o, s);
   SEED_STEP_SLOTS(1)
   SEED_STEP_SLOTS(2)
   SEED_STEP_SLOTS(3)
@@ -222,47 +282,47 @@ hipError_t step_slots(int units, int heads, int cap, int r, float* a, float* U, 
 
 template <int RULE, typename IN_T>
 hipError_t step_dims(int units, int heads, int d_k, int d_v, int cap, int r, float* a, float* U,
-                     float* V, const float* vbar, const void* q, const void* k, const void* v,
+                     float* V, float* gam, const float* vbar, const void* q, const void* k, const void* v,
                      const float* g, const float* beta, float* o, hipStream_t s) {
   if (d_k == 128 && d_v == 128)
-    return step_slots<RULE, 128, 128, IN_T>(units, heads, cap, r, a, U, V, vbar, q, k, v, g, beta,
+    return step_slots<RULE, 128, 128, IN_T>(units, heads, cap, r, a, U, V, gam, vbar, q, k, v, g, beta,
                                             o, s);
   if (d_k == 128 && d_v == 64)
-    return step_slots<RULE, 128, 64, IN_T>(units, heads, cap, r, a, U, V, vbar, q, k, v, g, beta,
+    return step_slots<RULE, 128, 64, IN_T>(units, heads, cap, r, a, U, V, gam, vbar, q, k, v, g, beta,
                                            o, s);
   if (d_k == 64 && d_v == 64)
-    return step_slots<RULE, 64, 64, IN_T>(units, heads, cap, r, a, U, V, vbar, q, k, v, g, beta,
+    return step_slots<RULE, 64, 64, IN_T>(units, heads, cap, r, a, U, V, gam, vbar, q, k, v, g, beta,
                                           o, s);
   return hipErrorInvalidValue;
 }
 
 template <int RULE>
 hipError_t step_dtype(bool bf16, int units, int heads, int d_k, int d_v, int cap, int r, float* a,
-                      float* U, float* V, const float* vbar, const void* q, const void* k,
+                      float* U, float* V, float* gam, const float* vbar, const void* q, const void* k,
                       const void* v, const float* g, const float* beta, float* o, hipStream_t s) {
   if (bf16)
-    return step_dims<RULE, bf16_t>(units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v, g, beta,
+    return step_dims<RULE, bf16_t>(units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v, g, beta,
                                    o, s);
-  return step_dims<RULE, float>(units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v, g, beta, o,
+  return step_dims<RULE, float>(units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v, g, beta, o,
                                 s);
 }
 
 }  // namespace
 
 hipError_t launch_step(int rule, bool in_bf16, int batch, int heads, int d_k, int d_v, int cap,
-                       int r, float* a, float* U, float* V, const float* vbar, const void* q,
+                       int r, float* a, float* U, float* V, float* gam, const float* vbar, const void* q,
                        const void* k, const void* v, const float* g, const float* beta, float* o,
                        hipStream_t stream) {
   const int units = batch * heads;
   switch (rule) {
     case kGDN:
-      return step_dtype<kGDN>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v, g,
+      return step_dtype<kGDN>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v, g,
                               beta, o, stream);
     case kKDA:
-      return step_dtype<kKDA>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v, g,
+      return step_dtype<kKDA>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v, g,
                               beta, o, stream);
     case kMAMBA2:
-      return step_dtype<kMAMBA2>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, vbar, q, k, v,
+      return step_dtype<kMAMBA2>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v,
                                  g, beta, o, stream);
     default:
       return hipErrorInvalidValue;

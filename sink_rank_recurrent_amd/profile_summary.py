@@ -22,7 +22,8 @@ import sys
 from collections import defaultdict
 
 GROUPS = {
-    "seed_step_kernel": r"seed_step_kernel<",
+    "seed_step_kernel (U decayed in place)": r"seed_step_kernel<.*false>",
+    "seed_step_kernel (lazy decay)": r"seed_step_kernel<.*true>",
     "compress_wave_kernel": r"compress_wave_kernel<",
     "from_dense_kernel": r"from_dense_kernel<",
     "dense_step_kernel": r"dense_step_kernel<",
@@ -83,7 +84,7 @@ def main() -> int:
     c.add_argument("--copy-fetch", required=True)
     c.add_argument("--copy-write", required=True)
     c.add_argument("--copy-bytes", type=float, default=float(1 << 30))
-    c.add_argument("--kernel", default=GROUPS["seed_step_kernel"])
+    c.add_argument("--kernel", default=GROUPS["seed_step_kernel (U decayed in place)"])
     c.add_argument("--source", required=True, help="kernel source whose hash is recorded")
     c.add_argument("--algorithmic-bytes", type=float, required=True,
                    help="algorithmic bytes per launch of the profiled runs")

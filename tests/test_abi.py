@@ -14,12 +14,12 @@ MISALIGNED = ctypes.c_void_p(0x10004)
 
 def test_exports_every_declared_function():
     names = binding.header_functions()
-    assert set(names) == {"seed_decode_step", "seed_compress", "seed_state_from_dense",
-                          "dense_decode_step", "seed_status_string", "seed_last_error",
-                          "seed_abi_version"}
+    assert set(names) == {"seed_decode_step", "seed_decode_step_lazy", "seed_compress",
+                          "seed_compress_lazy", "seed_state_from_dense", "dense_decode_step",
+                          "seed_status_string", "seed_last_error", "seed_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.seed_abi_version() == 100
+    assert L.seed_abi_version() == 101
 
 
 def test_status_strings():
@@ -64,6 +64,24 @@ def test_compress_validation():
     # r <= R is a no-op that touches nothing (pointers are never dereferenced)
     assert L.seed_compress(1, 1, 128, 128, 48, 16, 16, p, p, None) == 0
     assert L.seed_last_error() == b""
+
+
+def test_lazy_validation():
+    p = ALIGNED
+    # the lazy step checks what the in-place step checks, and gam
+    assert L.seed_decode_step_lazy(0, 2, 3, 128, 128, 48, 48, p, p, p, p, p, p, p, p, 1, p, p, p,
+                                   None) == 4
+    assert L.seed_decode_step_lazy(0, 2, 3, 128, 128, 48, 16, p, p, p, None, p, p, p, p, 1, p, p,
+                                   p, None) == 1
+    assert b"gam" in L.seed_last_error()
+    assert L.seed_decode_step_lazy(0, 2, 3, 128, 128, 48, 16, p, p, p, MISALIGNED, p, p, p, p, 1,
+                                   p, p, p, None) == 1
+    assert L.seed_compress_lazy(1, 1, 1, 128, 128, 48, 48, 16, p, p, None, None) == 1
+    assert b"gam" in L.seed_last_error()
+    assert L.seed_compress_lazy(9, 1, 1, 128, 128, 48, 48, 16, p, p, p, None) == 1
+    assert L.seed_compress_lazy(1, 1, 1, 128, 128, 48, 48, 33, p, p, p, None) == 3
+    # r <= R: nothing launched, gam untouched
+    assert L.seed_compress_lazy(1, 1, 1, 128, 128, 48, 16, 16, p, p, p, None) == 0
 
 
 def test_from_dense_validation():

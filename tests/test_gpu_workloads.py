@@ -18,7 +18,9 @@ compression whenever R + W columns are held.  The oracle follows sampled
     are re-synchronised to the GPU state and counted.
 
 The 36-layer workload is checked on one layer's launch (256 requests x 32
-heads), its per-layer shape, over all 16384 decode steps.
+heads), its per-layer shape, over all 16384 decode steps.  Workloads 1-4
+are also run in the lazily decayed form (U = Diag(gam) U~, the decay kept
+as a running product), whose state is compared at true scale.
 """
 import numpy as np
 import pytest
@@ -44,7 +46,7 @@ def _sample_units(total, k, seed):
 def _units_state(st, idx, r):
     cap = st.cap
     a = f64(st.a.reshape(-1, st.d_k)[idx])
-    U = f64(st.U.reshape(-1, cap, st.d_k)[idx, :r]).transpose(0, 2, 1)
+    U = f64(st.true_U().reshape(-1, cap, st.d_k)[idx, :r]).transpose(0, 2, 1)
     V = f64(st.V.reshape(-1, cap, st.d_v)[idx, :r]).transpose(0, 2, 1)
     return a, U, V
 
@@ -60,7 +62,7 @@ def _units_inputs(x, idx):
     return out
 
 
-def run_workload(num, n_sample=8, steps=None, layer=0, checked_windows=(0, 1, -1)):
+def run_workload(num, n_sample=8, steps=None, layer=0, checked_windows=(0, 1, -1), lazy=False):
     w = wl.WORKLOADS[num]
     steps = w.steps if steps is None else steps
     dev = "cuda"
@@ -74,7 +76,8 @@ def run_workload(num, n_sample=8, steps=None, layer=0, checked_windows=(0, 1, -1
     for t in range(-w.prefill, 0):
         x = wl.workload_step(w, vbar, t, layer, dev)
         binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-    st = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar, device=dev)
+    st = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar, device=dev,
+                              lazy=lazy)
     st.from_dense(S)
     torch.cuda.synchronize()
     S_np = f64(S.reshape(-1, w.d_k, w.d_v)[idx])
@@ -149,3 +152,11 @@ def test_workload_parity(num):
     n_sample = 1 if num == 1 else (6 if num == 5 else 8)
     stats = run_workload(num, n_sample=n_sample)
     print(f"workload {num}: {stats}")
+
+
+@pytest.mark.parametrize("num", [1, 2, 3, 4])
+def test_workload_parity_lazy_decay(num):
+    """The same checks on the lazily decayed form (seed_decode_step_lazy /
+    seed_compress_lazy), its state read at true scale, U = Diag(gam) U~."""
+    stats = run_workload(num, n_sample=1 if num == 1 else 6, lazy=True)
+    print(f"workload {num}, lazy decay: {stats}")
