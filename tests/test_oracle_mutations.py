@@ -12,9 +12,10 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "oracle", "seed_oracle.py")
+ORACLE = os.path.join(ROOT, "oracle")
 PIN_FILES = ["tests/test_oracle_dense.py", "tests/test_oracle_svd.py",
              "tests/test_oracle_factored.py", "tests/test_oracle_bytes.py"]
+ROUNDING_PINS = ["tests/test_oracle_rounding.py"]
 
 MUTATIONS = {
     "lemma2_sign_of_kGa": ("(beta * (omega - kGa))", "(beta * (omega + kGa))"),
@@ -34,6 +35,21 @@ MUTATIONS = {
                                    "if True:\n            a, C = sink_extract"),
 }
 
+# mistakes planted in the 16-bit storage oracle (seed_rounding.py)
+ROUNDING_MUTATIONS = {
+    "philox_no_key_bump": ("        if rnd:\n            k0 = (k0 + np.uint64(_W0)) & _MASK",
+                           "        if False:\n            k0 = (k0 + np.uint64(_W0)) & _MASK"),
+    "philox_swapped_products": ("p1 & _MASK,\n", "p0 & _MASK,\n"),
+    "nearest_ties_away": ("up = (frac > 0.5) | ((frac == 0.5) & tie_up)", "up = frac >= 0.5"),
+    "nearest_no_subnormal_binade": ("e = np.maximum(ex - 1, emin)", "e = ex - 1"),
+    "stochastic_compares_ge": ("np.where(frac > u, lo + sp, lo)", "np.where(frac >= u, lo + sp, lo)"),
+    "stochastic_u_from_low_bits": ("(np.asarray(words, dtype=np.uint32) >> 8)",
+                                   "(np.asarray(words, dtype=np.uint32) & 0xFFFFFF)"),
+    "words_v_block_not_offset": ("w[R * d_k:].reshape(R, d_v).T", "w[:R * d_v].reshape(R, d_v).T"),
+    "compress_scales_a_factor": ("round_factors(L.astype(np.float32), F.astype(np.float32)",
+                                    "round_factors(L.astype(np.float32) * 1.001, F.astype(np.float32)"),
+}
+
 RUNNER = r"""
 import sys
 sys.path.insert(0, sys.argv[1])
@@ -44,15 +60,29 @@ sys.exit(pytest.main(sys.argv[2:] + ["-x", "-q", "-p", "no:cacheprovider"]))
 """
 
 
+def _run_mutated(tmp_path, fname, old, new, pins):
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    for f in os.listdir(ORACLE):
+        if f.endswith(".py"):
+            src = open(os.path.join(ORACLE, f)).read()
+            if f == fname:
+                assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+                src = src.replace(old, new)
+            (pkg / f).write_text(src)
+    return subprocess.run([sys.executable, "-c", RUNNER, str(tmp_path)] + pins,
+                          cwd=ROOT, capture_output=True, text=True, timeout=300)
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, tmp_path):
     old, new = MUTATIONS[name]
-    src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
-    pkg = tmp_path / "oracle"
-    pkg.mkdir()
-    (pkg / "seed_oracle.py").write_text(src.replace(old, new))
-    (pkg / "__init__.py").write_text(open(os.path.join(ROOT, "oracle", "__init__.py")).read())
-    r = subprocess.run([sys.executable, "-c", RUNNER, str(tmp_path)] + PIN_FILES,
-                       cwd=ROOT, capture_output=True, text=True, timeout=300)
+    r = _run_mutated(tmp_path, "seed_oracle.py", old, new, PIN_FILES)
+    assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(ROUNDING_MUTATIONS))
+def test_planted_rounding_mistake_is_caught(name, tmp_path):
+    old, new = ROUNDING_MUTATIONS[name]
+    r = _run_mutated(tmp_path, "seed_rounding.py", old, new, ROUNDING_PINS)
     assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
