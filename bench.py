@@ -15,9 +15,11 @@ per compression).
 The metric is decode head-steps/s (whole job).  Also reported: the step
 kernel's achieved HBM bandwidth from its algorithmic bytes and its average
 launch duration (HIP events on the launch stream), the dense-state baseline
-kernel on the same workload, the lazily decayed form (U's decay kept as a
-running product, seed_decode_step_lazy) timed on the same state and
-inputs, and the CPU oracle timed on a bounded sample.  Prints one JSON line.
+kernel on the same workload, two variants timed on the same state and
+inputs -- the lazily decayed form (U's decay kept as a running product,
+seed_decode_step_lazy) and the 16-bit form (kept factors fp16, rounded at
+every compression, seed_decode_step_h16) -- and the CPU oracle timed on a
+bounded sample.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -54,16 +56,20 @@ def log(msg: str) -> None:
 # and o (fp32).
 # ---------------------------------------------------------------------------
 
-def step_bytes_per_unit(w: wl.Workload, r: int, lazy: bool = False) -> float:
+def step_bytes_per_unit(w: wl.Workload, r: int, form: str = "in_place") -> float:
     """In place: U is read and written whole.  Lazy decay: U is only read,
     one new column is written, and the decay product (one float, or d_k for
-    KDA) is read and written."""
+    KDA) is read and written.  16-bit kept factors (lazy): the R kept
+    columns are read at 2 bytes an entry, the r - R appended ones at 4."""
     s_in = 2 if w.in_dtype == torch.bfloat16 else 4
     g_bytes = 4 * w.d_k if w.rule == "kda" else 4
     beta_bytes = 0 if w.rule == "mamba2" else 4
-    read = 4 * w.d_k + 4 * (w.d_k + w.d_v) * r + s_in * (2 * w.d_k + w.d_v) + g_bytes + beta_bytes
+    cols = 4 * (w.d_k + w.d_v) * r
+    if form == "h16":
+        cols = 2 * (w.d_k + w.d_v) * w.R + 4 * (w.d_k + w.d_v) * (r - w.R)
+    read = 4 * w.d_k + cols + s_in * (2 * w.d_k + w.d_v) + g_bytes + beta_bytes
     read += 4 * w.d_v / w.batch          # vbar, shared by the requests of a head
-    if lazy:
+    if form in ("lazy", "h16"):
         gam_bytes = 4 * w.d_k if w.rule == "kda" else 4
         read += gam_bytes
         write = 4 * w.d_k + 4 * w.d_k + 4 * w.d_v + 4 * w.d_v + gam_bytes
@@ -132,16 +138,16 @@ def _plan(st, warmup: int, steps: int):
     return seq, r
 
 
-def _do(st, inputs, o, action) -> None:
+def _do(st, step, inputs, o, action) -> None:
+    """One action of the plan; `step` is the state's bound step call."""
     if action[0] == "steps":
         for t, r in action[1]:
             x = inputs[t]
-            if st.lazy:
-                binding.seed_decode_step_lazy(st.rule, st.a, st.U, st.V, st.gam, st.vbar, x["q"],
-                                              x["k"], x["v"], x["g"], x["beta"], o, r)
-            else:
-                binding.seed_decode_step(st.rule, st.a, st.U, st.V, st.vbar, x["q"], x["k"],
-                                         x["v"], x["g"], x["beta"], o, r)
+            step(x["q"], x["k"], x["v"], x["g"], x["beta"], r)
+    elif isinstance(st, binding.ShallowState16):
+        binding.seed_compress_h16(st.rule, st.Uk, st.Vk, st.Uw, st.Vw, st.gam, action[1],
+                                  st.rounding, st.seed, st.epoch)
+        st.epoch += 1
     elif st.lazy:
         binding.seed_compress_lazy(st.rule, st.U, st.V, st.gam, action[1], st.R)
     else:
@@ -161,12 +167,13 @@ def run_shallow(st, inputs, o, warmup: int, steps: int, graphs: bool):
         st.step_and_maybe_compress(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
     torch.cuda.synchronize()
     seq, r_end = _plan(st, warmup, steps)
+    step = st.bind_step(o)
     captured = []
     if graphs:
         for action in seq:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                _do(st, inputs, o, action)
+                _do(st, step, inputs, o, action)
             captured.append(g)
         torch.cuda.synchronize()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -178,7 +185,7 @@ def run_shallow(st, inputs, o, warmup: int, steps: int, graphs: bool):
         if graphs:
             captured[i].replay()
         else:
-            _do(st, inputs, o, action)
+            _do(st, step, inputs, o, action)
     marks[-1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -289,7 +296,7 @@ def main() -> int:
                     help="keep U's decay as a running product (seed_decode_step_lazy) instead of "
                          "rewriting U every step")
     ap.add_argument("--no-variant", action="store_true",
-                    help="skip the lazily decayed form that is otherwise timed as well")
+                    help="skip the lazily decayed and 16-bit forms that are otherwise timed as well")
     ap.add_argument("--graphs", action="store_true",
                     help="replay HIP graphs captured from the same calls instead of launching "
                          "every kernel from Python")
@@ -340,26 +347,38 @@ def main() -> int:
     res = run_shallow(st, inputs, o, warmup, steps, graphs=args.graphs)
     log(f"shallow: {res['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
 
-    # the lazily decayed form on the same converted state and inputs
-    variant = None
+    # the lazily decayed form and the 16-bit form on the same converted
+    # state and inputs
+    variants = {}
     if S_var is not None:
-        st2 = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
-                                   device=dev, lazy=True)
-        st2.from_dense(S_var)
+        for name, make, form in (
+                ("lazy_decay_variant",
+                 lambda: binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W,
+                                              vbar, device=dev, lazy=True), "lazy"),
+                ("fp16_factor_variant",
+                 lambda: binding.ShallowState16(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W,
+                                                vbar, store=torch.float16, rounding="nearest",
+                                                device=dev), "h16")):
+            st2 = make()
+            st2.from_dense(S_var)
+            r2 = run_shallow(st2, inputs, o, warmup, steps, graphs=args.graphs)
+            s2 = sum(ms for ms, _ in r2["step_window_ms"]) / 1e3
+            n2 = sum(n for _, n in r2["step_window_ms"])
+            b2 = sum(step_bytes_per_unit(w, r, form) * units for r in r2["step_r"])
+            variants[name] = {
+                "value": units * steps / r2["elapsed_s"], "unit": "head-steps/s",
+                "ms_per_step": r2["elapsed_s"] * 1e3 / steps,
+                "step_bytes_per_head_step": b2 / n2 / units,
+                "step_avg_launch_us": s2 / n2 * 1e6,
+                "step_achieved_GBs": b2 / s2 / 1e9,
+                "step_frac_of_peak": b2 / s2 / 1e9 / HBM_PEAK_GBS,
+                "compress_avg_us": sum(r2["compress_ms"]) / max(1, len(r2["compress_ms"])) * 1e3}
+            if form == "h16":
+                variants[name]["factors"] = ("kept R columns fp16 (rounded to nearest at every "
+                                             "compression), appended columns fp32, lazy decay")
+            del st2
+            log(f"{name}: {r2['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
         del S_var
-        r2 = run_shallow(st2, inputs, o, warmup, steps, graphs=args.graphs)
-        s2 = sum(ms for ms, _ in r2["step_window_ms"]) / 1e3
-        n2 = sum(n for _, n in r2["step_window_ms"])
-        b2 = sum(step_bytes_per_unit(w, r, True) * units for r in r2["step_r"])
-        variant = {"value": units * steps / r2["elapsed_s"], "unit": "head-steps/s",
-                   "ms_per_step": r2["elapsed_s"] * 1e3 / steps,
-                   "step_bytes_per_head_step": b2 / n2 / units,
-                   "step_avg_launch_us": s2 / n2 * 1e6,
-                   "step_achieved_GBs": b2 / s2 / 1e9,
-                   "step_frac_of_peak": b2 / s2 / 1e9 / HBM_PEAK_GBS,
-                   "compress_avg_us": sum(r2["compress_ms"]) / max(1, len(r2["compress_ms"])) * 1e3}
-        del st2
-        log(f"lazy decay: {r2['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
 
     dense = None
     if not args.no_dense:
@@ -380,7 +399,8 @@ def main() -> int:
     value = units * steps / elapsed
     step_total_s = sum(ms for ms, _ in res["step_window_ms"]) / 1e3
     comp_total_s = sum(res["compress_ms"]) / 1e3
-    step_bytes = sum(step_bytes_per_unit(w, r, args.lazy) * units for r in res["step_r"])
+    step_bytes = sum(step_bytes_per_unit(w, r, "lazy" if args.lazy else "in_place") * units
+                     for r in res["step_r"])
     n_launch = sum(n for _, n in res["step_window_ms"])
     assert n_launch == len(res["step_r"])
     avg_launch_s = step_total_s / n_launch
@@ -421,7 +441,8 @@ def main() -> int:
                       "step_only_head_steps_per_s": units * n_launch / step_total_s,
                       "wall_s": res["wall_s"]},
         "dense_baseline": dense,
-        "lazy_decay_variant": variant,
+        "lazy_decay_variant": variants.get("lazy_decay_variant"),
+        "fp16_factor_variant": variants.get("fp16_factor_variant"),
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -72,7 +72,14 @@ typedef enum {
   SEED_RULE_MAMBA2 = 2  /* Mamba-2 (d_k = state dim, d_v = head dim):  S' = g S + k v^T    */
 } seed_rule;
 
-typedef enum { SEED_F32 = 0, SEED_BF16 = 1 } seed_dtype;  /* storage type of q, k, v */
+/* Storage types.  q, k, v: SEED_F32 or SEED_BF16.  Kept factors of the
+ * 16-bit form (seed_decode_step_h16 and after): SEED_BF16 or SEED_F16. */
+typedef enum { SEED_F32 = 0, SEED_BF16 = 1, SEED_F16 = 2 } seed_dtype;
+
+typedef enum {
+  SEED_ROUND_NEAREST = 0,    /* IEEE round to nearest, ties to even               */
+  SEED_ROUND_STOCHASTIC = 1  /* up with probability (|x| - lo)/(hi - lo), Philox words */
+} seed_rounding;
 
 /*
  * seed_decode_step -- one decode step of every (request, head) unit.
@@ -144,6 +151,72 @@ seed_status seed_decode_step_lazy(int rule, int batch, int heads, int d_k, int d
  */
 seed_status seed_compress_lazy(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
                                int R, float *U, float *V, float *gam, void *stream);
+
+/*
+ * The 16-bit form: factors kept in fp16 or bf16 (SEED figures and tables,
+ * Table 4 and its caption: 16-bit storage composes with the shallow state;
+ * Table 9 and its caption: the factors rounded to nearest or stochastically
+ * at every compression).  Read here as: the R columns a compression writes
+ * are rounded once and kept as 16-bit patterns; the columns appended until
+ * the next compression are fp32; nothing else is rounded.  The decay of U is
+ * lazy, as in seed_decode_step_lazy.
+ *
+ *   Uk  uint16 [batch][heads][R][d_k]  kept columns of U~ (bf16 or fp16 patterns)
+ *   Vk  uint16 [batch][heads][R][d_v]  kept columns of V
+ *   Uw  float  [batch][heads][W][d_k]  columns of U~ appended since the last compression
+ *   Vw  float  [batch][heads][W][d_v]  columns of V appended since the last compression
+ *   gam float  as for seed_decode_step_lazy
+ *
+ * The state holds r columns, R <= r <= R + W: column j < R is column j of
+ * Uk / Vk, column j >= R is column j - R of Uw / Vw.  Right after a
+ * compression r = R.
+ *
+ * Stochastic rounding: element f of a unit's block -- U column c row i at
+ * f = c d_k + i, V column c row i at f = R d_k + c d_v + i -- takes the word
+ * w = word (f mod 4) of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011)
+ * at counter (f / 4, unit, epoch, 0) and key (seed mod 2^32, seed / 2^32),
+ * and rounds its magnitude up iff (|x| - lo)/(hi - lo) > (w >> 8) 2^-24, with
+ * lo <= |x| < hi the neighbouring 16-bit magnitudes.  Pass a new epoch (for
+ * example the number of compressions so far) to every call.  fp16 overflows
+ * to infinity from 2^16 (stochastic) or 65520 (nearest) up.
+ */
+
+/*
+ * seed_decode_step_h16 -- seed_decode_step_lazy on the 16-bit form: reads
+ * the kept columns (widened exactly) and the r - R appended ones, appends
+ * column r (to Uw / Vw at index r - R, fp32) and writes a, gam and o as the
+ * lazy step does.  Uk and Vk are only read.  Returns SEED_E_FULL if
+ * r == R + W.  store_dtype: SEED_BF16 or SEED_F16.
+ */
+seed_status seed_decode_step_h16(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
+                                 int r, float *a, const void *Uk, const void *Vk, float *Uw,
+                                 float *Vw, float *gam, const float *vbar, const void *q,
+                                 const void *k, const void *v, int in_dtype, int store_dtype,
+                                 const float *g, const float *beta, float *o, void *stream);
+
+/*
+ * seed_compress_h16 -- compression of the 16-bit form: the content
+ * Diag(gam) U~ V^T of the r columns is replaced by its rank-R truncation
+ * (as seed_compress_lazy), computed in fp32, and U' (orthonormal) and V' are
+ * rounded into Uk / Vk with the given rounding; gam is set to 1 and the
+ * caller sets r = R.  If r <= R nothing is launched.  Uw / Vw are only
+ * read.  `rule` selects the layout of gam.
+ */
+seed_status seed_compress_h16(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
+                              int r, void *Uk, void *Vk, float *Uw, float *Vw, float *gam,
+                              int store_dtype, int rounding, uint64_t seed, uint32_t epoch,
+                              void *stream);
+
+/*
+ * seed_round_factors -- round fp32 rank-R factors U [batch][heads][R][d_k],
+ * V [batch][heads][R][d_v] (for example the output of seed_state_from_dense
+ * with cap = R) into the kept columns Uk, Vk of the 16-bit form, with the
+ * element numbering and words of seed_compress_h16.  U and V are only read;
+ * they must not overlap Uk, Vk.  Requires 0 < R <= 96.
+ */
+seed_status seed_round_factors(int batch, int heads, int d_k, int d_v, int R, const float *U,
+                               const float *V, void *Uk, void *Vk, int store_dtype, int rounding,
+                               uint64_t seed, uint32_t epoch, void *stream);
 
 /*
  * seed_state_from_dense -- convert dense states to the shallow form.

@@ -57,8 +57,14 @@ def lib() -> ctypes.CDLL:
     L.seed_compress_lazy.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p]
     L.seed_state_from_dense.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p]
     L.dense_decode_step.argtypes = [i, i, i, i, i, p, p, p, p, i, p, p, p, p]
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    L.seed_decode_step_h16.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p, p, i, i,
+                                       p, p, p, p]
+    L.seed_compress_h16.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, i, i, u64, u32, p]
+    L.seed_round_factors.argtypes = [i, i, i, i, i, p, p, p, p, i, i, u64, u32, p]
     for fn in ("seed_decode_step", "seed_decode_step_lazy", "seed_compress", "seed_compress_lazy",
-               "seed_state_from_dense", "dense_decode_step", "seed_abi_version"):
+               "seed_state_from_dense", "dense_decode_step", "seed_decode_step_h16",
+               "seed_compress_h16", "seed_round_factors", "seed_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
     L.seed_status_string.argtypes = [i]
     L.seed_status_string.restype = ctypes.c_char_p
@@ -218,6 +224,117 @@ def dense_decode_step(rule: str, S, q, k, v, g, beta, o, stream=None) -> None:
     _check("dense_decode_step", st)
 
 
+# 16-bit kept factors: the tensor dtype names the pattern format
+_STORE = {torch.bfloat16: 1, torch.float16: 2}
+_H16 = tuple(_STORE)
+ROUNDING = {"nearest": 0, "stochastic": 1}
+
+
+def _store_dtype(Uk, Vk) -> int:
+    if Uk.dtype != Vk.dtype or Uk.dtype not in _STORE:
+        raise ValueError("Uk and Vk must share one dtype, bfloat16 or float16")
+    return _STORE[Uk.dtype]
+
+
+def seed_decode_step_h16(rule: str, a, Uk, Vk, Uw, Vw, gam, vbar, q, k, v, g, beta, o, r: int,
+                         stream=None) -> None:
+    """One decode step on the 16-bit form (see include/seed.h)."""
+    B, H, R, d_k = Uk.shape
+    W, d_v = Uw.shape[2], Vk.shape[-1]
+    _need(a, "a", (B, H, d_k), _F32)
+    _need(Uk, "Uk", (B, H, R, d_k), _H16)
+    _need(Vk, "Vk", (B, H, R, d_v), _H16)
+    _need(Uw, "Uw", (B, H, W, d_k), _F32)
+    _need(Vw, "Vw", (B, H, W, d_v), _F32)
+    _need(gam, "gam", _gam_shape(rule, B, H, d_k), _F32)
+    _need(vbar, "vbar", (H, d_v), _F32)
+    _need(q, "q", (B, H, d_k), _IN)
+    _need(k, "k", (B, H, d_k), _IN)
+    _need(v, "v", (B, H, d_v), _IN)
+    _need(g, "g", (B, H, d_k) if rule == "kda" else (B, H), _F32)
+    if beta is not None:
+        _need(beta, "beta", (B, H), _F32)
+    _need(o, "o", (B, H, d_v), _F32)
+    st = lib().seed_decode_step_h16(RULES[rule], B, H, d_k, d_v, R, W, int(r), _ptr(a), _ptr(Uk),
+                                    _ptr(Vk), _ptr(Uw), _ptr(Vw), _ptr(gam), _ptr(vbar), _ptr(q),
+                                    _ptr(k), _ptr(v), _in_dtype(q, k, v), _store_dtype(Uk, Vk),
+                                    _ptr(g), _ptr(beta), _ptr(o), _stream(stream, Uk.device.index))
+    _check("seed_decode_step_h16", st)
+
+
+def seed_compress_h16(rule: str, Uk, Vk, Uw, Vw, gam, r: int, rounding: str = "nearest",
+                      seed: int = 0, epoch: int = 0, stream=None) -> None:
+    """Compress the 16-bit form from r to R columns, rounding into Uk, Vk
+    (see include/seed.h)."""
+    B, H, R, d_k = Uk.shape
+    W, d_v = Uw.shape[2], Vk.shape[-1]
+    _need(Uk, "Uk", (B, H, R, d_k), _H16)
+    _need(Vk, "Vk", (B, H, R, d_v), _H16)
+    _need(Uw, "Uw", (B, H, W, d_k), _F32)
+    _need(Vw, "Vw", (B, H, W, d_v), _F32)
+    _need(gam, "gam", _gam_shape(rule, B, H, d_k), _F32)
+    st = lib().seed_compress_h16(RULES[rule], B, H, d_k, d_v, R, W, int(r), _ptr(Uk), _ptr(Vk),
+                                 _ptr(Uw), _ptr(Vw), _ptr(gam), _store_dtype(Uk, Vk),
+                                 ROUNDING[rounding], int(seed), int(epoch),
+                                 _stream(stream, Uk.device.index))
+    _check("seed_compress_h16", st)
+
+
+def seed_round_factors(U, V, Uk, Vk, rounding: str = "nearest", seed: int = 0, epoch: int = 0,
+                       stream=None) -> None:
+    """Round fp32 rank-R factors into 16-bit kept columns (see include/seed.h)."""
+    B, H, R, d_k = U.shape
+    d_v = V.shape[-1]
+    _need(U, "U", (B, H, R, d_k), _F32)
+    _need(V, "V", (B, H, R, d_v), _F32)
+    _need(Uk, "Uk", (B, H, R, d_k), _H16)
+    _need(Vk, "Vk", (B, H, R, d_v), _H16)
+    st = lib().seed_round_factors(B, H, d_k, d_v, R, _ptr(U), _ptr(V), _ptr(Uk), _ptr(Vk),
+                                  _store_dtype(Uk, Vk), ROUNDING[rounding], int(seed), int(epoch),
+                                  _stream(stream, U.device.index))
+    _check("seed_round_factors", st)
+
+
+def _bound_step(fn, name: str, head: tuple, tail_state: tuple, rule: str, B: int, H: int,
+                d_k: int, d_v: int, o, extra_code: tuple = ()):
+    """A decode-step call whose state arguments are fixed: `head` are the
+    leading integer arguments before r, `tail_state` the state pointers that
+    follow r.  Each call checks only the step inputs (one combined test, the
+    detailed checks only on failure) and passes their pointers."""
+    _need(o, "o", (B, H, d_v), _F32)
+    sq = torch.Size((B, H, d_k))
+    sv = torch.Size((B, H, d_v))
+    sg = torch.Size((B, H, d_k) if rule == "kda" else (B, H))
+    sb = torch.Size((B, H))
+    op = o.data_ptr()
+    dev = o.device.index
+    mamba = rule == "mamba2"
+
+    def step(q, k, v, g, beta, r: int, stream=None) -> None:
+        dt = q.dtype
+        if not (q.shape == sq and k.shape == sq and v.shape == sv and g.shape == sg
+                and k.dtype is dt and v.dtype is dt and (dt is torch.bfloat16 or dt is torch.float32)
+                and g.dtype is torch.float32 and q.is_cuda and k.is_cuda and v.is_cuda and g.is_cuda
+                and q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+                and g.is_contiguous()
+                and (beta is None if mamba else (beta.shape == sb and beta.dtype is torch.float32
+                                                 and beta.is_cuda and beta.is_contiguous()))):
+            _need(q, "q", tuple(sq), _IN)
+            _need(k, "k", tuple(sq), _IN)
+            _need(v, "v", tuple(sv), _IN)
+            _need(g, "g", tuple(sg), _F32)
+            if beta is not None:
+                _need(beta, "beta", tuple(sb), _F32)
+            _in_dtype(q, k, v)
+        st = fn(*head, int(r), *tail_state, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                1 if dt is torch.bfloat16 else 0, *extra_code, g.data_ptr(),
+                None if beta is None else beta.data_ptr(), op, _stream(stream, dev))
+        if st != 0:
+            _check(name, st)
+
+    return step
+
+
 class ShallowState:
     """Device tensors of one layer's shallow states plus the column count r.
 
@@ -259,6 +376,22 @@ class ShallowState:
                              self.r, stream)
         self.r += 1
 
+    def bind_step(self, o):
+        """A fast form of `step` for a loop that writes read-outs to `o`:
+        the state's tensors and o are checked once, each call checks only
+        the step's inputs.  Call it as f(q, k, v, g, beta, r); it does not
+        advance self.r.  Valid while the state's tensors are not replaced."""
+        B, H, d_k, d_v = self.batch, self.heads, self.d_k, self.d_v
+        head = (RULES[self.rule], B, H, d_k, d_v, self.cap)
+        if self.lazy:
+            tail = (self.a.data_ptr(), self.U.data_ptr(), self.V.data_ptr(),
+                    self.gam.data_ptr(), self.vbar.data_ptr())
+            return _bound_step(lib().seed_decode_step_lazy, "seed_decode_step_lazy", head, tail,
+                               self.rule, B, H, d_k, d_v, o)
+        tail = (self.a.data_ptr(), self.U.data_ptr(), self.V.data_ptr(), self.vbar.data_ptr())
+        return _bound_step(lib().seed_decode_step, "seed_decode_step", head, tail, self.rule, B, H,
+                           d_k, d_v, o)
+
     def compress(self, stream=None) -> None:
         if self.lazy:
             seed_compress_lazy(self.rule, self.U, self.V, self.gam, self.r, self.R, stream)
@@ -272,6 +405,88 @@ class ShallowState:
             return self.U
         gs = self.gam if self.rule == "kda" else self.gam[..., None]
         return self.U * gs[:, :, None, :]
+
+    def step_and_maybe_compress(self, q, k, v, g, beta, o, stream=None) -> bool:
+        """One decode step; compress afterwards when all R + W columns are held."""
+        self.step(q, k, v, g, beta, o, stream)
+        if self.r >= self.cap:
+            self.compress(stream)
+            return True
+        return False
+
+
+class ShallowState16:
+    """Device tensors of one layer's shallow states in the 16-bit form.
+
+    a [B, H, d_k] fp32, kept factors Uk [B, H, R, d_k], Vk [B, H, R, d_v] as
+    bfloat16 or float16 patterns, the window Uw [B, H, W, d_k], Vw [B, H, W,
+    d_v] fp32, the decay product gam and the shared vbar [H, d_v].  r runs
+    from R (right after a compression) to R + W.  Every rounding (from_dense
+    and each compression) takes the next epoch of the generator.
+    """
+
+    def __init__(self, rule: str, batch: int, heads: int, d_k: int, d_v: int, R: int, W: int,
+                 vbar: torch.Tensor, store=torch.float16, rounding: str = "nearest",
+                 seed: int = 0, device="cuda"):
+        if store not in _STORE:
+            raise ValueError("store must be torch.bfloat16 or torch.float16")
+        self.rule, self.R, self.W, self.store = rule, R, W, store
+        self.rounding, self.seed, self.epoch = rounding, int(seed), 0
+        self.batch, self.heads, self.d_k, self.d_v = batch, heads, d_k, d_v
+        f32 = torch.float32
+        self.a = torch.zeros(batch, heads, d_k, device=device, dtype=f32)
+        self.Uk = torch.zeros(batch, heads, R, d_k, device=device, dtype=store)
+        self.Vk = torch.zeros(batch, heads, R, d_v, device=device, dtype=store)
+        self.Uw = torch.zeros(batch, heads, W, d_k, device=device, dtype=f32)
+        self.Vw = torch.zeros(batch, heads, W, d_v, device=device, dtype=f32)
+        self.vbar = vbar.to(device=device, dtype=f32).contiguous()
+        self.gam = torch.ones(_gam_shape(rule, batch, heads, d_k), device=device, dtype=f32)
+        self.r = R
+
+    @property
+    def cap(self) -> int:
+        return self.R + self.W
+
+    def from_dense(self, S: torch.Tensor, stream=None) -> None:
+        """End-of-prefill compression into the 16-bit form (fp32 factors
+        from seed_state_from_dense, then rounded)."""
+        B, H, R = self.batch, self.heads, self.R
+        U = torch.empty(B, H, R, self.d_k, device=self.a.device, dtype=torch.float32)
+        V = torch.empty(B, H, R, self.d_v, device=self.a.device, dtype=torch.float32)
+        seed_state_from_dense(S, self.vbar, self.a, U, V, R, stream)
+        seed_round_factors(U, V, self.Uk, self.Vk, self.rounding, self.seed, self.epoch, stream)
+        self.epoch += 1
+        self.gam.fill_(1.0)
+        self.r = R
+
+    def step(self, q, k, v, g, beta, o, stream=None) -> None:
+        seed_decode_step_h16(self.rule, self.a, self.Uk, self.Vk, self.Uw, self.Vw, self.gam,
+                             self.vbar, q, k, v, g, beta, o, self.r, stream)
+        self.r += 1
+
+    def bind_step(self, o):
+        """A fast form of `step` (see ShallowState.bind_step)."""
+        B, H, d_k, d_v = self.batch, self.heads, self.d_k, self.d_v
+        head = (RULES[self.rule], B, H, d_k, d_v, self.R, self.W)
+        tail = (self.a.data_ptr(), self.Uk.data_ptr(), self.Vk.data_ptr(), self.Uw.data_ptr(),
+                self.Vw.data_ptr(), self.gam.data_ptr(), self.vbar.data_ptr())
+        return _bound_step(lib().seed_decode_step_h16, "seed_decode_step_h16", head, tail,
+                           self.rule, B, H, d_k, d_v, o, (_STORE[self.store],))
+
+    def compress(self, stream=None) -> None:
+        if self.r > self.R:
+            seed_compress_h16(self.rule, self.Uk, self.Vk, self.Uw, self.Vw, self.gam, self.r,
+                              self.rounding, self.seed, self.epoch, stream)
+            self.epoch += 1
+        self.r = self.R
+
+    def true_factors(self):
+        """(U, V) at true scale over the r columns held, fp32 (new tensors)."""
+        w = self.r - self.R
+        U = torch.cat([self.Uk.float(), self.Uw[:, :, :w]], dim=2)
+        V = torch.cat([self.Vk.float(), self.Vw[:, :, :w]], dim=2)
+        gs = self.gam if self.rule == "kda" else self.gam[..., None]
+        return U * gs[:, :, None, :], V
 
     def step_and_maybe_compress(self, q, k, v, g, beta, o, stream=None) -> bool:
         """One decode step; compress afterwards when all R + W columns are held."""

@@ -103,9 +103,31 @@ seed_status decode_step(const char* fn, int rule, int batch, int heads, int d_k,
   SEED_PTR(V);
   SEED_PTR(vbar);
   if (lazy) SEED_PTR(gam);
-  return device_status(fn, seed::launch_step(rule, in_dtype == SEED_BF16, batch, heads, d_k, d_v,
-                                             cap, r, a, U, V, lazy ? gam : nullptr, vbar, q, k, v,
-                                             g, beta, o, static_cast<hipStream_t>(stream)));
+  return device_status(fn, seed::launch_step(rule, in_dtype == SEED_BF16, seed::kStoreF32, batch,
+                                             heads, d_k, d_v, cap, r, 0, a, U, V, nullptr, nullptr,
+                                             lazy ? gam : nullptr, vbar, q, k, v, g, beta, o,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int store_fmt_of(int store_dtype) {
+  return store_dtype == SEED_BF16 ? seed::kStoreBF16 : seed::kStoreF16;
+}
+
+// Shapes of the 16-bit form: R kept columns, a window of W fp32 columns,
+// r columns held in all.
+seed_status check_h16(const char* fn, int batch, int heads, int d_k, int d_v, int R, int W, int r,
+                      int store_dtype) {
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (store_dtype != SEED_BF16 && store_dtype != SEED_F16)
+    return fail(SEED_E_ARG, "%s: store dtype must be SEED_BF16 or SEED_F16 (got %d)", fn,
+                store_dtype);
+  if (R <= 0 || W <= 0 || r < R || r > R + W)
+    return fail(SEED_E_SHAPE, "%s: need R > 0, W > 0 and R <= r <= R + W (got R=%d W=%d r=%d)", fn,
+                R, W, r);
+  if (R + W > seed::kMaxCap)
+    return fail(SEED_E_UNSUPPORTED, "%s: capacity R + W = %d above %d", fn, R + W, seed::kMaxCap);
+  return SEED_OK;
 }
 
 seed_status compress(const char* fn, int rule, int batch, int heads, int d_k, int d_v, int cap,
@@ -127,8 +149,9 @@ seed_status compress(const char* fn, int rule, int batch, int heads, int d_k, in
   if (seed::compress_lds_bytes(r, R) > seed::kMaxLds)
     return fail(SEED_E_UNSUPPORTED, "%s: %d columns at rank %d need more LDS than a CU has", fn,
                 r, R);
-  return device_status(fn, seed::launch_compress(batch, heads, d_k, d_v, cap, r, R, U, V,
-                                                 lazy ? gam : nullptr, rule == SEED_RULE_KDA,
+  seed::CompressArgs args{batch * heads, cap, r, R, U, V, nullptr, nullptr,
+                          lazy ? gam : nullptr, rule == SEED_RULE_KDA, 0, 0u, 0u, 0u};
+  return device_status(fn, seed::launch_compress(d_k, d_v, seed::kStoreF32, args,
                                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -163,6 +186,86 @@ seed_status seed_compress_lazy(int rule, int batch, int heads, int d_k, int d_v,
                                int R, float* U, float* V, float* gam, void* stream) {
   return compress("seed_compress_lazy", rule, batch, heads, d_k, d_v, cap, r, R, U, V, gam, true,
                   stream);
+}
+
+seed_status seed_decode_step_h16(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
+                                 int r, float* a, const void* Uk, const void* Vk, float* Uw,
+                                 float* Vw, float* gam, const float* vbar, const void* q,
+                                 const void* k, const void* v, int in_dtype, int store_dtype,
+                                 const float* g, const float* beta, float* o, void* stream) {
+  const char* fn = "seed_decode_step_h16";
+  seed_status st = check_h16(fn, batch, heads, d_k, d_v, R, W, r, store_dtype);
+  if (st != SEED_OK) return st;
+  if (r == R + W)
+    return fail(SEED_E_FULL, "%s: all %d window columns are in use; compress first", fn, W);
+  st = check_step_inputs(fn, rule, q, k, v, in_dtype, g, beta, o);
+  if (st != SEED_OK) return st;
+  SEED_PTR(a);
+  SEED_PTR(Uk);
+  SEED_PTR(Vk);
+  SEED_PTR(Uw);
+  SEED_PTR(Vw);
+  SEED_PTR(gam);
+  SEED_PTR(vbar);
+  return device_status(
+      fn, seed::launch_step(rule, in_dtype == SEED_BF16, store_fmt_of(store_dtype), batch, heads,
+                            d_k, d_v, W, r, R, a, Uw, Vw, static_cast<const uint16_t*>(Uk),
+                            static_cast<const uint16_t*>(Vk), gam, vbar, q, k, v, g, beta, o,
+                            static_cast<hipStream_t>(stream)));
+}
+
+seed_status seed_compress_h16(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
+                              int r, void* Uk, void* Vk, float* Uw, float* Vw, float* gam,
+                              int store_dtype, int rounding, uint64_t seed, uint32_t epoch,
+                              void* stream) {
+  const char* fn = "seed_compress_h16";
+  seed_status st = check_h16(fn, batch, heads, d_k, d_v, R, W, r, store_dtype);
+  if (st != SEED_OK) return st;
+  if (rule != SEED_RULE_GDN && rule != SEED_RULE_KDA && rule != SEED_RULE_MAMBA2)
+    return fail(SEED_E_ARG, "%s: unknown rule %d", fn, rule);
+  if (rounding != SEED_ROUND_NEAREST && rounding != SEED_ROUND_STOCHASTIC)
+    return fail(SEED_E_ARG, "%s: unknown rounding %d", fn, rounding);
+  if (R > 32) return fail(SEED_E_UNSUPPORTED, "%s: rank %d above 32", fn, R);
+  SEED_PTR(Uk);
+  SEED_PTR(Vk);
+  SEED_PTR(Uw);
+  SEED_PTR(Vw);
+  SEED_PTR(gam);
+  if (r <= R) return ok();
+  if (seed::compress_lds_bytes(r, R) > seed::kMaxLds)
+    return fail(SEED_E_UNSUPPORTED, "%s: %d columns at rank %d need more LDS than a CU has", fn,
+                r, R);
+  seed::CompressArgs args{batch * heads, W, r, R, Uw, Vw,
+                          static_cast<uint16_t*>(Uk), static_cast<uint16_t*>(Vk), gam,
+                          rule == SEED_RULE_KDA, rounding == SEED_ROUND_STOCHASTIC, epoch,
+                          (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32)};
+  return device_status(fn, seed::launch_compress(d_k, d_v, store_fmt_of(store_dtype), args,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+seed_status seed_round_factors(int batch, int heads, int d_k, int d_v, int R, const float* U,
+                               const float* V, void* Uk, void* Vk, int store_dtype, int rounding,
+                               uint64_t seed, uint32_t epoch, void* stream) {
+  const char* fn = "seed_round_factors";
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (store_dtype != SEED_BF16 && store_dtype != SEED_F16)
+    return fail(SEED_E_ARG, "%s: store dtype must be SEED_BF16 or SEED_F16 (got %d)", fn,
+                store_dtype);
+  if (rounding != SEED_ROUND_NEAREST && rounding != SEED_ROUND_STOCHASTIC)
+    return fail(SEED_E_ARG, "%s: unknown rounding %d", fn, rounding);
+  if (R <= 0 || R > seed::kMaxCap)
+    return fail(SEED_E_SHAPE, "%s: need 0 < R <= %d (got %d)", fn, seed::kMaxCap, R);
+  SEED_PTR(U);
+  SEED_PTR(V);
+  SEED_PTR(Uk);
+  SEED_PTR(Vk);
+  return device_status(
+      fn, seed::launch_round_factors(store_fmt_of(store_dtype), batch * heads, R, d_k, d_v, U, V,
+                                     static_cast<uint16_t*>(Uk), static_cast<uint16_t*>(Vk),
+                                     rounding == SEED_ROUND_STOCHASTIC, epoch,
+                                     (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32),
+                                     static_cast<hipStream_t>(stream)));
 }
 
 seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
@@ -217,6 +320,6 @@ const char* seed_status_string(int status) {
 
 const char* seed_last_error(void) { return g_err; }
 
-int seed_abi_version(void) { return 101; }
+int seed_abi_version(void) { return 102; }
 
 }  // extern "C"

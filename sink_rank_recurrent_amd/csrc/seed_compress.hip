@@ -359,11 +359,6 @@ size_t compress_lds_bytes(int n, int R) { return compress_wave_lds_bytes(n, R); 
 
 size_t from_dense_lds_bytes(int d_k, int R) { return 4 * lds_floats(padded(d_k), R); }
 
-hipError_t launch_compress(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
-                           float* U, float* V, float* gam, int gam_per_row, hipStream_t stream) {
-  return launch_compress_wave(batch, heads, d_k, d_v, cap, n, R, U, V, gam, gam_per_row, stream);
-}
-
 hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                              const float* S, const float* vbar, float* a, float* U, float* V,
                              hipStream_t stream) {

@@ -184,14 +184,16 @@ struct Lay {
 
 // ---------------------------------------------------------------------------
 // A: G[i][j] = s_ij sum_e X[e][i] X[e][j] for i, j < NMAX (zero beyond n),
-// s_ij = d_i d_j when SCALE, else 1.  X holds one unit's columns, D entries
-// each.  MFMA 16x16x4: lane l feeds column 16 t + l % 16 of tile t at the
-// k-slot l / 16.  Wave w sums e over [w D / NW, (w + 1) D / NW), slot kk
-// over its quarter of that range; with two waves the partial sums meet in
-// LDS (wave 1 stores, wave 0 adds and stores the total).  If rs is not
-// NULL, row e of X is first multiplied by rs[e] (rs_per_row) or by rs[0].
-template <int NMAX, int NW, int D, bool SCALE>
-__device__ __forceinline__ void gram(const float* __restrict__ X, int n, float* __restrict__ G,
+// s_ij = d_i d_j when SCALE, else 1.  Column j < kR of X is the 16-bit
+// column j of Xk (format FMT), column j >= kR is column j - kR of X (fp32);
+// each holds D entries.  MFMA 16x16x4: lane l feeds column 16 t + l % 16 of
+// tile t at the k-slot l / 16.  Wave w sums e over [w D / NW, (w + 1) D / NW),
+// slot kk over its quarter of that range; with two waves the partial sums
+// meet in LDS (wave 1 stores, wave 0 adds and stores the total).  If rs is
+// not NULL, row e of X is first multiplied by rs[e] (rs_per_row) or by rs[0].
+template <int NMAX, int NW, int D, bool SCALE, int FMT>
+__device__ __forceinline__ void gram(const float* __restrict__ X, const uint16_t* __restrict__ Xk,
+                                     int kR, int n, float* __restrict__ G,
                                      const float* __restrict__ dv, const float* __restrict__ rs,
                                      bool rs_per_row) {
   constexpr int LDN = NMAX + 4;
@@ -210,8 +212,18 @@ __device__ __forceinline__ void gram(const float* __restrict__ X, int n, float* 
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int col = t * 16 + ci;
-      if (col < n) {
-        const float* src = X + (size_t)col * D + (w * 4 + kk) * KPL + s0;
+      const int off = (w * 4 + kk) * KPL + s0;
+      if (col < n && FMT != kStoreF32 && col < kR) {
+        const uint16_t* src = Xk + (size_t)col * D + off;
+#pragma unroll
+        for (int q = 0; q < KC / 4; ++q) {
+          float y[4];
+          load_vec16<FMT, 4>(src + 4 * q, y);
+          x[t][4 * q + 0] = y[0]; x[t][4 * q + 1] = y[1];
+          x[t][4 * q + 2] = y[2]; x[t][4 * q + 3] = y[3];
+        }
+      } else if (col < n) {
+        const float* src = X + (size_t)(col - kR) * D + off;
 #pragma unroll
         for (int q = 0; q < KC / 4; ++q) {
           const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * q);
@@ -426,10 +438,16 @@ __device__ __forceinline__ void tri_step(float (&h)[NMAX], int k, float hk, floa
 
 // ---------------------------------------------------------------------------
 
-template <int NMAX, int RMAX, int DK, int DV_>
-__global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
-    float* __restrict__ U, float* __restrict__ V, float* __restrict__ gam, int gam_per_row, int cap,
-    int n, int R) {
+template <int NMAX, int RMAX, int DK, int DV_, int FMT>
+__global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(CompressArgs args) {
+  const int cap = args.cap, n = args.n, R = args.R;
+  float* const __restrict__ U = args.U;
+  float* const __restrict__ V = args.V;
+  float* const __restrict__ gam = args.gam;
+  const int gam_per_row = args.gam_per_row;
+  // 16-bit layout: columns 0..R-1 are kept patterns, the fp32 arrays hold
+  // columns R..n-1 from their index 0
+  const int kR = (FMT == kStoreF32) ? 0 : R;
   using L = Lay<NMAX, RMAX>;
   constexpr int NW = L::NW, NTH = L::NTH, LDN = L::LDN;
   constexpr int PARTS = L::PARTS, CH = L::CH, NACT = L::NACT;
@@ -470,6 +488,8 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   const size_t ub = blockIdx.x;
   float* const Uh = U + ub * cap * DK;
   float* const Vh = V + ub * cap * DV_;
+  uint16_t* const Ukh = (FMT == kStoreF32) ? nullptr : args.Uk + ub * R * DK;
+  uint16_t* const Vkh = (FMT == kStoreF32) ? nullptr : args.Vk + ub * R * DV_;
   // lazily decayed form: U = Diag(gam) U~ (gam per key channel, or one scalar)
   float* const gamh = gam != nullptr ? gam + ub * (gam_per_row ? DK : 1) : nullptr;
 
@@ -490,7 +510,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
 
   // @phase A: Gram of U and column norms
-  gram<NMAX, NW, DK, false>(Uh, n, G, nullptr, gamh, gam_per_row);
+  gram<NMAX, NW, DK, false, FMT>(Uh, Ukh, kR, n, G, nullptr, gamh, gam_per_row);
   __syncthreads();
   if (act) {
     const float gtt = G[t * LDN + t];
@@ -509,7 +529,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
   __syncthreads();
   // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
-  gram<NMAX, NW, DV_, true>(Vh, n, G, DVs, nullptr, false);
+  gram<NMAX, NW, DV_, true, FMT>(Vh, Vkh, kR, n, G, DVs, nullptr, false);
 
   // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
   if constexpr (NW == 1) {
@@ -1027,10 +1047,22 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       const int E = q * NW + w;
       const float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
       const int ld = isu ? DK : DV_;
+      if constexpr (FMT == kStoreF32) {
 #pragma unroll
-      for (int K = 0; K < NK; ++K) {
-        const int j = 4 * K + kk;
-        dst[K] = (j < n) ? base[(size_t)j * ld + ci] : 0.f;
+        for (int K = 0; K < NK; ++K) {
+          const int j = 4 * K + kk;
+          dst[K] = (j < n) ? base[(size_t)j * ld + ci] : 0.f;
+        }
+      } else {
+        const uint16_t* basek = isu ? Ukh + 16 * E : Vkh + 16 * (E - TU);
+#pragma unroll
+        for (int K = 0; K < NK; ++K) {
+          const int j = 4 * K + kk;
+          float x = 0.f;
+          if (j < kR) x = widen16<FMT>(basek[(size_t)j * ld + ci]);
+          else if (j < n) x = base[(size_t)(j - kR) * ld + ci];
+          dst[K] = x;
+        }
       }
       if (isu) {
 #pragma unroll
@@ -1052,14 +1084,32 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
         for (int C = 0; C < NC; ++C)
           acc[C] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[K], isu ? bt[C][K] : bp[C][K], acc[C],
                                                         0, 0, 0);
-      float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
       const int ld = isu ? DK : DV_;
+      if constexpr (FMT == kStoreF32) {
+        float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
 #pragma unroll
-      for (int C = 0; C < NC; ++C) {
-        const int cc = 16 * C + ci;
-        if (cc < R)
-          *reinterpret_cast<float4*>(base + (size_t)cc * ld + 4 * kk) =
-              make_float4(acc[C][0], acc[C][1], acc[C][2], acc[C][3]);
+        for (int C = 0; C < NC; ++C) {
+          const int cc = 16 * C + ci;
+          if (cc < R)
+            *reinterpret_cast<float4*>(base + (size_t)cc * ld + 4 * kk) =
+                make_float4(acc[C][0], acc[C][1], acc[C][2], acc[C][3]);
+        }
+      } else {
+        // rows 16 E' + 4 kk .. + 3 of column cc: one group of four elements
+        // of the unit's factor block (U column cc at f = cc d_k + row, V
+        // column cc at f = R d_k + cc d_v + row)
+        uint16_t* basek = isu ? Ukh + 16 * E : Vkh + 16 * (E - TU);
+        const uint32_t fb = isu ? 16u * E + 4u * kk : (uint32_t)R * DK + 16u * (E - TU) + 4u * kk;
+#pragma unroll
+        for (int C = 0; C < NC; ++C) {
+          const int cc = 16 * C + ci;
+          if (cc < R) {
+            const float xv[4] = {acc[C][0], acc[C][1], acc[C][2], acc[C][3]};
+            *reinterpret_cast<uint2*>(basek + (size_t)cc * ld + 4 * kk) =
+                round_pack4<FMT>(xv, args.stochastic != 0, fb + (uint32_t)(cc * ld),
+                                 (uint32_t)blockIdx.x, args.epoch, args.key_lo, args.key_hi);
+          }
+        }
       }
 #pragma unroll
       for (int K = 0; K < NK; ++K) av[K] = an[K];
@@ -1081,9 +1131,8 @@ constexpr size_t wave_lds_bytes() {
   return 4 * (size_t)Lay<NMAX, RMAX>::TOTAL;
 }
 
-template <int NMAX, int RMAX, int DK, int DV_>
-hipError_t wave_go(int units, int cap, int n, int R, float* U, float* V, float* gam,
-                   int gam_per_row, hipStream_t s) {
+template <int NMAX, int RMAX, int DK, int DV_, int FMT>
+hipError_t wave_go(const CompressArgs& args, hipStream_t s) {
   constexpr size_t bytes = wave_lds_bytes<NMAX, RMAX>();
   // the LDS limit is raised once per device, so that later calls (also
   // under stream capture) only enqueue the kernel
@@ -1094,13 +1143,13 @@ hipError_t wave_go(int units, int cap, int n, int R, float* U, float* V, float* 
   const unsigned long long bit = 1ull << (dev & 63);
   if (!(lds_set.load(std::memory_order_acquire) & bit)) {
     err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(compress_wave_kernel<NMAX, RMAX, DK, DV_>),
+        reinterpret_cast<const void*>(compress_wave_kernel<NMAX, RMAX, DK, DV_, FMT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (err != hipSuccess) return err;
     lds_set.fetch_or(bit, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL((compress_wave_kernel<NMAX, RMAX, DK, DV_>), dim3(units),
-                     dim3(Lay<NMAX, RMAX>::NTH), bytes, s, U, V, gam, gam_per_row, cap, n, R);
+  hipLaunchKernelGGL((compress_wave_kernel<NMAX, RMAX, DK, DV_, FMT>), dim3(args.units),
+                     dim3(Lay<NMAX, RMAX>::NTH), bytes, s, args);
   return hipGetLastError();
 }
 
@@ -1120,27 +1169,26 @@ inline size_t wave_lds_bytes_for(int n, int R) {
   }
 }
 
-template <int DK, int DV_>
-hipError_t wave_dispatch(int units, int cap, int n, int R, float* U, float* V, float* gam,
-                         int gam_per_row, hipStream_t s) {
-  const int nm = wave_nmax(n);
-  if (R <= 16) {
+template <int DK, int DV_, int FMT>
+hipError_t wave_dispatch(const CompressArgs& a, hipStream_t s) {
+  const int nm = wave_nmax(a.n);
+  if (a.R <= 16) {
     switch (nm) {
-      case 16: return wave_go<16, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-      case 32: return wave_go<32, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-      case 48: return wave_go<48, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-      case 64: return wave_go<64, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-      case 80: return wave_go<80, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-      case 96: return wave_go<96, 16, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+      case 16: return wave_go<16, 16, DK, DV_, FMT>(a, s);
+      case 32: return wave_go<32, 16, DK, DV_, FMT>(a, s);
+      case 48: return wave_go<48, 16, DK, DV_, FMT>(a, s);
+      case 64: return wave_go<64, 16, DK, DV_, FMT>(a, s);
+      case 80: return wave_go<80, 16, DK, DV_, FMT>(a, s);
+      case 96: return wave_go<96, 16, DK, DV_, FMT>(a, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (nm) {
-    case 32: return wave_go<32, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-    case 48: return wave_go<48, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-    case 64: return wave_go<64, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-    case 80: return wave_go<80, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
-    case 96: return wave_go<96, 32, DK, DV_>(units, cap, n, R, U, V, gam, gam_per_row, s);
+    case 32: return wave_go<32, 32, DK, DV_, FMT>(a, s);
+    case 48: return wave_go<48, 32, DK, DV_, FMT>(a, s);
+    case 64: return wave_go<64, 32, DK, DV_, FMT>(a, s);
+    case 80: return wave_go<80, 32, DK, DV_, FMT>(a, s);
+    case 96: return wave_go<96, 32, DK, DV_, FMT>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,5 +1,6 @@
 // Host dispatch of the wave compression kernel (seed_compress_wave.h) by
-// head shape; each shape is compiled in its own source file.
+// head shape and storage format; each (shape, format) pair is compiled in
+// its own source file.
 #include "seed_compress_wave.h"
 #include "seed_launch.h"
 
@@ -7,16 +8,19 @@ namespace seed {
 
 size_t compress_wave_lds_bytes(int n, int R) { return wave::wave_lds_bytes_for(n, R); }
 
-hipError_t launch_compress_wave(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
-                                float* U, float* V, float* gam, int gam_per_row,
-                                hipStream_t stream) {
-  const int units = batch * heads;
-  if (d_k == 128 && d_v == 128)
-    return compress_wave_128x128(units, cap, n, R, U, V, gam, gam_per_row, stream);
-  if (d_k == 128 && d_v == 64)
-    return compress_wave_128x64(units, cap, n, R, U, V, gam, gam_per_row, stream);
-  if (d_k == 64 && d_v == 64)
-    return compress_wave_64x64(units, cap, n, R, U, V, gam, gam_per_row, stream);
+hipError_t launch_compress(int d_k, int d_v, int store_fmt, const CompressArgs& args,
+                           hipStream_t stream) {
+#define SEED_COMPRESS_SHAPE(DK, DV)                                              \
+  if (d_k == DK && d_v == DV) {                                                  \
+    if (store_fmt == kStoreF32) return compress_wave_##DK##x##DV(args, stream);  \
+    if (store_fmt == kStoreBF16) return compress_wave_##DK##x##DV##_bf16(args, stream); \
+    if (store_fmt == kStoreF16) return compress_wave_##DK##x##DV##_fp16(args, stream);  \
+    return hipErrorInvalidValue;                                                 \
+  }
+  SEED_COMPRESS_SHAPE(128, 128)
+  SEED_COMPRESS_SHAPE(128, 64)
+  SEED_COMPRESS_SHAPE(64, 64)
+#undef SEED_COMPRESS_SHAPE
   return hipErrorInvalidValue;
 }
 

@@ -1,11 +1,11 @@
-// Compression kernels for 128 x 128 heads (kernel template in seed_compress_wave.h).
+// Compression kernels for 128 x 128 heads with fp32 factor columns
+// (kernel template in seed_compress_wave.h).
 #include "seed_compress_wave.h"
 
 namespace seed {
 
-hipError_t compress_wave_128x128(int units, int cap, int n, int R, float* U, float* V, float* gam,
-                              int gam_per_row, hipStream_t stream) {
-  return wave::wave_dispatch<128, 128>(units, cap, n, R, U, V, gam, gam_per_row, stream);
+hipError_t compress_wave_128x128(const CompressArgs& args, hipStream_t stream) {
+  return wave::wave_dispatch<128, 128, kStoreF32>(args, stream);
 }
 
 }  // namespace seed

@@ -1,0 +1,11 @@
+// Compression kernels for 64 x 64 heads with 16-bit (fp16) kept columns
+// (kernel template in seed_compress_wave.h).
+#include "seed_compress_wave.h"
+
+namespace seed {
+
+hipError_t compress_wave_64x64_fp16(const CompressArgs& args, hipStream_t stream) {
+  return wave::wave_dispatch<64, 64, kStoreF16>(args, stream);
+}
+
+}  // namespace seed

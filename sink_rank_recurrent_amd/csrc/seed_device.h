@@ -1,9 +1,13 @@
 // Device helpers shared by the gfx950 kernels: vector loads/stores of fp32
-// and bf16 data, and reductions over a 32-lane half of a wave64.
+// and bf16 data, reductions over a 32-lane half of a wave64, and the 16-bit
+// storage formats of the factors (widening, rounding, and the Philox
+// counter-based generator that stochastic rounding draws from).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "seed_launch.h"
 
 namespace seed {
 
@@ -73,6 +77,137 @@ __device__ __forceinline__ float sum32(float x) {
   const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
   const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
   return (__lane_id() & 32) ? hi : lo;
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit factor storage (StoreFmt in seed_launch.h).  kStoreF32 is the
+// all-fp32 layout; with kStoreBF16 or kStoreF16 the R columns a compression
+// writes are held as 16-bit patterns and every other column in fp32.
+
+// (Instantiated with kStoreF32 only in branches that the fp32 layout never
+// takes; it reads the pattern as bf16 there.)
+template <int FMT>
+__host__ __device__ __forceinline__ float widen16(uint32_t h16) {
+  if constexpr (FMT == kStoreF16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+  } else {
+    return __builtin_bit_cast(float, h16 << 16);
+  }
+}
+
+// N (2 or 4) consecutive 16-bit patterns, widened exactly.
+template <int FMT, int N>
+__device__ __forceinline__ void load_vec16(const uint16_t* __restrict__ p, float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "vector width");
+  if constexpr (N == 4) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    x[0] = widen16<FMT>(t.x & 0xffffu); x[1] = widen16<FMT>(t.x >> 16);
+    x[2] = widen16<FMT>(t.y & 0xffffu); x[3] = widen16<FMT>(t.y >> 16);
+  } else {
+    const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
+    x[0] = widen16<FMT>(t & 0xffffu); x[1] = widen16<FMT>(t >> 16);
+  }
+}
+
+// Round to nearest, ties to the even pattern.  bf16: the carry of
+// 0x7fff + (bit 16) into the kept half does exactly that, overflow included;
+// NaN stays a (quiet) NaN.  fp16: the hardware conversion, which rounds to
+// nearest-even in the default mode and overflows to infinity.
+template <int FMT>
+__host__ __device__ __forceinline__ uint32_t round_nearest16(float x) {
+  if constexpr (FMT == kStoreBF16) {
+    uint32_t b = __builtin_bit_cast(uint32_t, x);
+    if ((b & 0x7f800000u) == 0x7f800000u) return (b >> 16) | ((b & 0x7fffffu) ? 0x40u : 0u);
+    b += 0x7fffu + ((b >> 16) & 1u);
+    return b >> 16;
+  } else {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+}
+
+// Stochastic rounding: with lo <= |x| < hi the adjacent magnitudes of the
+// format, the magnitude goes to hi iff (|x| - lo)/(hi - lo) > u, where
+// u = (w >> 8) 2^-24.  In integers: the dropped low bits D of the fp32
+// pattern (2^m (|x| - lo)/(hi - lo) = D) against u: up iff D 2^(24-m) > u.
+// Magnitudes from 2^16 up become infinity in fp16.
+template <int FMT>
+__host__ __device__ __forceinline__ uint32_t round_stochastic16(float x, uint32_t w) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  const uint32_t u = w >> 8;
+  if constexpr (FMT == kStoreBF16) {
+    if ((b & 0x7f800000u) == 0x7f800000u) return (b >> 16) | ((b & 0x7fffffu) ? 0x40u : 0u);
+    return (b >> 16) + (((b & 0xffffu) << 8) > u ? 1u : 0u);
+  } else {
+    const uint32_t sign = (b >> 16) & 0x8000u;
+    const uint32_t m = b & 0x7fffffffu;
+    if (m >= 0x47800000u) return sign | (m > 0x7f800000u ? 0x7e00u : 0x7c00u);
+    const int e = (int)(m >> 23) - 127;
+    if (e >= -14) {
+      // fp16 normal range: 13 dropped bits
+      const uint32_t h = ((uint32_t)(e + 15) << 10) | ((m >> 13) & 0x3ffu);
+      return sign | (h + (((m & 0x1fffu) << 11) > u ? 1u : 0u));
+    }
+    // fp16 subnormal range, in units of 2^-24: |x| = M 2^-s with the 24-bit
+    // significand M; lo = M >> s and D = M mod 2^s, up iff D 2^24 > u 2^s
+    const bool sub32 = (m >> 23) == 0;
+    const uint32_t M = sub32 ? m : ((m & 0x7fffffu) | 0x800000u);
+    const int s = sub32 ? 125 : -(e + 1);
+    uint32_t lo, up;
+    if (s < 24) {
+      lo = M >> s;
+      up = ((M & ((1u << s) - 1u)) << (24 - s)) > u ? 1u : 0u;
+    } else {
+      lo = 0u;
+      const int t = s - 24;
+      up = (t >= 24) ? ((u == 0u && M != 0u) ? 1u : 0u)
+                     : (((uint64_t)u << t) < (uint64_t)M ? 1u : 0u);
+    }
+    return sign | (lo + up);
+  }
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC 2011): ten rounds on a 4 x 32-bit counter, each two
+// 32 x 32 -> 64-bit products mixed with the key, the key advanced by the
+// Weyl increments between rounds.  The counter is replaced by the output.
+__host__ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = (uint32_t)p1;
+    c[2] = n2;
+    c[3] = (uint32_t)p0;
+  }
+}
+
+// Four consecutive elements f0 .. f0 + 3 (f0 a multiple of 4) of a unit's
+// rank-R factor block -- U column c row i at f = c d_k + i, then V column c
+// row i at f = R d_k + c d_v + i -- rounded and packed into two words.
+// Stochastic rounding takes word f mod 4 of Philox(counter = (f0 / 4, unit,
+// epoch, 0), key = (seed low, seed high)).
+template <int FMT>
+__device__ __forceinline__ uint2 round_pack4(const float (&x)[4], bool stochastic, uint32_t f0,
+                                             uint32_t unit, uint32_t epoch, uint32_t key_lo,
+                                             uint32_t key_hi) {
+  uint32_t h[4];
+  if (stochastic) {
+    uint32_t c[4] = {f0 >> 2, unit, epoch, 0u};
+    philox4x32_10(c, key_lo, key_hi);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = round_stochastic16<FMT>(x[e], c[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = round_nearest16<FMT>(x[e]);
+  }
+  return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
 }
 
 }  // namespace seed

@@ -4,8 +4,13 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace seed {
+
+// Storage of the factor columns: all fp32, or the R columns the last
+// compression wrote as 16-bit patterns (bf16 or fp16) and the rest fp32.
+enum StoreFmt { kStoreF32 = 0, kStoreBF16 = 1, kStoreF16 = 2 };
 
 // Largest factor capacity (R + W) the kernels are compiled for.
 constexpr int kMaxCap = 96;
@@ -14,10 +19,15 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 // gam == NULL: U decayed in place; otherwise the lazily decayed form
 // U = Diag(gam) U~ (gam per key channel for KDA, one scalar per unit else).
-hipError_t launch_step(int rule, bool in_bf16, int batch, int heads, int d_k, int d_v, int cap,
-                       int r, float* a, float* U, float* V, float* gam, const float* vbar, const void* q,
-                       const void* k, const void* v, const float* g, const float* beta, float* o,
-                       hipStream_t stream);
+// store_fmt (StoreFmt) kStoreF32: every column in U, V (capacity cap);
+// kStoreBF16 / kStoreF16: columns j < kR are the 16-bit Uk, Vk ([unit][kR]
+// columns) and columns j >= kR are U, V at index j - kR (capacity cap);
+// these need gam.
+hipError_t launch_step(int rule, bool in_bf16, int store_fmt, int batch, int heads, int d_k,
+                       int d_v, int cap, int r, int kR, float* a, float* U, float* V,
+                       const uint16_t* Uk, const uint16_t* Vk, float* gam, const float* vbar,
+                       const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float* o, hipStream_t stream);
 
 hipError_t launch_dense(int rule, bool in_bf16, int batch, int heads, int d_k, int d_v, float* S,
                         const void* q, const void* k, const void* v, const float* g,
@@ -33,19 +43,44 @@ size_t compress_wave_lds_bytes(int n, int R);
 // Dynamic LDS bytes the dense-to-shallow kernel needs.
 size_t from_dense_lds_bytes(int d_k, int R);
 
-// Compression of n <= kWaveMaxN columns to rank R (seed_compress_wave.h).
-// gam as for launch_step (NULL: U at true scale); it is reset to 1.
-hipError_t launch_compress(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
-                           float* U, float* V, float* gam, int gam_per_row, hipStream_t stream);
-hipError_t launch_compress_wave(int batch, int heads, int d_k, int d_v, int cap, int n, int R,
-                                float* U, float* V, float* gam, int gam_per_row,
+// Arguments of the compression of n <= kWaveMaxN columns to rank R
+// (seed_compress_wave.h).  fp32 layout (Uk == NULL): columns 0..n-1 in U, V
+// (capacity cap), the result written in place to columns 0..R-1.  16-bit
+// layout: columns 0..R-1 are the patterns in Uk, Vk ([unit][R] columns) and
+// columns R..n-1 are U, V at index j - R (capacity cap); the result is
+// rounded into Uk, Vk (to nearest, or stochastically with the Philox words
+// of (unit, epoch, key)).  gam as for launch_step (NULL: U at true scale);
+// it is reset to 1.
+struct CompressArgs {
+  int units, cap, n, R;
+  float* U;
+  float* V;
+  uint16_t* Uk;
+  uint16_t* Vk;
+  float* gam;
+  int gam_per_row;
+  int stochastic;
+  uint32_t epoch, key_lo, key_hi;
+};
+
+hipError_t launch_compress(int d_k, int d_v, int store_fmt, const CompressArgs& args,
+                           hipStream_t stream);
+#define SEED_DECLARE_COMPRESS_SHAPE(DK, DV)                                                    \
+  hipError_t compress_wave_##DK##x##DV(const CompressArgs& args, hipStream_t stream);          \
+  hipError_t compress_wave_##DK##x##DV##_bf16(const CompressArgs& args, hipStream_t stream);   \
+  hipError_t compress_wave_##DK##x##DV##_fp16(const CompressArgs& args, hipStream_t stream);
+SEED_DECLARE_COMPRESS_SHAPE(128, 128)
+SEED_DECLARE_COMPRESS_SHAPE(128, 64)
+SEED_DECLARE_COMPRESS_SHAPE(64, 64)
+#undef SEED_DECLARE_COMPRESS_SHAPE
+
+// Rounds fp32 rank-R factors U [unit][R][d_k], V [unit][R][d_v] into the
+// 16-bit Uk, Vk (same layouts), element numbering and words as in the
+// compression.
+hipError_t launch_round_factors(int store_fmt, int units, int R, int d_k, int d_v, const float* U,
+                                const float* V, uint16_t* Uk, uint16_t* Vk, int stochastic,
+                                uint32_t epoch, uint32_t key_lo, uint32_t key_hi,
                                 hipStream_t stream);
-hipError_t compress_wave_128x128(int units, int cap, int n, int R, float* U, float* V, float* gam,
-                                 int gam_per_row, hipStream_t stream);
-hipError_t compress_wave_128x64(int units, int cap, int n, int R, float* U, float* V, float* gam,
-                                int gam_per_row, hipStream_t stream);
-hipError_t compress_wave_64x64(int units, int cap, int n, int R, float* U, float* V, float* gam,
-                               int gam_per_row, hipStream_t stream);
 
 hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                              const float* S, const float* vbar, float* a, float* U, float* V,

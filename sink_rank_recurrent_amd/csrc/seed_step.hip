@@ -28,25 +28,35 @@
 // reads U~ without rewriting it (c_k = U~^T (gam k), c_q = U~^T (gam q))
 // and appends U~_r = k / gam.  The arithmetic is Lemma 2's; only the U
 // write-back disappears.
+//
+// FMT != kStoreF32 (16-bit kept factors, always with LAZY): columns j < kR
+// are the 16-bit patterns the last compression rounded (SEED figures and
+// tables, Table 4 and Table 9: factors rounded at every compression) and are
+// widened exactly on load; columns j >= kR, appended since, are fp32 at
+// index j - kR of U and V.  A step never writes the 16-bit columns.
 #include "seed_device.h"
 #include "seed_launch.h"
 
 namespace seed {
 
-template <int RULE, int DK, int DV, typename IN_T, int SLOTS, bool LAZY>
+template <int RULE, int DK, int DV, typename IN_T, int SLOTS, bool LAZY, int FMT>
 __global__ __launch_bounds__(256) void seed_step_kernel(
     float* __restrict__ a, float* __restrict__ U, float* __restrict__ V,
-    float* __restrict__ gam, const float* __restrict__ vbar, const IN_T* __restrict__ q,
-    const IN_T* __restrict__ k, const IN_T* __restrict__ v, const float* __restrict__ g,
-    const float* __restrict__ beta, float* __restrict__ o, int heads, int cap, int r) {
+    const uint16_t* __restrict__ Uk, const uint16_t* __restrict__ Vk, float* __restrict__ gam,
+    const float* __restrict__ vbar, const IN_T* __restrict__ q, const IN_T* __restrict__ k,
+    const IN_T* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
+    float* __restrict__ o, int heads, int cap, int r, int kR_arg) {
+  static_assert(FMT == kStoreF32 || LAZY, "16-bit kept columns are never decayed in place");
   constexpr int EK = DK / 32;  // key-space entries per lane
   constexpr int EV = DV / 32;  // value-space entries per lane
+  const int kR = (FMT == kStoreF32) ? 0 : kR_arg;
   const int unit = blockIdx.x;
   const int h = unit % heads;
   const int tid = threadIdx.x;
   const int grp = tid >> 5;
   const int lane = tid & 31;
   const size_t ub = (size_t)unit;
+  // fp32 columns j >= kR at index j - kR
   float* Uh = U + ub * cap * DK;
   float* Vh = V + ub * cap * DV;
 
@@ -56,9 +66,12 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     const int j = grp + 8 * s;
-    if (j < r) {
-      load_vec<EK>(Uh + (size_t)j * DK + lane * EK, u[s]);
-      load_vec<EV>(Vh + (size_t)j * DV + lane * EV, w[s]);
+    if (FMT != kStoreF32 && j < r && j < kR) {
+      load_vec16<FMT, EK>(Uk + (ub * kR + j) * DK + lane * EK, u[s]);
+      load_vec16<FMT, EV>(Vk + (ub * kR + j) * DV + lane * EV, w[s]);
+    } else if (j < r) {
+      load_vec<EK>(Uh + (size_t)(j - kR) * DK + lane * EK, u[s]);
+      load_vec<EV>(Vh + (size_t)(j - kR) * DV + lane * EV, w[s]);
     } else {
 #pragma unroll
       for (int e = 0; e < EK; ++e) u[s][e] = 0.f;
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
       float kd[EK];
 #pragma unroll
       for (int e = 0; e < EK; ++e) kd[e] = kk[e] / gn[e];
-      store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kd);
+      store_vec<EK>(Uh + (size_t)(r - kR) * DK + lane * EK, kd);
     } else {
       store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kk);
     }
@@ -233,40 +246,57 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
     }
     const float eps = eps_s[tid];
     const float vn = (RULE == kMAMBA2) ? eps : bt * (eps - tk);
-    Vh[(size_t)r * DV + tid] = vn;
+    Vh[(size_t)(r - kR) * DV + tid] = vn;
     o[ub * DV + tid] = sink_s[tid] + tq + vn * kq;
   }
 }
 
 namespace {
 
+struct StepArgs {
+  int units, heads, cap, r, kR;
+  float* a;
+  float* U;
+  float* V;
+  const uint16_t* Uk;
+  const uint16_t* Vk;
+  float* gam;
+  const float* vbar;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  float* o;
+};
+
+template <int RULE, int DK, int DV, typename IN_T, int SLOTS, bool LAZY, int FMT>
+void step_launch(const StepArgs& p, hipStream_t s) {
+  hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS, LAZY, FMT>), dim3(p.units),
+                     dim3(256), 0, s, p.a, p.U, p.V, p.Uk, p.Vk, p.gam, p.vbar,
+                     static_cast<const IN_T*>(p.q), static_cast<const IN_T*>(p.k),
+                     static_cast<const IN_T*>(p.v), p.g, p.beta, p.o, p.heads, p.cap, p.r, p.kR);
+}
+
 template <int RULE, int DK, int DV, typename IN_T, int SLOTS>
-hipError_t step_go(int units, int heads, int cap, int r, float* a, float* U, float* V, float* gam,
-                   const float* vbar, const void* q, const void* k, const void* v, const float* g,
-                   const float* beta, float* o, hipStream_t s) {
-  if (gam != nullptr) {
-    hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS, true>), dim3(units), dim3(256),
-                       0, s, a, U, V, gam, vbar, static_cast<const IN_T*>(q),
-                       static_cast<const IN_T*>(k), static_cast<const IN_T*>(v), g, beta, o,
-                       heads, cap, r);
+hipError_t step_go(int fmt, const StepArgs& p, hipStream_t s) {
+  if (fmt == kStoreBF16) {
+    step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreBF16>(p, s);
+  } else if (fmt == kStoreF16) {
+    step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreF16>(p, s);
+  } else if (p.gam != nullptr) {
+    step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreF32>(p, s);
   } else {
-    hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS, false>), dim3(units),
-                       dim3(256), 0, s, a, U, V, gam, vbar, static_cast<const IN_T*>(q),
-                       static_cast<const IN_T*>(k), static_cast<const IN_T*>(v), g, beta, o,
-                       heads, cap, r);
+    step_launch<RULE, DK, DV, IN_T, SLOTS, false, kStoreF32>(p, s);
   }
   return hipGetLastError();
 }
 
 template <int RULE, int DK, int DV, typename IN_T>
-hipError_t step_slots(int units, int heads, int cap, int r, float* a, float* U, float* V,
-                      float* gam, const float* vbar, const void* q, const void* k, const void* v,
-                      const float* g, const float* beta, float* o, hipStream_t s) {
-  const int need = (r + 7) / 8;
-#define SEED_STEP_SLOTS(N)                                                                    \
-  if (need <= N)                                                                              \
-    return step_go<RULE, DK, DV, IN_T, N>(units, heads, cap, r, a, U, V, gam, vbar, q, k, v, g, \
-                                          beta, o, s);
+hipError_t step_slots(int fmt, const StepArgs& p, hipStream_t s) {
+  const int need = (p.r + 7) / 8;
+#define SEED_STEP_SLOTS(N) \
+  if (need <= N) return step_go<RULE, DK, DV, IN_T, N>(fmt, p, s);
   SEED_STEP_SLOTS(1)
   SEED_STEP_SLOTS(2)
   SEED_STEP_SLOTS(3)
@@ -281,51 +311,34 @@ hipError_t step_slots(int units, int heads, int cap, int r, float* a, float* U, 
 }
 
 template <int RULE, typename IN_T>
-hipError_t step_dims(int units, int heads, int d_k, int d_v, int cap, int r, float* a, float* U,
-                     float* V, float* gam, const float* vbar, const void* q, const void* k, const void* v,
-                     const float* g, const float* beta, float* o, hipStream_t s) {
-  if (d_k == 128 && d_v == 128)
-    return step_slots<RULE, 128, 128, IN_T>(units, heads, cap, r, a, U, V, gam, vbar, q, k, v, g, beta,
-                                            o, s);
-  if (d_k == 128 && d_v == 64)
-    return step_slots<RULE, 128, 64, IN_T>(units, heads, cap, r, a, U, V, gam, vbar, q, k, v, g, beta,
-                                           o, s);
-  if (d_k == 64 && d_v == 64)
-    return step_slots<RULE, 64, 64, IN_T>(units, heads, cap, r, a, U, V, gam, vbar, q, k, v, g, beta,
-                                          o, s);
+hipError_t step_dims(int d_k, int d_v, int fmt, const StepArgs& p, hipStream_t s) {
+  if (d_k == 128 && d_v == 128) return step_slots<RULE, 128, 128, IN_T>(fmt, p, s);
+  if (d_k == 128 && d_v == 64) return step_slots<RULE, 128, 64, IN_T>(fmt, p, s);
+  if (d_k == 64 && d_v == 64) return step_slots<RULE, 64, 64, IN_T>(fmt, p, s);
   return hipErrorInvalidValue;
 }
 
 template <int RULE>
-hipError_t step_dtype(bool bf16, int units, int heads, int d_k, int d_v, int cap, int r, float* a,
-                      float* U, float* V, float* gam, const float* vbar, const void* q, const void* k,
-                      const void* v, const float* g, const float* beta, float* o, hipStream_t s) {
-  if (bf16)
-    return step_dims<RULE, bf16_t>(units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v, g, beta,
-                                   o, s);
-  return step_dims<RULE, float>(units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v, g, beta, o,
-                                s);
+hipError_t step_dtype(bool bf16, int d_k, int d_v, int fmt, const StepArgs& p, hipStream_t s) {
+  if (bf16) return step_dims<RULE, bf16_t>(d_k, d_v, fmt, p, s);
+  return step_dims<RULE, float>(d_k, d_v, fmt, p, s);
 }
 
 }  // namespace
 
-hipError_t launch_step(int rule, bool in_bf16, int batch, int heads, int d_k, int d_v, int cap,
-                       int r, float* a, float* U, float* V, float* gam, const float* vbar, const void* q,
-                       const void* k, const void* v, const float* g, const float* beta, float* o,
-                       hipStream_t stream) {
-  const int units = batch * heads;
+hipError_t launch_step(int rule, bool in_bf16, int store_fmt, int batch, int heads, int d_k,
+                       int d_v, int cap, int r, int kR, float* a, float* U, float* V,
+                       const uint16_t* Uk, const uint16_t* Vk, float* gam, const float* vbar,
+                       const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float* o, hipStream_t stream) {
+  if (store_fmt != kStoreF32 && gam == nullptr) return hipErrorInvalidValue;
+  const StepArgs p{batch * heads, heads, cap, r, store_fmt == kStoreF32 ? 0 : kR, a, U, V, Uk, Vk,
+                   gam, vbar, q, k, v, g, beta, o};
   switch (rule) {
-    case kGDN:
-      return step_dtype<kGDN>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v, g,
-                              beta, o, stream);
-    case kKDA:
-      return step_dtype<kKDA>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v, g,
-                              beta, o, stream);
-    case kMAMBA2:
-      return step_dtype<kMAMBA2>(in_bf16, units, heads, d_k, d_v, cap, r, a, U, V, gam, vbar, q, k, v,
-                                 g, beta, o, stream);
-    default:
-      return hipErrorInvalidValue;
+    case kGDN: return step_dtype<kGDN>(in_bf16, d_k, d_v, store_fmt, p, stream);
+    case kKDA: return step_dtype<kKDA>(in_bf16, d_k, d_v, store_fmt, p, stream);
+    case kMAMBA2: return step_dtype<kMAMBA2>(in_bf16, d_k, d_v, store_fmt, p, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

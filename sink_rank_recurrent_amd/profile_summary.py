@@ -22,9 +22,12 @@ import sys
 from collections import defaultdict
 
 GROUPS = {
-    "seed_step_kernel (U decayed in place)": r"seed_step_kernel<.*false>",
-    "seed_step_kernel (lazy decay)": r"seed_step_kernel<.*true>",
-    "compress_wave_kernel": r"compress_wave_kernel<",
+    "seed_step_kernel (U decayed in place)": r"seed_step_kernel<.*false, 0>",
+    "seed_step_kernel (lazy decay)": r"seed_step_kernel<.*true, 0>",
+    "seed_step_kernel (16-bit kept factors)": r"seed_step_kernel<.*true, [12]>",
+    "compress_wave_kernel (fp32 factors)": r"compress_wave_kernel<.*, 0>",
+    "compress_wave_kernel (16-bit kept factors)": r"compress_wave_kernel<.*, [12]>",
+    "round_factors_kernel": r"round_factors_kernel<",
     "from_dense_kernel": r"from_dense_kernel<",
     "dense_step_kernel": r"dense_step_kernel<",
 }

@@ -16,10 +16,11 @@ def test_exports_every_declared_function():
     names = binding.header_functions()
     assert set(names) == {"seed_decode_step", "seed_decode_step_lazy", "seed_compress",
                           "seed_compress_lazy", "seed_state_from_dense", "dense_decode_step",
+                          "seed_decode_step_h16", "seed_compress_h16", "seed_round_factors",
                           "seed_status_string", "seed_last_error", "seed_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.seed_abi_version() == 101
+    assert L.seed_abi_version() == 102
 
 
 def test_status_strings():
@@ -82,6 +83,48 @@ def test_lazy_validation():
     assert L.seed_compress_lazy(1, 1, 1, 128, 128, 48, 48, 33, p, p, p, None) == 3
     # r <= R: nothing launched, gam untouched
     assert L.seed_compress_lazy(1, 1, 1, 128, 128, 48, 16, 16, p, p, p, None) == 0
+
+
+def _step_h16(rule=0, R=16, W=32, r=20, store=2, ptr=ALIGNED, gam=ALIGNED, Uk=ALIGNED):
+    p = ptr
+    return L.seed_decode_step_h16(rule, 2, 3, 128, 128, R, W, r, p, Uk, p, p, p, gam, p, p, p, p,
+                                  1, store, p, p, p, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(r=48), 4, "compress first"),
+    (dict(r=15), 2, "R <= r"),
+    (dict(r=49), 2, "R <= r"),
+    (dict(R=0, r=0), 2, "R > 0"),
+    (dict(W=90, r=20), 3, "capacity"),
+    (dict(store=0), 1, "store dtype"),
+    (dict(store=3), 1, "store dtype"),
+    (dict(gam=None), 1, "gam is NULL"),
+    (dict(Uk=MISALIGNED), 1, "Uk is not 16-byte aligned"),
+])
+def test_step_h16_rejects(kwargs, status, needle):
+    assert _step_h16(**kwargs) == status
+    assert needle in L.seed_last_error().decode()
+
+
+def test_compress_h16_and_round_validation():
+    p = ALIGNED
+    # rule, B, H, d_k, d_v, R, W, r, Uk, Vk, Uw, Vw, gam, store, rounding, seed, epoch, stream
+    assert L.seed_compress_h16(0, 1, 1, 128, 128, 16, 32, 48, p, p, p, p, p, 2, 2, 0, 0, None) == 1
+    assert b"rounding" in L.seed_last_error()
+    assert L.seed_compress_h16(5, 1, 1, 128, 128, 16, 32, 48, p, p, p, p, p, 2, 0, 0, 0, None) == 1
+    assert L.seed_compress_h16(0, 1, 1, 128, 128, 33, 32, 48, p, p, p, p, p, 2, 0, 0, 0, None) == 3
+    assert L.seed_compress_h16(0, 1, 1, 128, 128, 16, 32, 49, p, p, p, p, p, 2, 0, 0, 0, None) == 2
+    assert L.seed_compress_h16(0, 1, 1, 128, 128, 16, 32, 48, p, p, p, p, None, 1, 0, 0, 0,
+                               None) == 1
+    # r == R: nothing to compress, nothing launched
+    assert L.seed_compress_h16(0, 1, 1, 128, 128, 16, 32, 16, p, p, p, p, p, 1, 1, 7, 3, None) == 0
+    assert L.seed_last_error() == b""
+    # B, H, d_k, d_v, R, U, V, Uk, Vk, store, rounding, seed, epoch, stream
+    assert L.seed_round_factors(1, 1, 128, 128, 0, p, p, p, p, 1, 0, 0, 0, None) == 2
+    assert L.seed_round_factors(1, 1, 128, 128, 16, p, p, p, p, 0, 0, 0, 0, None) == 1
+    assert L.seed_round_factors(1, 1, 128, 128, 16, p, p, None, p, 1, 0, 0, 0, None) == 1
+    assert L.seed_round_factors(1, 1, 96, 128, 16, p, p, p, p, 1, 0, 0, 0, None) == 3
 
 
 def test_from_dense_validation():
