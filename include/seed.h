@@ -169,7 +169,8 @@ seed_status seed_compress_lazy(int rule, int batch, int heads, int d_k, int d_v,
  *
  * The state holds r columns, R <= r <= R + W: column j < R is column j of
  * Uk / Vk, column j >= R is column j - R of Uw / Vw.  Right after a
- * compression r = R.
+ * compression r = R.  Built for R = 16 or 32 (other R: SEED_E_UNSUPPORTED)
+ * and R + W <= 96.
  *
  * Stochastic rounding: element f of a unit's block -- U column c row i at
  * f = c d_k + i, V column c row i at f = R d_k + c d_v + i -- takes the word

@@ -127,6 +127,9 @@ seed_status check_h16(const char* fn, int batch, int heads, int d_k, int d_v, in
                 R, W, r);
   if (R + W > seed::kMaxCap)
     return fail(SEED_E_UNSUPPORTED, "%s: capacity R + W = %d above %d", fn, R + W, seed::kMaxCap);
+  if (R != 16 && R != 32)
+    return fail(SEED_E_UNSUPPORTED, "%s: the 16-bit form is built for R = 16 or 32 (got %d)", fn,
+                R);
   return SEED_OK;
 }
 
@@ -225,7 +228,6 @@ seed_status seed_compress_h16(int rule, int batch, int heads, int d_k, int d_v, 
     return fail(SEED_E_ARG, "%s: unknown rule %d", fn, rule);
   if (rounding != SEED_ROUND_NEAREST && rounding != SEED_ROUND_STOCHASTIC)
     return fail(SEED_E_ARG, "%s: unknown rounding %d", fn, rounding);
-  if (R > 32) return fail(SEED_E_UNSUPPORTED, "%s: rank %d above 32", fn, R);
   SEED_PTR(Uk);
   SEED_PTR(Vk);
   SEED_PTR(Uw);

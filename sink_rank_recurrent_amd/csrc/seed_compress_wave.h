@@ -184,16 +184,16 @@ struct Lay {
 
 // ---------------------------------------------------------------------------
 // A: G[i][j] = s_ij sum_e X[e][i] X[e][j] for i, j < NMAX (zero beyond n),
-// s_ij = d_i d_j when SCALE, else 1.  Column j < kR of X is the 16-bit
-// column j of Xk (format FMT), column j >= kR is column j - kR of X (fp32);
+// s_ij = d_i d_j when SCALE, else 1.  Column j < KR of X is the 16-bit
+// column j of Xk (format FMT), column j >= KR is column j - KR of X (fp32);
 // each holds D entries.  MFMA 16x16x4: lane l feeds column 16 t + l % 16 of
 // tile t at the k-slot l / 16.  Wave w sums e over [w D / NW, (w + 1) D / NW),
 // slot kk over its quarter of that range; with two waves the partial sums
 // meet in LDS (wave 1 stores, wave 0 adds and stores the total).  If rs is
 // not NULL, row e of X is first multiplied by rs[e] (rs_per_row) or by rs[0].
-template <int NMAX, int NW, int D, bool SCALE, int FMT>
+template <int NMAX, int NW, int D, bool SCALE, int FMT, int KR>
 __device__ __forceinline__ void gram(const float* __restrict__ X, const uint16_t* __restrict__ Xk,
-                                     int kR, int n, float* __restrict__ G,
+                                     int n, float* __restrict__ G,
                                      const float* __restrict__ dv, const float* __restrict__ rs,
                                      bool rs_per_row) {
   constexpr int LDN = NMAX + 4;
@@ -213,7 +213,7 @@ __device__ __forceinline__ void gram(const float* __restrict__ X, const uint16_t
     for (int t = 0; t < NT; ++t) {
       const int col = t * 16 + ci;
       const int off = (w * 4 + kk) * KPL + s0;
-      if (col < n && FMT != kStoreF32 && col < kR) {
+      if (col < n && col < KR) {
         const uint16_t* src = Xk + (size_t)col * D + off;
 #pragma unroll
         for (int q = 0; q < KC / 4; ++q) {
@@ -223,7 +223,7 @@ __device__ __forceinline__ void gram(const float* __restrict__ X, const uint16_t
           x[t][4 * q + 2] = y[2]; x[t][4 * q + 3] = y[3];
         }
       } else if (col < n) {
-        const float* src = X + (size_t)(col - kR) * D + off;
+        const float* src = X + (size_t)(col - KR) * D + off;
 #pragma unroll
         for (int q = 0; q < KC / 4; ++q) {
           const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * q);
@@ -446,8 +446,9 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   float* const __restrict__ gam = args.gam;
   const int gam_per_row = args.gam_per_row;
   // 16-bit layout: columns 0..R-1 are kept patterns, the fp32 arrays hold
-  // columns R..n-1 from their index 0
-  const int kR = (FMT == kStoreF32) ? 0 : R;
+  // columns R..n-1 from their index 0.  It is compiled for R = RMAX only,
+  // so that every column's source is known at compile time.
+  constexpr int KR = (FMT == kStoreF32) ? 0 : RMAX;
   using L = Lay<NMAX, RMAX>;
   constexpr int NW = L::NW, NTH = L::NTH, LDN = L::LDN;
   constexpr int PARTS = L::PARTS, CH = L::CH, NACT = L::NACT;
@@ -510,7 +511,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
 
   // @phase A: Gram of U and column norms
-  gram<NMAX, NW, DK, false, FMT>(Uh, Ukh, kR, n, G, nullptr, gamh, gam_per_row);
+  gram<NMAX, NW, DK, false, FMT, KR>(Uh, Ukh, n, G, nullptr, gamh, gam_per_row);
   __syncthreads();
   if (act) {
     const float gtt = G[t * LDN + t];
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
   __syncthreads();
   // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
-  gram<NMAX, NW, DV_, true, FMT>(Vh, Vkh, kR, n, G, DVs, nullptr, false);
+  gram<NMAX, NW, DV_, true, FMT, KR>(Vh, Vkh, n, G, DVs, nullptr, false);
 
   // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
   if constexpr (NW == 1) {
@@ -1059,8 +1060,8 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
         for (int K = 0; K < NK; ++K) {
           const int j = 4 * K + kk;
           float x = 0.f;
-          if (j < kR) x = widen16<FMT>(basek[(size_t)j * ld + ci]);
-          else if (j < n) x = base[(size_t)(j - kR) * ld + ci];
+          if (j < KR) x = widen16<FMT>(basek[(size_t)j * ld + ci]);
+          else if (j < n) x = base[(size_t)(j - KR) * ld + ci];
           dst[K] = x;
         }
       }
@@ -1172,6 +1173,8 @@ inline size_t wave_lds_bytes_for(int n, int R) {
 template <int DK, int DV_, int FMT>
 hipError_t wave_dispatch(const CompressArgs& a, hipStream_t s) {
   const int nm = wave_nmax(a.n);
+  // the 16-bit layout is compiled for R = RMAX
+  if (FMT != kStoreF32 && a.R != 16 && a.R != 32) return hipErrorInvalidValue;
   if (a.R <= 16) {
     switch (nm) {
       case 16: return wave_go<16, 16, DK, DV_, FMT>(a, s);

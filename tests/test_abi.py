@@ -97,6 +97,7 @@ def _step_h16(rule=0, R=16, W=32, r=20, store=2, ptr=ALIGNED, gam=ALIGNED, Uk=AL
     (dict(r=49), 2, "R <= r"),
     (dict(R=0, r=0), 2, "R > 0"),
     (dict(W=90, r=20), 3, "capacity"),
+    (dict(R=12, r=20), 3, "R = 16 or 32"),
     (dict(store=0), 1, "store dtype"),
     (dict(store=3), 1, "store dtype"),
     (dict(gam=None), 1, "gam is NULL"),
@@ -114,6 +115,7 @@ def test_compress_h16_and_round_validation():
     assert b"rounding" in L.seed_last_error()
     assert L.seed_compress_h16(5, 1, 1, 128, 128, 16, 32, 48, p, p, p, p, p, 2, 0, 0, 0, None) == 1
     assert L.seed_compress_h16(0, 1, 1, 128, 128, 33, 32, 48, p, p, p, p, p, 2, 0, 0, 0, None) == 3
+    assert L.seed_compress_h16(0, 1, 1, 128, 128, 8, 32, 38, p, p, p, p, p, 2, 0, 0, 0, None) == 3
     assert L.seed_compress_h16(0, 1, 1, 128, 128, 16, 32, 49, p, p, p, p, p, 2, 0, 0, 0, None) == 2
     assert L.seed_compress_h16(0, 1, 1, 128, 128, 16, 32, 48, p, p, p, p, None, 1, 0, 0, 0,
                                None) == 1

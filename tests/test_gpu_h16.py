@@ -198,7 +198,7 @@ def _inputs_np(x):
 @pytest.mark.parametrize("fmt", ["bf16", "fp16"])
 @pytest.mark.parametrize("rule,dims,R,W,in_dtype", [
     ("gdn", (128, 128), 16, 32, torch.bfloat16), ("kda", (128, 128), 16, 64, torch.bfloat16),
-    ("mamba2", (128, 64), 16, 32, torch.bfloat16), ("gdn", (64, 64), 12, 20, torch.float32),
+    ("mamba2", (128, 64), 16, 32, torch.bfloat16), ("gdn", (64, 64), 16, 20, torch.float32),
     ("kda", (128, 64), 32, 64, torch.float32)])
 def test_step_h16_matches_oracle(fmt, rule, dims, R, W, in_dtype):
     d_k, d_v = dims
@@ -238,7 +238,7 @@ def _unique_factors(U, V, R, gap=1e-3):
 @pytest.mark.parametrize("mode", ["nearest", "stochastic"])
 @pytest.mark.parametrize("rule,dims,R,W", [
     ("gdn", (128, 128), 16, 32), ("kda", (128, 128), 16, 64), ("mamba2", (128, 64), 16, 32),
-    ("gdn", (64, 64), 8, 24), ("kda", (128, 64), 32, 64)])
+    ("gdn", (64, 64), 16, 24), ("kda", (128, 64), 32, 64)])
 def test_compress_h16_matches_oracle(fmt, mode, rule, dims, R, W):
     d_k, d_v = dims
     tdt, ofmt, _ = FMTS[fmt]
