@@ -18,8 +18,9 @@ launch duration (HIP events on the launch stream), the dense-state baseline
 kernel on the same workload, two variants timed on the same state and
 inputs -- the lazily decayed form (U's decay kept as a running product,
 seed_decode_step_lazy) and the 16-bit form (kept factors fp16, rounded at
-every compression, seed_decode_step_h16) -- and the CPU oracle timed on a
-bounded sample.  Prints one JSON line.
+every compression, seed_decode_step_h16) -- the handoff of the converted
+states (seed_pack_states / seed_unpack_states of every request), and the CPU
+oracle timed on a bounded sample.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -380,6 +381,37 @@ def main() -> int:
             log(f"{name}: {r2['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
         del S_var
 
+    # handoff of the converted states (prefill -> decode): pack every
+    # request into one buffer, then unpack it into the slots of a batch
+    handoff = None
+    if not args.no_variant:
+        hst = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
+                                   device=dev)
+        hst.from_dense(S_dense)
+        sel = torch.arange(w.batch, dtype=torch.int32, device=dev)
+        buf = hst.pack(sel)
+        reps = 20
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            hst.pack(sel, buf)
+        ev[1].record()
+        for _ in range(reps):
+            hst.unpack(buf, sel)
+        ev[2].record()
+        torch.cuda.synchronize()
+        nbytes = buf.numel()
+        t_pack = ev[0].elapsed_time(ev[1]) / reps / 1e3
+        t_unpack = ev[1].elapsed_time(ev[2]) / reps / 1e3
+        handoff = {"head_bytes": nbytes // units, "dense_head_bytes": 4 * w.d_k * w.d_v,
+                   "requests": w.batch, "buffer_bytes": nbytes,
+                   "pack_us": t_pack * 1e6, "unpack_us": t_unpack * 1e6,
+                   "pack_GBs": 2 * nbytes / t_pack / 1e9, "unpack_GBs": 2 * nbytes / t_unpack / 1e9}
+        del hst, buf
+        log(f"handoff: pack {t_pack * 1e6:.1f} us, unpack {t_unpack * 1e6:.1f} us for "
+            f"{nbytes / 1e6:.1f} MB")
+
     dense = None
     if not args.no_dense:
         dres = run_dense(w, S_copy, inputs, o, warmup, steps, graphs=args.graphs)
@@ -443,6 +475,7 @@ def main() -> int:
         "dense_baseline": dense,
         "lazy_decay_variant": variants.get("lazy_decay_variant"),
         "fp16_factor_variant": variants.get("fp16_factor_variant"),
+        "handoff": handoff,
     }
     print(json.dumps(out), flush=True)
     return 0

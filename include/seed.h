@@ -220,6 +220,40 @@ seed_status seed_round_factors(int batch, int heads, int d_k, int d_v, int R, co
                                uint64_t seed, uint32_t epoch, void *stream);
 
 /*
+ * Handoff of shallow-form states (prefill -> decode).  At the end of the
+ * prefill a state is compressed to the sink plus rank-R factors (SEED
+ * figures and tables, Fig. 1 (a) caption, Table 1), 4 [d_k + (d_k + d_v) R]
+ * bytes per head in fp32 (Table 17 at w = 0; half the factor bytes in the
+ * 16-bit form).  Packed layout: the selected requests one after another,
+ * each with its heads in order, each head
+ *     a [d_k] fp32 | U columns 0..R-1 [R][d_k] | V columns 0..R-1 [R][d_v]
+ * with the factors in the state's storage type, seed_handoff_head_bytes()
+ * bytes per head.  store_dtype SEED_F32: U, V are the fp32 column rings
+ * [batch][heads][cap][d]; SEED_BF16 / SEED_F16: the kept arrays Uk, Vk of
+ * the 16-bit form, [batch][heads][R][d] (pass cap = R).  The state must be
+ * right after a compression or conversion (r = R; a lazy form's gam is 1
+ * then), so that columns 0..R-1 are the whole state at true scale.
+ * sel / slot: device int arrays of n_sel request indices; an index outside
+ * [0, batch) selects nothing (its part of the buffer, or its slot, is left
+ * as it was).  buf: device memory of n_sel * heads * head bytes, 16-byte
+ * aligned, not overlapping the state.
+ */
+
+/* Bytes of one packed head (0 for an unsupported shape or dtype). */
+size_t seed_handoff_head_bytes(int d_k, int d_v, int R, int store_dtype);
+
+/* seed_pack_states -- copy requests sel[0..n_sel) of a state into buf. */
+seed_status seed_pack_states(int batch, int heads, int d_k, int d_v, int cap, int R,
+                             int store_dtype, int n_sel, const int *sel, const float *a,
+                             const void *U, const void *V, void *buf, void *stream);
+
+/* seed_unpack_states -- write the n_sel packed requests of buf into batch
+ * slots slot[0..n_sel): a and columns 0..R-1 of U and V. */
+seed_status seed_unpack_states(int batch, int heads, int d_k, int d_v, int cap, int R,
+                               int store_dtype, int n_sel, const int *slot, const void *buf,
+                               float *a, void *U, void *V, void *stream);
+
+/*
  * seed_state_from_dense -- convert dense states to the shallow form.
  *
  * At the end of the prefill the states are compressed to the sink plus

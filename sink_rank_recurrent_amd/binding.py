@@ -62,9 +62,14 @@ def lib() -> ctypes.CDLL:
                                        p, p, p, p]
     L.seed_compress_h16.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, i, i, u64, u32, p]
     L.seed_round_factors.argtypes = [i, i, i, i, i, p, p, p, p, i, i, u64, u32, p]
+    L.seed_pack_states.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p]
+    L.seed_unpack_states.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p]
+    L.seed_handoff_head_bytes.argtypes = [i, i, i, i]
+    L.seed_handoff_head_bytes.restype = ctypes.c_size_t
     for fn in ("seed_decode_step", "seed_decode_step_lazy", "seed_compress", "seed_compress_lazy",
                "seed_state_from_dense", "dense_decode_step", "seed_decode_step_h16",
-               "seed_compress_h16", "seed_round_factors", "seed_abi_version"):
+               "seed_compress_h16", "seed_round_factors", "seed_pack_states",
+               "seed_unpack_states", "seed_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
     L.seed_status_string.argtypes = [i]
     L.seed_status_string.restype = ctypes.c_char_p
@@ -335,6 +340,48 @@ def _bound_step(fn, name: str, head: tuple, tail_state: tuple, rule: str, B: int
     return step
 
 
+_STORE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+
+def handoff_head_bytes(d_k: int, d_v: int, R: int, store=torch.float32) -> int:
+    """Bytes of one packed head (see include/seed.h)."""
+    return int(lib().seed_handoff_head_bytes(d_k, d_v, R, _STORE_CODE[store]))
+
+
+def _handoff_args(a, U, V, R, idx, buf, n_sel):
+    B, H, cap, d_k = U.shape
+    d_v = V.shape[-1]
+    if U.dtype not in _STORE_CODE or V.dtype != U.dtype:
+        raise ValueError("U and V must share one dtype: float32, bfloat16 or float16")
+    _need(a, "a", (B, H, d_k), _F32)
+    _need(U, "U", (B, H, cap, d_k), (U.dtype,))
+    _need(V, "V", (B, H, cap, d_v), (U.dtype,))
+    _need(idx, "indices", (n_sel,), (torch.int32,))
+    nbytes = n_sel * H * handoff_head_bytes(d_k, d_v, R, U.dtype)
+    _need(buf, "buf", (nbytes,), (torch.uint8,))
+    return B, H, d_k, d_v, cap, _STORE_CODE[U.dtype]
+
+
+def seed_pack_states(a, U, V, R: int, sel, buf, stream=None) -> None:
+    """Pack requests `sel` (int32, device) of a state into `buf` (uint8,
+    device, n_sel * heads * head bytes); see include/seed.h."""
+    n_sel = sel.shape[0]
+    B, H, d_k, d_v, cap, code = _handoff_args(a, U, V, R, sel, buf, n_sel)
+    st = lib().seed_pack_states(B, H, d_k, d_v, cap, int(R), code, n_sel, _ptr(sel), _ptr(a),
+                                _ptr(U), _ptr(V), _ptr(buf), _stream(stream, a.device.index))
+    _check("seed_pack_states", st)
+
+
+def seed_unpack_states(buf, a, U, V, R: int, slots, stream=None) -> None:
+    """Write the packed requests of `buf` into batch slots `slots`; see
+    include/seed.h."""
+    n_sel = slots.shape[0]
+    B, H, d_k, d_v, cap, code = _handoff_args(a, U, V, R, slots, buf, n_sel)
+    st = lib().seed_unpack_states(B, H, d_k, d_v, cap, int(R), code, n_sel, _ptr(slots), _ptr(buf),
+                                  _ptr(a), _ptr(U), _ptr(V), _stream(stream, a.device.index))
+    _check("seed_unpack_states", st)
+
+
 class ShallowState:
     """Device tensors of one layer's shallow states plus the column count r.
 
@@ -398,6 +445,25 @@ class ShallowState:
         else:
             seed_compress(self.U, self.V, self.r, self.R, stream)
         self.r = min(self.r, self.R)
+
+    def pack(self, sel, buf=None, stream=None) -> torch.Tensor:
+        """Pack requests `sel` (int32 device tensor) right after a
+        compression or conversion (r = R) into a handoff buffer."""
+        if self.r != self.R:
+            raise RuntimeError("pack needs a compressed state (r = R)")
+        if buf is None:
+            buf = torch.empty(sel.shape[0] * self.heads
+                              * handoff_head_bytes(self.d_k, self.d_v, self.R),
+                              dtype=torch.uint8, device=self.a.device)
+        seed_pack_states(self.a, self.U, self.V, self.R, sel, buf, stream)
+        return buf
+
+    def unpack(self, buf, slots, stream=None) -> None:
+        """Write packed requests into batch slots `slots`; the batch must be
+        right after a compression (r = R), where gam is 1."""
+        if self.r != self.R:
+            raise RuntimeError("unpack needs the batch at r = R (aligned schedule)")
+        seed_unpack_states(buf, self.a, self.U, self.V, self.R, slots, stream)
 
     def true_U(self) -> torch.Tensor:
         """U at true scale (Diag(gam) U~ in the lazy form); a new tensor when lazy."""
@@ -479,6 +545,23 @@ class ShallowState16:
                               self.rounding, self.seed, self.epoch, stream)
             self.epoch += 1
         self.r = self.R
+
+    def pack(self, sel, buf=None, stream=None) -> torch.Tensor:
+        """Pack requests `sel` right after a compression (see ShallowState.pack)."""
+        if self.r != self.R:
+            raise RuntimeError("pack needs a compressed state (r = R)")
+        if buf is None:
+            buf = torch.empty(sel.shape[0] * self.heads
+                              * handoff_head_bytes(self.d_k, self.d_v, self.R, self.store),
+                              dtype=torch.uint8, device=self.a.device)
+        seed_pack_states(self.a, self.Uk, self.Vk, self.R, sel, buf, stream)
+        return buf
+
+    def unpack(self, buf, slots, stream=None) -> None:
+        """Write packed requests into batch slots (see ShallowState.unpack)."""
+        if self.r != self.R:
+            raise RuntimeError("unpack needs the batch at r = R (aligned schedule)")
+        seed_unpack_states(buf, self.a, self.Uk, self.Vk, self.R, slots, stream)
 
     def true_factors(self):
         """(U, V) at true scale over the r columns held, fp32 (new tensors)."""

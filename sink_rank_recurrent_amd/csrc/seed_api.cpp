@@ -270,6 +270,60 @@ seed_status seed_round_factors(int batch, int heads, int d_k, int d_v, int R, co
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t seed_handoff_head_bytes(int d_k, int d_v, int R, int store_dtype) {
+  if (!supported_dims(d_k, d_v) || R <= 0 || R > seed::kMaxCap) return 0;
+  if (store_dtype != SEED_F32 && store_dtype != SEED_BF16 && store_dtype != SEED_F16) return 0;
+  const size_t fb = store_dtype == SEED_F32 ? 4 : 2;
+  return 4 * (size_t)d_k + fb * (size_t)(d_k + d_v) * R;
+}
+
+}  // extern "C"
+
+namespace {
+
+seed_status handoff(const char* fn, bool pack, int batch, int heads, int d_k, int d_v, int cap,
+                    int R, int store_dtype, int n_sel, const int* idx, float* a, void* U, void* V,
+                    void* buf, void* stream) {
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (store_dtype != SEED_F32 && store_dtype != SEED_BF16 && store_dtype != SEED_F16)
+    return fail(SEED_E_ARG, "%s: unknown store dtype %d", fn, store_dtype);
+  if (R <= 0 || cap < R || n_sel < 0)
+    return fail(SEED_E_SHAPE, "%s: need 0 < R <= cap and n_sel >= 0 (got R=%d cap=%d n_sel=%d)",
+                fn, R, cap, n_sel);
+  if (cap > seed::kMaxCap)
+    return fail(SEED_E_UNSUPPORTED, "%s: capacity %d above %d", fn, cap, seed::kMaxCap);
+  if ((long long)n_sel * heads > 0x7fffffffLL)
+    return fail(SEED_E_SHAPE, "%s: n_sel * heads exceeds the grid limit", fn);
+  if (n_sel == 0) return ok();
+  SEED_PTR(idx);
+  SEED_PTR(a);
+  SEED_PTR(U);
+  SEED_PTR(V);
+  SEED_PTR(buf);
+  return device_status(
+      fn, seed::launch_handoff(pack, batch, heads, d_k, d_v, cap, R, store_dtype == SEED_F32 ? 4 : 2,
+                               n_sel, idx, a, U, V, buf, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+seed_status seed_pack_states(int batch, int heads, int d_k, int d_v, int cap, int R,
+                             int store_dtype, int n_sel, const int* sel, const float* a,
+                             const void* U, const void* V, void* buf, void* stream) {
+  return handoff("seed_pack_states", true, batch, heads, d_k, d_v, cap, R, store_dtype, n_sel, sel,
+                 const_cast<float*>(a), const_cast<void*>(U), const_cast<void*>(V), buf, stream);
+}
+
+seed_status seed_unpack_states(int batch, int heads, int d_k, int d_v, int cap, int R,
+                               int store_dtype, int n_sel, const int* slot, const void* buf,
+                               float* a, void* U, void* V, void* stream) {
+  return handoff("seed_unpack_states", false, batch, heads, d_k, d_v, cap, R, store_dtype, n_sel,
+                 slot, a, U, V, const_cast<void*>(buf), stream);
+}
+
 seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                                   const float* S, const float* vbar, float* a, float* U,
                                   float* V, void* stream) {
@@ -322,6 +376,6 @@ const char* seed_status_string(int status) {
 
 const char* seed_last_error(void) { return g_err; }
 
-int seed_abi_version(void) { return 102; }
+int seed_abi_version(void) { return 103; }
 
 }  // extern "C"

@@ -82,6 +82,13 @@ hipError_t launch_round_factors(int store_fmt, int units, int R, int d_k, int d_
                                 uint32_t epoch, uint32_t key_lo, uint32_t key_hi,
                                 hipStream_t stream);
 
+// Copies the rank-R states of the units of requests idx[0..n_sel) between
+// the state arrays (a fp32; U, V with cap columns of factor_bytes entries)
+// and the packed buffer (seed_handoff.hip); pack: state -> buffer.
+hipError_t launch_handoff(bool pack, int batch, int heads, int d_k, int d_v, int cap, int R,
+                          int factor_bytes, int n_sel, const int* idx, float* a, void* U, void* V,
+                          void* buf, hipStream_t stream);
+
 hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                              const float* S, const float* vbar, float* a, float* U, float* V,
                              hipStream_t stream);

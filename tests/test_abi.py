@@ -17,10 +17,11 @@ def test_exports_every_declared_function():
     assert set(names) == {"seed_decode_step", "seed_decode_step_lazy", "seed_compress",
                           "seed_compress_lazy", "seed_state_from_dense", "dense_decode_step",
                           "seed_decode_step_h16", "seed_compress_h16", "seed_round_factors",
+                          "seed_handoff_head_bytes", "seed_pack_states", "seed_unpack_states",
                           "seed_status_string", "seed_last_error", "seed_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.seed_abi_version() == 102
+    assert L.seed_abi_version() == 103
 
 
 def test_status_strings():
@@ -127,6 +128,22 @@ def test_compress_h16_and_round_validation():
     assert L.seed_round_factors(1, 1, 128, 128, 16, p, p, p, p, 0, 0, 0, 0, None) == 1
     assert L.seed_round_factors(1, 1, 128, 128, 16, p, p, None, p, 1, 0, 0, 0, None) == 1
     assert L.seed_round_factors(1, 1, 96, 128, 16, p, p, p, p, 1, 0, 0, 0, None) == 3
+
+
+def test_handoff_validation():
+    p = ALIGNED
+    assert binding.handoff_head_bytes(128, 128, 16) == 4 * (128 + 256 * 16)
+    assert L.seed_handoff_head_bytes(128, 64, 16, 2) == 4 * 128 + 2 * 192 * 16
+    assert L.seed_handoff_head_bytes(96, 64, 16, 0) == 0
+    # B, H, d_k, d_v, cap, R, store, n_sel, sel, a, U, V, buf, stream
+    assert L.seed_pack_states(2, 3, 128, 128, 48, 16, 0, 0, None, None, None, None, None,
+                              None) == 0                                  # nothing selected
+    assert L.seed_pack_states(2, 3, 128, 128, 48, 16, 0, 2, None, p, p, p, p, None) == 1
+    assert L.seed_pack_states(2, 3, 128, 128, 8, 16, 0, 2, p, p, p, p, p, None) == 2   # cap < R
+    assert L.seed_pack_states(2, 3, 128, 128, 48, 16, 7, 2, p, p, p, p, p, None) == 1
+    assert L.seed_unpack_states(2, 3, 128, 100, 48, 16, 0, 2, p, p, p, p, p, None) == 3
+    assert L.seed_unpack_states(2, 3, 128, 128, 48, 16, 0, -1, p, p, p, p, p, None) == 2
+    assert L.seed_unpack_states(2, 3, 128, 128, 48, 16, 0, 2, p, p, p, MISALIGNED, p, None) == 1
 
 
 def test_from_dense_validation():
