@@ -16,6 +16,7 @@ ORACLE = os.path.join(ROOT, "oracle")
 PIN_FILES = ["tests/test_oracle_dense.py", "tests/test_oracle_svd.py",
              "tests/test_oracle_factored.py", "tests/test_oracle_bytes.py"]
 ROUNDING_PINS = ["tests/test_oracle_rounding.py"]
+STATS_PINS = ["tests/test_oracle_stats.py"]
 
 MUTATIONS = {
     "lemma2_sign_of_kGa": ("(beta * (omega - kGa))", "(beta * (omega + kGa))"),
@@ -48,6 +49,16 @@ ROUNDING_MUTATIONS = {
     "words_v_block_not_offset": ("w[R * d_k:].reshape(R, d_v).T", "w[:R * d_v].reshape(R, d_v).T"),
     "compress_scales_a_factor": ("round_factors(L.astype(np.float32), F.astype(np.float32)",
                                     "round_factors(L.astype(np.float32) * 1.001, F.astype(np.float32)"),
+}
+
+# mistakes planted in the state-statistics oracle (seed_stats.py)
+STATS_MUTATIONS = {
+    "sink_energy_norm_not_squared": ("np.sum(a * a) * np.sum(vbar * vbar)",
+                                     "np.sum(a * a) * np.sqrt(np.sum(vbar * vbar))"),
+    "rank_holding_strict": ("np.argmax(c >= p * tot)", "np.argmax(c > p * tot)"),
+    "vstar_from_last_direction": ("vstar = Vt[0]", "vstar = Vt[-1]"),
+    "beyond_rank_off_by_one": ("np.sum(s2C[R:])", "np.sum(s2C[R + 1:])"),
+    "top_share_of_content": ("float(s2S[0]) / e_state", "float(s2C[0]) / e_state"),
 }
 
 RUNNER = r"""
@@ -85,4 +96,11 @@ def test_planted_mistake_is_caught(name, tmp_path):
 def test_planted_rounding_mistake_is_caught(name, tmp_path):
     old, new = ROUNDING_MUTATIONS[name]
     r = _run_mutated(tmp_path, "seed_rounding.py", old, new, ROUNDING_PINS)
+    assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(STATS_MUTATIONS))
+def test_planted_stats_mistake_is_caught(name, tmp_path):
+    old, new = STATS_MUTATIONS[name]
+    r = _run_mutated(tmp_path, "seed_stats.py", old, new, STATS_PINS)
     assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
