@@ -19,8 +19,10 @@ kernel on the same workload, two variants timed on the same state and
 inputs -- the lazily decayed form (U's decay kept as a running product,
 seed_decode_step_lazy) and the 16-bit form (kept factors fp16, rounded at
 every compression, seed_decode_step_h16) -- the handoff of the converted
-states (seed_pack_states / seed_unpack_states of every request), and the CPU
-oracle timed on a bounded sample.  Prints one JSON line.
+states (seed_pack_states / seed_unpack_states of every request), the
+statistics of the prefilled states (seed_state_stats: sink energy share, top
+direction, content ranks), and the CPU oracle timed on a bounded sample.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -412,6 +414,26 @@ def main() -> int:
         log(f"handoff: pack {t_pack * 1e6:.1f} us, unpack {t_unpack * 1e6:.1f} us for "
             f"{nbytes / 1e6:.1f} MB")
 
+    # statistics of the converted workload's dense states (the quantities
+    # the pages measure on model states), with the kernel's time
+    stats = None
+    if not args.no_variant:
+        nf = binding.lib().seed_stat_fields()
+        rec = torch.empty(w.batch, w.heads, nf, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        binding.seed_state_stats(S_dense, vbar, w.R, rec)
+        e1.record()
+        torch.cuda.synchronize()
+        r = rec.reshape(units, nf)[:, :len(binding.STAT_FIELDS)].double()
+        med = {f: float(r[:, i].median()) for i, f in enumerate(binding.STAT_FIELDS)}
+        stats = {"kernel_ms": e0.elapsed_time(e1), "units": units,
+                 "median_sink_share": med["sink_share"], "median_top_share": med["top_share"],
+                 "median_abs_cos_vstar_vbar": med["abs_cos_vstar_vbar"],
+                 "median_rank90": med["rank90"], "median_rank99": med["rank99"],
+                 "median_beyond_R_share": med["beyond_R_share"]}
+        log(f"state statistics: {stats['kernel_ms']:.1f} ms for {units} heads")
+
     dense = None
     if not args.no_dense:
         dres = run_dense(w, S_copy, inputs, o, warmup, steps, graphs=args.graphs)
@@ -476,6 +498,7 @@ def main() -> int:
         "lazy_decay_variant": variants.get("lazy_decay_variant"),
         "fp16_factor_variant": variants.get("fp16_factor_variant"),
         "handoff": handoff,
+        "state_stats": stats,
     }
     print(json.dumps(out), flush=True)
     return 0

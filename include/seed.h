@@ -269,6 +269,28 @@ seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int ca
                                   float *a, float *U, float *V, void *stream);
 
 /*
+ * seed_state_stats -- statistics of dense states, the quantities the SEED
+ * figures and tables measure on model states (Fig. 3 (e), (g), (h); Fig. 12
+ * (f); Fig. 13 (a), (b), (d)).  Per (request, head), with a = S vbar/|vbar|^2
+ * and the content C = S - a vbar^T, rec[unit][0 .. seed_stat_fields()) is
+ *   0 |S|_F^2   1 |a vbar^T|_F^2   2 |C|_F^2
+ *   3 sink share |a vbar^T|_F^2 / |S|_F^2
+ *   4 top share sigma_1(S)^2 / |S|_F^2
+ *   5 |cos(v*, vbar)|, v* the leading right singular vector of S
+ *   6, 7 the smallest k whose k largest sigma_i(C)^2 hold 90 % / 99 % of
+ *        |C|_F^2 (0 for a zero content)
+ *   8 the share of |C|_F^2 beyond rank R
+ *   9 .. zero
+ * spec_S, spec_C (float [batch][heads][d_k], optional, NULL to skip): the
+ * eigenvalues of S S^T and C C^T (sigma^2 of S and C), descending.  fp32,
+ * by cyclic Jacobi run to convergence; S and vbar are only read.
+ */
+int seed_stat_fields(void);
+seed_status seed_state_stats(int batch, int heads, int d_k, int d_v, int R, const float *S,
+                             const float *vbar, float *rec, float *spec_S, float *spec_C,
+                             void *stream);
+
+/*
  * dense_decode_step -- the dense-state baseline: one step of the head's own
  * recurrence on S (updated in place), then o = S'^T q.  The three rules are
  * the ones listed under seed_rule (the updates named in the picx.dev

@@ -64,12 +64,15 @@ def lib() -> ctypes.CDLL:
     L.seed_round_factors.argtypes = [i, i, i, i, i, p, p, p, p, i, i, u64, u32, p]
     L.seed_pack_states.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p]
     L.seed_unpack_states.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p]
+    L.seed_state_stats.argtypes = [i, i, i, i, i, p, p, p, p, p, p]
+    L.seed_stat_fields.argtypes = []
     L.seed_handoff_head_bytes.argtypes = [i, i, i, i]
     L.seed_handoff_head_bytes.restype = ctypes.c_size_t
     for fn in ("seed_decode_step", "seed_decode_step_lazy", "seed_compress", "seed_compress_lazy",
                "seed_state_from_dense", "dense_decode_step", "seed_decode_step_h16",
                "seed_compress_h16", "seed_round_factors", "seed_pack_states",
-               "seed_unpack_states", "seed_abi_version"):
+               "seed_unpack_states", "seed_state_stats", "seed_stat_fields",
+               "seed_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
     L.seed_status_string.argtypes = [i]
     L.seed_status_string.restype = ctypes.c_char_p
@@ -380,6 +383,26 @@ def seed_unpack_states(buf, a, U, V, R: int, slots, stream=None) -> None:
     st = lib().seed_unpack_states(B, H, d_k, d_v, cap, int(R), code, n_sel, _ptr(slots), _ptr(buf),
                                   _ptr(a), _ptr(U), _ptr(V), _stream(stream, a.device.index))
     _check("seed_unpack_states", st)
+
+
+STAT_FIELDS = ("e_state", "e_sink", "e_content", "sink_share", "top_share",
+               "abs_cos_vstar_vbar", "rank90", "rank99", "beyond_R_share")
+
+
+def seed_state_stats(S, vbar, R: int, rec, spec_S=None, spec_C=None, stream=None) -> None:
+    """Statistics of dense states into rec [B, H, seed_stat_fields()] and,
+    optionally, the sorted spectra [B, H, d_k] (see include/seed.h)."""
+    B, H, d_k, d_v = S.shape
+    nf = lib().seed_stat_fields()
+    _need(S, "S", (B, H, d_k, d_v), _F32)
+    _need(vbar, "vbar", (H, d_v), _F32)
+    _need(rec, "rec", (B, H, nf), _F32)
+    for name, t in (("spec_S", spec_S), ("spec_C", spec_C)):
+        if t is not None:
+            _need(t, name, (B, H, d_k), _F32)
+    st = lib().seed_state_stats(B, H, d_k, d_v, int(R), _ptr(S), _ptr(vbar), _ptr(rec),
+                                _ptr(spec_S), _ptr(spec_C), _stream(stream, S.device.index))
+    _check("seed_state_stats", st)
 
 
 class ShallowState:

@@ -324,6 +324,28 @@ seed_status seed_unpack_states(int batch, int heads, int d_k, int d_v, int cap, 
                  slot, a, U, V, const_cast<void*>(buf), stream);
 }
 
+int seed_stat_fields(void) { return seed::stat_fields(); }
+
+seed_status seed_state_stats(int batch, int heads, int d_k, int d_v, int R, const float* S,
+                             const float* vbar, float* rec, float* spec_S, float* spec_C,
+                             void* stream) {
+  const char* fn = "seed_state_stats";
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (R < 0 || R > d_k)
+    return fail(SEED_E_SHAPE, "%s: need 0 <= R <= d_k (got %d)", fn, R);
+  SEED_PTR(S);
+  SEED_PTR(vbar);
+  SEED_PTR(rec);
+  if (spec_S != nullptr) SEED_PTR(spec_S);
+  if (spec_C != nullptr) SEED_PTR(spec_C);
+  if (seed::from_dense_lds_bytes(d_k, 1) > seed::kMaxLds)
+    return fail(SEED_E_UNSUPPORTED, "%s: d_k=%d needs more LDS than a CU has", fn, d_k);
+  return device_status(fn, seed::launch_state_stats(batch, heads, d_k, d_v, R, S, vbar, rec,
+                                                    spec_S, spec_C,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                                   const float* S, const float* vbar, float* a, float* U,
                                   float* V, void* stream) {
@@ -376,6 +398,6 @@ const char* seed_status_string(int status) {
 
 const char* seed_last_error(void) { return g_err; }
 
-int seed_abi_version(void) { return 103; }
+int seed_abi_version(void) { return 104; }
 
 }  // extern "C"

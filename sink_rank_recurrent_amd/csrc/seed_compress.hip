@@ -153,8 +153,10 @@ __device__ __forceinline__ void rank_diagonal(const Lds& L) {
 
 // Cyclic Jacobi on the symmetric L.H (np x np, padding zero), accumulating
 // eigenvectors into L.X (set to the identity here).  On exit the diagonal
-// of H holds the eigenvalues and L.rank their descending ranks.
-__device__ __forceinline__ void jacobi(const Lds& L, int R) {
+// of H holds the eigenvalues and L.rank their descending ranks.  Stops when
+// the top-R eigenvectors are separated from the rest (full_tol == 0), or,
+// with full_tol > 0, when every off-diagonal entry is at most full_tol.
+__device__ __forceinline__ void jacobi(const Lds& L, int R, float full_tol = 0.f) {
   const int tid = threadIdx.x;
   const int np = L.np, ld = L.ld, nb = np / 2;
   float* H = L.H;
@@ -233,7 +235,9 @@ __device__ __forceinline__ void jacobi(const Lds& L, int R) {
     bool bad = false;
     for (int w = tid; w < np * np; w += kNT) {
       const int i = w / np, j = w % np;
-      if (L.rank[i] < R && L.rank[j] >= R) {
+      if (full_tol > 0.f) {
+        if (i != j && fabsf(H[i * ld + j]) > full_tol) bad = true;
+      } else if (L.rank[i] < R && L.rank[j] >= R) {
         const float gap = H[i * ld + i] - H[j * ld + j];
         const float hij = fabsf(H[i * ld + j]);
         if (hij > kAngleTol * gap) bad = true;
@@ -336,6 +340,172 @@ __global__ __launch_bounds__(256) void from_dense_kernel(const float* __restrict
   }
 }
 
+// Statistics of dense states (SEED figures and tables: Fig. 3 (e), (g),
+// (h); Fig. 12 (f); Fig. 13 (a), (b), (d)).  Per unit: the sink split as in
+// from_dense_kernel; the energies |S|^2 (trace of S S^T), |a vbar^T|^2 =
+// |a|^2 |vbar|^2 and |C|^2; the eigenvectors x_i of S S^T and of C C^T by
+// Jacobi run to convergence, each eigenvalue then taken as the Rayleigh
+// quotient |M^T x_i|^2 from the matrix itself (second order in the
+// eigenvector's error, so fp32 Jacobi's drift on the diagonal does not
+// enter); v* = S^T x_1 / |S^T x_1|; the smallest ranks holding 90 % and 99 %
+// of the content's energy and the share beyond rank R.  Record per unit
+// (kStatFields floats): e_state, e_sink, e_content, sink share, top share,
+// |cos(v*, vbar)|, rank90, rank99, share beyond R, then zeros.
+constexpr int kStatFields = 16;
+constexpr float kFullTol = 1e-7f;   // off-diagonal / trace at convergence
+
+// M (DK x DV, row j from mrow(j, e)) into the rows of L.H, after a Jacobi
+// has finished with it.
+template <int DK, int DV, typename RowFn>
+__device__ __forceinline__ void stage_rows(const Lds& L, RowFn mrow) {
+  __syncthreads();
+  for (int w = threadIdx.x; w < DK * DV; w += kNT) {
+    const int j = w / DV, e = w % DV;
+    L.H[j * L.ld + e] = mrow(j, e);
+  }
+  __syncthreads();
+}
+
+// lam[i] = |M^T x_i|^2 for the columns x_i of L.X (M staged in L.H); two
+// groups of threads split the value entries, their partial sums meet in
+// p0 and p1 (DK floats each).  Then rank[i] = descending rank of lam[i].
+template <int DK, int DV>
+__device__ __forceinline__ void rayleigh(const Lds& L, float* p0, float* p1, float* lam,
+                                         int* rank) {
+  const int tid = threadIdx.x;
+  const int i = tid % DK, half = tid / DK;
+  if (half < 2) {
+    float acc = 0.f;
+    for (int e = half * (DV / 2); e < (half + 1) * (DV / 2); ++e) {
+      float y = 0.f;
+      for (int j = 0; j < DK; ++j) y += L.H[j * L.ld + e] * L.X[j * L.ld + i];
+      acc += y * y;
+    }
+    (half ? p1 : p0)[i] = acc;
+  }
+  __syncthreads();
+  for (int k = tid; k < DK; k += kNT) lam[k] = p0[k] + p1[k];
+  __syncthreads();
+  for (int k = tid; k < DK; k += kNT) {
+    int r = 0;
+    for (int j = 0; j < DK; ++j) r += (lam[j] > lam[k]) || (lam[j] == lam[k] && j < k);
+    rank[k] = r;
+  }
+  __syncthreads();
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ S,
+                                                     const float* __restrict__ vbar, int heads,
+                                                     int R, float* __restrict__ rec,
+                                                     float* __restrict__ specS,
+                                                     float* __restrict__ specC) {
+  extern __shared__ float smem[];
+  const Lds L = carve(smem, DK, 1);
+  const int tid = threadIdx.x;
+  const int ld = L.ld;
+  const size_t ub = blockIdx.x;
+  const int h = (int)(ub % heads);
+  const float* Sh = S + ub * DK * DV;
+  float* av = L.aux;          // [DK] sink coefficient
+  float* vb = L.aux + 128;    // [DV] vbar
+  // after a Jacobi: cs and pq hold the two partial sums, T the eigenvalues
+  // (np * 1 floats), rank their order
+  float* p0 = L.cs;
+  float* p1 = reinterpret_cast<float*>(L.pq);
+  float* lam = L.T;
+
+  for (int e = tid; e < DV; e += kNT) vb[e] = vbar[(size_t)h * DV + e];
+  __syncthreads();
+  float nv2 = 0.f;
+  for (int e = 0; e < DV; ++e) nv2 += vb[e] * vb[e];
+  {
+    constexpr int EV = DV / 32;
+    const int grp = tid >> 5, lane = tid & 31;
+    for (int i = grp; i < DK; i += 8) {
+      float x[EV];
+      load_vec<EV>(Sh + (size_t)i * DV + lane * EV, x);
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) p += x[e] * vb[lane * EV + e];
+      p = sum32(p) / nv2;
+      if (lane == 0) av[i] = p;
+    }
+  }
+  __syncthreads();
+  float na = 0.f;
+  for (int i = 0; i < DK; ++i) na += av[i] * av[i];
+  const float e_sink = na * nv2;
+  float* out = rec + ub * kStatFields;
+
+  // S S^T: spectrum of S and its top direction
+  gram_dispatch([=](int j, int e) { return Sh[(size_t)j * DV + e]; }, DK, DV, L.H, ld, L.X);
+  __syncthreads();
+  // the trace, summed by every thread in the same order
+  float e_state = 0.f;
+  for (int i = 0; i < DK; ++i) e_state += L.H[i * ld + i];
+  jacobi(L, 1, kFullTol * e_state);
+  stage_rows<DK, DV>(L, [=](int j, int e) { return Sh[(size_t)j * DV + e]; });
+  rayleigh<DK, DV>(L, p0, p1, lam, L.rank);
+  int i0 = 0;
+  for (int i = 0; i < DK; ++i)
+    if (L.rank[i] == 0) i0 = i;
+  if (specS != nullptr)
+    for (int i = tid; i < DK; i += kNT) specS[ub * DK + L.rank[i]] = lam[i];
+  // v* = S^T x_1 (value space): its direction against vbar
+  for (int e = tid; e < DV; e += kNT) {
+    float y = 0.f;
+    for (int j = 0; j < DK; ++j) y += L.H[j * ld + e] * L.X[j * ld + i0];
+    p0[e] = y;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float nn = 0.f, dot = 0.f;
+    for (int e = 0; e < DV; ++e) {
+      nn += p0[e] * p0[e];
+      dot += p0[e] * vb[e];
+    }
+    out[0] = e_state;
+    out[1] = e_sink;
+    out[3] = e_state > 0.f ? e_sink / e_state : 0.f;
+    out[4] = e_state > 0.f ? lam[i0] / e_state : 0.f;
+    out[5] = (nn > 0.f && nv2 > 0.f) ? fabsf(dot) / sqrtf(nn * nv2) : 0.f;
+    for (int f = 9; f < kStatFields; ++f) out[f] = 0.f;
+  }
+  __syncthreads();
+
+  // C C^T: spectrum of the content
+  gram_dispatch([=](int j, int e) { return Sh[(size_t)j * DV + e] - av[j] * vb[e]; }, DK, DV, L.H,
+                ld, L.X);
+  __syncthreads();
+  float e_content = 0.f;
+  for (int i = 0; i < DK; ++i) e_content += L.H[i * ld + i];
+  jacobi(L, 1, kFullTol * e_content);
+  stage_rows<DK, DV>(L, [=](int j, int e) { return Sh[(size_t)j * DV + e] - av[j] * vb[e]; });
+  rayleigh<DK, DV>(L, p0, p1, lam, L.rank);
+  for (int i = tid; i < DK; i += kNT) {
+    p0[L.rank[i]] = lam[i];
+    if (specC != nullptr) specC[ub * DK + L.rank[i]] = lam[i];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float tot = 0.f;
+    for (int i = 0; i < DK; ++i) tot += p0[i];
+    int r90 = 0, r99 = 0;
+    float c = 0.f, beyond = 0.f;
+    for (int i = 0; i < DK; ++i) {
+      c += p0[i];
+      if (r90 == 0 && tot > 0.f && c >= 0.90f * tot) r90 = i + 1;
+      if (r99 == 0 && tot > 0.f && c >= 0.99f * tot) r99 = i + 1;
+      if (i >= R) beyond += p0[i];
+    }
+    out[2] = e_content;
+    out[6] = (float)r90;
+    out[7] = (float)r99;
+    out[8] = tot > 0.f ? beyond / tot : 0.f;
+  }
+}
+
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -353,9 +523,35 @@ hipError_t from_dense_go(int units, int heads, int cap, int R, const float* S, c
   return hipGetLastError();
 }
 
+template <int DK, int DV>
+hipError_t stats_go(int units, int heads, int R, const float* S, const float* vbar, float* rec,
+                    float* specS, float* specC, hipStream_t s) {
+  const size_t bytes = from_dense_lds_bytes(DK, 1);
+  hipError_t err = set_lds(stats_kernel<DK, DV>, bytes);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((stats_kernel<DK, DV>), dim3(units), dim3(kNT), bytes, s, S, vbar, heads, R,
+                     rec, specS, specC);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t compress_lds_bytes(int n, int R) { return compress_wave_lds_bytes(n, R); }
+
+int stat_fields() { return kStatFields; }
+
+hipError_t launch_state_stats(int batch, int heads, int d_k, int d_v, int R, const float* S,
+                              const float* vbar, float* rec, float* specS, float* specC,
+                              hipStream_t stream) {
+  const int units = batch * heads;
+  if (d_k == 128 && d_v == 128)
+    return stats_go<128, 128>(units, heads, R, S, vbar, rec, specS, specC, stream);
+  if (d_k == 128 && d_v == 64)
+    return stats_go<128, 64>(units, heads, R, S, vbar, rec, specS, specC, stream);
+  if (d_k == 64 && d_v == 64)
+    return stats_go<64, 64>(units, heads, R, S, vbar, rec, specS, specC, stream);
+  return hipErrorInvalidValue;
+}
 
 size_t from_dense_lds_bytes(int d_k, int R) { return 4 * lds_floats(padded(d_k), R); }
 

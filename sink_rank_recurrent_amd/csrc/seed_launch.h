@@ -89,6 +89,14 @@ hipError_t launch_handoff(bool pack, int batch, int heads, int d_k, int d_v, int
                           int factor_bytes, int n_sel, const int* idx, float* a, void* U, void* V,
                           void* buf, hipStream_t stream);
 
+// Statistics of dense states (seed_compress.hip): stat_fields() floats per
+// unit in rec; the sorted eigenvalues of S S^T and C C^T in specS, specC
+// ([unit][d_k], either may be NULL).
+int stat_fields();
+hipError_t launch_state_stats(int batch, int heads, int d_k, int d_v, int R, const float* S,
+                              const float* vbar, float* rec, float* specS, float* specC,
+                              hipStream_t stream);
+
 hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                              const float* S, const float* vbar, float* a, float* U, float* V,
                              hipStream_t stream);

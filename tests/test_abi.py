@@ -18,10 +18,11 @@ def test_exports_every_declared_function():
                           "seed_compress_lazy", "seed_state_from_dense", "dense_decode_step",
                           "seed_decode_step_h16", "seed_compress_h16", "seed_round_factors",
                           "seed_handoff_head_bytes", "seed_pack_states", "seed_unpack_states",
+                          "seed_state_stats", "seed_stat_fields",
                           "seed_status_string", "seed_last_error", "seed_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.seed_abi_version() == 103
+    assert L.seed_abi_version() == 104
 
 
 def test_status_strings():
@@ -144,6 +145,15 @@ def test_handoff_validation():
     assert L.seed_unpack_states(2, 3, 128, 100, 48, 16, 0, 2, p, p, p, p, p, None) == 3
     assert L.seed_unpack_states(2, 3, 128, 128, 48, 16, 0, -1, p, p, p, p, p, None) == 2
     assert L.seed_unpack_states(2, 3, 128, 128, 48, 16, 0, 2, p, p, p, MISALIGNED, p, None) == 1
+
+
+def test_stats_validation():
+    p = ALIGNED
+    assert L.seed_stat_fields() == 16
+    assert L.seed_state_stats(1, 1, 128, 128, 129, p, p, p, None, None, None) == 2
+    assert L.seed_state_stats(1, 1, 128, 96, 16, p, p, p, None, None, None) == 3
+    assert L.seed_state_stats(1, 1, 128, 128, 16, p, p, None, None, None, None) == 1
+    assert L.seed_state_stats(1, 1, 128, 128, 16, p, p, p, MISALIGNED, None, None) == 1
 
 
 def test_from_dense_validation():
