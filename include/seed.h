@@ -220,6 +220,57 @@ seed_status seed_round_factors(int batch, int heads, int d_k, int d_v, int R, co
                                uint64_t seed, uint32_t epoch, void *stream);
 
 /*
+ * Per-request schedules.  Requests start at different times, so each has
+ * its own column count and its own compression step (the pages compress
+ * every W steps: SEED figures and tables, Fig. 1 (b) caption).  Request b
+ * has taken A = t - t_start[b] steps at step t (it is idle, and its
+ * read-out zero, while A < 0).  When its window reaches W columns (after
+ * its step number k W) its content [R kept | W window] is compressed while
+ * it keeps stepping; D steps later (A = k W + D) the truncation, decayed
+ * by those steps' gates, replaces the compressed columns and the D columns
+ * appended since are kept.  D = 0 compresses before the next step: the
+ * aligned reading per request.  The decay of U is lazy as in
+ * seed_decode_step_lazy.
+ *
+ *   t_start  int   [batch]                    step at which request b starts
+ *   KU       float [2][batch][heads][R][d_k]  kept columns of U~, two buffers
+ *   KV       float [2][batch][heads][R][d_v]  kept columns of V
+ *   Uw       float [batch][heads][W + D][d_k] window ring: column number j
+ *   Vw       float [batch][heads][W + D][d_v]   of a request in slot j mod (W + D)
+ *   gam      float as for seed_decode_step_lazy (the running decay product)
+ *   gam_snap float same shape: the product at the latest snapshot
+ * With c = (A < W + D ? 0 : (A - D) / W) merges done, a request's kept
+ * columns are buffer c & 1 and its window the column numbers c W .. A - 1;
+ * it holds R + A - c W columns.  A state converted by seed_state_from_dense
+ * (cap = R) goes into buffer 0 with gam = 1 and an empty window.
+ * Built for R = 16 or 32, 0 <= D < W and R + W + D <= 96.
+ *
+ * seed_decode_step_sched -- step t of every request (Lemma 2 as in
+ * seed_decode_step_lazy); at A = k W + D it first folds gam into every held
+ * column and restarts gam at 1; at (A + 1) mod W = 0 it also stores the new
+ * gam in gam_snap.
+ *
+ * seed_compress_sched -- compress the units units[0 .. n_units) whose
+ * request has A = t_snap - t_start[b] = k W, k >= 1 (other listed units are
+ * left alone; entries outside the batch are skipped): the rank-R
+ * truncation of the snapshot into kept buffer k & 1, scaled by 1 / gam_snap.
+ * Call it with t_snap = t + 1 after step t, on any stream ordered after
+ * that step; step t_snap + D must be ordered after it.  Reads Uw, Vw and
+ * the old kept buffer; writes only the new kept buffer.
+ */
+seed_status seed_decode_step_sched(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
+                                   int D, int t, const int *t_start, float *a, float *KU,
+                                   float *KV, float *Uw, float *Vw, float *gam, float *gam_snap,
+                                   const float *vbar, const void *q, const void *k,
+                                   const void *v, int in_dtype, const float *g, const float *beta,
+                                   float *o, void *stream);
+
+seed_status seed_compress_sched(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
+                                int D, int t_snap, const int *t_start, int n_units,
+                                const int *units, float *KU, float *KV, const float *Uw,
+                                const float *Vw, const float *gam_snap, void *stream);
+
+/*
  * Handoff of shallow-form states (prefill -> decode).  At the end of the
  * prefill a state is compressed to the sink plus rank-R factors (SEED
  * figures and tables, Fig. 1 (a) caption, Table 1), 4 [d_k + (d_k + d_v) R]

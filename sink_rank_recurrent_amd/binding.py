@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
     L.seed_pack_states.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p]
     L.seed_unpack_states.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p]
     L.seed_state_stats.argtypes = [i, i, i, i, i, p, p, p, p, p, p]
+    L.seed_decode_step_sched.argtypes = [i, i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, p, p,
+                                         p, p, i, p, p, p, p]
+    L.seed_compress_sched.argtypes = [i, i, i, i, i, i, i, i, i, p, i, p, p, p, p, p, p, p]
     L.seed_stat_fields.argtypes = []
     L.seed_handoff_head_bytes.argtypes = [i, i, i, i]
     L.seed_handoff_head_bytes.restype = ctypes.c_size_t
@@ -72,6 +75,7 @@ def lib() -> ctypes.CDLL:
                "seed_state_from_dense", "dense_decode_step", "seed_decode_step_h16",
                "seed_compress_h16", "seed_round_factors", "seed_pack_states",
                "seed_unpack_states", "seed_state_stats", "seed_stat_fields",
+               "seed_decode_step_sched", "seed_compress_sched",
                "seed_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
     L.seed_status_string.argtypes = [i]
@@ -601,3 +605,126 @@ class ShallowState16:
             self.compress(stream)
             return True
         return False
+
+
+class ScheduledState:
+    """Shallow states of requests that start at different times, each on its
+    own compression schedule (see include/seed.h, seed_decode_step_sched).
+
+    Device tensors: a, the kept buffers KU [2, B, H, R, d_k], KV, the window
+    rings Uw [B, H, W + D, d_k], Vw, gam, gam_snap, t_start [B] (int32).
+    `step` launches one decode step of every request on torch's current
+    stream and, for the requests whose window it fills, their compression on
+    a side stream (default priority); the step that merges a compression
+    first waits for it.  D = 0 makes every compression finish before the
+    next step.
+    """
+
+    def __init__(self, rule: str, batch: int, heads: int, d_k: int, d_v: int, R: int, W: int,
+                 D: int, vbar: torch.Tensor, t_start, device="cuda"):
+        import numpy as np
+
+        self.rule, self.R, self.W, self.D = rule, R, W, D
+        self.batch, self.heads, self.d_k, self.d_v = batch, heads, d_k, d_v
+        f32 = torch.float32
+        self.a = torch.zeros(batch, heads, d_k, device=device, dtype=f32)
+        self.KU = torch.zeros(2, batch, heads, R, d_k, device=device, dtype=f32)
+        self.KV = torch.zeros(2, batch, heads, R, d_v, device=device, dtype=f32)
+        self.Uw = torch.zeros(batch, heads, W + D, d_k, device=device, dtype=f32)
+        self.Vw = torch.zeros(batch, heads, W + D, d_v, device=device, dtype=f32)
+        self.vbar = vbar.to(device=device, dtype=f32).contiguous()
+        gshape = _gam_shape(rule, batch, heads, d_k)
+        self.gam = torch.ones(gshape, device=device, dtype=f32)
+        self.gam_snap = torch.ones(gshape, device=device, dtype=f32)
+        ts = np.asarray(t_start, dtype=np.int64)
+        if ts.shape != (batch,):
+            raise ValueError("t_start needs one step per request")
+        self.t_start_host = ts
+        self.t_start = torch.tensor(ts, dtype=torch.int32, device=device)
+        # the units of the requests whose windows fill at the same steps
+        self.cohorts = []
+        for p in range(W):
+            reqs = np.nonzero(ts % W == p)[0]
+            units = (reqs[:, None] * heads + np.arange(heads)[None, :]).reshape(-1)
+            self.cohorts.append(torch.tensor(units, dtype=torch.int32, device=device)
+                                if units.size else None)
+        self.side = torch.cuda.Stream(device=device)
+        self.pending = {}
+        self.t = 0
+
+    def from_dense(self, S: torch.Tensor, stream=None) -> None:
+        """Every request's state from its dense state (kept buffer 0)."""
+        U = torch.empty(self.batch, self.heads, self.R, self.d_k, device=self.a.device)
+        V = torch.empty(self.batch, self.heads, self.R, self.d_v, device=self.a.device)
+        seed_state_from_dense(S, self.vbar, self.a, U, V, self.R, stream)
+        self.KU[0].copy_(U)
+        self.KV[0].copy_(V)
+        self.gam.fill_(1.0)
+        self.gam_snap.fill_(1.0)
+
+    def held_columns(self, b: int, t=None) -> int:
+        """Columns request b holds before step t (default: the next step)."""
+        A = (self.t if t is None else t) - int(self.t_start_host[b])
+        if A < 0:
+            return self.R
+        c = 0 if A < self.W + self.D else (A - self.D) // self.W
+        return self.R + A - c * self.W
+
+    def step(self, q, k, v, g, beta, o, stream=None) -> None:
+        B, H, d_k, d_v = self.batch, self.heads, self.d_k, self.d_v
+        cur = torch.cuda.current_stream(self.a.device) if stream is None else stream
+        ev = self.pending.pop(self.t, None)
+        if ev is not None:
+            cur.wait_event(ev)
+        for name, t_, shape, dts in (("q", q, (B, H, d_k), _IN), ("k", k, (B, H, d_k), _IN),
+                                     ("v", v, (B, H, d_v), _IN),
+                                     ("g", g, (B, H, d_k) if self.rule == "kda" else (B, H), _F32),
+                                     ("o", o, (B, H, d_v), _F32)):
+            _need(t_, name, shape, dts)
+        if beta is not None:
+            _need(beta, "beta", (B, H), _F32)
+        st = lib().seed_decode_step_sched(
+            RULES[self.rule], B, H, d_k, d_v, self.R, self.W, self.D, self.t, _ptr(self.t_start),
+            _ptr(self.a), _ptr(self.KU), _ptr(self.KV), _ptr(self.Uw), _ptr(self.Vw),
+            _ptr(self.gam), _ptr(self.gam_snap), _ptr(self.vbar), _ptr(q), _ptr(k), _ptr(v),
+            _in_dtype(q, k, v), _ptr(g), _ptr(beta), _ptr(o), cur.cuda_stream)
+        _check("seed_decode_step_sched", st)
+        lst = self.cohorts[(self.t + 1) % self.W]
+        if lst is not None:
+            snap = torch.cuda.Event()
+            snap.record(cur)
+            self.side.wait_event(snap)
+            st = lib().seed_compress_sched(
+                RULES[self.rule], B, H, d_k, d_v, self.R, self.W, self.D, self.t + 1,
+                _ptr(self.t_start), lst.shape[0], _ptr(lst), _ptr(self.KU), _ptr(self.KV),
+                _ptr(self.Uw), _ptr(self.Vw), _ptr(self.gam_snap), self.side.cuda_stream)
+            _check("seed_compress_sched", st)
+            done = torch.cuda.Event()
+            done.record(self.side)
+            self.pending[self.t + 1 + self.D] = done
+        self.t += 1
+
+    def join(self, stream=None) -> None:
+        """Order `stream` (default: the current one) after every compression
+        launched so far."""
+        cur = torch.cuda.current_stream(self.a.device) if stream is None else stream
+        cur.wait_stream(self.side)
+
+    def true_factors(self, b: int, h: int):
+        """(U at true scale [d_k, r], V [d_v, r]) of one unit before the next
+        step, fp32 (after join())."""
+        A = self.t - int(self.t_start_host[b])
+        R, W, D = self.R, self.W, self.D
+        c = 0 if A < W + D else (A - D) // W
+        w = max(A, 0) - c * W if A >= 0 else 0
+        sel = c & 1
+        cols_u = [self.KU[sel, b, h]]
+        cols_v = [self.KV[sel, b, h]]
+        if w > 0:
+            slots = [(c * W + i) % (W + D) for i in range(w)]
+            cols_u.append(self.Uw[b, h, slots])
+            cols_v.append(self.Vw[b, h, slots])
+        U = torch.cat(cols_u, 0)
+        V = torch.cat(cols_v, 0)
+        gs = self.gam[b, h] if self.rule == "kda" else self.gam[b, h].reshape(1)
+        return (U * gs[None, :]).T, V.T

@@ -346,6 +346,98 @@ seed_status seed_state_stats(int batch, int heads, int d_k, int d_v, int R, cons
                                                     static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+seed_status check_sched(const char* fn, int rule, int batch, int heads, int d_k, int d_v, int R,
+                        int W, int D) {
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (rule != SEED_RULE_GDN && rule != SEED_RULE_KDA && rule != SEED_RULE_MAMBA2)
+    return fail(SEED_E_ARG, "%s: unknown rule %d", fn, rule);
+  if (W <= 0 || D < 0 || D >= W)
+    return fail(SEED_E_SHAPE, "%s: need W > 0 and 0 <= D < W (got W=%d D=%d)", fn, W, D);
+  if (R != 16 && R != 32)
+    return fail(SEED_E_UNSUPPORTED, "%s: built for R = 16 or 32 (got %d)", fn, R);
+  if (R + W + D > seed::kMaxCap)
+    return fail(SEED_E_UNSUPPORTED, "%s: R + W + D = %d above %d", fn, R + W + D, seed::kMaxCap);
+  return SEED_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+seed_status seed_decode_step_sched(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
+                                   int D, int t, const int* t_start, float* a, float* KU,
+                                   float* KV, float* Uw, float* Vw, float* gam, float* gam_snap,
+                                   const float* vbar, const void* q, const void* k,
+                                   const void* v, int in_dtype, const float* g, const float* beta,
+                                   float* o, void* stream) {
+  const char* fn = "seed_decode_step_sched";
+  seed_status st = check_sched(fn, rule, batch, heads, d_k, d_v, R, W, D);
+  if (st != SEED_OK) return st;
+  st = check_step_inputs(fn, rule, q, k, v, in_dtype, g, beta, o);
+  if (st != SEED_OK) return st;
+  SEED_PTR(t_start);
+  SEED_PTR(a);
+  SEED_PTR(KU);
+  SEED_PTR(KV);
+  SEED_PTR(Uw);
+  SEED_PTR(Vw);
+  SEED_PTR(gam);
+  SEED_PTR(gam_snap);
+  SEED_PTR(vbar);
+  const seed::RingArgs ring{t_start, t, W, D, KU, KV, gam_snap};
+  return device_status(
+      fn, seed::launch_step(rule, in_dtype == SEED_BF16, seed::kStoreRing, batch, heads, d_k, d_v,
+                            W + D, R + W + D - 1, R, a, Uw, Vw, nullptr, nullptr, gam, vbar, q, k,
+                            v, g, beta, o, static_cast<hipStream_t>(stream), &ring));
+}
+
+seed_status seed_compress_sched(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
+                                int D, int t_snap, const int* t_start, int n_units,
+                                const int* units, float* KU, float* KV, const float* Uw,
+                                const float* Vw, const float* gam_snap, void* stream) {
+  const char* fn = "seed_compress_sched";
+  seed_status st = check_sched(fn, rule, batch, heads, d_k, d_v, R, W, D);
+  if (st != SEED_OK) return st;
+  if (n_units < 0 || (long long)n_units > (long long)batch * heads)
+    return fail(SEED_E_SHAPE, "%s: need 0 <= n_units <= batch * heads (got %d)", fn, n_units);
+  if (n_units == 0) return ok();
+  SEED_PTR(t_start);
+  SEED_PTR(units);
+  SEED_PTR(KU);
+  SEED_PTR(KV);
+  SEED_PTR(Uw);
+  SEED_PTR(Vw);
+  SEED_PTR(gam_snap);
+  if (seed::compress_lds_bytes(R + W, R) > seed::kMaxLds)
+    return fail(SEED_E_UNSUPPORTED, "%s: %d columns at rank %d need more LDS than a CU has", fn,
+                R + W, R);
+  seed::CompressArgs args{};
+  args.units = n_units;
+  args.cap = W + D;
+  args.n = R + W;
+  args.R = R;
+  args.U = const_cast<float*>(Uw);
+  args.V = const_cast<float*>(Vw);
+  args.gam = const_cast<float*>(gam_snap);
+  args.gam_per_row = rule == SEED_RULE_KDA;
+  args.list = units;
+  args.t_start = t_start;
+  args.heads = heads;
+  args.t_snap = t_snap;
+  args.W = W;
+  args.D = D;
+  args.units_total = batch * heads;
+  args.KU = KU;
+  args.KV = KV;
+  return device_status(fn, seed::launch_compress(d_k, d_v, seed::kStoreRing, args,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                                   const float* S, const float* vbar, float* a, float* U,
                                   float* V, void* stream) {
@@ -398,6 +490,6 @@ const char* seed_status_string(int status) {
 
 const char* seed_last_error(void) { return g_err; }
 
-int seed_abi_version(void) { return 104; }
+int seed_abi_version(void) { return 105; }
 
 }  // extern "C"

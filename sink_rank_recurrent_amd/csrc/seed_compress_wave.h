@@ -185,14 +185,14 @@ struct Lay {
 // ---------------------------------------------------------------------------
 // A: G[i][j] = s_ij sum_e X[e][i] X[e][j] for i, j < NMAX (zero beyond n),
 // s_ij = d_i d_j when SCALE, else 1.  Column j < KR of X is the 16-bit
-// column j of Xk (format FMT), column j >= KR is column j - KR of X (fp32);
-// each holds D entries.  MFMA 16x16x4: lane l feeds column 16 t + l % 16 of
+// column j of Xk (format FMT), any other column is fp32 at colf(j); each
+// holds D entries.  MFMA 16x16x4: lane l feeds column 16 t + l % 16 of
 // tile t at the k-slot l / 16.  Wave w sums e over [w D / NW, (w + 1) D / NW),
 // slot kk over its quarter of that range; with two waves the partial sums
 // meet in LDS (wave 1 stores, wave 0 adds and stores the total).  If rs is
 // not NULL, row e of X is first multiplied by rs[e] (rs_per_row) or by rs[0].
-template <int NMAX, int NW, int D, bool SCALE, int FMT, int KR>
-__device__ __forceinline__ void gram(const float* __restrict__ X, const uint16_t* __restrict__ Xk,
+template <int NMAX, int NW, int D, bool SCALE, int FMT, int KR, typename ColF>
+__device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
                                      int n, float* __restrict__ G,
                                      const float* __restrict__ dv, const float* __restrict__ rs,
                                      bool rs_per_row) {
@@ -213,7 +213,7 @@ __device__ __forceinline__ void gram(const float* __restrict__ X, const uint16_t
     for (int t = 0; t < NT; ++t) {
       const int col = t * 16 + ci;
       const int off = (w * 4 + kk) * KPL + s0;
-      if (col < n && col < KR) {
+      if ((FMT == kStoreBF16 || FMT == kStoreF16) && col < n && col < KR) {
         const uint16_t* src = Xk + (size_t)col * D + off;
 #pragma unroll
         for (int q = 0; q < KC / 4; ++q) {
@@ -223,7 +223,7 @@ __device__ __forceinline__ void gram(const float* __restrict__ X, const uint16_t
           x[t][4 * q + 2] = y[2]; x[t][4 * q + 3] = y[3];
         }
       } else if (col < n) {
-        const float* src = X + (size_t)(col - KR) * D + off;
+        const float* src = colf(col) + off;
 #pragma unroll
         for (int q = 0; q < KC / 4; ++q) {
           const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * q);
@@ -447,8 +447,11 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   const int gam_per_row = args.gam_per_row;
   // 16-bit layout: columns 0..R-1 are kept patterns, the fp32 arrays hold
   // columns R..n-1 from their index 0.  It is compiled for R = RMAX only,
-  // so that every column's source is known at compile time.
-  constexpr int KR = (FMT == kStoreF32) ? 0 : RMAX;
+  // so that every column's source is known at compile time.  The ring
+  // layout's kept columns are fp32 (CompressArgs in seed_launch.h).
+  constexpr bool H16 = FMT == kStoreBF16 || FMT == kStoreF16;
+  constexpr bool RING = FMT == kStoreRing;
+  constexpr int KR = H16 ? RMAX : 0;
   using L = Lay<NMAX, RMAX>;
   constexpr int NW = L::NW, NTH = L::NTH, LDN = L::LDN;
   constexpr int PARTS = L::PARTS, CH = L::CH, NACT = L::NACT;
@@ -486,11 +489,36 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
 
   const int t = threadIdx.x;
   const bool act = t < NMAX;
-  const size_t ub = blockIdx.x;
+  const size_t ub = args.list != nullptr ? (size_t)args.list[blockIdx.x] : blockIdx.x;
+  int kcyc = 0;
+  if constexpr (RING) {
+    if (ub >= (size_t)args.units_total) return;  // not a unit of this batch
+    const int A = args.t_snap - args.t_start[ub / args.heads];
+    if (A < args.W || A % args.W != 0) return;   // not due: the whole block leaves
+    kcyc = A / args.W;
+  }
   float* const Uh = U + ub * cap * DK;
   float* const Vh = V + ub * cap * DV_;
-  uint16_t* const Ukh = (FMT == kStoreF32) ? nullptr : args.Uk + ub * R * DK;
-  uint16_t* const Vkh = (FMT == kStoreF32) ? nullptr : args.Vk + ub * R * DV_;
+  uint16_t* const Ukh = H16 ? args.Uk + ub * R * DK : nullptr;
+  uint16_t* const Vkh = H16 ? args.Vk + ub * R * DV_ : nullptr;
+  // ring layout: the kept buffer read and the one written
+  const size_t kold = RING ? ((size_t)((kcyc - 1) & 1) * args.units_total + ub) * R : 0;
+  const size_t knew = RING ? ((size_t)(kcyc & 1) * args.units_total + ub) * R : 0;
+  // fp32 column j of U and V
+  auto ucol = [&](int j) -> float* {
+    if constexpr (RING)
+      return j < R ? args.KU + (kold + j) * DK
+                   : Uh + (size_t)(((kcyc - 1) * args.W + j - R) % cap) * DK;
+    else
+      return Uh + (size_t)(j - KR) * DK;
+  };
+  auto vcol = [&](int j) -> float* {
+    if constexpr (RING)
+      return j < R ? args.KV + (kold + j) * DV_
+                   : Vh + (size_t)(((kcyc - 1) * args.W + j - R) % cap) * DV_;
+    else
+      return Vh + (size_t)(j - KR) * DV_;
+  };
   // lazily decayed form: U = Diag(gam) U~ (gam per key channel, or one scalar)
   float* const gamh = gam != nullptr ? gam + ub * (gam_per_row ? DK : 1) : nullptr;
 
@@ -511,7 +539,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
 
   // @phase A: Gram of U and column norms
-  gram<NMAX, NW, DK, false, FMT, KR>(Uh, Ukh, n, G, nullptr, gamh, gam_per_row);
+  gram<NMAX, NW, DK, false, FMT, KR>(ucol, Ukh, n, G, nullptr, gamh, gam_per_row);
   __syncthreads();
   if (act) {
     const float gtt = G[t * LDN + t];
@@ -530,7 +558,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
   __syncthreads();
   // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
-  gram<NMAX, NW, DV_, true, FMT, KR>(Vh, Vkh, n, G, DVs, nullptr, false);
+  gram<NMAX, NW, DV_, true, FMT, KR>(vcol, Vkh, n, G, DVs, nullptr, false);
 
   // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
   if constexpr (NW == 1) {
@@ -1046,15 +1074,16 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     auto load_tile = [&](int q, float (&dst)[NK]) {
       const bool isu = q < TU / NW;
       const int E = q * NW + w;
-      const float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
       const int ld = isu ? DK : DV_;
-      if constexpr (FMT == kStoreF32) {
+      const int row = isu ? 16 * E : 16 * (E - TU);
+      if constexpr (!H16) {
 #pragma unroll
         for (int K = 0; K < NK; ++K) {
           const int j = 4 * K + kk;
-          dst[K] = (j < n) ? base[(size_t)j * ld + ci] : 0.f;
+          dst[K] = (j < n) ? (isu ? ucol(j) : vcol(j))[row + ci] : 0.f;
         }
       } else {
+        const float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
         const uint16_t* basek = isu ? Ukh + 16 * E : Vkh + 16 * (E - TU);
 #pragma unroll
         for (int K = 0; K < NK; ++K) {
@@ -1086,7 +1115,24 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           acc[C] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[K], isu ? bt[C][K] : bp[C][K], acc[C],
                                                         0, 0, 0);
       const int ld = isu ? DK : DV_;
-      if constexpr (FMT == kStoreF32) {
+      if constexpr (RING) {
+        // U~' = Diag(1 / gam) U' (the decay product at the snapshot keeps
+        // running), into the other kept buffer
+        float* base = isu ? args.KU + knew * DK + 16 * E : args.KV + knew * DV_ + 16 * (E - TU);
+        float sc[4] = {1.f, 1.f, 1.f, 1.f};
+        if (isu) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[i] = 1.f / *gs_at(16 * E + 4 * kk + i);
+        }
+#pragma unroll
+        for (int C = 0; C < NC; ++C) {
+          const int cc = 16 * C + ci;
+          if (cc < R)
+            *reinterpret_cast<float4*>(base + (size_t)cc * ld + 4 * kk) =
+                make_float4(acc[C][0] * sc[0], acc[C][1] * sc[1], acc[C][2] * sc[2],
+                            acc[C][3] * sc[3]);
+        }
+      } else if constexpr (FMT == kStoreF32) {
         float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
 #pragma unroll
         for (int C = 0; C < NC; ++C) {
@@ -1108,7 +1154,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
             const float xv[4] = {acc[C][0], acc[C][1], acc[C][2], acc[C][3]};
             *reinterpret_cast<uint2*>(basek + (size_t)cc * ld + 4 * kk) =
                 round_pack4<FMT>(xv, args.stochastic != 0, fb + (uint32_t)(cc * ld),
-                                 (uint32_t)blockIdx.x, args.epoch, args.key_lo, args.key_hi);
+                                 (uint32_t)ub, args.epoch, args.key_lo, args.key_hi);
           }
         }
       }
@@ -1116,7 +1162,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       for (int K = 0; K < NK; ++K) av[K] = an[K];
     }
   }
-  if (gamh != nullptr) {
+  if (gamh != nullptr && !RING) {
     // U' is stored at true scale: the decay product starts again from 1
     __syncthreads();
     if (gam_per_row) {

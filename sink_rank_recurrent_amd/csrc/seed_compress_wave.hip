@@ -15,6 +15,7 @@ hipError_t launch_compress(int d_k, int d_v, int store_fmt, const CompressArgs& 
     if (store_fmt == kStoreF32) return compress_wave_##DK##x##DV(args, stream);  \
     if (store_fmt == kStoreBF16) return compress_wave_##DK##x##DV##_bf16(args, stream); \
     if (store_fmt == kStoreF16) return compress_wave_##DK##x##DV##_fp16(args, stream);  \
+    if (store_fmt == kStoreRing) return compress_wave_##DK##x##DV##_ring(args, stream);  \
     return hipErrorInvalidValue;                                                 \
   }
   SEED_COMPRESS_SHAPE(128, 128)

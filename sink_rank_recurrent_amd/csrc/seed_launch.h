@@ -10,7 +10,25 @@ namespace seed {
 
 // Storage of the factor columns: all fp32, or the R columns the last
 // compression wrote as 16-bit patterns (bf16 or fp16) and the rest fp32.
-enum StoreFmt { kStoreF32 = 0, kStoreBF16 = 1, kStoreF16 = 2 };
+// kStoreRing: per-request schedules -- R kept fp32 columns in one of two
+// buffers, the window in a ring of W + D columns (seed_sched.hip's layout).
+enum StoreFmt { kStoreF32 = 0, kStoreBF16 = 1, kStoreF16 = 2, kStoreRing = 3 };
+
+// Per-request schedule of the ring layout.  A request b has taken
+// A = t - t_start[b] steps (it is idle while A < 0).  With
+// c = A < W + D ? 0 : (A - D) / W merges done, its kept columns are buffer
+// c & 1 of KU / KV ([2][units][R][d]); window column i (0 <= i < A - c W) is
+// column number c W + i, stored in ring slot (c W + i) mod (W + D); the step
+// appends column number A.  The step with A = c W + D (c >= 1) first folds
+// the running decay product into every held column and resets it to 1; the
+// step with (A + 1) mod W == 0 also writes the decay product to gam_snap.
+struct RingArgs {
+  const int* t_start;
+  int t, W, D;
+  float* KU;
+  float* KV;
+  float* gam_snap;
+};
 
 // Largest factor capacity (R + W) the kernels are compiled for.
 constexpr int kMaxCap = 96;
@@ -23,11 +41,15 @@ constexpr size_t kMaxLds = 160 * 1024;
 // kStoreBF16 / kStoreF16: columns j < kR are the 16-bit Uk, Vk ([unit][kR]
 // columns) and columns j >= kR are U, V at index j - kR (capacity cap);
 // these need gam.
+// kStoreRing: U, V are the rings (cap = W + D columns), kR = R, r the
+// largest column count any request holds (R + W + D - 1), ring describes the
+// schedule.
 hipError_t launch_step(int rule, bool in_bf16, int store_fmt, int batch, int heads, int d_k,
                        int d_v, int cap, int r, int kR, float* a, float* U, float* V,
                        const uint16_t* Uk, const uint16_t* Vk, float* gam, const float* vbar,
                        const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, float* o, hipStream_t stream);
+                       const float* beta, float* o, hipStream_t stream,
+                       const RingArgs* ring = nullptr);
 
 hipError_t launch_dense(int rule, bool in_bf16, int batch, int heads, int d_k, int d_v, float* S,
                         const void* q, const void* k, const void* v, const float* g,
@@ -51,6 +73,12 @@ size_t from_dense_lds_bytes(int d_k, int R);
 // rounded into Uk, Vk (to nearest, or stochastically with the Philox words
 // of (unit, epoch, key)).  gam as for launch_step (NULL: U at true scale);
 // it is reset to 1.
+// Ring layout (kStoreRing, per-request schedules): block i compresses unit
+// list[i]; a unit whose request has A = t_snap - t_start[b] steps with
+// A = k W, k >= 1, compresses its kept buffer (k - 1) & 1 and window column
+// numbers (k - 1) W .. k W - 1 (ring U, V with cap = W + D slots), with gam
+// the decay product at the snapshot, into kept buffer k & 1 scaled by
+// 1 / gam; gam is not reset.  Other units of the list are left alone.
 struct CompressArgs {
   int units, cap, n, R;
   float* U;
@@ -61,6 +89,11 @@ struct CompressArgs {
   int gam_per_row;
   int stochastic;
   uint32_t epoch, key_lo, key_hi;
+  const int* list;
+  const int* t_start;
+  int heads, t_snap, W, D, units_total;
+  float* KU;
+  float* KV;
 };
 
 hipError_t launch_compress(int d_k, int d_v, int store_fmt, const CompressArgs& args,
@@ -68,7 +101,8 @@ hipError_t launch_compress(int d_k, int d_v, int store_fmt, const CompressArgs& 
 #define SEED_DECLARE_COMPRESS_SHAPE(DK, DV)                                                    \
   hipError_t compress_wave_##DK##x##DV(const CompressArgs& args, hipStream_t stream);          \
   hipError_t compress_wave_##DK##x##DV##_bf16(const CompressArgs& args, hipStream_t stream);   \
-  hipError_t compress_wave_##DK##x##DV##_fp16(const CompressArgs& args, hipStream_t stream);
+  hipError_t compress_wave_##DK##x##DV##_fp16(const CompressArgs& args, hipStream_t stream);   \
+  hipError_t compress_wave_##DK##x##DV##_ring(const CompressArgs& args, hipStream_t stream);
 SEED_DECLARE_COMPRESS_SHAPE(128, 128)
 SEED_DECLARE_COMPRESS_SHAPE(128, 64)
 SEED_DECLARE_COMPRESS_SHAPE(64, 64)

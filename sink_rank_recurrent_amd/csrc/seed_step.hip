@@ -45,20 +45,58 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
     const uint16_t* __restrict__ Uk, const uint16_t* __restrict__ Vk, float* __restrict__ gam,
     const float* __restrict__ vbar, const IN_T* __restrict__ q, const IN_T* __restrict__ k,
     const IN_T* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
-    float* __restrict__ o, int heads, int cap, int r, int kR_arg) {
+    float* __restrict__ o, int heads, int cap, int r_arg, int kR_arg, RingArgs rg) {
   static_assert(FMT == kStoreF32 || LAZY, "16-bit kept columns are never decayed in place");
+  constexpr bool RING = FMT == kStoreRing;
+  constexpr bool H16 = FMT == kStoreBF16 || FMT == kStoreF16;
   constexpr int EK = DK / 32;  // key-space entries per lane
   constexpr int EV = DV / 32;  // value-space entries per lane
-  const int kR = (FMT == kStoreF32) ? 0 : kR_arg;
+  const int kR = H16 ? kR_arg : 0;
   const int unit = blockIdx.x;
   const int h = unit % heads;
   const int tid = threadIdx.x;
   const int grp = tid >> 5;
   const int lane = tid & 31;
   const size_t ub = (size_t)unit;
-  // fp32 columns j >= kR at index j - kR
+  // fp32 columns j >= kR at index j - kR (the ring: see column())
   float* Uh = U + ub * cap * DK;
   float* Vh = V + ub * cap * DV;
+
+  // the ring layout's per-request schedule (RingArgs in seed_launch.h)
+  int r = r_arg;
+  int win0 = 0;
+  bool merge = false, snap = false;
+  float* keptU = nullptr;
+  float* keptV = nullptr;
+  if constexpr (RING) {
+    const int A = rg.t - rg.t_start[unit / heads];
+    if (A < 0) {
+      // not started: the state is left as it is, the read-out is zero
+      if (tid < DV) o[ub * DV + tid] = 0.f;
+      return;
+    }
+    const int c = (A < rg.W + rg.D) ? 0 : (A - rg.D) / rg.W;
+    win0 = c * rg.W;
+    r = kR_arg + A - win0;
+    merge = c >= 1 && A == win0 + rg.D;
+    snap = (A + 1) % rg.W == 0;
+    const size_t kb = ((size_t)(c & 1) * gridDim.x + ub) * kR_arg;
+    keptU = rg.KU + kb * DK;
+    keptV = rg.KV + kb * DV;
+  }
+  // fp32 column j of U / V
+  auto ucol = [&](int j) -> float* {
+    if constexpr (RING)
+      return j < kR_arg ? keptU + (size_t)j * DK : Uh + (size_t)((win0 + j - kR_arg) % cap) * DK;
+    else
+      return Uh + (size_t)(j - kR) * DK;
+  };
+  auto vcol = [&](int j) -> float* {
+    if constexpr (RING)
+      return j < kR_arg ? keptV + (size_t)j * DV : Vh + (size_t)((win0 + j - kR_arg) % cap) * DV;
+    else
+      return Vh + (size_t)(j - kR) * DV;
+  };
 
   // 1. the factors: every column this half-wave owns, loaded once
   float u[SLOTS][EK];
@@ -66,12 +104,12 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     const int j = grp + 8 * s;
-    if (FMT != kStoreF32 && j < r && j < kR) {
+    if (H16 && j < r && j < kR) {
       load_vec16<FMT, EK>(Uk + (ub * kR + j) * DK + lane * EK, u[s]);
       load_vec16<FMT, EV>(Vk + (ub * kR + j) * DV + lane * EV, w[s]);
     } else if (j < r) {
-      load_vec<EK>(Uh + (size_t)(j - kR) * DK + lane * EK, u[s]);
-      load_vec<EV>(Vh + (size_t)(j - kR) * DV + lane * EV, w[s]);
+      load_vec<EK>(ucol(j) + lane * EK, u[s]);
+      load_vec<EV>(vcol(j) + lane * EV, w[s]);
     } else {
 #pragma unroll
       for (int e = 0; e < EK; ++e) u[s][e] = 0.f;
@@ -109,6 +147,22 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
       const float g0 = gam[ub];
 #pragma unroll
       for (int e = 0; e < EK; ++e) gn[e] = g0;
+    }
+    if constexpr (RING) {
+      if (merge) {
+        // fold the decay product into every held column, then restart it
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+          const int j = grp + 8 * s;
+          if (j < r) {
+#pragma unroll
+            for (int e = 0; e < EK; ++e) u[s][e] *= gn[e];
+            store_vec<EK>(ucol(j) + lane * EK, u[s]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < EK; ++e) gn[e] = 1.f;
+      }
     }
 #pragma unroll
     for (int e = 0; e < EK; ++e) {
@@ -178,7 +232,7 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
         pq += x * qq[e];
       }
       const int j = grp + 8 * s;
-      if (j < r) store_vec<EK>(Uh + (size_t)j * DK + lane * EK, u[s]);
+      if (j < r) store_vec<EK>(ucol(j) + lane * EK, u[s]);
     }
     ck[s] = pk;
     cq[s] = pq;
@@ -188,9 +242,9 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
       float kd[EK];
 #pragma unroll
       for (int e = 0; e < EK; ++e) kd[e] = kk[e] / gn[e];
-      store_vec<EK>(Uh + (size_t)(r - kR) * DK + lane * EK, kd);
+      store_vec<EK>(ucol(r) + lane * EK, kd);
     } else {
-      store_vec<EK>(Uh + (size_t)r * DK + lane * EK, kk);
+      store_vec<EK>(ucol(r) + lane * EK, kk);
     }
   }
 #pragma unroll
@@ -235,6 +289,12 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
       if constexpr (RULE == kKDA) store_vec<EK>(gam + ub * DK + lane * EK, gn);
       else if (lane == 0) gam[ub] = gn[0];
     }
+    if constexpr (RING) {
+      if (snap) {
+        if constexpr (RULE == kKDA) store_vec<EK>(rg.gam_snap + ub * DK + lane * EK, gn);
+        else if (lane == 0) rg.gam_snap[ub] = gn[0];
+      }
+    }
   }
   __syncthreads();
   if (tid < DV) {
@@ -246,7 +306,7 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
     }
     const float eps = eps_s[tid];
     const float vn = (RULE == kMAMBA2) ? eps : bt * (eps - tk);
-    Vh[(size_t)(r - kR) * DV + tid] = vn;
+    vcol(r)[tid] = vn;
     o[ub * DV + tid] = sink_s[tid] + tq + vn * kq;
   }
 }
@@ -254,6 +314,7 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
 namespace {
 
 struct StepArgs {
+  RingArgs ring;
   int units, heads, cap, r, kR;
   float* a;
   float* U;
@@ -275,12 +336,15 @@ void step_launch(const StepArgs& p, hipStream_t s) {
   hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS, LAZY, FMT>), dim3(p.units),
                      dim3(256), 0, s, p.a, p.U, p.V, p.Uk, p.Vk, p.gam, p.vbar,
                      static_cast<const IN_T*>(p.q), static_cast<const IN_T*>(p.k),
-                     static_cast<const IN_T*>(p.v), p.g, p.beta, p.o, p.heads, p.cap, p.r, p.kR);
+                     static_cast<const IN_T*>(p.v), p.g, p.beta, p.o, p.heads, p.cap, p.r, p.kR,
+                     p.ring);
 }
 
 template <int RULE, int DK, int DV, typename IN_T, int SLOTS>
 hipError_t step_go(int fmt, const StepArgs& p, hipStream_t s) {
-  if (fmt == kStoreBF16) {
+  if (fmt == kStoreRing) {
+    step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreRing>(p, s);
+  } else if (fmt == kStoreBF16) {
     step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreBF16>(p, s);
   } else if (fmt == kStoreF16) {
     step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreF16>(p, s);
@@ -330,10 +394,12 @@ hipError_t launch_step(int rule, bool in_bf16, int store_fmt, int batch, int hea
                        int d_v, int cap, int r, int kR, float* a, float* U, float* V,
                        const uint16_t* Uk, const uint16_t* Vk, float* gam, const float* vbar,
                        const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, float* o, hipStream_t stream) {
+                       const float* beta, float* o, hipStream_t stream, const RingArgs* ring) {
   if (store_fmt != kStoreF32 && gam == nullptr) return hipErrorInvalidValue;
-  const StepArgs p{batch * heads, heads, cap, r, store_fmt == kStoreF32 ? 0 : kR, a, U, V, Uk, Vk,
-                   gam, vbar, q, k, v, g, beta, o};
+  if (store_fmt == kStoreRing && ring == nullptr) return hipErrorInvalidValue;
+  const RingArgs rg = ring != nullptr ? *ring : RingArgs{nullptr, 0, 1, 0, nullptr, nullptr, nullptr};
+  const StepArgs p{rg, batch * heads, heads, cap, r, store_fmt == kStoreF32 ? 0 : kR, a, U, V, Uk,
+                   Vk, gam, vbar, q, k, v, g, beta, o};
   switch (rule) {
     case kGDN: return step_dtype<kGDN>(in_bf16, d_k, d_v, store_fmt, p, stream);
     case kKDA: return step_dtype<kKDA>(in_bf16, d_k, d_v, store_fmt, p, stream);

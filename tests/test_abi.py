@@ -19,10 +19,11 @@ def test_exports_every_declared_function():
                           "seed_decode_step_h16", "seed_compress_h16", "seed_round_factors",
                           "seed_handoff_head_bytes", "seed_pack_states", "seed_unpack_states",
                           "seed_state_stats", "seed_stat_fields",
+                          "seed_decode_step_sched", "seed_compress_sched",
                           "seed_status_string", "seed_last_error", "seed_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.seed_abi_version() == 104
+    assert L.seed_abi_version() == 105
 
 
 def test_status_strings():
@@ -154,6 +155,23 @@ def test_stats_validation():
     assert L.seed_state_stats(1, 1, 128, 96, 16, p, p, p, None, None, None) == 3
     assert L.seed_state_stats(1, 1, 128, 128, 16, p, p, None, None, None, None) == 1
     assert L.seed_state_stats(1, 1, 128, 128, 16, p, p, p, MISALIGNED, None, None) == 1
+
+
+def test_sched_validation():
+    p = ALIGNED
+    def step(R=16, W=32, D=8, t_start=p, dtype=1):
+        return L.seed_decode_step_sched(0, 2, 3, 128, 128, R, W, D, 5, t_start, p, p, p, p, p, p, p,
+                                        p, p, p, p, dtype, p, p, p, None)
+    assert step(D=32) == 2 and step(D=-1) == 2 and step(W=0, D=0) == 2
+    assert step(R=8) == 3 and step(W=64, D=20) == 3
+    assert step(t_start=None) == 1 and step(dtype=3) == 1
+    # rule, B, H, d_k, d_v, R, W, D, t_snap, t_start, n, units, KU, KV, Uw, Vw, gam_snap, stream
+    assert L.seed_compress_sched(0, 2, 3, 128, 128, 16, 32, 8, 32, p, 0, None, None, None, None,
+                                 None, None, None) == 0                      # nothing listed
+    assert L.seed_compress_sched(0, 2, 3, 128, 128, 16, 32, 8, 32, p, 7, p, p, p, p, p, p,
+                                 None) == 2                                  # more than B*H
+    assert L.seed_compress_sched(0, 2, 3, 128, 128, 16, 32, 8, 32, p, 2, None, p, p, p, p, p,
+                                 None) == 1
 
 
 def test_from_dense_validation():

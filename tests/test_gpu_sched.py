@@ -1,0 +1,101 @@
+"""Per-request schedules (seed_decode_step_sched / seed_compress_sched, the
+binding's ScheduledState) on the GPU against the oracle's schedule
+(oracle/seed_schedule.py), each unit from the same converted state on the
+same inputs, the oracle running its own schedule from its own conversion.
+
+Requests start at different steps (one starts late, so it idles first).
+Bars: every read-out of a started request to 1e-4 relative, an idle
+request's read-out exactly zero; states at checkpoints to 1e-4 relative
+(they follow compressions).  A unit whose snapshot content has a near-tie
+at rank R ((s_R - s_{R+1})/s_1 < 1e-4: the truncation is not unique) is
+left out from that snapshot on and counted."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TIE_GAP, TOL_READOUT, TOL_STATE_COMPRESS, f64, rel_err, requires_gpu
+from oracle import seed_oracle as so
+from oracle import seed_schedule as sc
+from sink_rank_recurrent_amd import binding
+from sink_rank_recurrent_amd import workloads as wl
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _inputs_of(x, u, H):
+    b, h = divmod(u, H)
+    return {k: (None if v is None else f64(v[b, h])) for k, v in x.items()}
+
+
+@pytest.mark.parametrize("rule,dims,W,D", [
+    ("gdn", (128, 128), 16, 0), ("gdn", (128, 128), 16, 6), ("kda", (128, 128), 32, 12),
+    ("mamba2", (128, 64), 16, 5), ("gdn", (64, 64), 16, 15)])
+def test_scheduled_run_matches_oracle(rule, dims, W, D):
+    d_k, d_v = dims
+    B, H, R = 5, 3, 16
+    t_start = [0, 1, 4, 9, 2 * W + 3]
+    T = max(t_start) + 2 * W + D + 3
+    seed = 900 + W + D
+    vbar = wl.make_vbar(H, d_v, seed, 0, "cpu")
+    vb = f64(vbar)
+    # the converted states: the oracle's conversion of dense states it
+    # prefilled itself, stored as the GPU's initial state
+    S = np.zeros((B * H, d_k, d_v))
+    for t in range(-48, 0):
+        x = wl.make_step(rule, B, H, d_k, d_v, vbar, seed, t, 0, torch.bfloat16, "cpu")
+        xi = {k: (None if v is None else f64(v).reshape((B * H,) + tuple(v.shape[2:])))
+              for k, v in x.items()}
+        S, _ = so.dense_step(rule, S, **xi)
+    vbu = np.broadcast_to(vb[None], (B, H, d_v)).reshape(-1, d_v)
+    a0, U0, V0 = so.state_from_dense(S, vbu, R)
+    a0, U0, V0 = (x.astype(np.float32).astype(np.float64) for x in (a0, U0, V0))
+    st = binding.ScheduledState(rule, B, H, d_k, d_v, R, W, D, vbar.cuda(), t_start)
+    st.a.copy_(torch.tensor(a0.reshape(B, H, d_k), dtype=torch.float32))
+    st.KU[0].copy_(torch.tensor(U0.transpose(0, 2, 1).reshape(B, H, R, d_k), dtype=torch.float32))
+    st.KV[0].copy_(torch.tensor(V0.transpose(0, 2, 1).reshape(B, H, R, d_v), dtype=torch.float32))
+
+    xs = [wl.make_step(rule, B, H, d_k, d_v, vbar, seed + 1, t, 0, torch.bfloat16, "cuda")
+          for t in range(T)]
+    o = torch.empty(B, H, d_v, device="cuda")
+    outs = []
+    checkpoints = {T // 2, T - 1}
+    gpu_states = {}
+    for t in range(T):
+        st.step(xs[t]["q"], xs[t]["k"], xs[t]["v"], xs[t]["g"], xs[t]["beta"], o)
+        outs.append(o.clone())
+        if t in checkpoints:
+            st.join()
+            torch.cuda.synchronize()
+            gpu_states[t] = {(b, h): [f64(m) for m in st.true_factors(b, h)] + [f64(st.a[b, h])]
+                             for b in range(B) for h in range(H)}
+    st.join()
+    torch.cuda.synchronize()
+    outs = [f64(x) for x in outs]
+
+    skipped = 0
+    for u in range(B * H):
+        b, h = divmod(u, H)
+        t0 = t_start[b]
+        steps = [_inputs_of(xs[t], u, H) for t in range(t0, T)]
+        a, U, V, o_ref, ev = sc.scheduled_run(rule, a0[u], U0[u], V0[u], vb[h], steps, R, W, D)
+        # the first snapshot whose truncation is not unique ends the comparison
+        bad = [A for A, kind, *gap in ev if kind == "snapshot" and gap[0] < TIE_GAP]
+        last = t0 + (bad[0] if bad else len(steps))
+        skipped += bool(bad)
+        for t in range(T):
+            if t < t0:
+                assert np.all(outs[t][b, h] == 0.0), (u, t)
+            elif t < last:
+                assert rel_err(outs[t][b, h], o_ref[t - t0], -1) < TOL_READOUT, (u, t)
+        for tc, states in gpu_states.items():
+            n = tc + 1 - t0
+            if n <= 0 or tc >= last:
+                continue
+            ra, rU, rV, _, _ = sc.scheduled_run(rule, a0[u], U0[u], V0[u], vb[h], steps[:n], R, W,
+                                                D)
+            gU, gV, ga = states[(b, h)]
+            assert gU.shape[1] == rU.shape[1] == sc.columns_before_step(n, R, W, D), (u, tc)
+            Sg = so.reconstruct(ga, gU, gV, vb[h])
+            Sr = so.reconstruct(ra, rU, rV, vb[h])
+            assert rel_err(Sg, Sr, (-2, -1)) < TOL_STATE_COMPRESS, (u, tc)
+    assert skipped <= B * H // 4, skipped

@@ -71,7 +71,7 @@ def test_delay_changes_the_result_and_keeps_the_columns():
     o0, oD = np.array(o0), np.array(oD)
     assert np.allclose(o0[:W], oD[:W])                  # identical until the first snapshot
     assert not np.allclose(o0[W:W + D], oD[W:W + D])   # then the delay shows
-    assert ev[:2] == [(W, "snapshot"), (W + D, "merge")]
+    assert [e[:2] for e in ev[:2]] == [(W, "snapshot"), (W + D, "merge")]
     for A in range(1, 4 * W):
         _, Ua, _, _, _ = sc.scheduled_run("gdn", a, U, V, vbar, steps[:A], R, W, D)
         assert Ua.shape[1] == sc.columns_before_step(A, R, W, D), A
