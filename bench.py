@@ -18,7 +18,9 @@ launch duration (HIP events on the launch stream), the dense-state baseline
 kernel on the same workload, two variants timed on the same state and
 inputs -- the lazily decayed form (U's decay kept as a running product,
 seed_decode_step_lazy) and the 16-bit form (kept factors fp16, rounded at
-every compression, seed_decode_step_h16) -- the handoff of the converted
+every compression, seed_decode_step_h16) -- staggered per-request
+compression schedules (seed_decode_step_sched, one HIP graph), the handoff
+of the converted
 states (seed_pack_states / seed_unpack_states of every request), the
 statistics of the prefilled states (seed_state_stats: sink energy share, top
 direction, content ranks), and the CPU oracle timed on a bounded sample.
@@ -210,6 +212,56 @@ def run_shallow(st, inputs, o, warmup: int, steps: int, graphs: bool):
     }
 
 
+def sched_bytes_per_unit(w: wl.Workload, r: int, D: int) -> float:
+    """The lazy step's bytes at r columns, plus the merge step's fold of the
+    decay product into the R + D held columns of U (once per W steps)."""
+    return step_bytes_per_unit(w, r, "lazy") + 4 * w.d_k * (w.R + D) / w.W
+
+
+def run_scheduled(w, S, vbar, inputs, warmup: int, steps: int, D: int, dev):
+    """Staggered starts (request b's phase b mod W) on the per-request
+    schedule with merge delay D.  Every request has passed its first merge
+    when timing starts.  The timed steps (and each cohort's compression on
+    the side stream) are captured once as one HIP graph and replayed, since
+    launching two kernels and two events per step from Python would bound
+    the run by the host."""
+    t_start = [-(b % w.W) - (w.W + D) for b in range(w.batch)]
+    st = binding.ScheduledState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, D, vbar,
+                                t_start, device=dev)
+    st.from_dense(S)
+    o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
+    for t in range(warmup):
+        x = inputs[t]
+        st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+    st.join()
+    torch.cuda.synchronize()
+    # the columns every request holds at each timed step
+    cols = [st.held_columns(b, t) for t in range(warmup, warmup + steps) for b in range(w.batch)]
+    # every compression of the warm-up has finished: nothing to wait for
+    st.pending.clear()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(warmup, warmup + steps):
+            x = inputs[t]
+            st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        st.join()
+    torch.cuda.synchronize()
+    st.pending.clear()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    el = e0.elapsed_time(e1) / 1e3
+    units = w.batch * w.heads
+    mean_bytes = sum(sched_bytes_per_unit(w, r, D) for r in cols) / len(cols)
+    return {"D": D, "value": units * steps / el, "unit": "head-steps/s",
+            "ms_per_step": el * 1e3 / steps, "mean_columns": sum(cols) / len(cols),
+            "step_bytes_per_head_step": mean_bytes,
+            "launch": "one hip graph of the timed steps; each cohort's compression on a side "
+                      "stream, joined by events"}
+
+
 def run_dense(w, S, inputs, o, warmup: int, steps: int, graphs: bool, chunk: int = 32):
     def do(ts):
         for t in ts:
@@ -383,6 +435,17 @@ def main() -> int:
             log(f"{name}: {r2['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
         del S_var
 
+    # staggered per-request schedules: D = 0 (each compression finishes
+    # before the next step) and a merge delay that hides it
+    sched = None
+    if not args.no_variant:
+        sched = []
+        for D in sorted({0, min(w.W - 1, 96 - w.R - w.W, w.W // 2)}):
+            if w.R not in (16, 32):
+                break
+            sched.append(run_scheduled(w, S_dense, vbar, inputs, warmup, steps, D, dev))
+            log(f"staggered schedule D={D}: {sched[-1]['ms_per_step'] * 1e3:.2f} us per step")
+
     # handoff of the converted states (prefill -> decode): pack every
     # request into one buffer, then unpack it into the slots of a batch
     handoff = None
@@ -497,6 +560,7 @@ def main() -> int:
         "dense_baseline": dense,
         "lazy_decay_variant": variants.get("lazy_decay_variant"),
         "fp16_factor_variant": variants.get("fp16_factor_variant"),
+        "staggered_schedule_variants": sched,
         "handoff": handoff,
         "state_stats": stats,
     }

@@ -28,6 +28,10 @@ GROUPS = {
     "compress_wave_kernel (fp32 factors)": r"compress_wave_kernel<.*, 0>",
     "compress_wave_kernel (16-bit kept factors)": r"compress_wave_kernel<.*, [12]>",
     "round_factors_kernel": r"round_factors_kernel<",
+    "seed_step_kernel (per-request schedule)": r"seed_step_kernel<.*true, 3>",
+    "compress_wave_kernel (per-request schedule)": r"compress_wave_kernel<.*, 3>",
+    "handoff_kernel": r"handoff_kernel<",
+    "stats_kernel": r"stats_kernel<",
     "from_dense_kernel": r"from_dense_kernel<",
     "dense_step_kernel": r"dense_step_kernel<",
 }
