@@ -394,3 +394,76 @@ def test_bound_step_equals_step(form):
         f(x["q"][:, :1], x["k"], x["v"], x["g"], x["beta"], states[1].r)
     with pytest.raises(binding.SeedError, match="SEED_E_FULL"):
         f(x["q"], x["k"], x["v"], x["g"], x["beta"], R + W)
+
+
+# ---------------------------------------------------------------------------
+# the 16-bit form at the benchmark's launch sizes, sampled units
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("num", [2, 3, 5])
+def test_h16_workload_launch_size(num):
+    """Workloads 2, 3 and 5 (one layer's launch: 1024, 8192 and 8192 heads)
+    in the fp16 form, as bench.py's variant runs them: GPU prefill and
+    conversion of every head, then two windows with compressions.  The
+    oracle prefills, converts, rounds and compresses sampled heads on its
+    own from the same inputs; read-outs and states agree to 4 u (fp16 to
+    nearest), plus the prefill's fp32 rounding."""
+    w = wl.WORKLOADS[num]
+    dev = "cuda"
+    units = w.batch * w.heads
+    rng = np.random.default_rng(num)
+    idx = np.unique(np.concatenate([[0, units - 1], rng.integers(0, units, 4)]))
+    vbar = wl.make_vbar(w.heads, w.d_v, w.seed, 0, dev)
+    vb = f64(vbar)[idx % w.heads]
+    S = torch.zeros(w.batch, w.heads, w.d_k, w.d_v, device=dev)
+    o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
+    S_ref = np.zeros((len(idx), w.d_k, w.d_v))
+
+    def sample(x):
+        return {k: (None if v is None else f64(v.reshape((units,) + tuple(v.shape[2:]))[idx]))
+                for k, v in x.items()}
+
+    for t in range(-w.prefill, 0):
+        x = wl.workload_step(w, vbar, t, 0, dev)
+        binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        S_ref, _ = oracle.dense_step(w.rule, S_ref, **sample(x))
+    st = binding.ShallowState16(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
+                                store=torch.float16, rounding="nearest", seed=SEED64)
+    st.from_dense(S)
+    # the oracle's own conversion, rounded (epoch 0), per sampled unit
+    a, L, F = oracle.state_from_dense(S_ref, vb, w.R)
+    U = np.empty_like(L)
+    V = np.empty_like(F)
+    for i, u in enumerate(idx):
+        bU, bV = rd.round_factors(L[i].astype(np.float32), F[i].astype(np.float32), rd.FP16,
+                                  "nearest", SEED64, 0, unit=int(u))
+        U[i], V[i] = rd.widen(bU, rd.FP16), rd.widen(bV, rd.FP16)
+    s0 = np.linalg.svd(S_ref - a[:, :, None] * vb[:, None, :], compute_uv=False)
+    ok = (s0[:, w.R - 1] - s0[:, w.R]) / s0[:, 0] > TIE_GAP
+    tol = 4 * _u_store("fp16", "nearest") + TOL_READOUT
+    epoch = 1
+    worst = 0.0
+    for t in range(2 * w.W + 3):
+        x = wl.workload_step(w, vbar, t, 0, dev)
+        st.step_and_maybe_compress(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        a, U, V, o_ref = oracle.seed_step(w.rule, a, U, V, vb, **sample(x))
+        if U.shape[-1] >= w.R + w.W:
+            s = np.linalg.svd(U @ np.swapaxes(V, -1, -2), compute_uv=False)
+            ok &= (s[:, w.R - 1] - s[:, w.R]) / s[:, 0] > TIE_GAP
+            Un, Vn = np.empty(U.shape[:-1] + (w.R,)), np.empty(V.shape[:-1] + (w.R,))
+            for i, u in enumerate(idx):
+                bU, bV, _, _ = rd.compress_rounded(U[i], V[i], w.R, rd.FP16, "nearest", SEED64,
+                                                   epoch, int(u))
+                Un[i], Vn[i] = rd.widen(bU, rd.FP16), rd.widen(bV, rd.FP16)
+            U, V = Un, Vn
+            epoch += 1
+        e = rel_err(f64(o.reshape(units, w.d_v)[idx]), o_ref, -1)[ok]
+        worst = max(worst, float(e.max()) if e.size else 0.0)
+        assert e.size == 0 or e.max() < tol, (t, e)
+    ga = f64(st.a.reshape(units, w.d_k)[idx])
+    Ut, Vt = st.true_factors()
+    gU = f64(Ut.reshape(units, st.r, w.d_k)[idx]).transpose(0, 2, 1)
+    gV = f64(Vt.reshape(units, st.r, w.d_v)[idx]).transpose(0, 2, 1)
+    assert state_rel_err(ga, gU, gV, a, U, V, vb)[ok].max() < tol
+    assert ok.sum() >= len(idx) - 1
+    print(f"workload {num} fp16: worst read-out error {worst:.2e} (bar {tol:.2e})")

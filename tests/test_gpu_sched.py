@@ -99,3 +99,59 @@ def test_scheduled_run_matches_oracle(rule, dims, W, D):
             Sr = so.reconstruct(ra, rU, rV, vb[h])
             assert rel_err(Sg, Sr, (-2, -1)) < TOL_STATE_COMPRESS, (u, tc)
     assert skipped <= B * H // 4, skipped
+
+
+def test_scheduled_launch_size_sampled():
+    """Workload 2's launch (64 requests x 16 GDN heads, R = 16, W = 32) with
+    starts spread over the W phases and D = 16, as bench.py times it;
+    sampled heads against the oracle's schedule from the oracle's own
+    conversion of its own prefill."""
+    w = wl.WORKLOADS[2]
+    B, H, R, W, D = w.batch, w.heads, w.R, w.W, 16
+    units = B * H
+    t_start = [b % W for b in range(B)]
+    idx = np.array([0, 17, 330, 700, units - 1])
+    vbar = wl.make_vbar(H, w.d_v, w.seed, 0, "cuda")
+    vb = f64(vbar)[idx % H]
+    S = torch.zeros(B, H, w.d_k, w.d_v, device="cuda")
+    o = torch.empty(B, H, w.d_v, device="cuda")
+    S_ref = np.zeros((len(idx), w.d_k, w.d_v))
+
+    def sample(x):
+        return {k: (None if v is None else f64(v.reshape((units,) + tuple(v.shape[2:]))[idx]))
+                for k, v in x.items()}
+
+    for t in range(-64, 0):
+        x = wl.workload_step(w, vbar, t, 0, "cuda")
+        binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        S_ref, _ = so.dense_step(w.rule, S_ref, **sample(x))
+    st = binding.ScheduledState(w.rule, B, H, w.d_k, w.d_v, R, W, D, vbar, t_start)
+    st.from_dense(S)
+    a0, U0, V0 = so.state_from_dense(S_ref, vb, R)
+    T = W - 1 + 2 * W + D + 2
+    xs = []
+    outs = []
+    for t in range(T):
+        x = wl.workload_step(w, vbar, t, 0, "cuda")
+        xs.append(sample(x))
+        st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        outs.append(f64(o.reshape(units, w.d_v)[idx]))
+    st.join()
+    torch.cuda.synchronize()
+    skipped = 0
+    for i, u in enumerate(idx):
+        b = u // H
+        t0 = t_start[b]
+        steps = [{k: (None if v is None else v[i]) for k, v in xs[t].items()}
+                 for t in range(t0, T)]
+        _, _, _, o_ref, ev = sc.scheduled_run(w.rule, a0[i], U0[i], V0[i], vb[i], steps, R, W, D)
+        bad = [A for A, kind, *gap in ev if kind == "snapshot" and gap[0] < TIE_GAP]
+        last = t0 + (bad[0] if bad else len(steps))
+        skipped += bool(bad)
+        for t in range(T):
+            if t < t0:
+                assert np.all(outs[t][i] == 0.0), (u, t)
+            elif t < last:
+                # the conversions differ by the prefill's fp32 rounding
+                assert rel_err(outs[t][i], o_ref[t - t0], -1) < TOL_READOUT, (u, t)
+    assert skipped <= 1
