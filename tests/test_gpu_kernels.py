@@ -55,9 +55,10 @@ def test_dense_step(rule, dims, in_dtype):
     gen = torch.Generator(device="cuda").manual_seed(12)
     S = torch.randn(B, H, d_k, d_v, generator=gen, device="cuda")
     o = torch.empty(B, H, d_v, device="cuda")
+    S_ref = f64(units_of(S))            # the seeded input; the oracle runs on from it
     for t in range(3):
         inp = wl.make_step(rule, B, H, d_k, d_v, vbar, 13, t, 0, in_dtype, "cuda")
-        S_ref, o_ref = oracle.dense_step(rule, f64(units_of(S)), **inputs_np(inp))
+        S_ref, o_ref = oracle.dense_step(rule, S_ref, **inputs_np(inp))
         binding.dense_decode_step(rule, S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o)
         torch.cuda.synchronize()
         assert rel_err(f64(units_of(S)), S_ref, (-2, -1)).max() < TOL_STATE_STEP

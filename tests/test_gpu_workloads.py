@@ -3,31 +3,33 @@
 Each workload runs exactly as bench.py runs it: a 512-step dense prefill
 (dense_decode_step), the conversion to the shallow form
 (seed_state_from_dense), then every decode step of the workload with a
-compression whenever R + W columns are held.  The oracle follows sampled
-(request, head) units from the GPU's converted state on the same inputs:
+compression whenever R + W columns are held.  The oracle runs sampled
+(request, head) units entirely on its own from the same seeded inputs: its
+own fp64 prefill, its own conversion, its own steps and compressions.
+Nothing it computes starts from a value the GPU produced.
 
-  * conversion: per call, sink <= 1e-5 and state <= 1e-4 (relative);
-  * read-outs: every step, <= 1e-4 relative per unit;
-  * states: at every window end (right after a compression), <= 1e-4
-    relative to the free-running oracle;
-  * between compressions: in a few windows the oracle restarts from the GPU
-    state at the window start and every step's state must agree to 1e-5;
-  * compressions: per call on the sampled units (truncation of the GPU's own
-    pre-compression factors) <= 1e-4, skipping units whose content has a
-    near-tie (s_R - s_{R+1}) / s_1 < 1e-4 at that compression; such units
-    are re-synchronised to the GPU state and counted.
+  * conversion: the GPU's converted state against the oracle's, 1e-4
+    relative (the two prefills differ by fp32 rounding);
+  * read-outs: every step, 1e-4 relative per unit;
+  * states: after every compression and at the last step, 1e-4 relative.
+A unit whose content has a near-tie at rank R ((s_R - s_{R+1}) / s_1 <
+1e-4: the truncation is not unique) at its conversion or at any
+compression is left out from then on and counted; at most 2 % of the
+compressions may be such.
 
 The 36-layer workload is checked on one layer's launch (256 requests x 32
 heads), its per-layer shape, over all 16384 decode steps.  Workloads 1-4
 are also run in the lazily decayed form (U = Diag(gam) U~, the decay kept
-as a running product), whose state is compared at true scale.
+as a running product), whose state is compared at true scale.  The
+per-call bar of 1e-5 on the state between compressions is held by the
+per-call tests (test_gpu_kernels.py) on oracle-generated states.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import (TIE_GAP, TOL_READOUT, TOL_STATE_COMPRESS, TOL_STATE_STEP, content_gap, f64,
+from gpu_util import (TIE_GAP, TOL_READOUT, TOL_STATE_COMPRESS, content_gap, f64,
                       rel_err, requires_gpu, state_rel_err)
 from sink_rank_recurrent_amd import binding
 from sink_rank_recurrent_amd import workloads as wl
@@ -62,7 +64,7 @@ def _units_inputs(x, idx):
     return out
 
 
-def run_workload(num, n_sample=8, steps=None, layer=0, checked_windows=(0, 1, -1), lazy=False):
+def run_workload(num, n_sample=8, steps=None, layer=0, lazy=False):
     w = wl.WORKLOADS[num]
     steps = w.steps if steps is None else steps
     dev = "cuda"
@@ -70,80 +72,53 @@ def run_workload(num, n_sample=8, steps=None, layer=0, checked_windows=(0, 1, -1
     idx = _sample_units(units, n_sample, 77 + num)
     vbar = wl.make_vbar(w.heads, w.d_v, w.seed, layer, dev)
     vb = f64(vbar)[idx % w.heads]
-    # dense prefill and conversion (GPU)
+    # dense prefill: the GPU for every unit, the oracle for the sampled ones
     S = torch.zeros(w.batch, w.heads, w.d_k, w.d_v, device=dev)
     o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
+    S_ref = np.zeros((len(idx), w.d_k, w.d_v))
     for t in range(-w.prefill, 0):
         x = wl.workload_step(w, vbar, t, layer, dev)
         binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        S_ref, _ = oracle.dense_step(w.rule, S_ref, **_units_inputs(x, idx))
     st = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar, device=dev,
                               lazy=lazy)
     st.from_dense(S)
     torch.cuda.synchronize()
-    S_np = f64(S.reshape(-1, w.d_k, w.d_v)[idx])
-    a_c, U_c, V_c = oracle.state_from_dense(S_np, vb, w.R)
-    a0, U0, V0 = _units_state(st, idx, st.r)
-    assert rel_err(a0, a_c, -1).max() < TOL_STATE_STEP
-    C = S_np - a_c[..., :, None] * vb[..., None, :]
-    gap0 = content_gap(C, np.broadcast_to(np.eye(w.d_v), C.shape[:-2] + (w.d_v, w.d_v)), w.R)
-    ok0 = gap0 >= TIE_GAP
-    e_conv = state_rel_err(a0, U0, V0, a_c, U_c, V_c, vb)
-    assert e_conv[ok0].max() < TOL_STATE_COMPRESS, e_conv
-
-    # free-running oracle from the GPU's converted state
-    a, U, V = a0, U0, V0
-    n_windows = (steps + w.W - 1) // w.W
-    check = {c % n_windows for c in checked_windows}
-    stats = {"o": 0.0, "window_state": 0.0, "within": 0.0, "compress": 0.0, "ties": 0,
+    a, U, V = oracle.state_from_dense(S_ref, vb, w.R)
+    C = S_ref - a[..., :, None] * vb[..., None, :]
+    ok = content_gap(C, np.broadcast_to(np.eye(w.d_v), C.shape[:-2] + (w.d_v, w.d_v)),
+                     w.R) >= TIE_GAP
+    stats = {"conversion": 0.0, "o": 0.0, "state": 0.0, "ties": int((~ok).sum()),
              "compressions": 0}
-    win = 0
-    win_ref = None
+    ga, gU, gV = _units_state(st, idx, st.r)
+    e_conv = state_rel_err(ga, gU, gV, a, U, V, vb)[ok]
+    stats["conversion"] = float(e_conv.max()) if e_conv.size else 0.0
+    assert stats["conversion"] < TOL_STATE_COMPRESS, e_conv
+
     for t in range(steps):
         x = wl.workload_step(w, vbar, t, layer, dev)
-        xi = _units_inputs(x, idx)
-        if win in check and st.r == w.R and win_ref is None:
-            win_ref = _units_state(st, idx, st.r)          # restart point of this window
         st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-        a, U, V, o_ref = oracle.seed_step(w.rule, a, U, V, vb, **xi)
-        o_gpu = f64(o.reshape(-1, w.d_v)[idx])
-        e_o = rel_err(o_gpu, o_ref, -1).max()
-        stats["o"] = max(stats["o"], e_o)
-        assert e_o < TOL_READOUT, (t, e_o)
-        if win_ref is not None:
-            # between compressions: the oracle restarted at this window's start
-            ra, rU, rV = win_ref
-            ra, rU, rV, _ = oracle.seed_step(w.rule, ra, rU, rV, vb, **xi)
-            win_ref = (ra, rU, rV)
-            ga, gU, gV = _units_state(st, idx, st.r)
-            e_w = state_rel_err(ga, gU, gV, ra, rU, rV, vb).max()
-            stats["within"] = max(stats["within"], e_w)
-            assert e_w < TOL_STATE_STEP, (t, e_w)
+        a, U, V, o_ref = oracle.seed_step(w.rule, a, U, V, vb, **_units_inputs(x, idx))
+        e_o = rel_err(f64(o.reshape(-1, w.d_v)[idx]), o_ref, -1)[ok]
+        if e_o.size:
+            stats["o"] = max(stats["o"], float(e_o.max()))
+            assert e_o.max() < TOL_READOUT, (t, e_o)
+        last = t == steps - 1
         if st.r >= st.cap:
-            gpu_pre = _units_state(st, idx, st.r)
             st.compress()
             stats["compressions"] += 1
-            ga, gU, gV = _units_state(st, idx, st.r)
-            # per call: truncation of the GPU's own pre-compression factors
-            Uc, Vc = oracle.compress(gpu_pre[1], gpu_pre[2], w.R)
-            gap = content_gap(gpu_pre[1], gpu_pre[2], w.R)
-            ok = gap >= TIE_GAP
-            e_c = state_rel_err(ga, gU, gV, gpu_pre[0], Uc, Vc, vb)
-            if ok.any():
-                stats["compress"] = max(stats["compress"], e_c[ok].max())
-                assert e_c[ok].max() < TOL_STATE_COMPRESS, (t, e_c)
-            # free-running oracle
-            gap_ref = content_gap(U, V, w.R)
+            tie = content_gap(U, V, w.R) < TIE_GAP
+            stats["ties"] += int((tie & ok).sum())
+            ok &= ~tie
             U, V = oracle.compress(U, V, w.R)
-            tie = (gap_ref < TIE_GAP) | ~ok
-            if tie.any():                     # non-unique truncation: follow the GPU
-                stats["ties"] += int(tie.sum())
-                a[tie], U[tie], V[tie] = ga[tie], gU[tie], gV[tie]
-            e_s = state_rel_err(ga, gU, gV, a, U, V, vb).max()
-            stats["window_state"] = max(stats["window_state"], e_s)
-            assert e_s < TOL_STATE_COMPRESS, (t, e_s)
-            win += 1
-            win_ref = None
-    assert stats["ties"] <= max(1, stats["compressions"] * len(idx) // 50), stats
+        if (st.r == st.R or last) and ok.any():
+            ga, gU, gV = _units_state(st, idx, st.r)
+            e_s = state_rel_err(ga, gU, gV, a, U, V, vb)[ok]
+            stats["state"] = max(stats["state"], float(e_s.max()))
+            assert e_s.max() < TOL_STATE_COMPRESS, (t, e_s)
+    n_checks = len(idx) * (1 + stats["compressions"])
+    assert stats["ties"] <= max(1, n_checks // 50), stats
+    assert ok.sum() >= len(idx) // 2, stats
     return stats
 
 
