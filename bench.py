@@ -571,11 +571,12 @@ def main() -> int:
         "dense_baseline": dense,
         "lazy_decay_variant": variants.get("lazy_decay_variant"),
         "fp16_factor_variant": variants.get("fp16_factor_variant"),
-        "conversion": {"kernel": "from_dense_kernel", "ms": CONVERSION_MS.get("ms"),
-                       "heads": units,
+        "conversion": {"kernel": "compress_wave_kernel (conversion instance)",
+                       "ms": CONVERSION_MS.get("ms"), "heads": units,
                        "us_per_head": CONVERSION_MS.get("ms", 0.0) * 1e3 / units,
                        "what": "end-of-prefill sink split and rank-R truncation of every head "
-                               "(cyclic Jacobi on C C^T, once per request)"},
+                               "(C C^T by MFMA, Householder, multisection, inverse iteration; "
+                               "once per request)"},
         "staggered_schedule_variants": sched,
         "handoff": handoff,
         "state_stats": stats,

@@ -312,8 +312,11 @@ seed_status seed_unpack_states(int batch, int heads, int d_k, int d_v, int cap, 
  * The sink is the state's projection on vbar (Fig. 3 (b), (c)):
  *   a = S vbar / |vbar|^2,   C = S - a vbar^T,
  * and U, V (columns 0..R-1) are the rank-R truncation of C, U orthonormal.
- * S is read only.  The caller sets r = R.  Requires 1 <= R <= min(d_k, d_v)
- * and R <= cap.
+ * S [batch][heads][d_k][d_v] and vbar [heads][d_v] are read only; a is
+ * [batch][heads][d_k], U and V the usual [batch][heads][cap][d_k | d_v].
+ * The caller sets r = R.  Requires 1 <= R <= min(d_k, d_v) and R <= cap;
+ * R above 32 returns SEED_E_UNSUPPORTED.  Where the truncation is not
+ * unique (s_R = s_{R+1}) any of the optimal ones may come back.
  */
 seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
                                   const float *S, const float *vbar,

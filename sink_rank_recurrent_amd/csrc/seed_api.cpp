@@ -339,7 +339,7 @@ seed_status seed_state_stats(int batch, int heads, int d_k, int d_v, int R, cons
   SEED_PTR(rec);
   if (spec_S != nullptr) SEED_PTR(spec_S);
   if (spec_C != nullptr) SEED_PTR(spec_C);
-  if (seed::from_dense_lds_bytes(d_k, 1) > seed::kMaxLds)
+  if (seed::stats_lds_bytes(d_k, 1) > seed::kMaxLds)
     return fail(SEED_E_UNSUPPORTED, "%s: d_k=%d needs more LDS than a CU has", fn, d_k);
   return device_status(fn, seed::launch_state_stats(batch, heads, d_k, d_v, R, S, vbar, rec,
                                                     spec_S, spec_C,
@@ -455,11 +455,21 @@ seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int ca
   SEED_PTR(a);
   SEED_PTR(U);
   SEED_PTR(V);
-  if (seed::from_dense_lds_bytes(d_k, R) > seed::kMaxLds)
+  if (seed::convert_lds_bytes(d_k, R) > seed::kMaxLds)
     return fail(SEED_E_UNSUPPORTED, "%s: d_k=%d at rank %d needs more LDS than a CU has", fn, d_k,
                 R);
-  return device_status(fn, seed::launch_from_dense(batch, heads, d_k, d_v, cap, R, S, vbar, a, U,
-                                                   V, static_cast<hipStream_t>(stream)));
+  seed::CompressArgs args{};
+  args.units = batch * heads;
+  args.cap = cap;
+  args.n = d_k;
+  args.R = R;
+  args.U = U;
+  args.V = V;
+  args.heads = heads;
+  args.S = S;
+  args.vbar = vbar;
+  args.a = a;
+  return device_status(fn, seed::launch_convert(d_k, d_v, args, static_cast<hipStream_t>(stream)));
 }
 
 seed_status dense_decode_step(int rule, int batch, int heads, int d_k, int d_v, float* S,

@@ -1,17 +1,13 @@
-// Conversion of dense states to the shallow form at the end of the prefill.
+// Statistics of dense states by cyclic Jacobi (seed_state_stats).
 //
-// What is computed.  A dense state S is split into its sink
-// a = S vbar/|vbar|^2 (SEED figures and tables on thelatestinai.com,
-// Fig. 3 (b)) and content C = S - a vbar^T, which is truncated to its best
-// rank-R approximation (Fig. 1 (a) caption): U = top-R left singular
-// vectors of C, V = C^T U.
-//
-// How (one 256-thread workgroup per unit, everything small lives in LDS):
-// H = C C^T (d_k x d_k) is diagonalised by cyclic Jacobi with parallel
-// ordering.  Only the separation of the top-R eigenvectors from the rest
-// matters for U V^T, so the sweeps stop once every rotation angle coupling
-// the two sets, |H_ij| / (H_ii - H_jj), is below 1e-5.  This runs once per
-// request; the per-step compression lives in seed_compress_wave.h.
+// A dense state S splits into its sink a = S vbar/|vbar|^2 (SEED figures and
+// tables on thelatestinai.com, Fig. 3 (b)) and content C = S - a vbar^T.
+// The statistics need whole spectra of S S^T and C C^T and their top
+// eigenvectors to full accuracy, once per inspected state, so one 256-thread
+// workgroup per unit diagonalises each d_k x d_k Gram in LDS by cyclic
+// Jacobi with parallel ordering, run to convergence.  (The end-of-prefill
+// conversion, which needs only the top R, runs on the compression kernel's
+// tridiagonal eigensolver in seed_compress_wave.h.)
 #include "seed_device.h"
 #include "seed_launch.h"
 
@@ -20,10 +16,8 @@ namespace seed {
 namespace {
 
 constexpr int kNT = 256;
-constexpr int kRMax = 32;           // largest rank kept
 constexpr int kChunk = 32;          // rows staged per Gram pass
 constexpr float kRotTol = 1e-6f;    // rotate when |h_pq| > kRotTol sqrt(h_pp h_qq)
-constexpr float kAngleTol = 1e-5f;  // top-R / rest coupling angle at convergence
 constexpr int kMaxSweeps = 15;
 
 struct Lds {
@@ -154,9 +148,8 @@ __device__ __forceinline__ void rank_diagonal(const Lds& L) {
 // Cyclic Jacobi on the symmetric L.H (np x np, padding zero), accumulating
 // eigenvectors into L.X (set to the identity here).  On exit the diagonal
 // of H holds the eigenvalues and L.rank their descending ranks.  Stops when
-// the top-R eigenvectors are separated from the rest (full_tol == 0), or,
-// with full_tol > 0, when every off-diagonal entry is at most full_tol.
-__device__ __forceinline__ void jacobi(const Lds& L, int R, float full_tol = 0.f) {
+// every off-diagonal entry is at most full_tol.
+__device__ __forceinline__ void jacobi(const Lds& L, float full_tol) {
   const int tid = threadIdx.x;
   const int np = L.np, ld = L.ld, nb = np / 2;
   float* H = L.H;
@@ -235,13 +228,7 @@ __device__ __forceinline__ void jacobi(const Lds& L, int R, float full_tol = 0.f
     bool bad = false;
     for (int w = tid; w < np * np; w += kNT) {
       const int i = w / np, j = w % np;
-      if (full_tol > 0.f) {
-        if (i != j && fabsf(H[i * ld + j]) > full_tol) bad = true;
-      } else if (L.rank[i] < R && L.rank[j] >= R) {
-        const float gap = H[i * ld + i] - H[j * ld + j];
-        const float hij = fabsf(H[i * ld + j]);
-        if (hij > kAngleTol * gap) bad = true;
-      }
+      if (i != j && fabsf(H[i * ld + j]) > full_tol) bad = true;
     }
     if (bad) L.flag[0] = 1;
     __syncthreads();
@@ -250,99 +237,9 @@ __device__ __forceinline__ void jacobi(const Lds& L, int R, float full_tol = 0.f
   }
 }
 
-// X_R (top-R eigenvectors, in rank order, first n rows) into L.T.
-__device__ __forceinline__ void select_top(const Lds& L, int n, int R) {
-  const int tid = threadIdx.x;
-  for (int i = tid; i < L.np; i += kNT) {
-    const int r = L.rank[i];
-    if (r < R) L.pq[r] = i;  // pq is free after Jacobi
-  }
-  __syncthreads();
-  for (int w = tid; w < n * R; w += kNT) {
-    const int j = w / R, c = w % R;
-    L.T[j * R + c] = L.X[j * L.ld + L.pq[c]];
-  }
-  __syncthreads();
-}
-
-template <int DK, int DV>
-__global__ __launch_bounds__(256) void from_dense_kernel(const float* __restrict__ S,
-                                                          const float* __restrict__ vbar,
-                                                          float* __restrict__ a,
-                                                          float* __restrict__ U,
-                                                          float* __restrict__ V, int heads,
-                                                          int cap, int R) {
-  extern __shared__ float smem[];
-  const int n = DK;
-  const Lds L = carve(smem, n, R);
-  const int tid = threadIdx.x;
-  const int ld = L.ld;
-  const size_t ub = blockIdx.x;
-  const int h = (int)(ub % heads);
-  const float* Sh = S + ub * DK * DV;
-  float* av = L.aux;          // [DK] sink coefficient
-  float* vb = L.aux + 128;    // [DV] vbar
-
-  for (int e = tid; e < DV; e += kNT) vb[e] = vbar[(size_t)h * DV + e];
-  __syncthreads();
-  float nv2 = 0.f;
-  for (int e = 0; e < DV; ++e) nv2 += vb[e] * vb[e];
-  // a_i = S_i . vbar / |vbar|^2, one half-wave per row
-  {
-    constexpr int EV = DV / 32;
-    const int grp = tid >> 5, lane = tid & 31;
-    for (int i = grp; i < DK; i += 8) {
-      float x[EV];
-      load_vec<EV>(Sh + (size_t)i * DV + lane * EV, x);
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < EV; ++e) p += x[e] * vb[lane * EV + e];
-      p = sum32(p) / nv2;
-      if (lane == 0) {
-        av[i] = p;
-        a[ub * DK + i] = p;
-      }
-    }
-  }
-  __syncthreads();
-
-  // H = C C^T with C_i = S_i - a_i vbar (rows of C are the "columns" here)
-  gram_dispatch([=](int j, int e) { return Sh[(size_t)j * DV + e] - av[j] * vb[e]; }, n, DV, L.H,
-                ld, L.X);
-  __syncthreads();
-
-  jacobi(L, R);
-  select_top(L, n, R);
-
-  // U' = X_R (columns in key space), V'_c = C^T X_R[:, c]
-  for (int w = tid; w < R * DK; w += kNT) {
-    const int c = w / DK, e = w % DK;
-    U[(ub * cap + c) * DK + e] = L.T[e * R + c];
-  }
-  constexpr int NCV = kNT / DV;
-  constexpr int CPV = kRMax / NCV;
-  const int ev = tid % DV, cv = tid / DV;
-  float accv[CPV];
-#pragma unroll
-  for (int m = 0; m < CPV; ++m) accv[m] = 0.f;
-  for (int j = 0; j < DK; ++j) {
-    const float cj = Sh[(size_t)j * DV + ev] - av[j] * vb[ev];
-#pragma unroll
-    for (int m = 0; m < CPV; ++m) {
-      const int c = cv + NCV * m;
-      if (c < R) accv[m] += cj * L.T[j * R + c];
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < CPV; ++m) {
-    const int c = cv + NCV * m;
-    if (c < R) V[(ub * cap + c) * DV + ev] = accv[m];
-  }
-}
-
 // Statistics of dense states (SEED figures and tables: Fig. 3 (e), (g),
-// (h); Fig. 12 (f); Fig. 13 (a), (b), (d)).  Per unit: the sink split as in
-// from_dense_kernel; the energies |S|^2 (trace of S S^T), |a vbar^T|^2 =
+// (h); Fig. 12 (f); Fig. 13 (a), (b), (d)).  Per unit: the sink split
+// a = S vbar / |vbar|^2; the energies |S|^2 (trace of S S^T), |a vbar^T|^2 =
 // |a|^2 |vbar|^2 and |C|^2; the eigenvectors x_i of S S^T and of C C^T by
 // Jacobi run to convergence, each eigenvalue then taken as the Rayleigh
 // quotient |M^T x_i|^2 from the matrix itself (second order in the
@@ -444,7 +341,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ S,
   // the trace, summed by every thread in the same order
   float e_state = 0.f;
   for (int i = 0; i < DK; ++i) e_state += L.H[i * ld + i];
-  jacobi(L, 1, kFullTol * e_state);
+  jacobi(L, kFullTol * e_state);
   stage_rows<DK, DV>(L, [=](int j, int e) { return Sh[(size_t)j * DV + e]; });
   rayleigh<DK, DV>(L, p0, p1, lam, L.rank);
   int i0 = 0;
@@ -480,7 +377,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ S,
   __syncthreads();
   float e_content = 0.f;
   for (int i = 0; i < DK; ++i) e_content += L.H[i * ld + i];
-  jacobi(L, 1, kFullTol * e_content);
+  jacobi(L, kFullTol * e_content);
   stage_rows<DK, DV>(L, [=](int j, int e) { return Sh[(size_t)j * DV + e] - av[j] * vb[e]; });
   rayleigh<DK, DV>(L, p0, p1, lam, L.rank);
   for (int i = tid; i < DK; i += kNT) {
@@ -513,20 +410,9 @@ hipError_t set_lds(K kernel, size_t bytes) {
 }
 
 template <int DK, int DV>
-hipError_t from_dense_go(int units, int heads, int cap, int R, const float* S, const float* vbar,
-                         float* a, float* U, float* V, hipStream_t s) {
-  const size_t bytes = from_dense_lds_bytes(DK, R);
-  hipError_t err = set_lds(from_dense_kernel<DK, DV>, bytes);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((from_dense_kernel<DK, DV>), dim3(units), dim3(kNT), bytes, s, S, vbar, a, U,
-                     V, heads, cap, R);
-  return hipGetLastError();
-}
-
-template <int DK, int DV>
 hipError_t stats_go(int units, int heads, int R, const float* S, const float* vbar, float* rec,
                     float* specS, float* specC, hipStream_t s) {
-  const size_t bytes = from_dense_lds_bytes(DK, 1);
+  const size_t bytes = stats_lds_bytes(DK, 1);
   hipError_t err = set_lds(stats_kernel<DK, DV>, bytes);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((stats_kernel<DK, DV>), dim3(units), dim3(kNT), bytes, s, S, vbar, heads, R,
@@ -553,19 +439,6 @@ hipError_t launch_state_stats(int batch, int heads, int d_k, int d_v, int R, con
   return hipErrorInvalidValue;
 }
 
-size_t from_dense_lds_bytes(int d_k, int R) { return 4 * lds_floats(padded(d_k), R); }
-
-hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
-                             const float* S, const float* vbar, float* a, float* U, float* V,
-                             hipStream_t stream) {
-  const int units = batch * heads;
-  if (d_k == 128 && d_v == 128)
-    return from_dense_go<128, 128>(units, heads, cap, R, S, vbar, a, U, V, stream);
-  if (d_k == 128 && d_v == 64)
-    return from_dense_go<128, 64>(units, heads, cap, R, S, vbar, a, U, V, stream);
-  if (d_k == 64 && d_v == 64)
-    return from_dense_go<64, 64>(units, heads, cap, R, S, vbar, a, U, V, stream);
-  return hipErrorInvalidValue;
-}
+size_t stats_lds_bytes(int d_k, int R) { return 4 * lds_floats(padded(d_k), R); }
 
 }  // namespace seed

@@ -38,12 +38,16 @@ namespace wave {
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kEps = 1.1920928955078125e-7f;   // 2^-23
-constexpr float kPivTol = 1e-5f;                   // dependent-column threshold (relative)
+constexpr float kPivTol = 1e-5f;
+constexpr float kMinNormal = 1.17549435e-38f;      // smallest normal fp32                   // dependent-column threshold (relative)
 // Eigenvalues closer than kClusterTol |T| form a run whose vectors are
 // computed one after another, each re-orthogonalised against the earlier
 // ones of its run.
 constexpr float kClusterTol = 1e-5f;
 constexpr int kInvIters = 2;
+// Eigenvalues below kEigFloor eps |T| are resolved only to that absolute
+// accuracy (they sit at the rounding level of T's entries).
+constexpr float kEigFloor = 1e-3f;
 // T is padded to NMAX rows with this diagonal and zero couplings; the padded
 // entries of every solve are exactly 0.
 constexpr float kPadDiag = 1.0e30f;
@@ -139,7 +143,8 @@ __device__ __forceinline__ float start_entry(int i, int c) {
 // ---------------------------------------------------------------------------
 // LDS layout (offsets in floats; every region a multiple of 4 floats)
 
-template <int NMAX, int RMAX>
+// NO_RB: the conversion's layout, which has no R~ (and no decay product).
+template <int NMAX, int RMAX, bool NO_RB = false>
 struct Lay {
   static constexpr int NW = (NMAX + 63) / 64;     // waves per unit
   static constexpr int NTH = 64 * NW;
@@ -149,7 +154,7 @@ struct Lay {
   static constexpr int CH = NMAX / PARTS;          // rows per lane
   static constexpr int G = 0;                      // [NMAX][LDN] Grams, Z, H, then reflectors (row k)
   static constexpr int RB = G + NMAX * LDN;        // [NMAX][LDN] R~ by columns: RB[m*LDN + i] = R~[i][m]
-  static constexpr int XR = RB + NMAX * LDN;       // [NMAX][RMAX] eigenvectors, Y, then T'
+  static constexpr int XR = RB + (NO_RB ? 0 : NMAX * LDN);   // [NMAX][RMAX] eigenvectors, Y, then T'
   static constexpr int FA = XR + NMAX * RMAX;      // [NMAX][RMAX] x 3: solve factors; FA then holds P2
   static constexpr int FB = FA + NMAX * RMAX;
   static constexpr int FC = FB + NMAX * RMAX;
@@ -172,7 +177,7 @@ struct Lay {
   // decay product per key row (lazy form), 128 entries: in the 4 padding
   // columns of the rows of RB (never read or written otherwise) when they
   // hold 128 entries, else in a region of its own
-  static constexpr bool GS_PAD = 4 * NMAX >= 128;
+  static constexpr bool GS_PAD = !NO_RB && 4 * NMAX >= 128;
   static constexpr int GS = STA + RMAX;
   static constexpr int RED = GS + (GS_PAD ? 0 : 128);   // [8][NW] cross-wave partials
   static constexpr int MISC = RED + 8 * NW + (8 * NW) % 4;
@@ -191,11 +196,15 @@ struct Lay {
 // slot kk over its quarter of that range; with two waves the partial sums
 // meet in LDS (wave 1 stores, wave 0 adds and stores the total).  If rs is
 // not NULL, row e of X is first multiplied by rs[e] (rs_per_row) or by rs[0].
-template <int NMAX, int NW, int D, bool SCALE, int FMT, int KR, typename ColF>
+// With CORR, column j is first replaced by X_j - ca[j] cb (the content of a
+// dense state: a row of S less its sink).
+template <int NMAX, int NW, int D, bool SCALE, int FMT, int KR, typename ColF,
+          bool CORR = false>
 __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
                                      int n, float* __restrict__ G,
                                      const float* __restrict__ dv, const float* __restrict__ rs,
-                                     bool rs_per_row) {
+                                     bool rs_per_row, const float* __restrict__ ca = nullptr,
+                                     const float* __restrict__ cb = nullptr) {
   constexpr int LDN = NMAX + 4;
   constexpr int NT = NMAX / 16;
   constexpr int NP = NT * (NT + 1) / 2;
@@ -233,6 +242,20 @@ __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
       } else {
 #pragma unroll
         for (int s = 0; s < KC; ++s) x[t][s] = 0.f;
+      }
+      if constexpr (CORR) {
+        // column col less ca[col] cb (entries off .. off + KC of cb)
+        if (col < n) {
+          const float c0 = ca[col];
+#pragma unroll
+          for (int q = 0; q < KC / 4; ++q) {
+            const float4 b4 = *reinterpret_cast<const float4*>(cb + off + 4 * q);
+            x[t][4 * q + 0] = fmaf(-c0, b4.x, x[t][4 * q + 0]);
+            x[t][4 * q + 1] = fmaf(-c0, b4.y, x[t][4 * q + 1]);
+            x[t][4 * q + 2] = fmaf(-c0, b4.z, x[t][4 * q + 2]);
+            x[t][4 * q + 3] = fmaf(-c0, b4.w, x[t][4 * q + 3]);
+          }
+        }
       }
     }
     if (rs != nullptr) {
@@ -362,7 +385,9 @@ __device__ __forceinline__ void tri_step(float (&h)[NMAX], int k, float hk, floa
   constexpr int LDN = NMAX + 4;
   const float xn2 = block_reduce<NW>(t > k + 1 ? hk * hk : 0.f, AddOp(), RED, 0);
   float tau = 0.f, beta = alpha, sc = 0.f;
-  if (xn2 != 0.f) {
+  // a column whose sub-subdiagonal part squares to a subnormal (below
+  // 1e-19 of H's scale, itself near 1) is taken as already reduced
+  if (xn2 >= kMinNormal) {
     const float nrm = fsqrt(fmaf(alpha, alpha, xn2));
     beta = alpha >= 0.f ? -nrm : nrm;
     tau = (beta - alpha) * frcp(beta);
@@ -451,8 +476,11 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   // layout's kept columns are fp32 (CompressArgs in seed_launch.h).
   constexpr bool H16 = FMT == kStoreBF16 || FMT == kStoreF16;
   constexpr bool RING = FMT == kStoreRing;
+  // the end-of-prefill conversion: H = C C^T of a dense state directly
+  // (no factors, no Cholesky), U' = X_R, V' = C^T X_R
+  constexpr bool CONV = FMT == kConvert;
   constexpr int KR = H16 ? RMAX : 0;
-  using L = Lay<NMAX, RMAX>;
+  using L = Lay<NMAX, RMAX, CONV>;
   constexpr int NW = L::NW, NTH = L::NTH, LDN = L::LDN;
   constexpr int PARTS = L::PARTS, CH = L::CH, NACT = L::NACT;
   extern __shared__ float4 smem4[];
@@ -524,8 +552,10 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
 
   // R~ (with its zero lower part), the eigenvector block and the published
   // vectors start at zero
-  for (int i = 4 * t; i < NMAX * LDN; i += 4 * NTH)
-    *reinterpret_cast<float4*>(RB + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (!CONV) {
+    for (int i = 4 * t; i < NMAX * LDN; i += 4 * NTH)
+      *reinterpret_cast<float4*>(RB + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   for (int i = 4 * t; i < NMAX * RMAX; i += 4 * NTH)
     *reinterpret_cast<float4*>(XR + i) = make_float4(0.f, 0.f, 0.f, 0.f);
   CB[t] = 0.f;
@@ -538,112 +568,158 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     __syncthreads();
   }
 
-  // @phase A: Gram of U and column norms
-  gram<NMAX, NW, DK, false, FMT, KR>(ucol, Ukh, n, G, nullptr, gamh, gam_per_row);
-  __syncthreads();
-  if (act) {
-    const float gtt = G[t * LDN + t];
-    const bool pos = t < n && gtt > 0.f;
-    DVs[t] = pos ? fsqrt(gtt) : 0.f;
-    IDV[t] = pos ? frsq(gtt) : 0.f;
-  }
-  __syncthreads();
-  float g[NMAX];
-  {
-    const float it = act ? IDV[t] : 0.f;
-    // the scale d_t^-1 d_i^-1 is one product for both (i, t) and (t, i), so
-    // the columns stay exactly symmetric through the Cholesky
-#pragma unroll
-    for (int i = 0; i < NMAX; ++i) g[i] = act ? G[i * LDN + t] * (it * IDV[i]) : 0.f;
-  }
-  __syncthreads();
-  // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
-  gram<NMAX, NW, DV_, true, FMT, KR>(vcol, Vkh, n, G, DVs, nullptr, false);
+  if constexpr (CONV) {
+    // @phase A (conversion): the sink a = S vbar / |vbar|^2 (row t of S by
+    // thread t), then H = C C^T with C = S - a vbar^T formed on the fly
+    float* const vbs = IDV;          // vbar (IDV and IRD: 2 NMAX >= d_v floats)
+    float* const asink = DVs;        // a
+    const float* const Sh = args.S + ub * DK * DV_;
+    for (int e = t; e < DV_; e += NTH) vbs[e] = args.vbar[(size_t)(ub % args.heads) * DV_ + e];
+    __syncthreads();
+    float nv2 = 0.f;
+    for (int e = 0; e < DV_; ++e) nv2 = fmaf(vbs[e], vbs[e], nv2);
+    if (act) {
+      float p0 = 0.f, p1 = 0.f;
+      for (int e = 0; e < DV_; e += 4) {
+        const float4 x4 = *reinterpret_cast<const float4*>(Sh + (size_t)t * DV_ + e);
+        p0 = fmaf(x4.x, vbs[e], p0);
+        p1 = fmaf(x4.y, vbs[e + 1], p1);
+        p0 = fmaf(x4.z, vbs[e + 2], p0);
+        p1 = fmaf(x4.w, vbs[e + 3], p1);
+      }
+      const float at = (p0 + p1) / nv2;
+      asink[t] = at;
+      args.a[ub * DK + t] = at;
+    }
+    __syncthreads();
+    auto scol = [&](int j) -> const float* { return Sh + (size_t)j * DV_; };
+    gram<NMAX, NW, DV_, false, kStoreF32, 0, decltype(scol), true>(scol, nullptr, n, G, nullptr,
+                                                                   nullptr, false, asink, vbs);
+    __syncthreads();
+  } else {
+    // @phase A: Gram of U and column norms
+    gram<NMAX, NW, DK, false, FMT, KR>(ucol, Ukh, n, G, nullptr, gamh, gam_per_row);
+    __syncthreads();
+    if (act) {
+      const float gtt = G[t * LDN + t];
+      const bool pos = t < n && gtt > 0.f;
+      DVs[t] = pos ? fsqrt(gtt) : 0.f;
+      IDV[t] = pos ? frsq(gtt) : 0.f;
+    }
+    __syncthreads();
+    float g[NMAX];
+    {
+      const float it = act ? IDV[t] : 0.f;
+      // the scale d_t^-1 d_i^-1 is one product for both (i, t) and (t, i), so
+      // the columns stay exactly symmetric through the Cholesky
+  #pragma unroll
+      for (int i = 0; i < NMAX; ++i) g[i] = act ? G[i * LDN + t] * (it * IDV[i]) : 0.f;
+    }
+    __syncthreads();
+    // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
+    gram<NMAX, NW, DV_, true, FMT, KR>(vcol, Vkh, n, G, DVs, nullptr, false);
 
-  // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
-  if constexpr (NW == 1) {
-    // one wave: fully unrolled, so g[j] is a fixed register; the Schur
-    // complement is symmetric, so it is this column's copy of G~[j][t]
-#pragma clang loop unroll(full)
-    for (int j = 0; j < NMAX; ++j) {
-      if (j < n) {
-        const float gj = g[j];
-        const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gj), j));
-        chol_step<NMAX, true>(g, j, gj, piv, t, act, RB, WB, IRD);
+    // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
+    if constexpr (NW == 1) {
+      // one wave: fully unrolled, so g[j] is a fixed register; the Schur
+      // complement is symmetric, so it is this column's copy of G~[j][t]
+  #pragma clang loop unroll(full)
+      for (int j = 0; j < NMAX; ++j) {
+        if (j < n) {
+          const float gj = g[j];
+          const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gj), j));
+          chol_step<NMAX, true>(g, j, gj, piv, t, act, RB, WB, IRD);
+        }
+      }
+    } else {
+      for (int j = 0; j < n; ++j) {
+        if (t == j) {
+  #pragma unroll
+          for (int i = 0; i < NMAX; i += 4)
+            *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
+        }
+        __syncthreads();
+        chol_step<NMAX, false>(g, j, CB[t], CB[j], t, act, RB, WB, IRD);
       }
     }
-  } else {
-    for (int j = 0; j < n; ++j) {
-      if (t == j) {
-#pragma unroll
-        for (int i = 0; i < NMAX; i += 4)
-          *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
+    for (int j = n + t; j < NMAX; j += NTH) IRD[j] = 0.f;
+    __syncthreads();
+
+    // @phase C: Z = R~ G~ in place by column tiles, then H = Z R~^T in place
+    // by row tiles (R~[i][m] = 0 for m < i, so those k-steps are skipped)
+    {
+      constexpr int NT = NMAX / 16;
+      const int l = t & 63, w = t >> 6;
+      const int ci = l & 15, kk = l >> 4;
+  #pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        if (J % NW != w) continue;
+        f4v acc[NT];
+  #pragma unroll
+        for (int I = 0; I < NT; ++I) acc[I] = f4v{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int K = 0; K < NMAX / 4; ++K) {
+          const int m = 4 * K + kk;
+          const float bv = G[m * LDN + 16 * J + ci];          // G~[m][j]
+  #pragma unroll
+          for (int I = 0; I < NT; ++I) {
+            if (4 * K + 3 < 16 * I) continue;
+            const float av = RB[m * LDN + 16 * I + ci];        // R~[i][m]
+            acc[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[I], 0, 0, 0);
+          }
+        }
+  #pragma unroll
+        for (int I = 0; I < NT; ++I)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDN + 16 * J + ci] = acc[I][r];
       }
       __syncthreads();
-      chol_step<NMAX, false>(g, j, CB[t], CB[j], t, act, RB, WB, IRD);
+  #pragma unroll
+      for (int I = 0; I < NT; ++I) {
+        if (I % NW != w) continue;
+        f4v acc[NT];
+  #pragma unroll
+        for (int J = 0; J < NT; ++J) acc[J] = f4v{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int K = 0; K < NMAX / 4; ++K) {
+          const int m = 4 * K + kk;
+          const float av = G[(16 * I + ci) * LDN + m];        // Z[i][m]
+  #pragma unroll
+          for (int J = 0; J < NT; ++J) {
+            if (4 * K + 3 < 16 * J) continue;
+            const float bv = RB[m * LDN + 16 * J + ci];        // R~[j][m]
+            acc[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[J], 0, 0, 0);
+          }
+        }
+  #pragma unroll
+        for (int J = 0; J < NT; ++J)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDN + 16 * J + ci] = acc[J][r];
+      }
+      __syncthreads();
     }
   }
-  for (int j = n + t; j < NMAX; j += NTH) IRD[j] = 0.f;
-  __syncthreads();
 
-  // @phase C: Z = R~ G~ in place by column tiles, then H = Z R~^T in place
-  // by row tiles (R~[i][m] = 0 for m < i, so those k-steps are skipped)
+  // @phase D: Householder tridiagonalisation, thread t owning column t of H.
+  // H is first scaled by the power of two that brings its largest diagonal
+  // entry (its largest entry: H is positive semidefinite) into [0.5, 1):
+  // exact, the eigenvectors are unchanged and every later stop is relative,
+  // and the squares the reflectors form stay clear of the subnormal range,
+  // where sqrt and rcp read zero (a content at 1e-6 of a dense state's sink
+  // puts H near 1e-12 and its small entries' squares below 1e-38).
+  float hs = 1.f;
   {
-    constexpr int NT = NMAX / 16;
-    const int l = t & 63, w = t >> 6;
-    const int ci = l & 15, kk = l >> 4;
-#pragma unroll
-    for (int J = 0; J < NT; ++J) {
-      if (J % NW != w) continue;
-      f4v acc[NT];
-#pragma unroll
-      for (int I = 0; I < NT; ++I) acc[I] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int K = 0; K < NMAX / 4; ++K) {
-        const int m = 4 * K + kk;
-        const float bv = G[m * LDN + 16 * J + ci];          // G~[m][j]
-#pragma unroll
-        for (int I = 0; I < NT; ++I) {
-          if (4 * K + 3 < 16 * I) continue;
-          const float av = RB[m * LDN + 16 * I + ci];        // R~[i][m]
-          acc[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[I], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int I = 0; I < NT; ++I)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDN + 16 * J + ci] = acc[I][r];
+    const float dg = (act && t < n) ? G[t * LDN + t] : 0.f;
+    const float mxd = block_reduce<NW>(dg, MaxOp(), RED, 5);
+    if (mxd > 0.f && mxd < 3.0e38f) {
+      int ex;
+      frexpf(mxd, &ex);
+      hs = ldexpf(1.f, -ex);
     }
-    __syncthreads();
-#pragma unroll
-    for (int I = 0; I < NT; ++I) {
-      if (I % NW != w) continue;
-      f4v acc[NT];
-#pragma unroll
-      for (int J = 0; J < NT; ++J) acc[J] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int K = 0; K < NMAX / 4; ++K) {
-        const int m = 4 * K + kk;
-        const float av = G[(16 * I + ci) * LDN + m];        // Z[i][m]
-#pragma unroll
-        for (int J = 0; J < NT; ++J) {
-          if (4 * K + 3 < 16 * J) continue;
-          const float bv = RB[m * LDN + 16 * J + ci];        // R~[j][m]
-          acc[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[J], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int J = 0; J < NT; ++J)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDN + 16 * J + ci] = acc[J][r];
-    }
-    __syncthreads();
   }
-
-  // @phase D: Householder tridiagonalisation, thread t owning column t of H
   float h[NMAX];
 #pragma unroll
-  for (int i = 0; i < NMAX; ++i) h[i] = act ? G[i * LDN + t] : 0.f;
+  for (int i = 0; i < NMAX; ++i) h[i] = act ? G[i * LDN + t] * hs : 0.f;
   __syncthreads();
   if constexpr (NW == 1) {
     // one wave: fully unrolled, so h[k] is a fixed register; H is
@@ -719,11 +795,18 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     const int target = n - 1 - grp;            // ascending index of the eigenvalue
     // NP points per thread, NP m per eigenvalue: each pass shrinks the
     // interval NP m + 1 times.  Two points keep the reciprocal (a
-    // quarter-rate instruction) chains busy without adding passes' work.  The shifts only need absolute accuracy
-    // against |T| (they seed inverse iteration), so the stop is absolute.
+    // quarter-rate instruction) chains busy without adding passes' work.
+    // A shift seeds inverse iteration, whose vector for lam_c picks up
+    // lam_{c+1}'s in the ratio (shift error) / (lam_c - lam_{c+1}) per
+    // solve.  The conversion's n = d_k spectrum is graded over many decades
+    // and its gap at the rank-R cut can be far below eps |T|, so there the
+    // stop is relative to the eigenvalue (floored at the noise level of
+    // |T|).  A compression's gaps at the cut sit well above eps |T|, and
+    // the absolute stop saves the passes a small eigenvalue would take.
     constexpr int NP = 2;
     const float frac = 1.f / (float)(NP * m + 1);
-    const float tol = 4.f * kEps * tnorm + pivmin;
+    const float tol_rel = CONV ? 2.f * kEps : 0.f;
+    const float tol_floor = (CONV ? kEigFloor * kEps : 4.f * kEps) * tnorm + pivmin;
     // up to 64 rows, T sits in registers (padded rows never count)
     constexpr bool TREG = NMAX <= 64;
     float dr[TREG ? NMAX : 4], er[TREG ? NMAX : 4];
@@ -733,7 +816,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     }
     float lo = lo0, hi = hi0;
     for (int it = 0; it < 48; ++it) {
-      const bool done = !live || (hi - lo) <= tol;
+      const bool done = !live || (hi - lo) <= tol_rel * (fabsf(lo) + fabsf(hi)) + tol_floor;
       if (block_all<NW>(done, RED, 4)) break;
       const float step = (hi - lo) * frac;
       float x[NP], qv[NP];
@@ -793,11 +876,16 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
 
   // @phase F: eigenvectors of T by inverse iteration
   if (t < 64) {
-    // separate equal shifts: lam'_c = min_{j <= c} (lam_j - (c - j) sep)
-    const float sep = 10.f * kEps * tnorm;
+    // separate equal shifts: lam'_c = min_{j <= c} (lam_j - (c - j) sep_j),
+    // sep_j = 10 eps |lam_j| (floored as the bisection's stop).  A
+    // separation scaled by |T| would move a small shift by more than the
+    // gap to its neighbour and mix their vectors.
     float lc = 3.0e38f;
     for (int j = 0; j < R; ++j)
-      if (j <= t) lc = fminf(lc, LAM[j] - (float)(t - j) * sep);
+      if (j <= t) {
+        const float sep = 10.f * kEps * fabsf(LAM[j]) + kEigFloor * kEps * tnorm;
+        lc = fminf(lc, LAM[j] - (float)(t - j) * sep);
+      }
     // runs of close eigenvalues: the vector of c is computed in round
     // c - (first index of its run)
     const float prev = __shfl_up(lc, 1);
@@ -863,16 +951,20 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           FB[(NMAX - 1) * RMAX + c] = 0.f;
           FC[(NMAX - 1) * RMAX + c] = 0.f;
           x[NMAX - 1] = rr;
+          // mx is the largest |x_i|; fmaxf drops NaN, so an overflow that
+          // turned into inf - inf or 0 inf is caught by fin
           float x1 = 0.f, x2 = 0.f, mx = 0.f;
+          bool fin = true;
 #pragma unroll
           for (int i = NMAX - 1; i >= 0; --i) {
             const float xi = (x[i] - FB[i * RMAX + c] * x1 - FC[i * RMAX + c] * x2) * FA[i * RMAX + c];
             x[i] = xi;
             mx = fmaxf(mx, fabsf(xi));
+            fin = fin && fabsf(xi) < 3.0e38f;
             x2 = x1;
             x1 = xi;
           }
-          if (!(mx > 0.f) || !(mx < 3.0e38f)) {
+          if (!fin || !(mx > 0.f)) {
 #pragma unroll
             for (int i = 0; i < NMAX; ++i) x[i] = (i < n) ? start_entry(i, c + 7 * it + 1) : 0.f;
             continue;
@@ -973,193 +1065,248 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
   __syncthreads();
 
-  // @phase H: P2 = D R~^T X_R (MFMA, into FA), then T' = D^-1 R~^-1 X_R
-  {
-    constexpr int NT = NMAX / 16;
-    const int l = t & 63, w = t >> 6;
-    const int ci = l & 15, kk = l >> 4;
-#pragma unroll
-    for (int J = 0; J < NT; ++J) {
-      if (J % NW != w) continue;
-#pragma unroll
-      for (int C = 0; C < RMAX / 16; ++C) {
-        f4v acc = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int K = 0; K < NMAX / 4; ++K) {
-          if (4 * K > 16 * J + 15) continue;                 // R~[i][j] = 0 for i > j
-          const float av = RB[(16 * J + ci) * LDN + 4 * K + kk];   // R~[i][j]
-          const float bv = XR[(4 * K + kk) * RMAX + 16 * C + ci];  // X_R[i][c]
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * J + 4 * kk + r;
-          FA[j * RMAX + 16 * C + ci] = DVs[j] * acc[r];
+  if constexpr (!CONV) {
+    // @phase H: P2 = D R~^T X_R (MFMA, into FA), then T' = D^-1 R~^-1 X_R
+    {
+      constexpr int NT = NMAX / 16;
+      const int l = t & 63, w = t >> 6;
+      const int ci = l & 15, kk = l >> 4;
+  #pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        if (J % NW != w) continue;
+  #pragma unroll
+        for (int C = 0; C < RMAX / 16; ++C) {
+          f4v acc = f4v{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int K = 0; K < NMAX / 4; ++K) {
+            if (4 * K > 16 * J + 15) continue;                 // R~[i][j] = 0 for i > j
+            const float av = RB[(16 * J + ci) * LDN + 4 * K + kk];   // R~[i][j]
+            const float bv = XR[(4 * K + kk) * RMAX + 16 * C + ci];  // X_R[i][c]
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+          }
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * J + 4 * kk + r;
+            FA[j * RMAX + 16 * C + ci] = DVs[j] * acc[r];
+          }
         }
       }
     }
+    __syncthreads();
+    if (w0) {
+      // R~ t = y from the last row up; the lane owning row i broadcasts t_i
+      // to its group and stores t_i / d_i as row i of T'.  The reciprocal
+      // pivots of the lane's own rows are read before the serial chain.
+      float ird[CH], idv[CH];
+  #pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        ird[s] = IRD[part * CH + s];
+        idv[s] = IDV[part * CH + s];
+      }
+      // column i of R~ (this lane's rows) is read one step ahead
+      float rc[CH], rn[CH];
+  #pragma unroll
+      for (int s = 0; s < CH; ++s) rc[s] = RB[(NMAX - 1) * LDN + part * CH + s];
+  #pragma unroll
+      for (int i = NMAX - 1; i >= 0; --i) {
+        if (i > 0) {
+  #pragma unroll
+          for (int s = 0; s < CH; ++s) rn[s] = RB[(i - 1) * LDN + part * CH + s];   // R~[m][i-1]
+        }
+        if (i < n) {
+          const int own = i / CH, si = i - (i / CH) * CH;
+          const float yi = y[si] * ird[si];
+          float ti = (part == own) ? yi : 0.f;
+          switch (own) {
+            case 0: ti = group_bcast<PARTS, 0>(ti); break;
+            case 1: ti = group_bcast<PARTS, 1>(ti); break;
+            case 2: if constexpr (PARTS > 2) ti = group_bcast<PARTS, 2>(ti); break;
+            default: if constexpr (PARTS > 3) ti = group_bcast<PARTS, 3>(ti); break;
+          }
+          if (part == own && c < R) XR[i * RMAX + c] = ti * idv[si];
+  #pragma unroll
+          for (int s = 0; s < CH; ++s) y[s] = fmaf(-rc[s], ti, y[s]);
+        }
+  #pragma unroll
+        for (int s = 0; s < CH; ++s) rc[s] = rn[s];
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (w0) {
-    // R~ t = y from the last row up; the lane owning row i broadcasts t_i
-    // to its group and stores t_i / d_i as row i of T'.  The reciprocal
-    // pivots of the lane's own rows are read before the serial chain.
-    float ird[CH], idv[CH];
-#pragma unroll
-    for (int s = 0; s < CH; ++s) {
-      ird[s] = IRD[part * CH + s];
-      idv[s] = IDV[part * CH + s];
-    }
-    // column i of R~ (this lane's rows) is read one step ahead
-    float rc[CH], rn[CH];
-#pragma unroll
-    for (int s = 0; s < CH; ++s) rc[s] = RB[(NMAX - 1) * LDN + part * CH + s];
-#pragma unroll
-    for (int i = NMAX - 1; i >= 0; --i) {
-      if (i > 0) {
-#pragma unroll
-        for (int s = 0; s < CH; ++s) rn[s] = RB[(i - 1) * LDN + part * CH + s];   // R~[m][i-1]
-      }
-      if (i < n) {
-        const int own = i / CH, si = i - (i / CH) * CH;
-        const float yi = y[si] * ird[si];
-        float ti = (part == own) ? yi : 0.f;
-        switch (own) {
-          case 0: ti = group_bcast<PARTS, 0>(ti); break;
-          case 1: ti = group_bcast<PARTS, 1>(ti); break;
-          case 2: if constexpr (PARTS > 2) ti = group_bcast<PARTS, 2>(ti); break;
-          default: if constexpr (PARTS > 3) ti = group_bcast<PARTS, 3>(ti); break;
-        }
-        if (part == own && c < R) XR[i * RMAX + c] = ti * idv[si];
-#pragma unroll
-        for (int s = 0; s < CH; ++s) y[s] = fmaf(-rc[s], ti, y[s]);
-      }
-#pragma unroll
-      for (int s = 0; s < CH; ++s) rc[s] = rn[s];
-    }
-  }
-  __syncthreads();
 
-  // @phase I: U' = U T' and V' = V P2, MFMA over 16-row tiles, written in
-  // place.  A tile reads and writes only its own rows; the next tile's rows
-  // are loaded before the current tile is computed.
-  {
-    constexpr int NK = NMAX / 4, NC = RMAX / 16;
-    constexpr int TU = DK / 16, TT = DK / 16 + DV_ / 16;
-    static_assert(TU % NW == 0 && TT % NW == 0, "row tiles per wave");
+  if constexpr (CONV) {
+    // @phase I (conversion): U' = X_R; V' = C^T X_R = S^T X_R - vbar beta^T
+    // with beta = X_R^T a, by MFMA over 16-row tiles of V'
+    const float* const Sh = args.S + ub * DK * DV_;
+    const float* const vbs = IDV;
+    const float* const asink = DVs;
+    float* const beta_s = LAM;       // the eigenvalues are not needed any more
+    for (int i = t; i < NMAX * RMAX; i += NTH) {
+      const int row = i / RMAX, c = i - (i / RMAX) * RMAX;
+      if (c < R) Uh[(size_t)c * DK + row] = XR[row * RMAX + c];
+    }
+    if (t < RMAX) {
+      float b = 0.f;
+      for (int j = 0; j < NMAX; ++j) b = fmaf(asink[j], XR[j * RMAX + t], b);
+      beta_s[t] = b;
+    }
+    __syncthreads();
+    constexpr int NK = NMAX / 4, NC = RMAX / 16, TV = DV_ / 16;
     const int l = t & 63, w = t >> 6;
     const int ci = l & 15, kk = l >> 4;
-    float bt[NC][NK], bp[NC][NK];
+    float bx[NC][NK];
 #pragma unroll
     for (int C = 0; C < NC; ++C)
 #pragma unroll
       for (int K = 0; K < NK; ++K) {
-        const int j = 4 * K + kk, cc = 16 * C + ci;
-        const bool ok = j < n && cc < R;
-        bt[C][K] = ok ? XR[j * RMAX + cc] : 0.f;
-        bp[C][K] = ok ? FA[j * RMAX + cc] : 0.f;
+        const int cc = 16 * C + ci;
+        bx[C][K] = cc < R ? XR[(4 * K + kk) * RMAX + cc] : 0.f;
       }
-    float av[NK], an[NK];
-    // in the lazy form, row 16 E + ci of U carries its decay factor: one
-    // scale per U tile of this wave, read before the tile pipeline
-    float rsc[TU / NW];
-#pragma unroll
-    for (int q = 0; q < TU / NW; ++q) rsc[q] = 1.f;
-    if (gamh != nullptr) {
-#pragma unroll
-      for (int q = 0; q < TU / NW; ++q) rsc[q] = *gs_at(16 * (q * NW + w) + ci);
-    }
-    // wave w takes tiles E = q NW + w; the U tiles come first and TU is a
-    // multiple of NW, so whether tile q is a U tile does not depend on w
-    auto load_tile = [&](int q, float (&dst)[NK]) {
-      const bool isu = q < TU / NW;
-      const int E = q * NW + w;
-      const int ld = isu ? DK : DV_;
-      const int row = isu ? 16 * E : 16 * (E - TU);
-      if constexpr (!H16) {
-#pragma unroll
-        for (int K = 0; K < NK; ++K) {
-          const int j = 4 * K + kk;
-          dst[K] = (j < n) ? (isu ? ucol(j) : vcol(j))[row + ci] : 0.f;
-        }
-      } else {
-        const float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
-        const uint16_t* basek = isu ? Ukh + 16 * E : Vkh + 16 * (E - TU);
-#pragma unroll
-        for (int K = 0; K < NK; ++K) {
-          const int j = 4 * K + kk;
-          float x = 0.f;
-          if (j < KR) x = widen16<FMT>(basek[(size_t)j * ld + ci]);
-          else if (j < n) x = base[(size_t)(j - KR) * ld + ci];
-          dst[K] = x;
-        }
-      }
-      if (isu) {
-#pragma unroll
-        for (int K = 0; K < NK; ++K) dst[K] *= rsc[q < TU / NW ? q : 0];
-      }
-    };
-    load_tile(0, av);
-#pragma unroll
-    for (int q = 0; q < TT / NW; ++q) {
-      if (q + 1 < TT / NW) load_tile(q + 1, an);
-      const bool isu = q < TU / NW;
-      const int E = q * NW + w;
+    for (int E = w; E < TV; E += NW) {
       f4v acc[NC];
 #pragma unroll
       for (int C = 0; C < NC; ++C) acc[C] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int K = 0; K < NK; ++K)
+      for (int K = 0; K < NK; ++K) {
+        const float av = Sh[(size_t)(4 * K + kk) * DV_ + 16 * E + ci];     // S[j][e]
 #pragma unroll
         for (int C = 0; C < NC; ++C)
-          acc[C] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[K], isu ? bt[C][K] : bp[C][K], acc[C],
-                                                        0, 0, 0);
-      const int ld = isu ? DK : DV_;
-      if constexpr (RING) {
-        // U~' = Diag(1 / gam) U' (the decay product at the snapshot keeps
-        // running), into the other kept buffer
-        float* base = isu ? args.KU + knew * DK + 16 * E : args.KV + knew * DV_ + 16 * (E - TU);
-        float sc[4] = {1.f, 1.f, 1.f, 1.f};
-        if (isu) {
+          acc[C] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bx[C][K], acc[C], 0, 0, 0);
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[i] = 1.f / *gs_at(16 * E + 4 * kk + i);
-        }
+      for (int C = 0; C < NC; ++C) {
+        const int cc = 16 * C + ci;
+        if (cc < R) {
 #pragma unroll
-        for (int C = 0; C < NC; ++C) {
-          const int cc = 16 * C + ci;
-          if (cc < R)
-            *reinterpret_cast<float4*>(base + (size_t)cc * ld + 4 * kk) =
-                make_float4(acc[C][0] * sc[0], acc[C][1] * sc[1], acc[C][2] * sc[2],
-                            acc[C][3] * sc[3]);
-        }
-      } else if constexpr (FMT == kStoreF32) {
-        float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
-#pragma unroll
-        for (int C = 0; C < NC; ++C) {
-          const int cc = 16 * C + ci;
-          if (cc < R)
-            *reinterpret_cast<float4*>(base + (size_t)cc * ld + 4 * kk) =
-                make_float4(acc[C][0], acc[C][1], acc[C][2], acc[C][3]);
-        }
-      } else {
-        // rows 16 E' + 4 kk .. + 3 of column cc: one group of four elements
-        // of the unit's factor block (U column cc at f = cc d_k + row, V
-        // column cc at f = R d_k + cc d_v + row)
-        uint16_t* basek = isu ? Ukh + 16 * E : Vkh + 16 * (E - TU);
-        const uint32_t fb = isu ? 16u * E + 4u * kk : (uint32_t)R * DK + 16u * (E - TU) + 4u * kk;
-#pragma unroll
-        for (int C = 0; C < NC; ++C) {
-          const int cc = 16 * C + ci;
-          if (cc < R) {
-            const float xv[4] = {acc[C][0], acc[C][1], acc[C][2], acc[C][3]};
-            *reinterpret_cast<uint2*>(basek + (size_t)cc * ld + 4 * kk) =
-                round_pack4<FMT>(xv, args.stochastic != 0, fb + (uint32_t)(cc * ld),
-                                 (uint32_t)ub, args.epoch, args.key_lo, args.key_hi);
+          for (int r = 0; r < 4; ++r) {
+            const int e = 16 * E + 4 * kk + r;
+            Vh[(size_t)cc * DV_ + e] = fmaf(-vbs[e], beta_s[cc], acc[C][r]);
           }
         }
       }
-#pragma unroll
-      for (int K = 0; K < NK; ++K) av[K] = an[K];
+    }
+  } else {
+    // @phase I: U' = U T' and V' = V P2, MFMA over 16-row tiles, written in
+    // place.  A tile reads and writes only its own rows; the next tile's rows
+    // are loaded before the current tile is computed.
+    {
+      constexpr int NK = NMAX / 4, NC = RMAX / 16;
+      constexpr int TU = DK / 16, TT = DK / 16 + DV_ / 16;
+      static_assert(TU % NW == 0 && TT % NW == 0, "row tiles per wave");
+      const int l = t & 63, w = t >> 6;
+      const int ci = l & 15, kk = l >> 4;
+      float bt[NC][NK], bp[NC][NK];
+  #pragma unroll
+      for (int C = 0; C < NC; ++C)
+  #pragma unroll
+        for (int K = 0; K < NK; ++K) {
+          const int j = 4 * K + kk, cc = 16 * C + ci;
+          const bool ok = j < n && cc < R;
+          bt[C][K] = ok ? XR[j * RMAX + cc] : 0.f;
+          bp[C][K] = ok ? FA[j * RMAX + cc] : 0.f;
+        }
+      float av[NK], an[NK];
+      // in the lazy form, row 16 E + ci of U carries its decay factor: one
+      // scale per U tile of this wave, read before the tile pipeline
+      float rsc[TU / NW];
+  #pragma unroll
+      for (int q = 0; q < TU / NW; ++q) rsc[q] = 1.f;
+      if (gamh != nullptr) {
+  #pragma unroll
+        for (int q = 0; q < TU / NW; ++q) rsc[q] = *gs_at(16 * (q * NW + w) + ci);
+      }
+      // wave w takes tiles E = q NW + w; the U tiles come first and TU is a
+      // multiple of NW, so whether tile q is a U tile does not depend on w
+      auto load_tile = [&](int q, float (&dst)[NK]) {
+        const bool isu = q < TU / NW;
+        const int E = q * NW + w;
+        const int ld = isu ? DK : DV_;
+        const int row = isu ? 16 * E : 16 * (E - TU);
+        if constexpr (!H16) {
+  #pragma unroll
+          for (int K = 0; K < NK; ++K) {
+            const int j = 4 * K + kk;
+            dst[K] = (j < n) ? (isu ? ucol(j) : vcol(j))[row + ci] : 0.f;
+          }
+        } else {
+          const float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
+          const uint16_t* basek = isu ? Ukh + 16 * E : Vkh + 16 * (E - TU);
+  #pragma unroll
+          for (int K = 0; K < NK; ++K) {
+            const int j = 4 * K + kk;
+            float x = 0.f;
+            if (j < KR) x = widen16<FMT>(basek[(size_t)j * ld + ci]);
+            else if (j < n) x = base[(size_t)(j - KR) * ld + ci];
+            dst[K] = x;
+          }
+        }
+        if (isu) {
+  #pragma unroll
+          for (int K = 0; K < NK; ++K) dst[K] *= rsc[q < TU / NW ? q : 0];
+        }
+      };
+      load_tile(0, av);
+  #pragma unroll
+      for (int q = 0; q < TT / NW; ++q) {
+        if (q + 1 < TT / NW) load_tile(q + 1, an);
+        const bool isu = q < TU / NW;
+        const int E = q * NW + w;
+        f4v acc[NC];
+  #pragma unroll
+        for (int C = 0; C < NC; ++C) acc[C] = f4v{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int K = 0; K < NK; ++K)
+  #pragma unroll
+          for (int C = 0; C < NC; ++C)
+            acc[C] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[K], isu ? bt[C][K] : bp[C][K], acc[C],
+                                                          0, 0, 0);
+        const int ld = isu ? DK : DV_;
+        if constexpr (RING) {
+          // U~' = Diag(1 / gam) U' (the decay product at the snapshot keeps
+          // running), into the other kept buffer
+          float* base = isu ? args.KU + knew * DK + 16 * E : args.KV + knew * DV_ + 16 * (E - TU);
+          float sc[4] = {1.f, 1.f, 1.f, 1.f};
+          if (isu) {
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = 1.f / *gs_at(16 * E + 4 * kk + i);
+          }
+  #pragma unroll
+          for (int C = 0; C < NC; ++C) {
+            const int cc = 16 * C + ci;
+            if (cc < R)
+              *reinterpret_cast<float4*>(base + (size_t)cc * ld + 4 * kk) =
+                  make_float4(acc[C][0] * sc[0], acc[C][1] * sc[1], acc[C][2] * sc[2],
+                              acc[C][3] * sc[3]);
+          }
+        } else if constexpr (FMT == kStoreF32) {
+          float* base = isu ? Uh + 16 * E : Vh + 16 * (E - TU);
+  #pragma unroll
+          for (int C = 0; C < NC; ++C) {
+            const int cc = 16 * C + ci;
+            if (cc < R)
+              *reinterpret_cast<float4*>(base + (size_t)cc * ld + 4 * kk) =
+                  make_float4(acc[C][0], acc[C][1], acc[C][2], acc[C][3]);
+          }
+        } else {
+          // rows 16 E' + 4 kk .. + 3 of column cc: one group of four elements
+          // of the unit's factor block (U column cc at f = cc d_k + row, V
+          // column cc at f = R d_k + cc d_v + row)
+          uint16_t* basek = isu ? Ukh + 16 * E : Vkh + 16 * (E - TU);
+          const uint32_t fb = isu ? 16u * E + 4u * kk : (uint32_t)R * DK + 16u * (E - TU) + 4u * kk;
+  #pragma unroll
+          for (int C = 0; C < NC; ++C) {
+            const int cc = 16 * C + ci;
+            if (cc < R) {
+              const float xv[4] = {acc[C][0], acc[C][1], acc[C][2], acc[C][3]};
+              *reinterpret_cast<uint2*>(basek + (size_t)cc * ld + 4 * kk) =
+                  round_pack4<FMT>(xv, args.stochastic != 0, fb + (uint32_t)(cc * ld),
+                                   (uint32_t)ub, args.epoch, args.key_lo, args.key_hi);
+            }
+          }
+        }
+  #pragma unroll
+        for (int K = 0; K < NK; ++K) av[K] = an[K];
+      }
     }
   }
   if (gamh != nullptr && !RING) {
@@ -1173,14 +1320,14 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
 }
 
-template <int NMAX, int RMAX>
+template <int NMAX, int RMAX, bool NO_RB = false>
 constexpr size_t wave_lds_bytes() {
-  return 4 * (size_t)Lay<NMAX, RMAX>::TOTAL;
+  return 4 * (size_t)Lay<NMAX, RMAX, NO_RB>::TOTAL;
 }
 
 template <int NMAX, int RMAX, int DK, int DV_, int FMT>
 hipError_t wave_go(const CompressArgs& args, hipStream_t s) {
-  constexpr size_t bytes = wave_lds_bytes<NMAX, RMAX>();
+  constexpr size_t bytes = wave_lds_bytes<NMAX, RMAX, FMT == kConvert>();
   // the LDS limit is raised once per device, so that later calls (also
   // under stream capture) only enqueue the kernel
   static std::atomic<unsigned long long> lds_set{0};
@@ -1196,7 +1343,7 @@ hipError_t wave_go(const CompressArgs& args, hipStream_t s) {
     lds_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   hipLaunchKernelGGL((compress_wave_kernel<NMAX, RMAX, DK, DV_, FMT>), dim3(args.units),
-                     dim3(Lay<NMAX, RMAX>::NTH), bytes, s, args);
+                     dim3(Lay<NMAX, RMAX, FMT == kConvert>::NTH), bytes, s, args);
   return hipGetLastError();
 }
 
@@ -1240,6 +1387,21 @@ hipError_t wave_dispatch(const CompressArgs& a, hipStream_t s) {
     case 96: return wave_go<96, 32, DK, DV_, FMT>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The conversion: n = d_k columns (NMAX = d_k), RMAX from R.
+template <int DK, int DV_>
+hipError_t convert_dispatch(const CompressArgs& a, hipStream_t s) {
+  if (a.n != DK) return hipErrorInvalidValue;
+  if (a.R <= 16) return wave_go<DK, 16, DK, DV_, kConvert>(a, s);
+  if (a.R <= 32) return wave_go<DK, 32, DK, DV_, kConvert>(a, s);
+  return hipErrorInvalidValue;
+}
+
+inline size_t convert_lds_bytes_for(int d_k, int R) {
+  const bool r16 = R <= 16;
+  if (d_k == 128) return r16 ? wave_lds_bytes<128, 16, true>() : wave_lds_bytes<128, 32, true>();
+  return r16 ? wave_lds_bytes<64, 16, true>() : wave_lds_bytes<64, 32, true>();
 }
 
 }  // namespace wave

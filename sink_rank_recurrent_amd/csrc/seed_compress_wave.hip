@@ -25,4 +25,13 @@ hipError_t launch_compress(int d_k, int d_v, int store_fmt, const CompressArgs& 
   return hipErrorInvalidValue;
 }
 
+size_t convert_lds_bytes(int d_k, int R) { return wave::convert_lds_bytes_for(d_k, R); }
+
+hipError_t launch_convert(int d_k, int d_v, const CompressArgs& args, hipStream_t stream) {
+  if (d_k == 128 && d_v == 128) return convert_wave_128x128(args, stream);
+  if (d_k == 128 && d_v == 64) return convert_wave_128x64(args, stream);
+  if (d_k == 64 && d_v == 64) return convert_wave_64x64(args, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace seed

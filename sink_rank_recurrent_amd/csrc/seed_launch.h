@@ -12,7 +12,9 @@ namespace seed {
 // compression wrote as 16-bit patterns (bf16 or fp16) and the rest fp32.
 // kStoreRing: per-request schedules -- R kept fp32 columns in one of two
 // buffers, the window in a ring of W + D columns (seed_sched.hip's layout).
-enum StoreFmt { kStoreF32 = 0, kStoreBF16 = 1, kStoreF16 = 2, kStoreRing = 3 };
+// kConvert is not a storage format but the compression kernel's other use:
+// the end-of-prefill conversion of dense states (launch_convert).
+enum StoreFmt { kStoreF32 = 0, kStoreBF16 = 1, kStoreF16 = 2, kStoreRing = 3, kConvert = 4 };
 
 // Per-request schedule of the ring layout.  A request b has taken
 // A = t - t_start[b] steps (it is idle while A < 0).  With
@@ -62,8 +64,8 @@ constexpr int kWaveMaxN = 96;
 // Dynamic LDS bytes the compression of n columns to rank R needs.
 size_t compress_lds_bytes(int n, int R);
 size_t compress_wave_lds_bytes(int n, int R);
-// Dynamic LDS bytes the dense-to-shallow kernel needs.
-size_t from_dense_lds_bytes(int d_k, int R);
+// Dynamic LDS bytes the statistics kernel needs.
+size_t stats_lds_bytes(int d_k, int R);
 
 // Arguments of the compression of n <= kWaveMaxN columns to rank R
 // (seed_compress_wave.h).  fp32 layout (Uk == NULL): columns 0..n-1 in U, V
@@ -94,7 +96,24 @@ struct CompressArgs {
   int heads, t_snap, W, D, units_total;
   float* KU;
   float* KV;
+  // conversion (kConvert): dense states S [units][d_k][d_v], vbar [heads][d_v];
+  // writes a [units][d_k] and columns 0..R-1 of U, V (capacity cap)
+  const float* S;
+  const float* vbar;
+  float* a;
 };
+
+// End-of-prefill conversion by the compression kernel's eigensolver:
+// H = C C^T = S S^T - |vbar|^2 a a^T (n = d_k columns), U' = its top-R
+// eigenvectors, V' = C^T U' = S^T U' - vbar (a^T U').
+hipError_t launch_convert(int d_k, int d_v, const CompressArgs& args, hipStream_t stream);
+size_t convert_lds_bytes(int d_k, int R);
+#define SEED_DECLARE_CONVERT_SHAPE(DK, DV) \
+  hipError_t convert_wave_##DK##x##DV(const CompressArgs& args, hipStream_t stream);
+SEED_DECLARE_CONVERT_SHAPE(128, 128)
+SEED_DECLARE_CONVERT_SHAPE(128, 64)
+SEED_DECLARE_CONVERT_SHAPE(64, 64)
+#undef SEED_DECLARE_CONVERT_SHAPE
 
 hipError_t launch_compress(int d_k, int d_v, int store_fmt, const CompressArgs& args,
                            hipStream_t stream);
@@ -130,9 +149,5 @@ int stat_fields();
 hipError_t launch_state_stats(int batch, int heads, int d_k, int d_v, int R, const float* S,
                               const float* vbar, float* rec, float* specS, float* specC,
                               hipStream_t stream);
-
-hipError_t launch_from_dense(int batch, int heads, int d_k, int d_v, int cap, int R,
-                             const float* S, const float* vbar, float* a, float* U, float* V,
-                             hipStream_t stream);
 
 }  // namespace seed

@@ -32,7 +32,7 @@ GROUPS = {
     "compress_wave_kernel (per-request schedule)": r"compress_wave_kernel<.*, 3>",
     "handoff_kernel": r"handoff_kernel<",
     "stats_kernel": r"stats_kernel<",
-    "from_dense_kernel": r"from_dense_kernel<",
+    "compress_wave_kernel (end-of-prefill conversion)": r"compress_wave_kernel<.*, 4>",
     "dense_step_kernel": r"dense_step_kernel<",
 }
 

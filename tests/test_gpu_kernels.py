@@ -316,3 +316,57 @@ def test_from_dense_of_pure_sink():
     np.testing.assert_allclose(a, f64(a_true)[..., 0].reshape(-1, 128), rtol=1e-5, atol=1e-6)
     prod = U @ np.swapaxes(V, -1, -2)
     assert np.abs(prod).max() < 1e-5 * np.abs(f64(S)).max()
+
+
+@pytest.mark.parametrize("e", [-40, 40])
+def test_far_from_unit_scale(e):
+    """States scaled by 2^-40 or 2^40: the eigensolver works on H brought to
+    unit range by a power of two, so neither squares below the normal range
+    (read as zero by sqrt and rcp) nor squares above fp32's range break the
+    conversion or the compression; both stay within the usual bar of the
+    oracle on the same scaled inputs."""
+    s = 2.0 ** e
+    # conversion of a graded dense state
+    d_k = d_v = 128
+    R = 16
+    gen = torch.Generator(device="cuda").manual_seed(81)
+    vbar = _vbar(d_v, 82)
+    a_true = torch.randn(B, H, d_k, 1, generator=gen, device="cuda")
+    L = torch.randn(B, H, d_k, 40, generator=gen, device="cuda")
+    Rm = torch.randn(B, H, 40, d_v, generator=gen, device="cuda") * torch.logspace(
+        0, -3, 40, device="cuda")[:, None]
+    S = ((a_true * vbar[None, :, None, :] + L @ Rm * 0.3) * s).contiguous()
+    st = make_state("gdn", B, H, d_k, d_v, R, 16, vbar)
+    st.from_dense(S)
+    torch.cuda.synchronize()
+    vb = np.broadcast_to(f64(vbar)[None], (B, H, d_v)).reshape(-1, d_v)
+    a_r, U_r, V_r = oracle.state_from_dense(f64(units_of(S)), vb, R)
+    a_g, U_g, V_g, _ = state_np(st)
+    assert np.isfinite(U_g).all() and np.isfinite(V_g).all()
+    C = f64(units_of(S)) - a_r[..., :, None] * vb[..., None, :]
+    ok = content_gap(C, np.broadcast_to(np.eye(d_v), C.shape[:-2] + (d_v, d_v)), R) >= TIE_GAP
+    assert ok.sum() >= B * H - 1
+    err = state_rel_err(a_g, U_g, V_g, a_r, U_r, V_r, vb)
+    assert err[ok].max() < TOL_STATE_COMPRESS, err
+
+    # compression of factors whose content is scaled by s
+    n, W = 48, 32
+    a, U, V, vbar_np = _oracle_precompress_states("gdn", d_k, d_v, R, n, 83, B * H)
+    U32 = (U * 2.0 ** (e // 2)).astype(np.float32)
+    V32 = (V * 2.0 ** (e - e // 2)).astype(np.float32)
+    st = make_state("gdn", B, H, d_k, d_v, R, W,
+                    torch.tensor(np.broadcast_to(vbar_np, (H, d_v)).copy(), dtype=torch.float32))
+    st.a.copy_(torch.tensor(a.reshape(B, H, d_k), dtype=torch.float32))
+    st.U[:, :, :n] = torch.tensor(U32.transpose(0, 2, 1).reshape(B, H, n, d_k), device="cuda")
+    st.V[:, :, :n] = torch.tensor(V32.transpose(0, 2, 1).reshape(B, H, n, d_v), device="cuda")
+    st.r = n
+    st.compress()
+    torch.cuda.synchronize()
+    Ug, Vg = state_np(st)[1:3]
+    assert np.isfinite(Ug).all() and np.isfinite(Vg).all()
+    U64, V64 = U32.astype(np.float64), V32.astype(np.float64)
+    Uc, Vc = oracle.compress(U64, V64, R)
+    ok = content_gap(U64, V64, R) >= TIE_GAP
+    assert ok.sum() >= B * H - 1
+    err = rel_err(Ug @ np.swapaxes(Vg, -1, -2), Uc @ np.swapaxes(Vc, -1, -2), (-2, -1))
+    assert err[ok].max() < 1e-3, err
