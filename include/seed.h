@@ -355,6 +355,16 @@ seed_status dense_decode_step(int rule, int batch, int heads, int d_k, int d_v, 
                               const void *q, const void *k, const void *v, int in_dtype,
                               const float *g, const float *beta, float *o, void *stream);
 
+/*
+ * seed_stream_copy -- a measurement helper, not a step of the method: copies
+ * `bytes` from src to dst with a plain streaming kernel (one 16-byte load
+ * and store per thread, a full grid), so that the bandwidth the
+ * state kernels reach can be set beside what a read-once, write-once
+ * kernel gets from this device's memory.  src and dst are device buffers,
+ * 16-byte aligned, not overlapping; bytes must be a multiple of 16.
+ */
+seed_status seed_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
 /* Static text for a status code. */
 const char *seed_status_string(int status);
 

@@ -71,11 +71,12 @@ def lib() -> ctypes.CDLL:
     L.seed_stat_fields.argtypes = []
     L.seed_handoff_head_bytes.argtypes = [i, i, i, i]
     L.seed_handoff_head_bytes.restype = ctypes.c_size_t
+    L.seed_stream_copy.argtypes = [p, p, ctypes.c_size_t, p]
     for fn in ("seed_decode_step", "seed_decode_step_lazy", "seed_compress", "seed_compress_lazy",
                "seed_state_from_dense", "dense_decode_step", "seed_decode_step_h16",
                "seed_compress_h16", "seed_round_factors", "seed_pack_states",
                "seed_unpack_states", "seed_state_stats", "seed_stat_fields",
-               "seed_decode_step_sched", "seed_compress_sched",
+               "seed_decode_step_sched", "seed_compress_sched", "seed_stream_copy",
                "seed_abi_version"):
         getattr(L, fn).restype = ctypes.c_int
     L.seed_status_string.argtypes = [i]
@@ -234,6 +235,20 @@ def dense_decode_step(rule: str, S, q, k, v, g, beta, o, stream=None) -> None:
                                  _in_dtype(q, k, v), _ptr(g), _ptr(beta), _ptr(o),
                                  _stream(stream, S.device.index))
     _check("dense_decode_step", st)
+
+
+def stream_copy(src, dst, stream=None) -> None:
+    """Bandwidth probe (see include/seed.h): copy src into dst, two
+    contiguous device tensors of the same byte size."""
+    if not (src.is_cuda and dst.is_cuda):
+        raise ValueError("stream_copy: tensors must be in device memory")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("stream_copy: tensors must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("stream_copy: src and dst differ in size")
+    st = lib().seed_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream, src.device.index))
+    _check("seed_stream_copy", st)
 
 
 # 16-bit kept factors: the tensor dtype names the pattern format

@@ -486,6 +486,19 @@ seed_status dense_decode_step(int rule, int batch, int heads, int d_k, int d_v, 
                                               static_cast<hipStream_t>(stream)));
 }
 
+seed_status seed_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  const char* fn = "seed_stream_copy";
+  SEED_PTR(src);
+  SEED_PTR(dst);
+  if (bytes % 16 != 0) return fail(SEED_E_ARG, "%s: bytes (%zu) must be a multiple of 16", fn, bytes);
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes)
+    return fail(SEED_E_ARG, "%s: src and dst overlap", fn);
+  return device_status(fn, seed::launch_stream_copy(src, dst, bytes,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 const char* seed_status_string(int status) {
   switch (status) {
     case SEED_OK: return "ok";
@@ -500,6 +513,6 @@ const char* seed_status_string(int status) {
 
 const char* seed_last_error(void) { return g_err; }
 
-int seed_abi_version(void) { return 105; }
+int seed_abi_version(void) { return 106; }
 
 }  // extern "C"

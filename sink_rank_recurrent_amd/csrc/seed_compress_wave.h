@@ -209,7 +209,10 @@ __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
   constexpr int NT = NMAX / 16;
   constexpr int NP = NT * (NT + 1) / 2;
   constexpr int KPL = D / (4 * NW);
-  constexpr int KC = ((NT > 4) ? 8 : 16) < KPL ? ((NT > 4) ? 8 : 16) : KPL;
+  // k-slots per load round: all of a lane's slots at once when they fit in
+  // 96 registers (one HBM round trip instead of two), else chunks
+  constexpr int KC0 = ((NT > 4) ? 8 : 16) < KPL ? ((NT > 4) ? 8 : 16) : KPL;
+  constexpr int KC = (NT * KPL <= 96) ? KPL : KC0;
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ci = l & 15, kk = l >> 4;
   f4v acc[NP];

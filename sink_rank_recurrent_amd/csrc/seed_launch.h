@@ -150,4 +150,8 @@ hipError_t launch_state_stats(int batch, int heads, int d_k, int d_v, int R, con
                               const float* vbar, float* rec, float* specS, float* specC,
                               hipStream_t stream);
 
+// Streaming copy of `bytes` (a multiple of 16, 16-byte aligned buffers that
+// do not overlap), the bandwidth probe of seed_probe.hip.
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
 }  // namespace seed

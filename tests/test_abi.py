@@ -19,11 +19,11 @@ def test_exports_every_declared_function():
                           "seed_decode_step_h16", "seed_compress_h16", "seed_round_factors",
                           "seed_handoff_head_bytes", "seed_pack_states", "seed_unpack_states",
                           "seed_state_stats", "seed_stat_fields",
-                          "seed_decode_step_sched", "seed_compress_sched",
+                          "seed_decode_step_sched", "seed_compress_sched", "seed_stream_copy",
                           "seed_status_string", "seed_last_error", "seed_abi_version"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.seed_abi_version() == 105
+    assert L.seed_abi_version() == 106
 
 
 def test_status_strings():
@@ -187,6 +187,15 @@ def test_dense_step_validation():
     assert L.dense_decode_step(0, 1, 1, 128, 96, p, p, p, p, 0, p, p, p, None) == 3
     assert L.dense_decode_step(2, 1, 1, 128, 64, p, p, p, p, 0, p, p, p, None) == 1  # beta non-NULL
     assert L.dense_decode_step(1, 1, 1, 128, 128, None, p, p, p, 0, p, p, p, None) == 1
+
+
+def test_stream_copy_validation():
+    a, b = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+    assert L.seed_stream_copy(a, b, 17, None) == 1                       # not whole vectors
+    assert L.seed_stream_copy(a, ctypes.c_void_p(0x10010), 64, None) == 1  # overlapping
+    assert b"overlap" in L.seed_last_error()
+    assert L.seed_stream_copy(None, b, 64, None) == 1
+    assert L.seed_stream_copy(MISALIGNED, b, 64, None) == 1
 
 
 def test_binding_refuses_host_tensors():

@@ -370,3 +370,15 @@ def test_far_from_unit_scale(e):
     assert ok.sum() >= B * H - 1
     err = rel_err(Ug @ np.swapaxes(Vg, -1, -2), Uc @ np.swapaxes(Vc, -1, -2), (-2, -1))
     assert err[ok].max() < 1e-3, err
+
+
+def test_stream_copy_is_exact():
+    """The bandwidth probe copies every byte, also a ragged size (not a whole
+    number of passes of its grid), and touches nothing beyond."""
+    n = (1 << 22) + 4 * 37                      # floats: 16 MiB plus 37 vectors
+    src = torch.randn(n, device="cuda")
+    dst = torch.full((n + 64,), 7.0, device="cuda")
+    binding.stream_copy(src, dst[:n])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src)
+    assert torch.all(dst[n:] == 7.0)
