@@ -231,11 +231,10 @@ def sched_bytes_per_unit(w: wl.Workload, r: int, D: int) -> float:
 
 def run_scheduled(w, S, vbar, inputs, warmup: int, steps: int, D: int, dev):
     """Staggered starts (request b's phase b mod W) on the per-request
-    schedule with merge delay D.  Every request has passed its first merge
-    when timing starts.  The timed steps (and each cohort's compression on
-    the side stream) are captured once as one HIP graph and replayed, since
-    launching two kernels and two events per step from Python would bound
-    the run by the host."""
+    schedule with merge delay D, the snapshots of max(D, 1) consecutive
+    steps compressed by one launch on the steps' stream.  Every request has
+    passed its first merge when timing starts.  The timed steps and their
+    compressions are captured once as one HIP graph and replayed."""
     t_start = [-(b % w.W) - (w.W + D) for b in range(w.batch)]
     st = binding.ScheduledState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, D, vbar,
                                 t_start, device=dev)
@@ -269,8 +268,9 @@ def run_scheduled(w, S, vbar, inputs, warmup: int, steps: int, D: int, dev):
     return {"D": D, "value": units * steps / el, "unit": "head-steps/s",
             "ms_per_step": el * 1e3 / steps, "mean_columns": sum(cols) / len(cols),
             "step_bytes_per_head_step": mean_bytes,
-            "launch": "one hip graph of the timed steps; each cohort's compression on a side "
-                      "stream, joined by events"}
+            "batch_steps": st.batch_steps, "side_streams": len(st.sides),
+            "launch": "one hip graph of the timed steps; the snapshots of batch_steps "
+                      "consecutive steps compressed by one launch on the steps' stream"}
 
 
 def run_dense(w, S, inputs, o, warmup: int, steps: int, graphs: bool, chunk: int = 32):
@@ -501,7 +501,8 @@ def main() -> int:
     sched = None
     if not args.no_variant:
         sched = []
-        for D in sorted({0, min(w.W - 1, 96 - w.R - w.W, w.W // 2)}):
+        for D in sorted({0, min(w.W - 1, 96 - w.R - w.W, w.W // 2),
+                         min(w.W - 1, 96 - w.R - w.W)}):
             if w.R not in (16, 32):
                 break
             sched.append(run_scheduled(w, S_dense, vbar, inputs, warmup, steps, D, dev))

@@ -251,12 +251,17 @@ seed_status seed_round_factors(int batch, int heads, int d_k, int d_v, int R, co
  * gam in gam_snap.
  *
  * seed_compress_sched -- compress the units units[0 .. n_units) whose
- * request has A = t_snap - t_start[b] = k W, k >= 1 (other listed units are
- * left alone; entries outside the batch are skipped): the rank-R
- * truncation of the snapshot into kept buffer k & 1, scaled by 1 / gam_snap.
- * Call it with t_snap = t + 1 after step t, on any stream ordered after
- * that step; step t_snap + D must be ordered after it.  Reads Uw, Vw and
- * the old kept buffer; writes only the new kept buffer.
+ * request, at A = t_snap - t_start[b] steps, has taken its snapshot number
+ * k = A / W >= 1 and not yet reached its merge: A - k W < D (A = k W when
+ * D = 0).  Other listed units are left alone; entries outside the batch
+ * are skipped.  Each is the rank-R truncation of snapshot k into kept
+ * buffer k & 1, scaled by 1 / gam_snap.  Call it with t_snap = t + 1 after
+ * step t, on any stream ordered after that step; the merge step of every
+ * unit it compresses must be ordered after it.  So one call can serve the
+ * requests whose snapshots fell in the last few steps, which amortises the
+ * launch over more units.  Compressing a snapshot again before its merge
+ * writes the same result.  Reads Uw, Vw and the old kept buffer; writes
+ * only the new kept buffer.
  */
 seed_status seed_decode_step_sched(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
                                    int D, int t, const int *t_start, float *a, float *KU,

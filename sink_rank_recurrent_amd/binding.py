@@ -629,14 +629,21 @@ class ScheduledState:
     Device tensors: a, the kept buffers KU [2, B, H, R, d_k], KV, the window
     rings Uw [B, H, W + D, d_k], Vw, gam, gam_snap, t_start [B] (int32).
     `step` launches one decode step of every request on torch's current
-    stream and, for the requests whose window it fills, their compression on
-    a side stream (default priority); the step that merges a compression
-    first waits for it.  D = 0 makes every compression finish before the
-    next step.
+    stream.  The snapshots of `batch_steps` consecutive steps (the requests
+    whose windows those steps fill) are compressed by one launch, issued
+    after the last of them; a snapshot must be compressed before its merge
+    D steps later, so batch_steps <= max(D, 1), and the default, max(D, 1),
+    amortises one launch over as many snapshots as the delay allows.  With
+    side_streams = 0 (the default) the launches run in order on the steps'
+    stream; with side_streams > 0 they take that many side streams (default
+    priority) in turn and overlap the steps, and the step that merges a
+    compression first waits for it.  D = 0 makes every compression finish
+    before the next step.
     """
 
     def __init__(self, rule: str, batch: int, heads: int, d_k: int, d_v: int, R: int, W: int,
-                 D: int, vbar: torch.Tensor, t_start, device="cuda"):
+                 D: int, vbar: torch.Tensor, t_start, device="cuda", batch_steps=None,
+                 side_streams: int = 0):
         import numpy as np
 
         self.rule, self.R, self.W, self.D = rule, R, W, D
@@ -663,9 +670,20 @@ class ScheduledState:
             units = (reqs[:, None] * heads + np.arange(heads)[None, :]).reshape(-1)
             self.cohorts.append(torch.tensor(units, dtype=torch.int32, device=device)
                                 if units.size else None)
-        self.side = torch.cuda.Stream(device=device)
+        if batch_steps is None:
+            batch_steps = max(D, 1)
+        if not 1 <= batch_steps <= max(D, 1):
+            raise ValueError("batch_steps must lie in 1 .. max(D, 1)")
+        if side_streams < 0:
+            raise ValueError("side_streams must be at least 0")
+        self.batch_steps = int(batch_steps)
+        # no side stream: the compressions run in order on the steps' stream
+        self.sides = [torch.cuda.Stream(device=device) for _ in range(side_streams)]
         self.pending = {}
         self.t = 0
+        self._acc = []         # (snapshot step, phase) of the snapshots not yet launched
+        self._lists = {}       # the unit list of each tuple of phases, made once
+        self._launches = 0
 
     def from_dense(self, S: torch.Tensor, stream=None) -> None:
         """Every request's state from its dense state (kept buffer 0)."""
@@ -704,26 +722,51 @@ class ScheduledState:
             _ptr(self.gam), _ptr(self.gam_snap), _ptr(self.vbar), _ptr(q), _ptr(k), _ptr(v),
             _in_dtype(q, k, v), _ptr(g), _ptr(beta), _ptr(o), cur.cuda_stream)
         _check("seed_decode_step_sched", st)
-        lst = self.cohorts[(self.t + 1) % self.W]
-        if lst is not None:
+        self.t += 1
+        p = self.t % self.W
+        if self.cohorts[p] is not None:
+            self._acc.append((self.t, p))
+        if self._acc and self.t - self._acc[0][0] + 1 >= self.batch_steps:
+            self._launch(cur)
+
+    def _launch(self, cur) -> None:
+        """One compression launch for the accumulated snapshots, on the next
+        side stream, after everything enqueued on `cur` so far."""
+        key = tuple(p for _, p in self._acc)
+        lst = self._lists.get(key)
+        if lst is None:
+            lst = torch.cat([self.cohorts[p] for p in key])
+            self._lists[key] = lst
+        if self.sides:
+            side = self.sides[self._launches % len(self.sides)]
             snap = torch.cuda.Event()
             snap.record(cur)
-            self.side.wait_event(snap)
-            st = lib().seed_compress_sched(
-                RULES[self.rule], B, H, d_k, d_v, self.R, self.W, self.D, self.t + 1,
-                _ptr(self.t_start), lst.shape[0], _ptr(lst), _ptr(self.KU), _ptr(self.KV),
-                _ptr(self.Uw), _ptr(self.Vw), _ptr(self.gam_snap), self.side.cuda_stream)
-            _check("seed_compress_sched", st)
+            side.wait_event(snap)
+        else:
+            side = cur
+        self._launches += 1
+        B, H, d_k, d_v = self.batch, self.heads, self.d_k, self.d_v
+        st = lib().seed_compress_sched(
+            RULES[self.rule], B, H, d_k, d_v, self.R, self.W, self.D, self.t,
+            _ptr(self.t_start), lst.shape[0], _ptr(lst), _ptr(self.KU), _ptr(self.KV),
+            _ptr(self.Uw), _ptr(self.Vw), _ptr(self.gam_snap), side.cuda_stream)
+        _check("seed_compress_sched", st)
+        if self.sides:
             done = torch.cuda.Event()
-            done.record(self.side)
-            self.pending[self.t + 1 + self.D] = done
-        self.t += 1
+            done.record(side)
+            for ts, _ in self._acc:
+                self.pending[ts + self.D] = done
+        self._acc = []
 
     def join(self, stream=None) -> None:
-        """Order `stream` (default: the current one) after every compression
-        launched so far."""
+        """Launch the snapshots still waiting for their batch, then order
+        `stream` (default: the current one) after every compression launched
+        so far."""
         cur = torch.cuda.current_stream(self.a.device) if stream is None else stream
-        cur.wait_stream(self.side)
+        if self._acc:
+            self._launch(cur)
+        for side in self.sides:
+            cur.wait_stream(side)
 
     def true_factors(self, b: int, h: int):
         """(U at true scale [d_k, r], V [d_v, r]) of one unit before the next

@@ -524,8 +524,10 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   int kcyc = 0;
   if constexpr (RING) {
     if (ub >= (size_t)args.units_total) return;  // not a unit of this batch
+    // the request's latest snapshot, k = A / W, is due while its merge
+    // (A = k W + D) has not been reached; else the whole block leaves
     const int A = args.t_snap - args.t_start[ub / args.heads];
-    if (A < args.W || A % args.W != 0) return;   // not due: the whole block leaves
+    if (A < args.W || A % args.W >= (args.D > 0 ? args.D : 1)) return;
     kcyc = A / args.W;
   }
   float* const Uh = U + ub * cap * DK;

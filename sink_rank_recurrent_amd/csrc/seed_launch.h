@@ -77,10 +77,11 @@ size_t stats_lds_bytes(int d_k, int R);
 // it is reset to 1.
 // Ring layout (kStoreRing, per-request schedules): block i compresses unit
 // list[i]; a unit whose request has A = t_snap - t_start[b] steps with
-// A = k W, k >= 1, compresses its kept buffer (k - 1) & 1 and window column
-// numbers (k - 1) W .. k W - 1 (ring U, V with cap = W + D slots), with gam
-// the decay product at the snapshot, into kept buffer k & 1 scaled by
-// 1 / gam; gam is not reset.  Other units of the list are left alone.
+// k = A / W >= 1 and A - k W < max(D, 1) (its snapshot k taken, not yet
+// merged) compresses its kept buffer (k - 1) & 1 and window column numbers
+// (k - 1) W .. k W - 1 (ring U, V with cap = W + D slots), with gam the
+// decay product at the snapshot, into kept buffer k & 1 scaled by 1 / gam;
+// gam is not reset.  Other units of the list are left alone.
 struct CompressArgs {
   int units, cap, n, R;
   float* U;

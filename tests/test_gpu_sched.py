@@ -27,10 +27,14 @@ def _inputs_of(x, u, H):
     return {k: (None if v is None else f64(v[b, h])) for k, v in x.items()}
 
 
-@pytest.mark.parametrize("rule,dims,W,D", [
-    ("gdn", (128, 128), 16, 0), ("gdn", (128, 128), 16, 6), ("kda", (128, 128), 32, 12),
-    ("mamba2", (128, 64), 16, 5), ("gdn", (64, 64), 16, 15)])
-def test_scheduled_run_matches_oracle(rule, dims, W, D):
+@pytest.mark.parametrize("rule,dims,W,D,K,NS", [
+    ("gdn", (128, 128), 16, 0, 1, 0), ("gdn", (128, 128), 16, 6, None, 0),
+    ("kda", (128, 128), 32, 12, 5, 3), ("mamba2", (128, 64), 16, 5, 3, 1),
+    ("gdn", (64, 64), 16, 15, None, 2)])
+def test_scheduled_run_matches_oracle(rule, dims, W, D, K, NS):
+    """K: the snapshots of K consecutive steps share one compression launch
+    (None: the default, max(D, 1)); NS: side streams the launches alternate
+    over (0: in order on the steps' stream)."""
     d_k, d_v = dims
     B, H, R = 5, 3, 16
     t_start = [0, 1, 4, 9, 2 * W + 3]
@@ -49,7 +53,8 @@ def test_scheduled_run_matches_oracle(rule, dims, W, D):
     vbu = np.broadcast_to(vb[None], (B, H, d_v)).reshape(-1, d_v)
     a0, U0, V0 = so.state_from_dense(S, vbu, R)
     a0, U0, V0 = (x.astype(np.float32).astype(np.float64) for x in (a0, U0, V0))
-    st = binding.ScheduledState(rule, B, H, d_k, d_v, R, W, D, vbar.cuda(), t_start)
+    st = binding.ScheduledState(rule, B, H, d_k, d_v, R, W, D, vbar.cuda(), t_start,
+                                batch_steps=K, side_streams=NS)
     st.a.copy_(torch.tensor(a0.reshape(B, H, d_k), dtype=torch.float32))
     st.KU[0].copy_(torch.tensor(U0.transpose(0, 2, 1).reshape(B, H, R, d_k), dtype=torch.float32))
     st.KV[0].copy_(torch.tensor(V0.transpose(0, 2, 1).reshape(B, H, R, d_v), dtype=torch.float32))
