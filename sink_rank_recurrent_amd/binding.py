@@ -646,6 +646,14 @@ class ScheduledState:
                  side_streams: int = 0):
         import numpy as np
 
+        if not 0 <= D < W:
+            raise ValueError("need 0 <= D < W")
+        if batch_steps is None:
+            batch_steps = max(D, 1)
+        if not 1 <= batch_steps <= max(D, 1):
+            raise ValueError("batch_steps must lie in 1 .. max(D, 1)")
+        if side_streams < 0:
+            raise ValueError("side_streams must be at least 0")
         self.rule, self.R, self.W, self.D = rule, R, W, D
         self.batch, self.heads, self.d_k, self.d_v = batch, heads, d_k, d_v
         f32 = torch.float32
@@ -670,12 +678,6 @@ class ScheduledState:
             units = (reqs[:, None] * heads + np.arange(heads)[None, :]).reshape(-1)
             self.cohorts.append(torch.tensor(units, dtype=torch.int32, device=device)
                                 if units.size else None)
-        if batch_steps is None:
-            batch_steps = max(D, 1)
-        if not 1 <= batch_steps <= max(D, 1):
-            raise ValueError("batch_steps must lie in 1 .. max(D, 1)")
-        if side_streams < 0:
-            raise ValueError("side_streams must be at least 0")
         self.batch_steps = int(batch_steps)
         # no side stream: the compressions run in order on the steps' stream
         self.sides = [torch.cuda.Stream(device=device) for _ in range(side_streams)]

@@ -204,3 +204,15 @@ def test_binding_refuses_host_tensors():
     V = torch.zeros(1, 1, 48, 128)
     with pytest.raises(ValueError, match="device memory"):
         binding.seed_compress(U, V, 48, 16)
+
+
+def test_scheduled_state_rejects_bad_batching():
+    """A snapshot must be compressed before its merge D steps later, so the
+    snapshots of at most max(D, 1) steps share a launch; checked before any
+    device memory is touched."""
+    import torch
+    vbar = torch.zeros(2, 128)
+    for kw, D in (({"batch_steps": 5}, 4), ({"batch_steps": 2}, 0), ({"batch_steps": 0}, 4),
+                  ({"side_streams": -1}, 4), ({}, 16)):
+        with pytest.raises(ValueError):
+            binding.ScheduledState("gdn", 1, 2, 128, 128, 16, 16, D, vbar, [0], **kw)
