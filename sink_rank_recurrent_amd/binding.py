@@ -737,7 +737,9 @@ class ScheduledState:
         key = tuple(p for _, p in self._acc)
         lst = self._lists.get(key)
         if lst is None:
-            lst = torch.cat([self.cohorts[p] for p in key])
+            # made on `cur`, so that every stream ordered after `cur` sees it
+            with torch.cuda.stream(cur):
+                lst = torch.cat([self.cohorts[p] for p in key])
             self._lists[key] = lst
         if self.sides:
             side = self.sides[self._launches % len(self.sides)]
