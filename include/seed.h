@@ -341,8 +341,10 @@ seed_status seed_state_from_dense(int batch, int heads, int d_k, int d_v, int ca
  *   8 the share of |C|_F^2 beyond rank R
  *   9 .. zero
  * spec_S, spec_C (float [batch][heads][d_k], optional, NULL to skip): the
- * eigenvalues of S S^T and C C^T (sigma^2 of S and C), descending.  fp32,
- * by cyclic Jacobi run to convergence; S and vbar are only read.
+ * eigenvalues of S S^T and C C^T (sigma^2 of S and C), descending, within
+ * a few fp32 ulps of sigma_1^2 (Householder tridiagonalisation, bisection
+ * on Sturm counts; sigma_1(S)^2 in field 4 is the Rayleigh quotient of the
+ * top vector).  S and vbar are only read.
  */
 int seed_stat_fields(void);
 seed_status seed_state_stats(int batch, int heads, int d_k, int d_v, int R, const float *S,

@@ -8,6 +8,8 @@ namespace seed {
 
 size_t compress_wave_lds_bytes(int n, int R) { return wave::wave_lds_bytes_for(n, R); }
 
+size_t compress_lds_bytes(int n, int R) { return compress_wave_lds_bytes(n, R); }
+
 hipError_t launch_compress(int d_k, int d_v, int store_fmt, const CompressArgs& args,
                            hipStream_t stream) {
 #define SEED_COMPRESS_SHAPE(DK, DV)                                              \

@@ -143,7 +143,7 @@ hipError_t launch_handoff(bool pack, int batch, int heads, int d_k, int d_v, int
                           int factor_bytes, int n_sel, const int* idx, float* a, void* U, void* V,
                           void* buf, hipStream_t stream);
 
-// Statistics of dense states (seed_compress.hip): stat_fields() floats per
+// Statistics of dense states (seed_stats.hip): stat_fields() floats per
 // unit in rec; the sorted eigenvalues of S S^T and C C^T in specS, specC
 // ([unit][d_k], either may be NULL).
 int stat_fields();

@@ -31,7 +31,7 @@ GROUPS = {
     "seed_step_kernel (per-request schedule)": r"seed_step_kernel<.*true, 3>",
     "compress_wave_kernel (per-request schedule)": r"compress_wave_kernel<.*, 3>",
     "handoff_kernel": r"handoff_kernel<",
-    "stats_kernel": r"stats_kernel<",
+    "stats_wave_kernel": r"stats_wave_kernel<",
     "compress_wave_kernel (end-of-prefill conversion)": r"compress_wave_kernel<.*, 4>",
     "dense_step_kernel": r"dense_step_kernel<",
 }
