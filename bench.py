@@ -501,8 +501,12 @@ def main() -> int:
     sched = None
     if not args.no_variant:
         sched = []
-        for D in sorted({0, min(w.W - 1, 96 - w.R - w.W, w.W // 2),
-                         min(w.W - 1, 96 - w.R - w.W)}):
+        # D = 0; the smallest delay whose batched launch fills every SIMD
+        # once; half a window; the longest the ring allows
+        cap_d = min(w.W - 1, 96 - w.R - w.W)
+        simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        d_fill = min(cap_d, -(-simds // (units // w.W)))
+        for D in sorted({0, d_fill, min(cap_d, w.W // 2), cap_d}):
             if w.R not in (16, 32):
                 break
             sched.append(run_scheduled(w, S_dense, vbar, inputs, warmup, steps, D, dev))

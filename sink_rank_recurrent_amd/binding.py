@@ -633,7 +633,8 @@ class ScheduledState:
     whose windows those steps fill) are compressed by one launch, issued
     after the last of them; a snapshot must be compressed before its merge
     D steps later, so batch_steps <= max(D, 1), and the default, max(D, 1),
-    amortises one launch over as many snapshots as the delay allows.  With
+    amortises one launch over as many snapshots as the delay allows (fewer,
+    larger launches measured faster than more, smaller ones).  With
     side_streams = 0 (the default) the launches run in order on the steps'
     stream; with side_streams > 0 they take that many side streams (default
     priority) in turn and overlap the steps, and the step that merges a
@@ -648,12 +649,12 @@ class ScheduledState:
 
         if not 0 <= D < W:
             raise ValueError("need 0 <= D < W")
+        if side_streams < 0:
+            raise ValueError("side_streams must be at least 0")
         if batch_steps is None:
             batch_steps = max(D, 1)
         if not 1 <= batch_steps <= max(D, 1):
             raise ValueError("batch_steps must lie in 1 .. max(D, 1)")
-        if side_streams < 0:
-            raise ValueError("side_streams must be at least 0")
         self.rule, self.R, self.W, self.D = rule, R, W, D
         self.batch, self.heads, self.d_k, self.d_v = batch, heads, d_k, d_v
         f32 = torch.float32
