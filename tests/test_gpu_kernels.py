@@ -167,7 +167,8 @@ def test_compress(rule, dims, R, W, n):
 
 
 @pytest.mark.parametrize("dims,R", [((128, 128), 16), ((128, 64), 16), ((64, 64), 8),
-                                    ((128, 128), 32)])
+                                    ((128, 128), 32), ((128, 64), 32), ((64, 64), 32),
+                                    ((128, 128), 1), ((64, 64), 23)])
 def test_state_from_dense(dims, R):
     d_k, d_v = dims
     gen = torch.Generator(device="cuda").manual_seed(41)
