@@ -27,16 +27,16 @@ def _inputs_of(x, u, H):
     return {k: (None if v is None else f64(v[b, h])) for k, v in x.items()}
 
 
-@pytest.mark.parametrize("rule,dims,W,D,K,NS", [
-    ("gdn", (128, 128), 16, 0, 1, 0), ("gdn", (128, 128), 16, 6, None, 0),
-    ("kda", (128, 128), 32, 12, 5, 3), ("mamba2", (128, 64), 16, 5, 3, 1),
-    ("gdn", (64, 64), 16, 15, None, 2)])
-def test_scheduled_run_matches_oracle(rule, dims, W, D, K, NS):
+@pytest.mark.parametrize("rule,dims,W,D,K,NS,R", [
+    ("gdn", (128, 128), 16, 0, 1, 0, 16), ("gdn", (128, 128), 16, 6, None, 0, 16),
+    ("kda", (128, 128), 32, 12, 5, 3, 16), ("mamba2", (128, 64), 16, 5, 3, 1, 16),
+    ("gdn", (64, 64), 16, 15, None, 2, 16), ("kda", (128, 128), 32, 8, None, 0, 32)])
+def test_scheduled_run_matches_oracle(rule, dims, W, D, K, NS, R):
     """K: the snapshots of K consecutive steps share one compression launch
     (None: the default, max(D, 1)); NS: side streams the launches alternate
-    over (0: in order on the steps' stream)."""
+    over (0: in order on the steps' stream); R: 16 or 32 kept columns."""
     d_k, d_v = dims
-    B, H, R = 5, 3, 16
+    B, H = 5, 3
     t_start = [0, 1, 4, 9, 2 * W + 3]
     T = max(t_start) + 2 * W + D + 3
     seed = 900 + W + D
