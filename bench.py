@@ -2,52 +2,67 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
-One benchmark step is one decode step of every (request, head) unit of the
-workload: the fused read-out + exact update kernel, plus the compression of
-all units whenever R + W columns are held (every W steps), exactly as a
-served decode loop would run them.  Inputs for every timed step are drawn
-before timing and are resident in HBM; the state starts from a dense
-prefill converted to the shallow form (both untimed).  Every kernel is
-launched from Python through the C ABI; --graphs replays HIP graphs
-captured from the same calls instead (one per run of step launches, one
-per compression).
+A benchmark step is one decode token of the whole workload: for every
+recurrent layer, one launch of the fused read-out + exact update kernel over
+all of that layer's (request, head) units, and every W steps per layer the
+compression of that layer's factors from R + W back to R columns.  The
+default workload is the 36-layer stack: 36 recurrent layers x 32 heads x 256
+resident requests of 128 x 128 Gated DeltaNet heads (R = 16, W = 32), all 36
+layers' states resident in HBM at once (14.5 GB of factors at R + W), so no
+layer's state is still in the memory-side cache when its next step comes.
 
-The metric is decode head-steps/s (whole job).  Also reported: the step
-kernel's achieved HBM bandwidth from its algorithmic bytes and its average
-launch duration (HIP events on the launch stream), the dense-state baseline
-kernel on the same workload, two variants timed on the same state and
-inputs -- the lazily decayed form (U's decay kept as a running product,
-seed_decode_step_lazy) and the 16-bit form (kept factors fp16, rounded at
-every compression, seed_decode_step_h16) -- staggered per-request
-compression schedules (seed_decode_step_sched, one HIP graph), the handoff
-of the converted
-states (seed_pack_states / seed_unpack_states of every request), the
-statistics of the prefilled states (seed_state_stats: sink energy share, top
-direction, content ranks), and the CPU oracle timed on a bounded sample.
+Compression inside the timed region.  Each layer compresses every W steps
+(SEED figures and tables, Fig. 1 (b) caption) on its own phase: layer l's
+first window after the end-of-prefill conversion is W - floor(l W / L)
+steps, every later one W.  So every timed step compresses about L / W
+layers, and any K consecutive timed steps hold the compression work at its
+true 1/W share per layer, whatever K is.  The compressions of a step run
+after all its layer steps (each before that layer's next step).
+
+Timing.  The inputs of every timed step are drawn beforehand and resident
+in HBM.  Every bench step is captured as two HIP graphs (the L step
+launches; the step's compressions) from the same C-ABI calls; the W warm-up
+steps are replayed first as an untimed settle pass (reported on its own,
+`settle`), then the K timed steps, with HIP events on the launch stream
+before and after each graph, so no event sits between two kernels of a
+graph.  `value` = head-steps (L x requests x heads x K) / the events' time
+from the first timed graph to the end of the last.  The step kernel's
+average launch duration is its graphs' event time / (L K); `roofline`
+divides its algorithmic bytes per launch by that.
+
+Also in the line: the dense-state baseline (dense_decode_step) on the same
+stack, the lazily decayed and the 16-bit forms timed the same way, the
+other four workloads (one layer each, timed over whole compression windows
+after a settle window) in `workloads`, the end-of-prefill conversion, the
+handoff of layer 0's converted states, their statistics, the library's
+streaming-copy rate and the CPU oracle on a bounded sample (`cpu_baseline`).
 Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import copy
 import hashlib
 import json
+import math
 import os
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-import torch  # noqa: E402
-
-from sink_rank_recurrent_amd import binding  # noqa: E402
-from sink_rank_recurrent_amd import workloads as wl  # noqa: E402
-
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
-DEFAULT_WORKLOAD = 2
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_seed_step_gdn_64x16_r16w32_bf16.json")
+DEFAULT_WORKLOAD = 5
 STEP_SOURCE = os.path.join(ROOT, "sink_rank_recurrent_amd", "csrc", "seed_step.hip")
+METRIC = ("decode head-steps/s + achieved HBM GB/s (% peak), sink+rank-R state update "
+          "(whole job: every layer's step and its compression every W steps, phases staggered "
+          "over the layers, all inside the timed region)")
+# the box's CPU share for one GPU: at most this many oracle processes
+CPU_SHARE = 16
 
 
 def log(msg: str) -> None:
@@ -55,18 +70,17 @@ def log(msg: str) -> None:
 
 
 # ---------------------------------------------------------------------------
-# algorithmic bytes (what the method must move; see the byte account in the
-# design notes): reads a, r columns of U and V, the inputs and vbar; writes a,
-# all r + 1 columns of U (in-place decay plus the new column), one V column
-# and o (fp32).
+# algorithmic bytes (what the method must move): a step reads a, r columns of
+# U and V, the inputs and vbar; it writes a, all r + 1 columns of U (in-place
+# decay plus the new column), one V column and o (fp32).
 # ---------------------------------------------------------------------------
 
-def step_bytes_per_unit(w: wl.Workload, r: int, form: str = "in_place") -> float:
+def step_bytes_per_unit(w, r: int, form: str = "in_place") -> float:
     """In place: U is read and written whole.  Lazy decay: U is only read,
     one new column is written, and the decay product (one float, or d_k for
     KDA) is read and written.  16-bit kept factors (lazy): the R kept
     columns are read at 2 bytes an entry, the r - R appended ones at 4."""
-    s_in = 2 if w.in_dtype == torch.bfloat16 else 4
+    s_in = 2 if w.in_dtype_name == "bf16" else 4
     g_bytes = 4 * w.d_k if w.rule == "kda" else 4
     beta_bytes = 0 if w.rule == "mamba2" else 4
     cols = 4 * (w.d_k + w.d_v) * r
@@ -83,8 +97,8 @@ def step_bytes_per_unit(w: wl.Workload, r: int, form: str = "in_place") -> float
     return read + write
 
 
-def dense_bytes_per_unit(w: wl.Workload) -> float:
-    s_in = 2 if w.in_dtype == torch.bfloat16 else 4
+def dense_bytes_per_unit(w) -> float:
+    s_in = 2 if w.in_dtype_name == "bf16" else 4
     g_bytes = 4 * w.d_k if w.rule == "kda" else 4
     beta_bytes = 0 if w.rule == "mamba2" else 4
     return 8 * w.d_k * w.d_v + s_in * (2 * w.d_k + w.d_v) + g_bytes + beta_bytes + 4 * w.d_v
@@ -95,270 +109,403 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(w: wl.Workload):
-    """HBM bytes per step-kernel launch from the committed counter summary,
-    or None if there is none or the kernel source changed since."""
-    if w.name != wl.WORKLOADS[DEFAULT_WORKLOAD].name or not os.path.exists(TRAFFIC_FILE):
+def traffic_file(w) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_seed_step_{w.name}.json")
+
+
+def load_traffic(w, steps: int, warmup: int):
+    """HBM bytes per step-kernel launch from the committed counter summary
+    of this very command (workload, timed and warm-up steps), or None if
+    there is none or the step kernel's source changed since."""
+    path = traffic_file(w)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_sha256_16") != source_hash(STEP_SOURCE):
+        return None
+    if t.get("bench_steps") != steps or t.get("bench_warmup") != warmup:
         return None
     return t.get("hbm_bytes_per_launch")
 
 
 # ---------------------------------------------------------------------------
+# the layer stack
+# ---------------------------------------------------------------------------
 
-CONVERSION_MS = {}
+class Spec:
+    """Host-side description of a workload (no torch types), for the byte
+    account and the CPU worker."""
+
+    def __init__(self, w):
+        self.name, self.rule, self.batch, self.heads = w.name, w.rule, w.batch, w.heads
+        self.layers, self.d_k, self.d_v, self.R, self.W = w.layers, w.d_k, w.d_v, w.R, w.W
+        self.in_dtype_name = "bf16" if "bfloat16" in str(w.in_dtype) else "f32"
+        self.units = w.batch * w.heads
 
 
-def prepare(w: wl.Workload, layer: int, n_steps: int, dev: str, lazy: bool = False):
-    """vbar, a converted shallow state and resident inputs for n_steps steps.
-    The conversion (seed_state_from_dense of every head) is timed on the
-    stream into CONVERSION_MS["ms"]."""
-    vbar = wl.make_vbar(w.heads, w.d_v, w.seed, layer, dev)
-    S = torch.zeros(w.batch, w.heads, w.d_k, w.d_v, device=dev)
+def layer_phases(L: int, W: int) -> list:
+    """Compression phase of each layer: layer l's first window after the
+    conversion is W - phase[l] steps, so the L layers' compressions spread
+    evenly over the W steps of a window."""
+    return [(l * W) // L for l in range(L)]
+
+
+def prefill_layers(w, layers: int, dev: str):
+    """vbar and the dense state after the 512-step dense prefill, per layer."""
+    import torch
+    from sink_rank_recurrent_amd import binding
+    from sink_rank_recurrent_amd import workloads as wl
+
+    vbars, Ss = [], []
     o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
-    for t in range(-w.prefill, 0):
-        x = wl.workload_step(w, vbar, t, layer, dev)
-        binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-    st = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar, device=dev,
-                              lazy=lazy)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    st.from_dense(S)            # first call sets the kernel's LDS limit
+    for layer in range(layers):
+        vbar = wl.make_vbar(w.heads, w.d_v, w.seed, layer, dev)
+        S = torch.zeros(w.batch, w.heads, w.d_k, w.d_v, device=dev)
+        for t in range(-w.prefill, 0):
+            x = wl.workload_step(w, vbar, t, layer, dev)
+            binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        vbars.append(vbar)
+        Ss.append(S)
+    return vbars, Ss
+
+
+def make_inputs(w, vbars, n_steps: int, dev: str):
+    """inputs[l][t]: the resident inputs of decode step t of layer l."""
+    from sink_rank_recurrent_amd import workloads as wl
+
+    return [[wl.workload_step(w, vbars[l], t, l, dev) for t in range(n_steps)]
+            for l in range(len(vbars))]
+
+
+def make_states(w, form: str, vbars, Ss, phases, dev: str, timed_conversion: bool = False):
+    """One state per layer, converted from its dense state (first window
+    W - phase).  Returns (states, conversion ms or None)."""
+    import torch
+    from sink_rank_recurrent_amd import binding
+
+    states = []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    conv_ms = 0.0
+    for l, (vbar, S) in enumerate(zip(vbars, Ss)):
+        fw = w.W - phases[l]
+        if form == "h16":
+            st = binding.ShallowState16(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
+                                        store=torch.float16, rounding="nearest", device=dev,
+                                        first_window=fw)
+        else:
+            st = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
+                                      device=dev, lazy=(form == "lazy"), first_window=fw)
+        if timed_conversion:
+            ev[0].record()
+            st.from_dense(S)
+            ev[1].record()
+            torch.cuda.synchronize()
+            conv_ms += ev[0].elapsed_time(ev[1])
+        else:
+            st.from_dense(S)
+        states.append(st)
+    return states, (conv_ms if timed_conversion else None)
+
+
+def plan(states, n: int):
+    """The next n bench steps: for each, the (layer, r) of its step launches
+    and the (layer, r) of the compressions that follow them.  Returns
+    (plan, final r per layer, final limit per layer); the states are not
+    touched."""
+    r = [st.r for st in states]
+    lim = [st.limit for st in states]
+    out = []
+    for _ in range(n):
+        steps = [(l, r[l]) for l in range(len(states))]
+        comps = []
+        for l in range(len(states)):
+            r[l] += 1
+            if r[l] >= lim[l]:
+                comps.append((l, r[l]))
+                r[l] = states[l].R
+                lim[l] = states[l].cap
+        out.append((steps, comps))
+    return out, r, lim
+
+
+def warm_compress_instances(w, form: str, rs, dev: str) -> None:
+    """Run every compression instance the plan uses once, eagerly, on a
+    one-unit scratch state, so that its one-time LDS attribute is set before
+    any graph capture."""
+    import torch
+    from sink_rank_recurrent_amd import binding
+
+    vbar = torch.ones(w.heads, w.d_v, device=dev)
+    for r in sorted(set(rs)):
+        if form == "h16":
+            st = binding.ShallowState16(w.rule, 1, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
+                                        device=dev)
+        else:
+            st = binding.ShallowState(w.rule, 1, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
+                                      device=dev, lazy=(form == "lazy"))
+        st.launch_compress(r)
     torch.cuda.synchronize()
-    e0.record()
-    st.from_dense(S)
-    e1.record()
-    inputs = [wl.workload_step(w, vbar, t, layer, dev) for t in range(n_steps)]
+
+
+def run_stack(w, states, inputs, outs, t0: int, n_settle: int, n_timed: int, form: str, dev: str):
+    """Capture n_settle + n_timed bench steps (from input step t0) as HIP
+    graphs, replay the first n_settle untimed-for-value (the settle pass),
+    then the n_timed timed ones with events around every graph."""
+    import torch
+
+    pl, r_end, lim_end = plan(states, n_settle + n_timed)
+    warm_compress_instances(w, form, [r for _, comps in pl for _, r in comps], dev)
+    fns = [st.bind_step(outs[l]) for l, st in enumerate(states)]
+    graphs = []
+    for i, (steps, comps) in enumerate(pl):
+        t = t0 + i
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            for l, r in steps:
+                x = inputs[l][t]
+                fns[l](x["q"], x["k"], x["v"], x["g"], x["beta"], r)
+        gc = None
+        if comps:
+            gc = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gc):
+                for l, r in comps:
+                    states[l].launch_compress(r)
+        graphs.append((gs, gc))
     torch.cuda.synchronize()
-    CONVERSION_MS["ms"] = e0.elapsed_time(e1)
-    return vbar, S, st, inputs
 
-
-def _plan(st, warmup: int, steps: int):
-    """The timed loop as a list of actions: ("steps", [(t, r), ...]) for each
-    run of step launches between two compressions, ("compress", r) for each
-    compression."""
-    seq, cur, r = [], [], st.r
-    for t in range(warmup, warmup + steps):
-        cur.append((t, r))
-        r += 1
-        if r >= st.cap:
-            seq.append(("steps", cur))
-            cur = []
-            seq.append(("compress", r))
-            r = st.R
-    if cur:
-        seq.append(("steps", cur))
-    return seq, r
-
-
-def _do(st, step, inputs, o, action) -> None:
-    """One action of the plan; `step` is the state's bound step call."""
-    if action[0] == "steps":
-        for t, r in action[1]:
-            x = inputs[t]
-            step(x["q"], x["k"], x["v"], x["g"], x["beta"], r)
-    elif isinstance(st, binding.ShallowState16):
-        binding.seed_compress_h16(st.rule, st.Uk, st.Vk, st.Uw, st.Vw, st.gam, action[1],
-                                  st.rounding, st.seed, st.epoch)
-        st.epoch += 1
-    elif st.lazy:
-        binding.seed_compress_lazy(st.rule, st.U, st.V, st.gam, action[1], st.R)
-    else:
-        binding.seed_compress(st.U, st.V, action[1], st.R)
-
-
-def run_shallow(st, inputs, o, warmup: int, steps: int, graphs: bool):
-    """Warm up eagerly, then time `steps` steps.
-
-    With `graphs`, each run of step launches between two compressions and
-    each compression is captured once as a HIP graph (untimed) and replayed
-    in the timed loop, so host launch cost does not enter the timing.  HIP
-    events on the launch stream bracket every action; no event marker sits
-    between two step kernels."""
-    for t in range(warmup):
-        x = inputs[t]
-        st.step_and_maybe_compress(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-    torch.cuda.synchronize()
-    seq, r_end = _plan(st, warmup, steps)
-    step = st.bind_step(o)
-    captured = []
-    if graphs:
-        for action in seq:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                _do(st, step, inputs, o, action)
-            captured.append(g)
-        torch.cuda.synchronize()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    marks = [ev() for _ in range(len(seq) + 1)]
+    s0, s1 = ev(), ev()
+    s0.record()
+    for gs, gc in graphs[:n_settle]:
+        gs.replay()
+        if gc is not None:
+            gc.replay()
+    s1.record()
+    timed = graphs[n_settle:]
+    ea = [ev() for _ in timed]
+    eb = [ev() for _ in timed]
+    e_end = ev()
+    for i, (gs, gc) in enumerate(timed):
+        ea[i].record()
+        gs.replay()
+        eb[i].record()
+        if gc is not None:
+            gc.replay()
+    e_end.record()
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i, action in enumerate(seq):
-        marks[i].record()
-        if graphs:
-            captured[i].replay()
-        else:
-            _do(st, step, inputs, o, action)
-    marks[-1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    st.r = r_end
-    windows, comp, step_r = [], [], []
-    for i, action in enumerate(seq):
-        ms = marks[i].elapsed_time(marks[i + 1])
-        if action[0] == "steps":
-            windows.append((ms, len(action[1])))
-            step_r += [r for _, r in action[1]]
-        else:
-            comp.append(ms)
+    for l, st in enumerate(states):
+        st.r, st.limit = r_end[l], lim_end[l]
+    step_ms = [ea[i].elapsed_time(eb[i]) for i in range(len(timed))]
+    comp_ms = [eb[i].elapsed_time(ea[i + 1] if i + 1 < len(timed) else e_end)
+               for i in range(len(timed))]
+    timed_pl = pl[n_settle:]
+    n_comp = sum(len(c) for _, c in timed_pl)
+    step_r = [r for steps, _ in timed_pl for _, r in steps]
+    comp_r = [r for _, comps in timed_pl for _, r in comps]
+    return {"elapsed_ms": ea[0].elapsed_time(e_end), "step_ms": sum(step_ms),
+            "compress_ms": sum(comp_ms), "compressions": n_comp, "step_r": step_r,
+            "compress_r": comp_r, "settle_ms": s0.elapsed_time(s1), "settle_steps": n_settle,
+            "timed_steps": n_timed, "graphs_captured": sum(1 + (gc is not None) for _, gc in graphs),
+            "epochs_before": epochs}
+
+
+def summarise(spec, res, form: str, L: int) -> dict:
+    """Whole-job rate, step-kernel roofline and compression share of one
+    run_stack result."""
+    units = spec.units
+    n_launch = len(res["step_r"])
+    step_bytes = sum(step_bytes_per_unit(spec, r, form) for r in res["step_r"]) * units
+    avg_launch_s = res["step_ms"] / 1e3 / n_launch
+    achieved = step_bytes / n_launch / avg_launch_s / 1e9
+    el = res["elapsed_ms"] / 1e3
+    n_comp = res["compressions"]
     return {
-        "elapsed_s": marks[0].elapsed_time(marks[-1]) / 1e3,
-        "wall_s": wall,
-        "step_window_ms": windows,
-        "step_r": step_r,
-        "compress_ms": comp,
+        "value": L * units * res["timed_steps"] / el,
+        "ms_per_step": res["elapsed_ms"] / res["timed_steps"],
+        "step_kernel_avg_us": avg_launch_s * 1e6,
+        "step_launches": n_launch,
+        "step_bytes_per_head_step": step_bytes / n_launch / units,
+        "step_algorithmic_bytes_per_launch": step_bytes / n_launch,
+        "step_achieved_GBs": achieved,
+        "step_frac_of_peak": achieved / HBM_PEAK_GBS,
+        "step_only_head_steps_per_s": units * n_launch / (res["step_ms"] / 1e3),
+        "compressions": n_comp,
+        "compress_avg_us": res["compress_ms"] * 1e3 / n_comp if n_comp else None,
+        "compress_share_of_time": res["compress_ms"] / res["elapsed_ms"],
+        "compressions_per_layer_step": n_comp / (L * res["timed_steps"]),
+        "settle": {"steps": res["settle_steps"],
+                   "ms_per_step": (res["settle_ms"] / res["settle_steps"]
+                                   if res["settle_steps"] else None)},
     }
 
 
-def sched_bytes_per_unit(w: wl.Workload, r: int, D: int) -> float:
-    """The lazy step's bytes at r columns, plus the merge step's fold of the
-    decay product into the R + D held columns of U (once per W steps)."""
-    return step_bytes_per_unit(w, r, "lazy") + 4 * w.d_k * (w.R + D) / w.W
+def run_dense(w, Ss, inputs, outs, t0: int, n_settle: int, n_timed: int) -> dict:
+    """The dense-state baseline over the same layers and inputs, one graph
+    per bench step (the L dense launches), a settle pass first."""
+    import torch
+    from sink_rank_recurrent_amd import binding
 
-
-def run_scheduled(w, S, vbar, inputs, warmup: int, steps: int, D: int, dev):
-    """Staggered starts (request b's phase b mod W) on the per-request
-    schedule with merge delay D, the snapshots of max(D, 1) consecutive
-    steps compressed by one launch on the steps' stream.  Every request has
-    passed its first merge when timing starts.  The timed steps and their
-    compressions are captured once as one HIP graph and replayed."""
-    t_start = [-(b % w.W) - (w.W + D) for b in range(w.batch)]
-    st = binding.ScheduledState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, D, vbar,
-                                t_start, device=dev)
-    st.from_dense(S)
-    o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
-    for t in range(warmup):
-        x = inputs[t]
-        st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-    st.join()
+    graphs = []
+    for i in range(n_settle + n_timed):
+        t = t0 + i
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l, S in enumerate(Ss):
+                x = inputs[l][t]
+                binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                          outs[l])
+        graphs.append(g)
     torch.cuda.synchronize()
-    # the columns every request holds at each timed step
-    cols = [st.held_columns(b, t) for t in range(warmup, warmup + steps) for b in range(w.batch)]
-    # every compression of the warm-up has finished: nothing to wait for
-    st.pending.clear()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for t in range(warmup, warmup + steps):
-            x = inputs[t]
-            st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-        st.join()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    for g in graphs[:n_settle]:
+        g.replay()
+    e[1].record()
+    for g in graphs[n_settle:]:
+        g.replay()
+    e[2].record()
     torch.cuda.synchronize()
-    st.pending.clear()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    el = e0.elapsed_time(e1) / 1e3
-    units = w.batch * w.heads
-    mean_bytes = sum(sched_bytes_per_unit(w, r, D) for r in cols) / len(cols)
-    return {"D": D, "value": units * steps / el, "unit": "head-steps/s",
-            "ms_per_step": el * 1e3 / steps, "mean_columns": sum(cols) / len(cols),
-            "step_bytes_per_head_step": mean_bytes,
-            "batch_steps": st.batch_steps, "side_streams": len(st.sides),
-            "launch": "one hip graph of the timed steps; the snapshots of batch_steps "
-                      "consecutive steps compressed by one launch on the steps' stream"}
+    return {"elapsed_ms": e[1].elapsed_time(e[2]), "settle_ms": e[0].elapsed_time(e[1])}
 
 
-def run_dense(w, S, inputs, o, warmup: int, steps: int, graphs: bool, chunk: int = 32):
-    def do(ts):
-        for t in ts:
-            x = inputs[t]
-            binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
-
-    do(range(warmup))
-    torch.cuda.synchronize()
-    chunks = [range(c, min(c + chunk, warmup + steps)) for c in range(warmup, warmup + steps, chunk)]
-    captured = []
-    if graphs:
-        for ts in chunks:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                do(ts)
-            captured.append(g)
-        torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i, ts in enumerate(chunks):
-        if graphs:
-            captured[i].replay()
-        else:
-            do(ts)
-    t1.record()
-    torch.cuda.synchronize()
-    return {"elapsed_s": t0.elapsed_time(t1) / 1e3}
+def dense_summary(spec, d, L: int, n_timed: int) -> dict:
+    units = spec.units
+    el = d["elapsed_ms"] / 1e3
+    avg = el / (L * n_timed)
+    return {"value": L * units * n_timed / el, "unit": "head-steps/s",
+            "ms_per_step": d["elapsed_ms"] / n_timed,
+            "bytes_per_head_step": dense_bytes_per_unit(spec), "kernel_avg_us": avg * 1e6,
+            "achieved_GBs": dense_bytes_per_unit(spec) * units / avg / 1e9,
+            "frac_of_peak": dense_bytes_per_unit(spec) * units / avg / 1e9 / HBM_PEAK_GBS}
 
 
-def _cpu_worker(job):
-    """One host process of the CPU baseline: the oracle's factored mode, as it
-    stands and on one thread, stepping its units through the inputs (cycled)
-    and compressing every W, until the budget is spent."""
-    rule, R, W, st0_np, inputs_np, budget_s = job
-    from threadpoolctl import threadpool_limits
+# ---------------------------------------------------------------------------
+# the CPU baseline: the oracle in separate processes
+# ---------------------------------------------------------------------------
+
+def cpu_worker_main(path: str) -> int:
+    """One oracle process (one thread): the factored mode (Lemma 2 steps,
+    compression every W) on its units until its budget is spent, then the
+    dense mode (the dense recurrence) on the same units.  Prints one JSON
+    line of counts and times.  Never touches the GPU."""
+    import numpy as np
 
     import oracle
 
-    a, U, V, vb = st0_np
+    z = np.load(path)
+    rule = str(z["rule"])
+    R, W = int(z["R"]), int(z["W"])
+    bf, bd = float(z["budget_factored"]), float(z["budget_dense"])
+    a, U, V, vb, S = z["a"], z["U"], z["V"], z["vb"], z["S"]
+    xs = [{k: (None if k == "beta" and z["beta"].size == 0 else z[k][i])
+           for k in ("q", "k", "v", "g", "beta")} for i in range(z["q"].shape[0])]
     done = 0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while time.perf_counter() - t0 < budget_s:
-            x = inputs_np[done % len(inputs_np)]
-            a, U, V, _ = oracle.seed_step(rule, a, U, V, vb, x["q"], x["k"], x["v"], x["g"],
-                                          x["beta"])
-            if U.shape[-1] >= R + W:
-                U, V = oracle.compress(U, V, R)
-            done += 1
-    return a.shape[0], done, time.perf_counter() - t0
+    while time.perf_counter() - t0 < bf:
+        x = xs[done % len(xs)]
+        a, U, V, _ = oracle.seed_step(rule, a, U, V, vb, x["q"], x["k"], x["v"], x["g"],
+                                      x["beta"])
+        if U.shape[-1] >= R + W:
+            U, V = oracle.compress(U, V, R)
+        done += 1
+    el_f = time.perf_counter() - t0
+    dd = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < bd:
+        x = xs[dd % len(xs)]
+        S, _ = oracle.dense_step(rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"])
+        dd += 1
+    el_d = time.perf_counter() - t0
+    print(json.dumps({"units": int(a.shape[0]), "factored_steps": done, "factored_s": el_f,
+                      "dense_steps": dd, "dense_s": el_d}), flush=True)
+    return 0
 
 
-def cpu_baseline(w, st0_np, inputs_np, budget_s: float, workers: int):
-    """The oracle on a bounded sample of the workload, on the host's cores:
-    `workers` processes (spawned, so none inherits the GPU context), each
-    with its own slice of the converted units and their inputs, all running
-    for `budget_s` seconds at once.  The value is the sum of their rates."""
-    import multiprocessing
-    from concurrent.futures import ProcessPoolExecutor
+def cpu_baseline(spec, snap, budget_f: float, budget_d: float, workers: int) -> dict:
+    """The oracle as it stands on a bounded sample of the workload: `workers`
+    child processes (plain subprocesses, one thread each, none touching the
+    GPU), each with its own slice of the sampled units, all at once; every
+    child is waited for, so none outlives the benchmark."""
+    import numpy as np
 
-    a, U, V, vb = st0_np
+    a, U, V, vb, S, xs = snap
     n = a.shape[0]
     per = n // workers
-    jobs = []
-    for p in range(workers):
-        sl = slice(p * per, (p + 1) * per)
-        xs = [{k: (None if v is None else v[sl]) for k, v in x.items()} for x in inputs_np]
-        jobs.append((w.rule, w.R, w.W, (a[sl], U[sl], V[sl], vb[sl]), xs, budget_s))
-    with ProcessPoolExecutor(max_workers=workers,
-                             mp_context=multiprocessing.get_context("spawn")) as ex:
-        res = list(ex.map(_cpu_worker, jobs))
-    rates = [units * done / el for units, done, el in res]
-    steps = sum(done for _, done, _ in res)
-    return {"value": sum(rates), "unit": "head-steps/s", "cores": workers, "kind": "oracle",
-            "per_process": sum(rates) / workers,
-            "sample": f"{workers} processes x {per} units, {steps} decode steps in all "
-                      f"(compression every {w.W}) of {w.name}, from the converted state, "
-                      f"fp64 numpy oracle, one thread per process, {budget_s:.0f} s each"}
+    tmp = tempfile.mkdtemp(prefix="seed_cpu_")
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    procs = []
+    try:
+        for p in range(workers):
+            sl = slice(p * per, (p + 1) * per)
+            path = os.path.join(tmp, f"w{p}.npz")
+            stack = lambda key: np.stack([x[key][sl] for x in xs])  # noqa: E731
+            np.savez(path, rule=spec.rule, R=spec.R, W=spec.W, budget_factored=budget_f,
+                     budget_dense=budget_d, a=a[sl], U=U[sl], V=V[sl], vb=vb[sl], S=S[sl],
+                     q=stack("q"), k=stack("k"), v=stack("v"), g=stack("g"),
+                     beta=(np.zeros(0) if xs[0]["beta"] is None else stack("beta")))
+            procs.append(subprocess.Popen([sys.executable, os.path.abspath(__file__),
+                                           "--cpu-worker", path], stdout=subprocess.PIPE,
+                                          env=env, cwd=ROOT, text=True))
+        res = []
+        for pr in procs:
+            out, _ = pr.communicate()
+            if pr.returncode != 0:
+                raise RuntimeError(f"CPU oracle worker failed with status {pr.returncode}")
+            res.append(json.loads(out.strip().splitlines()[-1]))
+    finally:
+        for pr in procs:
+            if pr.poll() is None:
+                pr.kill()
+                pr.wait()
+        for f in os.listdir(tmp):
+            os.remove(os.path.join(tmp, f))
+        os.rmdir(tmp)
+    f_rates = [r["units"] * r["factored_steps"] / r["factored_s"] for r in res]
+    d_rates = [r["units"] * r["dense_steps"] / r["dense_s"] for r in res]
+    steps = sum(r["factored_steps"] for r in res)
+    return {"value": sum(f_rates), "unit": "head-steps/s", "cores": workers, "kind": "oracle",
+            "single_thread_value": sum(f_rates) / workers,
+            "dense_value": sum(d_rates), "dense_single_thread_value": sum(d_rates) / workers,
+            "host_cpus_visible": os.cpu_count(),
+            "host_cpus_usable": len(os.sched_getaffinity(0)),
+            "host_cpu_share": CPU_SHARE,
+            "sample": f"{workers} processes x {per} units of layer 0 of {spec.name} (one thread "
+                      f"each, the box's CPU share for one GPU), {steps} factored decode steps in "
+                      f"all (compression every {spec.W}) from the converted state for "
+                      f"{budget_f:.0f} s, then the dense recurrence on the same units for "
+                      f"{budget_d:.0f} s; fp64 numpy oracle; `single_thread_value` is the mean "
+                      f"per-process (one-thread) rate"}
 
+
+def cpu_snapshot(spec, state, S, vbar, xs_dev, n_units: int):
+    """fp64 host copies of the first n_units units: converted state, dense
+    state and step inputs (bf16 widened exactly)."""
+    import torch
+
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    units, cap = spec.units, state.cap
+    a = f64(state.a.reshape(units, spec.d_k)[:n_units])
+    U = f64(state.U.reshape(units, cap, spec.d_k)[:n_units, :state.r]).transpose(0, 2, 1)
+    V = f64(state.V.reshape(units, cap, spec.d_v)[:n_units, :state.r]).transpose(0, 2, 1)
+    vb = f64(vbar)[[u % spec.heads for u in range(n_units)]]
+    Sn = f64(S.reshape(units, spec.d_k, spec.d_v)[:n_units])
+    xs = [{k: (None if v is None else f64(v.reshape((units,) + v.shape[2:])[:n_units]))
+           for k, v in x.items()} for x in xs_dev]
+    return a, U, V, vb, Sn, xs
+
+
+# ---------------------------------------------------------------------------
 
 def achievable_copy_GBs(n_bytes: int = 1 << 31, reps: int = 5) -> float:
     """Read + write GB/s of the library's streaming copy (seed_stream_copy)
     over a buffer far larger than the 256 MB memory-side cache: what HBM
     delivers to a read-once, write-once kernel here, set beside the nominal
     8 TB/s."""
+    import torch
+    from sink_rank_recurrent_amd import binding
+
     src = torch.ones(n_bytes // 4, device="cuda:0", dtype=torch.float32)
     dst = torch.empty_like(src)
     binding.stream_copy(src, dst)
@@ -378,6 +525,8 @@ def achievable_copy_GBs(n_bytes: int = 1 << 31, reps: int = 5) -> float:
 def copy_probe(n_bytes: int = 1 << 30, reps: int = 8) -> None:
     """A plain device copy of known size (calibration of the HBM byte
     counters): `reps` launches of dst.copy_(src) over n_bytes each."""
+    import torch
+
     src = torch.ones(n_bytes // 4, device="cuda:0", dtype=torch.float32)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -391,254 +540,259 @@ def copy_probe(n_bytes: int = 1 << 30, reps: int = 8) -> None:
                       "GBs_read_plus_write": 2 * n_bytes * reps / el / 1e9}), flush=True)
 
 
+def handoff_of(w, st, dev: str) -> dict:
+    """Pack every request of one layer's converted states into one buffer,
+    then unpack it into the same slots (20 times each, events around)."""
+    import torch
+
+    sel = torch.arange(w.batch, dtype=torch.int32, device=dev)
+    buf = st.pack(sel)
+    reps = 20
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        st.pack(sel, buf)
+    ev[1].record()
+    for _ in range(reps):
+        st.unpack(buf, sel)
+    ev[2].record()
+    torch.cuda.synchronize()
+    nbytes = buf.numel()
+    t_pack = ev[0].elapsed_time(ev[1]) / reps / 1e3
+    t_unpack = ev[1].elapsed_time(ev[2]) / reps / 1e3
+    units = w.batch * w.heads
+    return {"head_bytes": nbytes // units, "dense_head_bytes": 4 * w.d_k * w.d_v,
+            "requests": w.batch, "buffer_bytes": nbytes,
+            "pack_us": t_pack * 1e6, "unpack_us": t_unpack * 1e6,
+            "pack_GBs": 2 * nbytes / t_pack / 1e9, "unpack_GBs": 2 * nbytes / t_unpack / 1e9}
+
+
+def stats_of(w, S, vbar, dev: str) -> dict:
+    """Statistics of one layer's prefilled dense states (the quantities the
+    pages measure on model states), with the kernel's time."""
+    import torch
+    from sink_rank_recurrent_amd import binding
+
+    nf = binding.lib().seed_stat_fields()
+    rec = torch.empty(w.batch, w.heads, nf, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    binding.seed_state_stats(S, vbar, w.R, rec)
+    e1.record()
+    torch.cuda.synchronize()
+    units = w.batch * w.heads
+    r = rec.reshape(units, nf)[:, :len(binding.STAT_FIELDS)].double()
+    med = {f: float(r[:, i].median()) for i, f in enumerate(binding.STAT_FIELDS)}
+    return {"kernel_ms": e0.elapsed_time(e1), "units": units,
+            "median_sink_share": med["sink_share"], "median_top_share": med["top_share"],
+            "median_abs_cos_vstar_vbar": med["abs_cos_vstar_vbar"],
+            "median_rank90": med["rank90"], "median_rank99": med["rank99"],
+            "median_beyond_R_share": med["beyond_R_share"]}
+
+
+def run_workload(w, layers: int, settle: int, timed: int, dev: str, forms, with_dense: bool,
+                 keep_layer0: bool = False):
+    """Prefill, convert and time `layers` layers of workload w in every form
+    of `forms`, then the dense baseline.  Returns (results by form, dense,
+    conversion ms, layer-0 objects for the CPU snapshot / handoff / stats)."""
+    import torch
+
+    spec = Spec(w)
+    phases = layer_phases(layers, w.W)
+    vbars, Ss = prefill_layers(w, layers, dev)
+    log(f"{w.name}: prefilled {layers} layer(s) x {spec.units} units")
+    inputs = make_inputs(w, vbars, settle + timed, dev)
+    outs = [torch.empty(w.batch, w.heads, w.d_v, device=dev) for _ in range(layers)]
+    results, conv_ms, layer0 = {}, None, None
+    for form in forms:
+        states, cm = make_states(w, form, vbars, Ss, phases, dev, timed_conversion=(form == "in_place"))
+        if cm is not None:
+            conv_ms = cm
+        if keep_layer0 and form == "in_place":
+            # layer 0's converted and dense states as they are before any
+            # timed step (copies: the runs below move the originals on)
+            st0 = copy.copy(states[0])
+            st0.a, st0.U, st0.V = states[0].a.clone(), states[0].U.clone(), states[0].V.clone()
+            layer0 = {"state": st0, "S": Ss[0].clone(), "vbar": vbars[0],
+                      "inputs": inputs[0][:min(settle + timed, 64)]}
+        res = run_stack(spec, states, inputs, outs, 0, settle, timed, form, dev)
+        results[form] = summarise(spec, res, form, layers)
+        log(f"{w.name} [{form}]: {results[form]['ms_per_step']:.3f} ms per step, "
+            f"{results[form]['compressions']} compressions in {timed} timed steps")
+        del states
+        torch.cuda.empty_cache()
+    dense = None
+    if with_dense:
+        d = run_dense(w, Ss, inputs, outs, 0, settle, timed)
+        dense = dense_summary(spec, d, layers, timed)
+        log(f"{w.name} [dense]: {dense['ms_per_step']:.3f} ms per step")
+    return results, dense, conv_ms, layer0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=sorted(wl.WORKLOADS))
-    ap.add_argument("--layer", type=int, default=0)
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--layers", type=int, default=None,
+                    help="recurrent layers resident and stepped per token (default: the "
+                         "workload's own count)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of the oracle's factored mode per process")
+    ap.add_argument("--cpu-dense-budget", type=float, default=5.0,
+                    help="seconds of the oracle's dense mode per process")
     ap.add_argument("--cpu-workers", type=int, default=0,
-                    help="host processes for the CPU baseline (default: the usable cores, "
-                         "at most 16)")
+                    help="oracle processes (default: the usable cores, at most 16)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--lazy", action="store_true",
-                    help="keep U's decay as a running product (seed_decode_step_lazy) instead of "
-                         "rewriting U every step")
     ap.add_argument("--no-variant", action="store_true",
-                    help="skip the lazily decayed and 16-bit forms that are otherwise timed as well")
-    ap.add_argument("--graphs", action="store_true",
-                    help="replay HIP graphs captured from the same calls instead of launching "
-                         "every kernel from Python")
+                    help="skip the lazily decayed and 16-bit forms")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="skip the other workloads' entries")
+    ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
+    if args.cpu_worker:
+        return cpu_worker_main(args.cpu_worker)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the shallow-state path has no cross-GPU exchange and "
               "this build runs on a single MI355X; --gpus must be 1", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("need --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    from sink_rank_recurrent_amd import binding
+    from sink_rank_recurrent_amd import workloads as wl
 
     if args.copy_probe:
         copy_probe()
         return 0
 
-    w = wl.WORKLOADS[args.workload]
-    steps = args.steps if args.steps is not None else min(w.steps, 1024)
-    warmup = args.warmup
     dev = "cuda:0"
     torch.cuda.set_device(0)
     binding.lib()
-    units = w.batch * w.heads
-    log(f"workload {w.name}: {units} units, {steps} timed steps after {warmup} warm-up")
+    w = wl.WORKLOADS[args.workload]
+    L = args.layers if args.layers is not None else w.layers
+    spec = Spec(w)
+    steps, warmup = args.steps, args.warmup
+    log(f"workload {w.name}: {L} layer(s) x {spec.units} units, {steps} timed steps after "
+        f"{warmup} settle steps")
+    forms = ["in_place"] if args.no_variant else ["in_place", "lazy", "h16"]
+    results, dense, conv_ms, layer0 = run_workload(w, L, warmup, steps, dev, forms,
+                                                   not args.no_dense, keep_layer0=True)
+    head = results["in_place"]
 
-    vbar, S_dense, st, inputs = prepare(w, args.layer, warmup + steps, dev, lazy=args.lazy)
-    log("prepared state and inputs")
+    handoff = stats = None
+    if not args.no_variant:
+        handoff = handoff_of(w, layer0["state"], dev)
+        stats = stats_of(w, layer0["S"], layer0["vbar"], dev)
+        log(f"handoff: pack {handoff['pack_us']:.1f} us, unpack {handoff['unpack_us']:.1f} us; "
+            f"statistics {stats['kernel_ms']:.1f} ms")
 
-    # snapshot for the CPU baseline (first units, converted state)
+    workers = 0
+    snap = None
+    if not args.no_cpu:
+        workers = args.cpu_workers or min(CPU_SHARE, len(os.sched_getaffinity(0)))
+        workers = max(1, min(workers, spec.units // 16))
+        n_cpu = min(spec.units, 64 * workers) // workers * workers
+        snap = cpu_snapshot(spec, layer0["state"], layer0["S"], layer0["vbar"],
+                            layer0["inputs"], n_cpu)
+    del layer0
+    torch.cuda.empty_cache()
+
+    subs = {}
+    if not args.no_sub:
+        for num in (1, 2, 3, 4):
+            if num == args.workload:
+                continue
+            ws = wl.WORKLOADS[num]
+            sp = Spec(ws)
+            n_timed = ws.W * max(1, math.ceil(steps / ws.W))
+            rs, ds, cms, _ = run_workload(ws, 1, ws.W, n_timed, dev, forms, not args.no_dense)
+            e = dict(rs["in_place"])
+            e["rule"] = "timed over whole windows: one settle window, then " \
+                        f"{n_timed // ws.W} window(s) of {ws.W} steps and their compressions"
+            e["us_per_step"] = e["ms_per_step"] * 1e3
+            e["conversion_ms"] = cms
+            e["dense_baseline"] = ds
+            e["speedup_over_dense"] = e["value"] / ds["value"] if ds else None
+            for form, key in (("lazy", "lazy_decay_variant"), ("h16", "fp16_factor_variant")):
+                if form in rs:
+                    e[key] = {"value": rs[form]["value"], "step_frac_of_peak":
+                              rs[form]["step_frac_of_peak"],
+                              "compress_avg_us": rs[form]["compress_avg_us"]}
+            subs[ws.name] = e
+            torch.cuda.empty_cache()
+
     cpu = None
-    if not args.no_cpu:
-        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
-        workers = max(1, min(workers, units // 16))
-        n_cpu = min(units, 64 * workers) // workers * workers
-        f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
-        a0 = f64(st.a.reshape(units, w.d_k)[:n_cpu])
-        U0 = f64(st.true_U().reshape(units, w.cap, w.d_k)[:n_cpu, :st.r]).transpose(0, 2, 1)
-        V0 = f64(st.V.reshape(units, w.cap, w.d_v)[:n_cpu, :st.r]).transpose(0, 2, 1)
-        vb0 = f64(vbar)[[u % w.heads for u in range(n_cpu)]]
-        cpu_inputs = []
-        for x in inputs[: min(len(inputs), 256)]:
-            cpu_inputs.append({k: (None if v is None else f64(v.reshape((units,) + v.shape[2:])[:n_cpu]))
-                               for k, v in x.items()})
-        cpu_state = (a0, U0, V0, vb0)
-
-    S_copy = S_dense.clone() if not args.no_dense else None
-    S_var = S_dense.clone() if not (args.lazy or args.no_variant) else None
-    o = torch.empty(w.batch, w.heads, w.d_v, device=dev)
-    res = run_shallow(st, inputs, o, warmup, steps, graphs=args.graphs)
-    log(f"shallow: {res['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
-
-    # the lazily decayed form and the 16-bit form on the same converted
-    # state and inputs
-    variants = {}
-    if S_var is not None:
-        for name, make, form in (
-                ("lazy_decay_variant",
-                 lambda: binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W,
-                                              vbar, device=dev, lazy=True), "lazy"),
-                ("fp16_factor_variant",
-                 lambda: binding.ShallowState16(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W,
-                                                vbar, store=torch.float16, rounding="nearest",
-                                                device=dev), "h16")):
-            st2 = make()
-            st2.from_dense(S_var)
-            r2 = run_shallow(st2, inputs, o, warmup, steps, graphs=args.graphs)
-            s2 = sum(ms for ms, _ in r2["step_window_ms"]) / 1e3
-            n2 = sum(n for _, n in r2["step_window_ms"])
-            b2 = sum(step_bytes_per_unit(w, r, form) * units for r in r2["step_r"])
-            variants[name] = {
-                "value": units * steps / r2["elapsed_s"], "unit": "head-steps/s",
-                "ms_per_step": r2["elapsed_s"] * 1e3 / steps,
-                "step_bytes_per_head_step": b2 / n2 / units,
-                "step_avg_launch_us": s2 / n2 * 1e6,
-                "step_achieved_GBs": b2 / s2 / 1e9,
-                "step_frac_of_peak": b2 / s2 / 1e9 / HBM_PEAK_GBS,
-                "compress_avg_us": sum(r2["compress_ms"]) / max(1, len(r2["compress_ms"])) * 1e3}
-            if form == "h16":
-                variants[name]["factors"] = ("kept R columns fp16 (rounded to nearest at every "
-                                             "compression), appended columns fp32, lazy decay")
-            del st2
-            log(f"{name}: {r2['elapsed_s'] * 1e3:.2f} ms for {steps} steps")
-        del S_var
-
-    # staggered per-request schedules: D = 0 (each compression finishes
-    # before the next step) and a merge delay that hides it
-    sched = None
-    if not args.no_variant:
-        sched = []
-        # D = 0; the smallest delay whose batched launch fills every SIMD
-        # once; half a window; the longest the ring allows
-        cap_d = min(w.W - 1, 96 - w.R - w.W)
-        simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
-        d_fill = min(cap_d, -(-simds // (units // w.W)))
-        for D in sorted({0, d_fill, min(cap_d, w.W // 2), cap_d}):
-            if w.R not in (16, 32):
-                break
-            sched.append(run_scheduled(w, S_dense, vbar, inputs, warmup, steps, D, dev))
-            log(f"staggered schedule D={D}: {sched[-1]['ms_per_step'] * 1e3:.2f} us per step")
-
-    # handoff of the converted states (prefill -> decode): pack every
-    # request into one buffer, then unpack it into the slots of a batch
-    handoff = None
-    if not args.no_variant:
-        hst = binding.ShallowState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, vbar,
-                                   device=dev)
-        hst.from_dense(S_dense)
-        sel = torch.arange(w.batch, dtype=torch.int32, device=dev)
-        buf = hst.pack(sel)
-        reps = 20
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for _ in range(reps):
-            hst.pack(sel, buf)
-        ev[1].record()
-        for _ in range(reps):
-            hst.unpack(buf, sel)
-        ev[2].record()
-        torch.cuda.synchronize()
-        nbytes = buf.numel()
-        t_pack = ev[0].elapsed_time(ev[1]) / reps / 1e3
-        t_unpack = ev[1].elapsed_time(ev[2]) / reps / 1e3
-        handoff = {"head_bytes": nbytes // units, "dense_head_bytes": 4 * w.d_k * w.d_v,
-                   "requests": w.batch, "buffer_bytes": nbytes,
-                   "pack_us": t_pack * 1e6, "unpack_us": t_unpack * 1e6,
-                   "pack_GBs": 2 * nbytes / t_pack / 1e9, "unpack_GBs": 2 * nbytes / t_unpack / 1e9}
-        del hst, buf
-        log(f"handoff: pack {t_pack * 1e6:.1f} us, unpack {t_unpack * 1e6:.1f} us for "
-            f"{nbytes / 1e6:.1f} MB")
-
-    # statistics of the converted workload's dense states (the quantities
-    # the pages measure on model states), with the kernel's time
-    stats = None
-    if not args.no_variant:
-        nf = binding.lib().seed_stat_fields()
-        rec = torch.empty(w.batch, w.heads, nf, device=dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        binding.seed_state_stats(S_dense, vbar, w.R, rec)
-        e1.record()
-        torch.cuda.synchronize()
-        r = rec.reshape(units, nf)[:, :len(binding.STAT_FIELDS)].double()
-        med = {f: float(r[:, i].median()) for i, f in enumerate(binding.STAT_FIELDS)}
-        stats = {"kernel_ms": e0.elapsed_time(e1), "units": units,
-                 "median_sink_share": med["sink_share"], "median_top_share": med["top_share"],
-                 "median_abs_cos_vstar_vbar": med["abs_cos_vstar_vbar"],
-                 "median_rank90": med["rank90"], "median_rank99": med["rank99"],
-                 "median_beyond_R_share": med["beyond_R_share"]}
-        log(f"state statistics: {stats['kernel_ms']:.1f} ms for {units} heads")
-
-    dense = None
-    if not args.no_dense:
-        dres = run_dense(w, S_copy, inputs, o, warmup, steps, graphs=args.graphs)
-        d_bytes = dense_bytes_per_unit(w) * units
-        d_avg = dres["elapsed_s"] / steps
-        dense = {"value": units * steps / dres["elapsed_s"], "unit": "head-steps/s",
-                 "bytes_per_head_step": dense_bytes_per_unit(w),
-                 "kernel_avg_us": d_avg * 1e6,
-                 "achieved_GBs": d_bytes / d_avg / 1e9}
-        log(f"dense: {dres['elapsed_s'] * 1e3:.2f} ms")
-
-    if not args.no_cpu:
-        cpu = cpu_baseline(w, cpu_state, cpu_inputs, args.cpu_budget, workers)
+    if snap is not None:
+        cpu = cpu_baseline(spec, snap, args.cpu_budget, args.cpu_dense_budget, workers)
         log(f"cpu oracle: {cpu['value']:.1f} head-steps/s on {workers} processes")
 
-    elapsed = res["elapsed_s"]
-    value = units * steps / elapsed
-    step_total_s = sum(ms for ms, _ in res["step_window_ms"]) / 1e3
-    comp_total_s = sum(res["compress_ms"]) / 1e3
-    step_bytes = sum(step_bytes_per_unit(w, r, "lazy" if args.lazy else "in_place") * units
-                     for r in res["step_r"])
-    n_launch = sum(n for _, n in res["step_window_ms"])
-    assert n_launch == len(res["step_r"])
-    avg_launch_s = step_total_s / n_launch
-    achieved = step_bytes / n_launch / avg_launch_s / 1e9
     copy_gbs = achievable_copy_GBs()
     log(f"plain 2 GiB device copy: {copy_gbs:.0f} GB/s read + write")
-    traffic = None if args.lazy else load_traffic(w)
-    mean_bytes = step_bytes / n_launch / units
+    traffic = load_traffic(w, steps, warmup) if L == w.layers else None
+    achieved = head["step_achieved_GBs"]
 
     out = {
-        "metric": "decode head-steps/s (sink + rank-R state update, whole job incl. compression)",
-        "value": value,
+        "metric": METRIC,
+        "value": head["value"],
         "unit": "head-steps/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": elapsed * 1e3 / steps,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded; no trace or checkpoint)",
-        "config": {"workload": w.name, "rule": w.rule, "requests": w.batch, "heads": w.heads,
-                   "layers_per_launch": 1, "d_k": w.d_k, "d_v": w.d_v, "R": w.R, "W": w.W,
-                   "inputs": "bf16 q/k/v, fp32 gates" if w.in_dtype == torch.bfloat16 else "fp32",
-                   "prefill": w.prefill,
-                   "decay_of_U": "running product (lazy)" if args.lazy else "in place",
-                   "launch": ("hip graphs (one per run of steps, one per compression)" if args.graphs
-                              else "eager (one launch per kernel)")},
+        "config": {"workload": w.name, "rule": w.rule, "layers": L, "requests": w.batch,
+                   "heads": w.heads, "heads_per_launch": spec.units,
+                   "heads_total": L * spec.units, "d_k": w.d_k, "d_v": w.d_v, "R": w.R,
+                   "W": w.W, "inputs": "bf16 q/k/v, fp32 gates" if spec.in_dtype_name == "bf16"
+                   else "fp32", "prefill": w.prefill, "decay_of_U": "in place",
+                   "schedule": "layer l compresses every W steps, first window W - floor(l W / L)",
+                   "launch": "one HIP graph per bench step (the layers' step launches) and one "
+                             "for its compressions, replayed after a settle pass",
+                   "resident_factor_bytes": L * spec.units * 4 * (w.d_k + w.d_v) * (w.R + w.W)
+                   + L * spec.units * 4 * w.d_k},
         "roofline": {"bound": "hbm", "kernel": "seed_step_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": step_bytes / n_launch,
-                     "avg_launch_us": avg_launch_s * 1e6,
+                     "algorithmic_bytes_per_launch": head["step_algorithmic_bytes_per_launch"],
+                     "avg_launch_us": head["step_kernel_avg_us"],
+                     "launches": head["step_launches"],
                      "achievable_copy_GBs": copy_gbs,
                      "frac_of_achievable": achieved / copy_gbs if copy_gbs else None},
         "cpu_baseline": cpu,
-        "breakdown": {"step_kernel_s": step_total_s, "compress_kernel_s": comp_total_s,
-                      "compressions": len(res["compress_ms"]),
-                      "compress_avg_us": (comp_total_s / max(1, len(res["compress_ms"]))) * 1e6,
-                      "step_bytes_per_head_step": mean_bytes,
-                      "step_only_head_steps_per_s": units * n_launch / step_total_s,
-                      "wall_s": res["wall_s"]},
+        "breakdown": {k: head[k] for k in ("step_kernel_avg_us", "step_bytes_per_head_step",
+                                           "step_only_head_steps_per_s", "compressions",
+                                           "compress_avg_us", "compress_share_of_time",
+                                           "compressions_per_layer_step")},
+        "settle": head["settle"],
         "dense_baseline": dense,
-        "lazy_decay_variant": variants.get("lazy_decay_variant"),
-        "fp16_factor_variant": variants.get("fp16_factor_variant"),
-        "conversion": {"kernel": "compress_wave_kernel (conversion instance)",
-                       "ms": CONVERSION_MS.get("ms"), "heads": units,
-                       "us_per_head": CONVERSION_MS.get("ms", 0.0) * 1e3 / units,
+        "speedup_over_dense": head["value"] / dense["value"] if dense else None,
+        "lazy_decay_variant": results.get("lazy"),
+        "fp16_factor_variant": results.get("h16"),
+        "conversion": {"kernel": "compress_wave_kernel (conversion instance)", "ms": conv_ms,
+                       "heads": L * spec.units,
+                       "us_per_head": conv_ms * 1e3 / (L * spec.units) if conv_ms else None,
                        "what": "end-of-prefill sink split and rank-R truncation of every head "
-                               "(C C^T by MFMA, Householder, multisection, inverse iteration; "
-                               "once per request)"},
-        "staggered_schedule_variants": sched,
+                               "(once per request)"},
         "handoff": handoff,
         "state_stats": stats,
+        "workloads": subs,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -372,6 +372,22 @@ seed_status dense_decode_step(int rule, int batch, int heads, int d_k, int d_v, 
  */
 seed_status seed_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/*
+ * seed_workspace_bytes -- bytes of caller-provided device workspace that the
+ * compressions (seed_compress, seed_compress_lazy, seed_compress_h16,
+ * seed_compress_sched) and the conversion (seed_state_from_dense) need for
+ * `batch` requests of `heads` heads of shape d_k x d_v, capacity cap = R + W
+ * and rank R.  The compression every W steps and the end-of-prefill
+ * conversion (SEED figures and tables, Fig. 1 (a) and (b) captions) run in
+ * one workgroup per (request, head) that keeps every intermediate (Gram
+ * matrices, the small eigenproblem, the rotation) in LDS and registers, so
+ * this is 0 for every shape these calls accept and none of them takes a
+ * workspace argument.  Returns (size_t)-1 for a shape they reject
+ * (non-positive sizes, an unsupported head shape, R > cap, cap above the
+ * compiled capacity or R above 32).
+ */
+size_t seed_workspace_bytes(int batch, int heads, int d_k, int d_v, int cap, int R);
+
 /* Static text for a status code. */
 const char *seed_status_string(int status);
 

@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.seed_handoff_head_bytes.argtypes = [i, i, i, i]
     L.seed_handoff_head_bytes.restype = ctypes.c_size_t
     L.seed_stream_copy.argtypes = [p, p, ctypes.c_size_t, p]
+    L.seed_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.seed_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("seed_decode_step", "seed_decode_step_lazy", "seed_compress", "seed_compress_lazy",
                "seed_state_from_dense", "dense_decode_step", "seed_decode_step_h16",
                "seed_compress_h16", "seed_round_factors", "seed_pack_states",
@@ -235,6 +237,16 @@ def dense_decode_step(rule: str, S, q, k, v, g, beta, o, stream=None) -> None:
                                  _in_dtype(q, k, v), _ptr(g), _ptr(beta), _ptr(o),
                                  _stream(stream, S.device.index))
     _check("dense_decode_step", st)
+
+
+def workspace_bytes(batch: int, heads: int, d_k: int, d_v: int, cap: int, R: int) -> int:
+    """Device workspace the compressions and the conversion need (see
+    include/seed.h); raises for a shape they reject."""
+    n = int(lib().seed_workspace_bytes(batch, heads, d_k, d_v, cap, R))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError(f"seed_workspace_bytes: shape rejected (batch={batch} heads={heads} "
+                         f"d_k={d_k} d_v={d_v} cap={cap} R={R})")
+    return n
 
 
 def stream_copy(src, dst, stream=None) -> None:
@@ -424,17 +436,30 @@ def seed_state_stats(S, vbar, R: int, rec, spec_S=None, spec_C=None, stream=None
     _check("seed_state_stats", st)
 
 
+def _first_window(W: int, first_window) -> int:
+    fw = W if first_window is None else int(first_window)
+    if not 1 <= fw <= W:
+        raise ValueError(f"first_window must lie in 1 .. W = {W} (got {fw})")
+    return fw
+
+
 class ShallowState:
     """Device tensors of one layer's shallow states plus the column count r.
 
     a [B, H, d_k], U [B, H, R+W, d_k], V [B, H, R+W, d_v] (fp32, zeroed) and the
-    shared vbar [H, d_v].  `step` advances r, `compress` resets it to R when
-    all R + W columns are in use.
+    shared vbar [H, d_v].  `step` advances r; `step_and_maybe_compress`
+    compresses when r reaches `limit`: R + first_window for the first window
+    after a conversion, R + W after that.  A first window shorter than W puts
+    this layer's compressions on another phase than those of layers that
+    start with a full one (the pages compress every W steps; at which step a
+    layer's cycle starts is the engine's choice).
     """
 
     def __init__(self, rule: str, batch: int, heads: int, d_k: int, d_v: int, R: int, W: int,
-                 vbar: torch.Tensor, device="cuda", lazy: bool = False):
+                 vbar: torch.Tensor, device="cuda", lazy: bool = False, first_window=None):
         self.rule, self.R, self.W, self.lazy = rule, R, W, lazy
+        self.first_window = _first_window(W, first_window)
+        self.limit = R + W
         self.batch, self.heads, self.d_k, self.d_v = batch, heads, d_k, d_v
         f32 = torch.float32
         self.a = torch.zeros(batch, heads, d_k, device=device, dtype=f32)
@@ -455,6 +480,7 @@ class ShallowState:
         if self.lazy:
             self.gam.fill_(1.0)
         self.r = self.R
+        self.limit = self.R + self.first_window
 
     def step(self, q, k, v, g, beta, o, stream=None) -> None:
         if self.lazy:
@@ -481,12 +507,18 @@ class ShallowState:
         return _bound_step(lib().seed_decode_step, "seed_decode_step", head, tail, self.rule, B, H,
                            d_k, d_v, o)
 
-    def compress(self, stream=None) -> None:
+    def launch_compress(self, r: int, stream=None) -> None:
+        """The compression of r held columns to R, without touching the
+        host bookkeeping (for a caller that plans r itself, e.g. a graph)."""
         if self.lazy:
-            seed_compress_lazy(self.rule, self.U, self.V, self.gam, self.r, self.R, stream)
+            seed_compress_lazy(self.rule, self.U, self.V, self.gam, r, self.R, stream)
         else:
-            seed_compress(self.U, self.V, self.r, self.R, stream)
+            seed_compress(self.U, self.V, r, self.R, stream)
+
+    def compress(self, stream=None) -> None:
+        self.launch_compress(self.r, stream)
         self.r = min(self.r, self.R)
+        self.limit = self.cap
 
     def pack(self, sel, buf=None, stream=None) -> torch.Tensor:
         """Pack requests `sel` (int32 device tensor) right after a
@@ -507,17 +539,10 @@ class ShallowState:
             raise RuntimeError("unpack needs the batch at r = R (aligned schedule)")
         seed_unpack_states(buf, self.a, self.U, self.V, self.R, slots, stream)
 
-    def true_U(self) -> torch.Tensor:
-        """U at true scale (Diag(gam) U~ in the lazy form); a new tensor when lazy."""
-        if not self.lazy:
-            return self.U
-        gs = self.gam if self.rule == "kda" else self.gam[..., None]
-        return self.U * gs[:, :, None, :]
-
     def step_and_maybe_compress(self, q, k, v, g, beta, o, stream=None) -> bool:
-        """One decode step; compress afterwards when all R + W columns are held."""
+        """One decode step; compress afterwards when the window is full."""
         self.step(q, k, v, g, beta, o, stream)
-        if self.r >= self.cap:
+        if self.r >= self.limit:
             self.compress(stream)
             return True
         return False
@@ -535,10 +560,12 @@ class ShallowState16:
 
     def __init__(self, rule: str, batch: int, heads: int, d_k: int, d_v: int, R: int, W: int,
                  vbar: torch.Tensor, store=torch.float16, rounding: str = "nearest",
-                 seed: int = 0, device="cuda"):
+                 seed: int = 0, device="cuda", first_window=None):
         if store not in _STORE:
             raise ValueError("store must be torch.bfloat16 or torch.float16")
         self.rule, self.R, self.W, self.store = rule, R, W, store
+        self.first_window = _first_window(W, first_window)
+        self.limit = R + W
         self.rounding, self.seed, self.epoch = rounding, int(seed), 0
         self.batch, self.heads, self.d_k, self.d_v = batch, heads, d_k, d_v
         f32 = torch.float32
@@ -566,6 +593,7 @@ class ShallowState16:
         self.epoch += 1
         self.gam.fill_(1.0)
         self.r = R
+        self.limit = R + self.first_window
 
     def step(self, q, k, v, g, beta, o, stream=None) -> None:
         seed_decode_step_h16(self.rule, self.a, self.Uk, self.Vk, self.Uw, self.Vw, self.gam,
@@ -581,12 +609,18 @@ class ShallowState16:
         return _bound_step(lib().seed_decode_step_h16, "seed_decode_step_h16", head, tail,
                            self.rule, B, H, d_k, d_v, o, (_STORE[self.store],))
 
-    def compress(self, stream=None) -> None:
-        if self.r > self.R:
-            seed_compress_h16(self.rule, self.Uk, self.Vk, self.Uw, self.Vw, self.gam, self.r,
+    def launch_compress(self, r: int, stream=None) -> None:
+        """The compression of r held columns into the kept columns with the
+        next epoch's words, without touching r (see ShallowState)."""
+        if r > self.R:
+            seed_compress_h16(self.rule, self.Uk, self.Vk, self.Uw, self.Vw, self.gam, r,
                               self.rounding, self.seed, self.epoch, stream)
             self.epoch += 1
+
+    def compress(self, stream=None) -> None:
+        self.launch_compress(self.r, stream)
         self.r = self.R
+        self.limit = self.cap
 
     def pack(self, sel, buf=None, stream=None) -> torch.Tensor:
         """Pack requests `sel` right after a compression (see ShallowState.pack)."""
@@ -605,18 +639,10 @@ class ShallowState16:
             raise RuntimeError("unpack needs the batch at r = R (aligned schedule)")
         seed_unpack_states(buf, self.a, self.Uk, self.Vk, self.R, slots, stream)
 
-    def true_factors(self):
-        """(U, V) at true scale over the r columns held, fp32 (new tensors)."""
-        w = self.r - self.R
-        U = torch.cat([self.Uk.float(), self.Uw[:, :, :w]], dim=2)
-        V = torch.cat([self.Vk.float(), self.Vw[:, :, :w]], dim=2)
-        gs = self.gam if self.rule == "kda" else self.gam[..., None]
-        return U * gs[:, :, None, :], V
-
     def step_and_maybe_compress(self, q, k, v, g, beta, o, stream=None) -> bool:
-        """One decode step; compress afterwards when all R + W columns are held."""
+        """One decode step; compress afterwards when the window is full."""
         self.step(q, k, v, g, beta, o, stream)
-        if self.r >= self.cap:
+        if self.r >= self.limit:
             self.compress(stream)
             return True
         return False
@@ -772,22 +798,3 @@ class ScheduledState:
             self._launch(cur)
         for side in self.sides:
             cur.wait_stream(side)
-
-    def true_factors(self, b: int, h: int):
-        """(U at true scale [d_k, r], V [d_v, r]) of one unit before the next
-        step, fp32 (after join())."""
-        A = self.t - int(self.t_start_host[b])
-        R, W, D = self.R, self.W, self.D
-        c = 0 if A < W + D else (A - D) // W
-        w = max(A, 0) - c * W if A >= 0 else 0
-        sel = c & 1
-        cols_u = [self.KU[sel, b, h]]
-        cols_v = [self.KV[sel, b, h]]
-        if w > 0:
-            slots = [(c * W + i) % (W + D) for i in range(w)]
-            cols_u.append(self.Uw[b, h, slots])
-            cols_v.append(self.Vw[b, h, slots])
-        U = torch.cat(cols_u, 0)
-        V = torch.cat(cols_v, 0)
-        gs = self.gam[b, h] if self.rule == "kda" else self.gam[b, h].reshape(1)
-        return (U * gs[None, :]).T, V.T

@@ -1,6 +1,6 @@
 """Build libseed.so (the gfx950 HIP library) in-tree with hipcc.
 
-    python -m sink_rank_recurrent_amd.build
+    python -m sink_rank_recurrent_amd.build [--incremental]
 
 Compiles every source under csrc/ for gfx950 (in parallel) into
 _build/ at the repository root and links sink_rank_recurrent_amd/libseed.so.
@@ -46,13 +46,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def _stale(src: str, headers: list) -> bool:
+    """True if src's object is missing or older than src or any header."""
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(f) > t for f in [src] + headers)
+
+
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every source (incremental=True: only those whose object is
+    older than the source or any header) and link libseed.so."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
-    jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
+    headers = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    headers.append(os.path.join(ROOT, "include", "seed.h"))
+    todo = [s for s in srcs if _stale(s, headers)] if incremental else srcs
+    jobs = max(1, min(len(todo), 16, os.cpu_count() or 1))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,10 +75,10 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources ({len(todo)} compiled)")
     return LIB
 
 
 if __name__ == "__main__":
-    build()
+    build(incremental="--incremental" in sys.argv[1:])
     sys.exit(0)

@@ -499,6 +499,14 @@ seed_status seed_stream_copy(const void* src, void* dst, size_t bytes, void* str
                                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t seed_workspace_bytes(int batch, int heads, int d_k, int d_v, int cap, int R) {
+  const size_t reject = static_cast<size_t>(-1);
+  if (batch <= 0 || heads <= 0 || (long long)batch * heads > 0x7fffffffLL) return reject;
+  if (!supported_dims(d_k, d_v)) return reject;
+  if (cap <= 0 || cap > seed::kMaxCap || R <= 0 || R > cap || R > 32) return reject;
+  return 0;
+}
+
 const char* seed_status_string(int status) {
   switch (status) {
     case SEED_OK: return "ok";
@@ -513,6 +521,6 @@ const char* seed_status_string(int status) {
 
 const char* seed_last_error(void) { return g_err; }
 
-int seed_abi_version(void) { return 106; }
+int seed_abi_version(void) { return 107; }
 
 }  // extern "C"

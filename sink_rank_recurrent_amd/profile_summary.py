@@ -2,8 +2,9 @@
 
     python -m sink_rank_recurrent_amd.profile_summary trace <kernel_stats.csv> <kernel_trace.csv> \
         --command "<the rocprofv3 command>" --out profiles/<name>.md
-    python -m sink_rank_recurrent_amd.profile_summary counters <counter_collection.csv> \
-        --kernel seed_step_kernel --out <file.json> ...
+    python -m sink_rank_recurrent_amd.profile_summary counters --fetch <csv> --write <csv> \
+        --copy-fetch <csv> --copy-write <csv> --bench-json <bench output> --source <kernel> \
+        --commands "..." --out profiles/traffic_<kernel>_<workload>.json
     python -m sink_rank_recurrent_amd.profile_summary pmc <a.csv> [<b.csv> ...] \
         --kernel compress_wave_kernel --units 1024 --command "..." --out profiles/<name>.md
 
@@ -43,7 +44,8 @@ def short(name: str) -> str:
     return name[:110]
 
 
-def trace_summary(stats_csv: str, trace_csv: str, command: str, title: str) -> str:
+def trace_summary(stats_csv: str, trace_csv: str, command: str, title: str,
+                  window=None, window_group: str = "seed_step_kernel (U decayed in place)"):
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
              "| kernel | calls | avg us | total ms | share % |", "|---|---|---|---|---|"]
@@ -62,18 +64,48 @@ def trace_summary(stats_csv: str, trace_csv: str, command: str, title: str) -> s
     for g, d in dur.items():
         merged[g] = {"dispatches": len(d), "avg_us": sum(d) / len(d) / 1e3, "total_ms": sum(d) / 1e6}
         lines.append(f"| {g} | {len(d)} | {sum(d) / len(d) / 1e3:.2f} | {sum(d) / 1e6:.3f} |")
+    if window is not None:
+        # the dispatches [start, start + count) of one group, in launch order
+        # (the benchmark's timed launches of its headline kernel)
+        start, count = window
+        rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+                      for r in csv.DictReader(open(trace_csv))
+                      if re.search(GROUPS[window_group], r["Kernel_Name"]))
+        sel = [e - b for b, e in rows[start:start + count]]
+        if len(sel) != count:
+            raise SystemExit(f"window {start}:{count} beyond the {len(rows)} dispatches")
+        merged["window"] = {"group": window_group, "start": start, "count": count,
+                            "avg_us": sum(sel) / count / 1e3}
+        lines += ["", f"{window_group}, dispatches {start} .. {start + count - 1} in launch "
+                  f"order (the timed launches): {count} dispatches, "
+                  f"avg {sum(sel) / count / 1e3:.2f} us"]
     lines.append("")
     return "\n".join(lines), merged
 
 
-def counter_totals(counter_csv: str, kernel_pat: str):
-    """Per-dispatch sums of each counter over the dispatches of matching kernels."""
+def counter_totals(counter_csv: str, kernel_pat: str, window=None):
+    """Per-dispatch sums of each counter over the dispatches of matching
+    kernels; with window = (start, count) only those dispatches, in
+    dispatch order."""
     per = defaultdict(lambda: defaultdict(float))
     for r in csv.DictReader(open(counter_csv)):
         if not re.search(kernel_pat, r["Kernel_Name"]):
             continue
-        per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+    if window is not None:
+        start, count = window
+        keys = sorted(per)[start:start + count]
+        if len(keys) != count:
+            raise SystemExit(f"window {start}:{count} beyond the {len(per)} dispatches")
+        per = {k: per[k] for k in keys}
     return per
+
+
+def _window(text):
+    if not text:
+        return None
+    a, b = text.split(":")
+    return int(a), int(b)
 
 
 def main() -> int:
@@ -85,6 +117,9 @@ def main() -> int:
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="rocprofv3 kernel trace")
     t.add_argument("--out", required=True)
+    t.add_argument("--window", default=None,
+                   help="START:COUNT -- also average the in-place step kernel over these "
+                        "dispatches in launch order")
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True, help="counter_collection.csv of the FETCH_SIZE run")
     c.add_argument("--write", required=True, help="counter_collection.csv of the WRITE_SIZE run")
@@ -93,8 +128,12 @@ def main() -> int:
     c.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     c.add_argument("--kernel", default=GROUPS["seed_step_kernel (U decayed in place)"])
     c.add_argument("--source", required=True, help="kernel source whose hash is recorded")
-    c.add_argument("--algorithmic-bytes", type=float, required=True,
-                   help="algorithmic bytes per launch of the profiled runs")
+    c.add_argument("--bench-json", required=True,
+                   help="the JSON line bench.py printed in the profiled run: its algorithmic "
+                        "bytes per launch, steps, warm-up steps and layers")
+    c.add_argument("--window", default=None,
+                   help="START:COUNT of the kernel's dispatches to average (default: the "
+                        "bench line's timed launches)")
     c.add_argument("--commands", required=True)
     c.add_argument("--out", required=True)
     m = sub.add_parser("pmc")
@@ -127,19 +166,29 @@ def main() -> int:
         return 0
 
     if args.cmd == "trace":
-        text, merged = trace_summary(args.stats, args.trace, args.command, args.title)
+        text, merged = trace_summary(args.stats, args.trace, args.command, args.title,
+                                     _window(args.window))
         with open(args.out, "w") as f:
             f.write(text)
         print(json.dumps(merged))
         return 0
 
-    def mean_kib(path, pat, name):
-        per = counter_totals(path, pat)
+    def mean_kib(path, pat, name, window=None):
+        per = counter_totals(path, pat, window)
         vals = [d[name] for d in per.values() if name in d]
         return sum(vals) / len(vals), len(vals)
 
-    fetch, nf = mean_kib(args.fetch, args.kernel, "FETCH_SIZE")
-    write, nw = mean_kib(args.write, args.kernel, "WRITE_SIZE")
+    line = None
+    for text in open(args.bench_json).read().splitlines():
+        if text.startswith("{"):
+            line = json.loads(text)
+    if line is None:
+        raise SystemExit(f"no JSON line in {args.bench_json}")
+    L = line["config"]["layers"]
+    window = _window(args.window) or (line["warmup"] * L, line["steps"] * L)
+    fetch, nf = mean_kib(args.fetch, args.kernel, "FETCH_SIZE", window)
+    write, nw = mean_kib(args.write, args.kernel, "WRITE_SIZE", window)
+    algorithmic = line["roofline"]["algorithmic_bytes_per_launch"]
     cf, _ = mean_kib(args.copy_fetch, r"copyBuffer", "FETCH_SIZE")
     cw, _ = mean_kib(args.copy_write, r"copyBuffer", "WRITE_SIZE")
     f_scale = args.copy_bytes / (cf * 1024.0)
@@ -151,8 +200,11 @@ def main() -> int:
            "copy_probe_fetch_KiB": cf, "copy_probe_write_KiB": cw,
            "fetch_scale": f_scale, "write_scale": w_scale,
            "hbm_bytes_per_launch": hbm,
-           "algorithmic_bytes_per_launch": args.algorithmic_bytes,
-           "traffic_over_algorithmic": hbm / args.algorithmic_bytes,
+           "algorithmic_bytes_per_launch": algorithmic,
+           "traffic_over_algorithmic": hbm / algorithmic,
+           "dispatch_window": list(window),
+           "bench_workload": line["config"]["workload"], "bench_layers": L,
+           "bench_steps": line["steps"], "bench_warmup": line["warmup"],
            "kernel_source": os.path.relpath(args.source),
            "kernel_source_sha256_16": src_hash,
            "commands": args.commands}

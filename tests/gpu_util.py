@@ -89,3 +89,49 @@ def dense_prefill(rule, batch, heads, d_k, d_v, vbar, seed, steps, in_dtype, lay
         inp = gpu_inputs(rule, batch, heads, d_k, d_v, vbar, seed, t, in_dtype, layer)
         binding.dense_decode_step(rule, S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o)
     return S
+
+
+# ---------------------------------------------------------------------------
+# Read-back of the lazily decayed forms at true scale.  The stored columns
+# are U~ with U = Diag(gam) U~ (gam one float per unit, or one per key
+# channel for Kimi Delta Attention); the library only marshals them, so the
+# tests apply the scale themselves, in torch on the device.
+
+def _gam_rows(st, gam):
+    return gam if st.rule == "kda" else gam[..., None]
+
+
+def true_U(st: binding.ShallowState) -> torch.Tensor:
+    """U [B, H, cap, d_k] at true scale: st.U itself when decayed in place."""
+    if not st.lazy:
+        return st.U
+    return st.U * _gam_rows(st, st.gam)[:, :, None, :]
+
+
+def true_factors16(st: binding.ShallowState16):
+    """(U, V) of the 16-bit form over the r columns held, fp32, U at true scale."""
+    w = st.r - st.R
+    U = torch.cat([st.Uk.float(), st.Uw[:, :, :w]], dim=2)
+    V = torch.cat([st.Vk.float(), st.Vw[:, :, :w]], dim=2)
+    return U * _gam_rows(st, st.gam)[:, :, None, :], V
+
+
+def sched_true_factors(st: binding.ScheduledState, b: int, h: int):
+    """(U at true scale [d_k, r], V [d_v, r]) of unit (b, h) of a per-request
+    schedule before its next step, fp32 (after st.join()): its kept buffer
+    c & 1 and window column numbers c W .. A - 1 in their ring slots."""
+    A = st.t - int(st.t_start_host[b])
+    R, W, D = st.R, st.W, st.D
+    c = 0 if A < W + D else (A - D) // W
+    w = max(A, 0) - c * W if A >= 0 else 0
+    sel = c & 1
+    cols_u = [st.KU[sel, b, h]]
+    cols_v = [st.KV[sel, b, h]]
+    if w > 0:
+        slots = [(c * W + i) % (W + D) for i in range(w)]
+        cols_u.append(st.Uw[b, h, slots])
+        cols_v.append(st.Vw[b, h, slots])
+    U = torch.cat(cols_u, 0)
+    V = torch.cat(cols_v, 0)
+    gs = st.gam[b, h] if st.rule == "kda" else st.gam[b, h].reshape(1)
+    return (U * gs[None, :]).T, V.T

@@ -20,10 +20,11 @@ def test_exports_every_declared_function():
                           "seed_handoff_head_bytes", "seed_pack_states", "seed_unpack_states",
                           "seed_state_stats", "seed_stat_fields",
                           "seed_decode_step_sched", "seed_compress_sched", "seed_stream_copy",
-                          "seed_status_string", "seed_last_error", "seed_abi_version"}
+                          "seed_status_string", "seed_last_error", "seed_abi_version",
+                          "seed_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.seed_abi_version() == 106
+    assert L.seed_abi_version() == 107
 
 
 def test_status_strings():
@@ -216,3 +217,20 @@ def test_scheduled_state_rejects_bad_batching():
                   ({"side_streams": -1}, 4), ({}, 16)):
         with pytest.raises(ValueError):
             binding.ScheduledState("gdn", 1, 2, 128, 128, 16, 16, D, vbar, [0], **kw)
+
+
+def test_workspace_bytes():
+    """Every compression and conversion keeps its intermediates on chip: the
+    workspace is 0 for every shape they accept, and the query rejects the
+    shapes they reject."""
+    reject = ctypes.c_size_t(-1).value
+    L.seed_workspace_bytes.restype = ctypes.c_size_t
+    for d_k, d_v in ((128, 128), (128, 64), (64, 64)):
+        for cap, R in ((32, 16), (48, 16), (80, 16), (96, 32), (16, 16)):
+            assert L.seed_workspace_bytes(256, 32, d_k, d_v, cap, R) == 0
+    assert binding.workspace_bytes(64, 16, 128, 128, 48, 16) == 0
+    for args in ((0, 1, 128, 128, 48, 16), (1, 1, 128, 100, 48, 16), (1, 1, 128, 128, 97, 16),
+                 (1, 1, 128, 128, 48, 49), (1, 1, 128, 128, 96, 33), (1, 1, 128, 128, 48, 0)):
+        assert L.seed_workspace_bytes(*args) == reject, args
+    with pytest.raises(ValueError):
+        binding.workspace_bytes(1, 1, 128, 100, 48, 16)

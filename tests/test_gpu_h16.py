@@ -36,7 +36,7 @@ import torch
 
 import oracle
 from gpu_util import (TIE_GAP, TOL_READOUT, TOL_STATE_COMPRESS, TOL_STATE_STEP, f64, rel_err,
-                      requires_gpu, state_rel_err)
+                      requires_gpu, state_rel_err, true_factors16)
 from oracle import seed_rounding as rd
 from sink_rank_recurrent_amd import binding
 from sink_rank_recurrent_amd import workloads as wl
@@ -168,7 +168,7 @@ def _h16_state(rule, d_k, d_v, R, W, w0, fmt, seed, rounding="nearest"):
 
 def _state_np(st):
     """(a, U at true scale [n, d_k, r], V [n, d_v, r]) of every unit, fp64."""
-    U, V = st.true_factors()
+    U, V = true_factors16(st)
     return (f64(st.a).reshape(-1, st.d_k), f64(U).reshape(B * H, st.r, st.d_k).transpose(0, 2, 1),
             f64(V).reshape(B * H, st.r, st.d_v).transpose(0, 2, 1))
 
@@ -461,7 +461,7 @@ def test_h16_workload_launch_size(num):
         worst = max(worst, float(e.max()) if e.size else 0.0)
         assert e.size == 0 or e.max() < tol, (t, e)
     ga = f64(st.a.reshape(units, w.d_k)[idx])
-    Ut, Vt = st.true_factors()
+    Ut, Vt = true_factors16(st)
     gU = f64(Ut.reshape(units, st.r, w.d_k)[idx]).transpose(0, 2, 1)
     gV = f64(Vt.reshape(units, st.r, w.d_v)[idx]).transpose(0, 2, 1)
     assert state_rel_err(ga, gU, gV, a, U, V, vb)[ok].max() < tol

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from gpu_util import (TOL_READOUT, TOL_STATE_COMPRESS, TOL_STATE_STEP, f64, inputs_np, make_state,
-                      rel_err, requires_gpu, state_np, state_rel_err)
+                      rel_err, requires_gpu, state_np, state_rel_err, true_U)
 from sink_rank_recurrent_amd import workloads as wl
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -22,7 +22,7 @@ B, H = 4, 8
 
 def _true_state(st, r):
     a = f64(st.a).reshape(-1, st.d_k)
-    U = f64(st.true_U()).reshape(-1, st.cap, st.d_k)[:, :r].transpose(0, 2, 1)
+    U = f64(true_U(st)).reshape(-1, st.cap, st.d_k)[:, :r].transpose(0, 2, 1)
     V = f64(st.V).reshape(-1, st.cap, st.d_v)[:, :r].transpose(0, 2, 1)
     return a, U, V
 
@@ -69,4 +69,4 @@ def test_lazy_matches_in_place_and_oracle(rule, dims, R, W):
     assert state_rel_err(la, lU, lV, ea, eU, eV, vb)[gap_ok].max() < TOL_STATE_COMPRESS
     assert state_rel_err(la, lU, lV, a, Uc, Vc, vb)[gap_ok].max() < TOL_STATE_COMPRESS
     # after the compression the stored columns are at true scale
-    assert torch.equal(lazy.true_U()[:, :, :R], lazy.U[:, :, :R])
+    assert torch.equal(true_U(lazy)[:, :, :R], lazy.U[:, :, :R])

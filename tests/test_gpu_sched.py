@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TIE_GAP, TOL_READOUT, TOL_STATE_COMPRESS, f64, rel_err, requires_gpu
+from gpu_util import (TIE_GAP, TOL_READOUT, TOL_STATE_COMPRESS, f64, rel_err, requires_gpu,
+                      sched_true_factors)
 from oracle import seed_oracle as so
 from oracle import seed_schedule as sc
 from sink_rank_recurrent_amd import binding
@@ -71,7 +72,7 @@ def test_scheduled_run_matches_oracle(rule, dims, W, D, K, NS, R):
         if t in checkpoints:
             st.join()
             torch.cuda.synchronize()
-            gpu_states[t] = {(b, h): [f64(m) for m in st.true_factors(b, h)] + [f64(st.a[b, h])]
+            gpu_states[t] = {(b, h): [f64(m) for m in sched_true_factors(st, b, h)] + [f64(st.a[b, h])]
                              for b in range(B) for h in range(H)}
     st.join()
     torch.cuda.synchronize()
