@@ -20,12 +20,14 @@ true 1/W share per layer, whatever K is.  The compressions of a step run
 after all its layer steps (each before that layer's next step).
 
 Timing.  The inputs of every timed step are drawn beforehand and resident
-in HBM.  Every bench step is captured as two HIP graphs (the L step
-launches; the step's compressions) from the same C-ABI calls; the W warm-up
-steps are replayed first as an untimed settle pass (reported on its own,
-`settle`), then the K timed steps, with HIP events on the launch stream
-before and after each graph, so no event sits between two kernels of a
-graph.  `value` = head-steps (L x requests x heads x K) / the events' time
+in HBM.  The bench steps are captured as HIP graphs from the same C-ABI
+calls: one graph per run of step launches with no compression between them
+(the L launches of one bench step on the staggered stack, W steps of a
+single layer), one per run of compressions.  The W warm-up steps' graphs
+are replayed first as an untimed settle pass (reported on its own,
+`settle`), then the K timed steps' graphs, with a HIP event on the launch
+stream before each graph and after the last, so no event sits between two
+kernels of a graph.  `value` = head-steps (L x requests x heads x K) / the events' time
 from the first timed graph to the end of the last.  The step kernel's
 average launch duration is its graphs' event time / (L K); `roofline`
 divides its algorithmic bytes per launch by that.
@@ -248,66 +250,83 @@ def warm_compress_instances(w, form: str, rs, dev: str) -> None:
     torch.cuda.synchronize()
 
 
+def _segments(pl, lo: int, hi: int):
+    """The bench steps lo .. hi-1 of a plan as alternating runs: ("steps",
+    [(t, l, r), ...]) for every maximal run of step launches with no
+    compression between them, ("compress", [(l, r), ...]) for the
+    compressions that follow it."""
+    segs, cur = [], []
+    for t in range(lo, hi):
+        steps, comps = pl[t]
+        cur += [(t, l, r) for l, r in steps]
+        if comps:
+            segs.append(("steps", cur))
+            segs.append(("compress", comps))
+            cur = []
+    if cur:
+        segs.append(("steps", cur))
+    return segs
+
+
 def run_stack(w, states, inputs, outs, t0: int, n_settle: int, n_timed: int, form: str, dev: str):
     """Capture n_settle + n_timed bench steps (from input step t0) as HIP
-    graphs, replay the first n_settle untimed-for-value (the settle pass),
-    then the n_timed timed ones with events around every graph."""
+    graphs -- one per run of step launches between compressions, one per
+    run of compressions -- replay the settle steps' graphs (the settle pass),
+    then the timed ones with an event on the launch stream before each
+    graph and after the last."""
     import torch
 
     pl, r_end, lim_end = plan(states, n_settle + n_timed)
     warm_compress_instances(w, form, [r for _, comps in pl for _, r in comps], dev)
     fns = [st.bind_step(outs[l]) for l, st in enumerate(states)]
-    graphs = []
-    for i, (steps, comps) in enumerate(pl):
-        t = t0 + i
-        gs = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gs):
-            for l, r in steps:
-                x = inputs[l][t]
-                fns[l](x["q"], x["k"], x["v"], x["g"], x["beta"], r)
-        gc = None
-        if comps:
-            gc = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gc):
-                for l, r in comps:
-                    states[l].launch_compress(r)
-        graphs.append((gs, gc))
+
+    def capture(segs):
+        out = []
+        for kind, items in segs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                if kind == "steps":
+                    for t, l, r in items:
+                        x = inputs[l][t0 + t]
+                        fns[l](x["q"], x["k"], x["v"], x["g"], x["beta"], r)
+                else:
+                    for l, r in items:
+                        states[l].launch_compress(r)
+            out.append((kind, len(items), g))
+        return out
+
+    settle = capture(_segments(pl, 0, n_settle))
+    timed = capture(_segments(pl, n_settle, n_settle + n_timed))
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     s0, s1 = ev(), ev()
     s0.record()
-    for gs, gc in graphs[:n_settle]:
-        gs.replay()
-        if gc is not None:
-            gc.replay()
+    for _, _, g in settle:
+        g.replay()
     s1.record()
-    timed = graphs[n_settle:]
-    ea = [ev() for _ in timed]
-    eb = [ev() for _ in timed]
-    e_end = ev()
-    for i, (gs, gc) in enumerate(timed):
-        ea[i].record()
-        gs.replay()
-        eb[i].record()
-        if gc is not None:
-            gc.replay()
-    e_end.record()
+    marks = [ev() for _ in range(len(timed) + 1)]
+    for i, (_, _, g) in enumerate(timed):
+        marks[i].record()
+        g.replay()
+    marks[-1].record()
     torch.cuda.synchronize()
     for l, st in enumerate(states):
         st.r, st.limit = r_end[l], lim_end[l]
-    step_ms = [ea[i].elapsed_time(eb[i]) for i in range(len(timed))]
-    comp_ms = [eb[i].elapsed_time(ea[i + 1] if i + 1 < len(timed) else e_end)
-               for i in range(len(timed))]
+    step_ms = comp_ms = 0.0
+    for i, (kind, _, _) in enumerate(timed):
+        ms = marks[i].elapsed_time(marks[i + 1])
+        if kind == "steps":
+            step_ms += ms
+        else:
+            comp_ms += ms
     timed_pl = pl[n_settle:]
-    n_comp = sum(len(c) for _, c in timed_pl)
     step_r = [r for steps, _ in timed_pl for _, r in steps]
     comp_r = [r for _, comps in timed_pl for _, r in comps]
-    return {"elapsed_ms": ea[0].elapsed_time(e_end), "step_ms": sum(step_ms),
-            "compress_ms": sum(comp_ms), "compressions": n_comp, "step_r": step_r,
+    return {"elapsed_ms": marks[0].elapsed_time(marks[-1]), "step_ms": step_ms,
+            "compress_ms": comp_ms, "compressions": len(comp_r), "step_r": step_r,
             "compress_r": comp_r, "settle_ms": s0.elapsed_time(s1), "settle_steps": n_settle,
-            "timed_steps": n_timed, "graphs_captured": sum(1 + (gc is not None) for _, gc in graphs),
-            "epochs_before": epochs}
+            "timed_steps": n_timed, "graphs": len(timed)}
 
 
 def summarise(spec, res, form: str, L: int) -> dict:
@@ -334,6 +353,7 @@ def summarise(spec, res, form: str, L: int) -> dict:
         "compress_avg_us": res["compress_ms"] * 1e3 / n_comp if n_comp else None,
         "compress_share_of_time": res["compress_ms"] / res["elapsed_ms"],
         "compressions_per_layer_step": n_comp / (L * res["timed_steps"]),
+        "graphs_replayed": res["graphs"],
         "settle": {"steps": res["settle_steps"],
                    "ms_per_step": (res["settle_ms"] / res["settle_steps"]
                                    if res["settle_steps"] else None)},

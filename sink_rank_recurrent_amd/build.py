@@ -46,13 +46,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _stale(src: str, headers: list) -> bool:
-    """True if src's object is missing or older than src or any header."""
+def _local_includes(path: str, seen: set) -> set:
+    """The repository headers `path` includes, directly or not."""
+    import re
+    for name in re.findall(r'^\s*#include\s+"([^"]+)"', open(path).read(), flags=re.M):
+        dep = os.path.normpath(os.path.join(os.path.dirname(path), name))
+        if os.path.exists(dep) and dep not in seen:
+            seen.add(dep)
+            _local_includes(dep, seen)
+    return seen
+
+
+def _stale(src: str) -> bool:
+    """True if src's object is missing or older than src or a header it includes."""
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if not os.path.exists(obj):
         return True
     t = os.path.getmtime(obj)
-    return any(os.path.getmtime(f) > t for f in [src] + headers)
+    return any(os.path.getmtime(f) > t for f in [src, *_local_includes(src, set())])
 
 
 def build(verbose: bool = True, incremental: bool = False) -> str:
@@ -61,9 +72,7 @@ def build(verbose: bool = True, incremental: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
-    headers = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
-    headers.append(os.path.join(ROOT, "include", "seed.h"))
-    todo = [s for s in srcs if _stale(s, headers)] if incremental else srcs
+    todo = [s for s in srcs if _stale(s)] if incremental else srcs
     jobs = max(1, min(len(todo), 16, os.cpu_count() or 1))
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(_compile, todo))

@@ -47,9 +47,11 @@ def short(name: str) -> str:
 def trace_summary(stats_csv: str, trace_csv: str, command: str, title: str,
                   window=None, window_group: str = "seed_step_kernel (U decayed in place)"):
     rows = list(csv.DictReader(open(stats_csv)))
+    top = 25
     lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+             f"The {min(top, len(rows))} kernels with the most total time, of {len(rows)}:", "",
              "| kernel | calls | avg us | total ms | share % |", "|---|---|---|---|---|"]
-    for r in rows:
+    for r in rows[:top]:
         lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
     # merged groups from the per-dispatch trace

@@ -122,3 +122,22 @@ def test_cpu_worker_and_no_leftover_process(tmp_path):
     assert res["cores"] == 2 and res["value"] > 0 and res["dense_value"] > 0
     assert res["single_thread_value"] == pytest.approx(res["value"] / 2)
     assert res["host_cpus_usable"] >= 1
+
+
+def test_segments_group_step_runs():
+    """Consecutive step launches with no compression between them form one
+    graph; each run of compressions another; every launch appears once, in
+    order."""
+    L, W, R = 36, 32, 16
+    ph = bench.layer_phases(L, W)
+    pl, _, _ = bench.plan([_St(R, W, W - p) for p in ph], 40)
+    segs = bench._segments(pl, 5, 25)
+    launches = [(t, l) for kind, items in segs if kind == "steps" for t, l, _ in items]
+    assert launches == [(t, l) for t in range(5, 25) for l in range(L)]
+    comps = [c for kind, items in segs if kind == "compress" for c in items]
+    assert comps == [c for t in range(5, 25) for c in pl[t][1]]
+    assert all(a[0] != b[0] for a, b in zip(segs, segs[1:]))
+    # one layer: a whole window of W steps is one run
+    pl1, _, _ = bench.plan([_St(R, W, W)], 3 * W)
+    segs1 = bench._segments(pl1, W, 3 * W)
+    assert [(k, len(i)) for k, i in segs1] == [("steps", W), ("compress", 1)] * 2
