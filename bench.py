@@ -17,7 +17,10 @@ first window after the end-of-prefill conversion is W - floor(l W / L)
 steps, every later one W.  So every timed step compresses about L / W
 layers, and any K consecutive timed steps hold the compression work at its
 true 1/W share per layer, whatever K is.  The compressions of a step run
-after all its layer steps (each before that layer's next step).
+after all its layer steps (each before that layer's next step).  An
+untimed pre-roll of W steps (graphs replayed before the settle pass) takes
+every layer past its shortened first window, so every settle and timed
+compression is of the full R + W columns.
 
 Timing.  The inputs of every timed step are drawn beforehand and resident
 in HBM.  The bench steps are captured as HIP graphs from the same C-ABI
@@ -268,15 +271,21 @@ def _segments(pl, lo: int, hi: int):
     return segs
 
 
-def run_stack(w, states, inputs, outs, t0: int, n_settle: int, n_timed: int, form: str, dev: str):
-    """Capture n_settle + n_timed bench steps (from input step t0) as HIP
-    graphs -- one per run of step launches between compressions, one per
-    run of compressions -- replay the settle steps' graphs (the settle pass),
-    then the timed ones with an event on the launch stream before each
-    graph and after the last."""
+def run_stack(w, states, inputs, outs, n_pre: int, n_settle: int, n_timed: int, form: str,
+              dev: str, joins=None, join_bufs=None):
+    """Capture n_pre + n_settle + n_timed bench steps as HIP graphs -- one
+    per run of step launches between compressions, one per run of
+    compressions -- replay the pre-roll's and the settle steps' graphs (the
+    settle pass), then the timed ones with an event on the launch stream
+    before each graph and after the last.  joins: {bench step: int32 slots}
+    -- before its step launch at that bench step, each layer takes the
+    requests of join_bufs[layer] into those slots (seed_join_states, at the
+    column count the plan gives it)."""
     import torch
+    from sink_rank_recurrent_amd import binding
 
-    pl, r_end, lim_end = plan(states, n_settle + n_timed)
+    t0 = 0
+    pl, r_end, lim_end = plan(states, n_pre + n_settle + n_timed)
     warm_compress_instances(w, form, [r for _, comps in pl for _, r in comps], dev)
     fns = [st.bind_step(outs[l]) for l, st in enumerate(states)]
 
@@ -287,6 +296,10 @@ def run_stack(w, states, inputs, outs, t0: int, n_settle: int, n_timed: int, for
             with torch.cuda.graph(g):
                 if kind == "steps":
                     for t, l, r in items:
+                        if joins is not None and t in joins:
+                            st = states[l]
+                            binding.seed_join_states(st.rule, join_bufs[l], st.a, st.U, st.V,
+                                                     st.gam, st.R, r, joins[t])
                         x = inputs[l][t0 + t]
                         fns[l](x["q"], x["k"], x["v"], x["g"], x["beta"], r)
                 else:
@@ -295,11 +308,14 @@ def run_stack(w, states, inputs, outs, t0: int, n_settle: int, n_timed: int, for
             out.append((kind, len(items), g))
         return out
 
-    settle = capture(_segments(pl, 0, n_settle))
-    timed = capture(_segments(pl, n_settle, n_settle + n_timed))
+    pre = capture(_segments(pl, 0, n_pre))
+    settle = capture(_segments(pl, n_pre, n_pre + n_settle))
+    timed = capture(_segments(pl, n_pre + n_settle, n_pre + n_settle + n_timed))
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for _, _, g in pre:
+        g.replay()
     s0, s1 = ev(), ev()
     s0.record()
     for _, _, g in settle:
@@ -320,13 +336,14 @@ def run_stack(w, states, inputs, outs, t0: int, n_settle: int, n_timed: int, for
             step_ms += ms
         else:
             comp_ms += ms
-    timed_pl = pl[n_settle:]
+    timed_pl = pl[n_pre + n_settle:]
     step_r = [r for steps, _ in timed_pl for _, r in steps]
     comp_r = [r for _, comps in timed_pl for _, r in comps]
     return {"elapsed_ms": marks[0].elapsed_time(marks[-1]), "step_ms": step_ms,
             "compress_ms": comp_ms, "compressions": len(comp_r), "step_r": step_r,
             "compress_r": comp_r, "settle_ms": s0.elapsed_time(s1), "settle_steps": n_settle,
-            "timed_steps": n_timed, "graphs": len(timed)}
+            "timed_steps": n_timed, "graphs": len(timed), "pre_roll_steps": n_pre,
+            "compress_columns": sorted(set(comp_r))}
 
 
 def summarise(spec, res, form: str, L: int) -> dict:
@@ -354,6 +371,8 @@ def summarise(spec, res, form: str, L: int) -> dict:
         "compress_share_of_time": res["compress_ms"] / res["elapsed_ms"],
         "compressions_per_layer_step": n_comp / (L * res["timed_steps"]),
         "graphs_replayed": res["graphs"],
+        "pre_roll_steps": res["pre_roll_steps"],
+        "compress_columns": res["compress_columns"],
         "settle": {"steps": res["settle_steps"],
                    "ms_per_step": (res["settle_ms"] / res["settle_steps"]
                                    if res["settle_steps"] else None)},
@@ -361,29 +380,31 @@ def summarise(spec, res, form: str, L: int) -> dict:
 
 
 def run_dense(w, Ss, inputs, outs, t0: int, n_settle: int, n_timed: int) -> dict:
-    """The dense-state baseline over the same layers and inputs, one graph
-    per bench step (the L dense launches), a settle pass first."""
+    """The dense-state baseline over the same layers and inputs: the settle
+    steps and the timed steps captured as one HIP graph each (the L dense
+    launches of every step, in order), the settle graph replayed first."""
     import torch
     from sink_rank_recurrent_amd import binding
 
-    graphs = []
-    for i in range(n_settle + n_timed):
-        t = t0 + i
+    def capture(ts):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for l, S in enumerate(Ss):
-                x = inputs[l][t]
-                binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"],
-                                          outs[l])
-        graphs.append(g)
+            for t in ts:
+                for l, S in enumerate(Ss):
+                    x = inputs[l][t]
+                    binding.dense_decode_step(w.rule, S, x["q"], x["k"], x["v"], x["g"],
+                                              x["beta"], outs[l])
+        return g
+
+    g_settle = capture(range(t0, t0 + n_settle)) if n_settle else None
+    g_timed = capture(range(t0 + n_settle, t0 + n_settle + n_timed))
     torch.cuda.synchronize()
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     e[0].record()
-    for g in graphs[:n_settle]:
-        g.replay()
+    if g_settle is not None:
+        g_settle.replay()
     e[1].record()
-    for g in graphs[n_settle:]:
-        g.replay()
+    g_timed.replay()
     e[2].record()
     torch.cuda.synchronize()
     return {"elapsed_ms": e[1].elapsed_time(e[2]), "settle_ms": e[0].elapsed_time(e[1])}
@@ -611,8 +632,89 @@ def stats_of(w, S, vbar, dev: str) -> dict:
             "median_beyond_R_share": med["beyond_R_share"]}
 
 
+def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, timed, dev,
+                         aligned):
+    """Requests that arrive at different times, on the stack, against the
+    aligned lazily decayed form (`aligned`):
+      * one global phase: an arriving request joins mid-window
+        (seed_join_states) and compresses with the batch -- one request
+        every 8 bench steps, joining every layer;
+      * per-request schedules (seed_decode_step_sched): request b starts at
+        phase b mod W and compresses on its own schedule, the snapshots of
+        D consecutive steps compressed by one launch, D the smallest delay
+        whose launch gives every SIMD of the GPU a unit."""
+    import torch
+    from sink_rank_recurrent_amd import binding
+
+    out = []
+    # one global phase with joins
+    states, _ = make_states(w, "lazy", vbars, Ss, phases, dev)
+    bufs = [st.pack(torch.zeros(1, dtype=torch.int32, device=dev)) for st in states]
+    joins = {t: torch.tensor([(t // 8) % w.batch], dtype=torch.int32, device=dev)
+             for t in range(pre, pre + settle + timed) if t % 8 == 0}
+    res = run_stack(spec, states, inputs, outs, pre, settle, timed, "lazy", dev, joins, bufs)
+    r = summarise(spec, res, "lazy", len(states))
+    n_join = sum(1 for t in joins if t >= pre + settle)
+    out.append({"kind": "one global phase: arriving requests join mid-window "
+                        "(seed_join_states) and compress with the batch",
+                "value": r["value"], "unit": "head-steps/s", "ms_per_step": r["ms_per_step"],
+                "joins_in_timed_steps": n_join, "requests_per_join": 1,
+                "vs_aligned_lazy": r["value"] / aligned["value"] if aligned else None})
+    log(f"{w.name} [global phase + joins]: {r['ms_per_step']:.3f} ms per step")
+    del states, bufs
+    torch.cuda.empty_cache()
+
+    # per-request schedules
+    units = spec.units
+    simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    cap_d = min(w.W - 1, 96 - w.R - w.W)
+    D = min(cap_d, -(-simds // (units // w.W)))
+    t_start = [-(b % w.W) - (w.W + D) for b in range(w.batch)]
+    scheds = []
+    for l, (vbar, S) in enumerate(zip(vbars, Ss)):
+        st = binding.ScheduledState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, D, vbar,
+                                    t_start, device=dev)
+        st.from_dense(S)
+        scheds.append(st)
+    for t in range(pre + settle):
+        for l, st in enumerate(scheds):
+            x = inputs[l][t]
+            st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], outs[l])
+    for st in scheds:
+        st.join()
+        st.pending.clear()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(pre + settle, pre + settle + timed):
+            for l, st in enumerate(scheds):
+                x = inputs[l][t]
+                st.step(x["q"], x["k"], x["v"], x["g"], x["beta"], outs[l])
+        for st in scheds:
+            st.join()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    el = e0.elapsed_time(e1) / 1e3
+    value = len(scheds) * units * timed / el
+    cols = [scheds[0].held_columns(b, t) for t in range(pre + settle, pre + settle + timed)
+            for b in range(w.batch)]
+    out.append({"kind": "per-request schedules (seed_decode_step_sched): request b starts at "
+                        "phase b mod W, the snapshots of D consecutive steps share one "
+                        "compression launch", "D": D, "value": value, "unit": "head-steps/s",
+                "ms_per_step": el * 1e3 / timed, "mean_columns": sum(cols) / len(cols),
+                "vs_aligned_lazy": value / aligned["value"] if aligned else None})
+    log(f"{w.name} [per-request schedules, D = {D}]: {el * 1e3 / timed:.3f} ms per step")
+    del g, scheds
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_workload(w, layers: int, settle: int, timed: int, dev: str, forms, with_dense: bool,
-                 keep_layer0: bool = False):
+                 keep_layer0: bool = False, no_stagger: bool = True):
     """Prefill, convert and time `layers` layers of workload w in every form
     of `forms`, then the dense baseline.  Returns (results by form, dense,
     conversion ms, layer-0 objects for the CPU snapshot / handoff / stats)."""
@@ -620,9 +722,12 @@ def run_workload(w, layers: int, settle: int, timed: int, dev: str, forms, with_
 
     spec = Spec(w)
     phases = layer_phases(layers, w.W)
+    # an untimed pre-roll brings every layer past its first (shortened)
+    # window, so that every settle and timed compression is of R + W columns
+    pre = w.W if layers > 1 else 0
     vbars, Ss = prefill_layers(w, layers, dev)
     log(f"{w.name}: prefilled {layers} layer(s) x {spec.units} units")
-    inputs = make_inputs(w, vbars, settle + timed, dev)
+    inputs = make_inputs(w, vbars, pre + settle + timed, dev)
     outs = [torch.empty(w.batch, w.heads, w.d_v, device=dev) for _ in range(layers)]
     results, conv_ms, layer0 = {}, None, None
     for form in forms:
@@ -635,16 +740,19 @@ def run_workload(w, layers: int, settle: int, timed: int, dev: str, forms, with_
             st0 = copy.copy(states[0])
             st0.a, st0.U, st0.V = states[0].a.clone(), states[0].U.clone(), states[0].V.clone()
             layer0 = {"state": st0, "S": Ss[0].clone(), "vbar": vbars[0],
-                      "inputs": inputs[0][:min(settle + timed, 64)]}
-        res = run_stack(spec, states, inputs, outs, 0, settle, timed, form, dev)
+                      "inputs": inputs[0][:min(pre + settle + timed, 64)]}
+        res = run_stack(spec, states, inputs, outs, pre, settle, timed, form, dev)
         results[form] = summarise(spec, res, form, layers)
         log(f"{w.name} [{form}]: {results[form]['ms_per_step']:.3f} ms per step, "
             f"{results[form]['compressions']} compressions in {timed} timed steps")
         del states
         torch.cuda.empty_cache()
+    if "lazy" in forms and layers > 1 and not no_stagger:
+        results["stagger"] = run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre,
+                                                  settle, timed, dev, results.get("lazy"))
     dense = None
     if with_dense:
-        d = run_dense(w, Ss, inputs, outs, 0, settle, timed)
+        d = run_dense(w, Ss, inputs, outs, pre, settle, timed)
         dense = dense_summary(spec, d, layers, timed)
         log(f"{w.name} [dense]: {dense['ms_per_step']:.3f} ms per step")
     return results, dense, conv_ms, layer0
@@ -709,7 +817,8 @@ def main() -> int:
         f"{warmup} settle steps")
     forms = ["in_place"] if args.no_variant else ["in_place", "lazy", "h16"]
     results, dense, conv_ms, layer0 = run_workload(w, L, warmup, steps, dev, forms,
-                                                   not args.no_dense, keep_layer0=True)
+                                                   not args.no_dense, keep_layer0=True,
+                                                   no_stagger=args.no_variant)
     head = results["in_place"]
 
     handoff = stats = None
@@ -799,12 +908,14 @@ def main() -> int:
         "breakdown": {k: head[k] for k in ("step_kernel_avg_us", "step_bytes_per_head_step",
                                            "step_only_head_steps_per_s", "compressions",
                                            "compress_avg_us", "compress_share_of_time",
-                                           "compressions_per_layer_step")},
+                                           "compressions_per_layer_step", "compress_columns",
+                                           "pre_roll_steps")},
         "settle": head["settle"],
         "dense_baseline": dense,
         "speedup_over_dense": head["value"] / dense["value"] if dense else None,
         "lazy_decay_variant": results.get("lazy"),
         "fp16_factor_variant": results.get("h16"),
+        "staggered_schedule_variants": results.get("stagger"),
         "conversion": {"kernel": "compress_wave_kernel (conversion instance)", "ms": conv_ms,
                        "heads": L * spec.units,
                        "us_per_head": conv_ms * 1e3 / (L * spec.units) if conv_ms else None,

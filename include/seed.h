@@ -133,9 +133,13 @@ seed_status seed_compress(int batch, int heads, int d_k, int d_v, int cap, int r
  * (Lemma 2)"; the caption of Table 2 of the SEED figures and tables has U
  * rescaled at every step, which gam does implicitly), so a, V and o agree
  * with it up to fp32 rounding.  A state from seed_state_from_dense or
- * seed_compress is in this form with gam = 1.  Valid while every product
- * in gam stays a normal fp32 number (above about 1e-37); compress with
+ * seed_compress is in this form with gam = 1; compress with
  * seed_compress_lazy, which resets gam to 1.  gam is read and written.
+ * The product must stay a normal fp32 number, so a step whose product for
+ * a key channel falls below 2^-64 applies it to that row of every held
+ * column (the in-place decay, for that channel) and restarts it at 1; the
+ * represented state is the same, and gates of any size (down to 0) are
+ * valid.
  */
 seed_status seed_decode_step_lazy(int rule, int batch, int heads, int d_k, int d_v, int cap, int r,
                                   float *a, float *U, float *V, float *gam, const float *vbar,
@@ -186,11 +190,14 @@ seed_status seed_compress_lazy(int rule, int batch, int heads, int d_k, int d_v,
  * seed_decode_step_h16 -- seed_decode_step_lazy on the 16-bit form: reads
  * the kept columns (widened exactly) and the r - R appended ones, appends
  * column r (to Uw / Vw at index r - R, fp32) and writes a, gam and o as the
- * lazy step does.  Uk and Vk are only read.  Returns SEED_E_FULL if
- * r == R + W.  store_dtype: SEED_BF16 or SEED_F16.
+ * lazy step does.  Vk is only read; Uk is written only where a decay product
+ * below 2^-64 is folded into a key row (seed_decode_step_lazy), that row of
+ * every kept column then rounded to nearest -- entries at most 2^-64 of
+ * their stored size, which no other term of the state can resolve.
+ * Returns SEED_E_FULL if r == R + W.  store_dtype: SEED_BF16 or SEED_F16.
  */
 seed_status seed_decode_step_h16(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
-                                 int r, float *a, const void *Uk, const void *Vk, float *Uw,
+                                 int r, float *a, void *Uk, const void *Vk, float *Uw,
                                  float *Vw, float *gam, const float *vbar, const void *q,
                                  const void *k, const void *v, int in_dtype, int store_dtype,
                                  const float *g, const float *beta, float *o, void *stream);
@@ -248,7 +255,11 @@ seed_status seed_round_factors(int batch, int heads, int d_k, int d_v, int R, co
  * seed_decode_step_sched -- step t of every request (Lemma 2 as in
  * seed_decode_step_lazy); at A = k W + D it first folds gam into every held
  * column and restarts gam at 1; at (A + 1) mod W = 0 it also stores the new
- * gam in gam_snap.
+ * gam in gam_snap.  A product below 2^-64 is folded in as in
+ * seed_decode_step_lazy, except in the D steps between a snapshot and its
+ * merge (k W <= A < k W + D), where the snapshot's compression may still
+ * read the held columns: there a product below 2^-110 makes the request's
+ * gam NaN, so its read-outs are NaN from then on (D = 0 has no such steps).
  *
  * seed_compress_sched -- compress the units units[0 .. n_units) whose
  * request, at A = t_snap - t_start[b] steps, has taken its snapshot number
@@ -308,6 +319,28 @@ seed_status seed_pack_states(int batch, int heads, int d_k, int d_v, int cap, in
 seed_status seed_unpack_states(int batch, int heads, int d_k, int d_v, int cap, int R,
                                int store_dtype, int n_sel, const int *slot, const void *buf,
                                float *a, void *U, void *V, void *stream);
+
+/*
+ * seed_join_states -- requests that arrive while a batch is mid-window join
+ * its compression phase.  For every slot[i] (an index outside [0, batch)
+ * selects nothing): a and columns 0..R-1 of U and V are written from buf
+ * (the layout of seed_pack_states with fp32 factors, e.g. a request packed
+ * right after its end-of-prefill conversion), columns R..r-1 -- the ones
+ * the batch has appended since its last compression -- are set to zero,
+ * and in the lazily decayed form (gam != NULL, laid out by `rule` as for
+ * seed_decode_step_lazy) the slot's decay product is set to 1.  Zero
+ * columns add nothing to U V^T, so each slot then holds exactly the
+ * handed-over state while sharing the batch's column count r: it steps with
+ * the batch and is compressed with it at the batch's next compression, its
+ * first window being R + W - r steps instead of W.  (Every W steps the
+ * factors are compressed, SEED figures and tables, Fig. 1 (b) caption;
+ * a server takes requests as they arrive, Fig. 8.)  U, V are the fp32
+ * rings [batch][heads][cap][d]; requires 0 < R <= r < cap.  buf is only
+ * read; calls on one batch are ordered by the caller's stream.
+ */
+seed_status seed_join_states(int rule, int batch, int heads, int d_k, int d_v, int cap, int R,
+                             int r, int n_sel, const int *slot, const void *buf, float *a,
+                             float *U, float *V, float *gam, void *stream);
 
 /*
  * seed_state_from_dense -- convert dense states to the shallow form.

@@ -44,9 +44,10 @@ def scheduled_run(rule, a, U, V, vbar, steps, R, W, D):
     of q, k, v, g, beta for this unit) under the schedule above.
 
     Returns (a, U, V, outs, events): the final state (true-scale U), the
-    read-outs, and the events in order: (A, "snapshot", gap) with
-    gap = (s_R - s_{R+1}) / s_1 of the snapshot's content (the truncation is
-    unique only where it is positive), and (A, "merge")."""
+    read-outs, and the events in order: (A, "snapshot", gap, tail) with
+    gap = (s_R - s_{R+1}) / s_1 and tail = s_{R+1} / s_1 of the snapshot's
+    content (the truncation is unique only where gap is positive; where tail
+    is at the rounding level every truncation is as good), and (A, "merge")."""
     if not 0 <= D < W:
         raise ValueError("need 0 <= D < W")
     a, U, V, vbar = (np.asarray(x, np.float64) for x in (a, U, V, vbar))
@@ -63,7 +64,8 @@ def scheduled_run(rule, a, U, V, vbar, steps, R, W, D):
             pend = (L, F, U.shape[-1])
             s = np.linalg.svd(U @ V.T, compute_uv=False)
             gap = (s[R - 1] - s[R]) / s[0] if s.size > R and s[0] > 0 else 1.0
-            events.append((A, "snapshot", float(gap)))
+            tail = s[R] / s[0] if s.size > R and s[0] > 0 else 0.0
+            events.append((A, "snapshot", float(gap), float(tail)))
         if pend is not None and A % W == D:
             L, F, n0 = pend
             U = np.concatenate([L, U[:, n0:]], axis=1)

@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libseed.so")
+# SEED_LIBRARY names another build of the same C ABI (the tests' host-only
+# sanitizer build); by default the in-tree libseed.so
+LIB_PATH = os.environ.get("SEED_LIBRARY") or os.path.join(_PKG, "libseed.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "seed.h")
 
 RULES = {"gdn": 0, "kda": 1, "mamba2": 2}
@@ -72,6 +74,7 @@ def lib() -> ctypes.CDLL:
     L.seed_handoff_head_bytes.argtypes = [i, i, i, i]
     L.seed_handoff_head_bytes.restype = ctypes.c_size_t
     L.seed_stream_copy.argtypes = [p, p, ctypes.c_size_t, p]
+    L.seed_join_states.argtypes = [i, i, i, i, i, i, i, i, i, p, p, p, p, p, p, p]
     L.seed_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.seed_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("seed_decode_step", "seed_decode_step_lazy", "seed_compress", "seed_compress_lazy",
@@ -79,7 +82,7 @@ def lib() -> ctypes.CDLL:
                "seed_compress_h16", "seed_round_factors", "seed_pack_states",
                "seed_unpack_states", "seed_state_stats", "seed_stat_fields",
                "seed_decode_step_sched", "seed_compress_sched", "seed_stream_copy",
-               "seed_abi_version"):
+               "seed_abi_version", "seed_join_states"):
         getattr(L, fn).restype = ctypes.c_int
     L.seed_status_string.argtypes = [i]
     L.seed_status_string.restype = ctypes.c_char_p
@@ -416,6 +419,26 @@ def seed_unpack_states(buf, a, U, V, R: int, slots, stream=None) -> None:
     _check("seed_unpack_states", st)
 
 
+def seed_join_states(rule: str, buf, a, U, V, gam, R: int, r: int, slots, stream=None) -> None:
+    """Write packed fp32 requests into batch slots `slots` of a batch that
+    holds r columns, zeroing its columns R..r-1 and (gam given) setting
+    its decay product to 1; see include/seed.h."""
+    n_sel = slots.shape[0]
+    B, H, cap, d_k = U.shape
+    d_v = V.shape[-1]
+    _need(a, "a", (B, H, d_k), _F32)
+    _need(U, "U", (B, H, cap, d_k), _F32)
+    _need(V, "V", (B, H, cap, d_v), _F32)
+    _need(slots, "slots", (n_sel,), (torch.int32,))
+    if gam is not None:
+        _need(gam, "gam", _gam_shape(rule, B, H, d_k), _F32)
+    _need(buf, "buf", (n_sel * H * handoff_head_bytes(d_k, d_v, R),), (torch.uint8,))
+    st = lib().seed_join_states(RULES[rule], B, H, d_k, d_v, cap, int(R), int(r), n_sel,
+                                _ptr(slots), _ptr(buf), _ptr(a), _ptr(U), _ptr(V), _ptr(gam),
+                                _stream(stream, a.device.index))
+    _check("seed_join_states", st)
+
+
 STAT_FIELDS = ("e_state", "e_sink", "e_content", "sink_share", "top_share",
                "abs_cos_vstar_vbar", "rank90", "rank99", "beyond_R_share")
 
@@ -538,6 +561,15 @@ class ShallowState:
         if self.r != self.R:
             raise RuntimeError("unpack needs the batch at r = R (aligned schedule)")
         seed_unpack_states(buf, self.a, self.U, self.V, self.R, slots, stream)
+
+    def join(self, buf, slots, stream=None) -> None:
+        """Requests packed in `buf` (fp32, seed_pack_states' layout) join the
+        batch in slots `slots` mid-window: they hold r columns from now on
+        (the ones beyond R zero) and compress with the batch."""
+        if not self.R <= self.r < self.cap:
+            raise RuntimeError("join needs R <= r < R + W (compress a full window first)")
+        seed_join_states(self.rule, buf, self.a, self.U, self.V, self.gam, self.R, self.r, slots,
+                         stream)
 
     def step_and_maybe_compress(self, q, k, v, g, beta, o, stream=None) -> bool:
         """One decode step; compress afterwards when the window is full."""

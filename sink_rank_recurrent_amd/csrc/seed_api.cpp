@@ -192,7 +192,7 @@ seed_status seed_compress_lazy(int rule, int batch, int heads, int d_k, int d_v,
 }
 
 seed_status seed_decode_step_h16(int rule, int batch, int heads, int d_k, int d_v, int R, int W,
-                                 int r, float* a, const void* Uk, const void* Vk, float* Uw,
+                                 int r, float* a, void* Uk, const void* Vk, float* Uw,
                                  float* Vw, float* gam, const float* vbar, const void* q,
                                  const void* k, const void* v, int in_dtype, int store_dtype,
                                  const float* g, const float* beta, float* o, void* stream) {
@@ -212,7 +212,7 @@ seed_status seed_decode_step_h16(int rule, int batch, int heads, int d_k, int d_
   SEED_PTR(vbar);
   return device_status(
       fn, seed::launch_step(rule, in_dtype == SEED_BF16, store_fmt_of(store_dtype), batch, heads,
-                            d_k, d_v, W, r, R, a, Uw, Vw, static_cast<const uint16_t*>(Uk),
+                            d_k, d_v, W, r, R, a, Uw, Vw, static_cast<uint16_t*>(Uk),
                             static_cast<const uint16_t*>(Vk), gam, vbar, q, k, v, g, beta, o,
                             static_cast<hipStream_t>(stream)));
 }
@@ -322,6 +322,34 @@ seed_status seed_unpack_states(int batch, int heads, int d_k, int d_v, int cap, 
                                float* a, void* U, void* V, void* stream) {
   return handoff("seed_unpack_states", false, batch, heads, d_k, d_v, cap, R, store_dtype, n_sel,
                  slot, a, U, V, const_cast<void*>(buf), stream);
+}
+
+seed_status seed_join_states(int rule, int batch, int heads, int d_k, int d_v, int cap, int R,
+                             int r, int n_sel, const int* slot, const void* buf, float* a,
+                             float* U, float* V, float* gam, void* stream) {
+  const char* fn = "seed_join_states";
+  seed_status st = check_units(fn, batch, heads, d_k, d_v);
+  if (st != SEED_OK) return st;
+  if (rule != SEED_RULE_GDN && rule != SEED_RULE_KDA && rule != SEED_RULE_MAMBA2)
+    return fail(SEED_E_ARG, "%s: unknown rule %d", fn, rule);
+  if (R <= 0 || r < R || r >= cap || n_sel < 0)
+    return fail(SEED_E_SHAPE, "%s: need 0 < R <= r < cap and n_sel >= 0 (got R=%d r=%d cap=%d "
+                "n_sel=%d)", fn, R, r, cap, n_sel);
+  if (cap > seed::kMaxCap)
+    return fail(SEED_E_UNSUPPORTED, "%s: capacity %d above %d", fn, cap, seed::kMaxCap);
+  if ((long long)n_sel * heads > 0x7fffffffLL)
+    return fail(SEED_E_SHAPE, "%s: n_sel * heads exceeds the grid limit", fn);
+  if (n_sel == 0) return ok();
+  SEED_PTR(slot);
+  SEED_PTR(buf);
+  SEED_PTR(a);
+  SEED_PTR(U);
+  SEED_PTR(V);
+  if (gam != nullptr) SEED_PTR(gam);
+  const int gam_len = gam == nullptr ? 0 : (rule == SEED_RULE_KDA ? d_k : 1);
+  return device_status(fn, seed::launch_join(batch, heads, d_k, d_v, cap, R, r, gam_len, n_sel,
+                                             slot, buf, a, U, V, gam,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int seed_stat_fields(void) { return seed::stat_fields(); }
@@ -521,6 +549,6 @@ const char* seed_status_string(int status) {
 
 const char* seed_last_error(void) { return g_err; }
 
-int seed_abi_version(void) { return 107; }
+int seed_abi_version(void) { return 109; }
 
 }  // extern "C"

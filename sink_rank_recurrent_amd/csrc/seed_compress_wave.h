@@ -10,8 +10,9 @@
 // and U' V'^T is the truncation of U V^T to its R largest singular values.
 // Phases:
 //   A  Gram matrices U^T U and V^T V by v_mfma_f32_16x16x4f32;
-//   B  Cholesky of the column-equilibrated U^T U (D^-1 U^T U D^-1 = R~^T R~,
-//      R_U = R~ D), thread t owning column t;
+//   B  Cholesky with diagonal pivoting of the column-equilibrated U^T U
+//      (P^T D^-1 U^T U D^-1 P = R~^T R~ over the kept columns, R_U = R~ D),
+//      thread t owning column t;
 //   C  H = R~ (D V^T V D) R~^T by two in-place MFMA products;
 //   D  Householder reduction of H to a tridiagonal T, thread t owning
 //      column t of H in registers; the reflectors go to LDS rows;
@@ -20,7 +21,8 @@
 //      re-orthogonalised inside runs of close eigenvalues, then one modified
 //      Gram-Schmidt pass;
 //   G  back-transform through the reflectors (X_R = Q Y);
-//   H  P2 = D R~^T X_R (MFMA) and T' = D^-1 R~^-1 X_R (back substitution);
+//   H  P2 = D R~^T X_R (MFMA) and T' = D^-1 P R~^-1 X_R (back substitution
+//      in pivot order);
 //   I  U' = U T' and V' = V P2 by MFMA, written in place.
 // Every LDS offset is a compile-time constant, so accesses use immediate
 // offsets and 16-byte vector forms.  With one wave the workgroup barriers
@@ -38,8 +40,12 @@ namespace wave {
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr float kEps = 1.1920928955078125e-7f;   // 2^-23
-constexpr float kPivTol = 1e-5f;
-constexpr float kMinNormal = 1.17549435e-38f;      // smallest normal fp32                   // dependent-column threshold (relative)
+// Dependent-column threshold of the pivoted Cholesky (relative to the unit
+// diagonal of the equilibrated Gram): the columns left when the largest
+// remaining diagonal is at most this have parts orthogonal to the kept ones
+// below sqrt(kPivTol) = 3.2e-4 of their norms, and are dropped.
+constexpr float kPivTol = 1e-7f;
+constexpr float kMinNormal = 1.17549435e-38f;      // smallest normal fp32
 // Eigenvalues closer than kClusterTol |T| form a run whose vectors are
 // computed one after another, each re-orthogonalised against the earlier
 // ones of its run.
@@ -97,6 +103,27 @@ __device__ __forceinline__ bool block_all(bool p, float* red, int slot) {
     return __all(p);
   } else {
     return block_reduce<NW>(p ? 1.f : 0.f, MinOp(), red, slot) > 0.5f;
+  }
+}
+
+// The lowest thread of the workgroup whose predicate holds, returned to
+// every thread (NTH if there is none).  With two waves the per-wave
+// candidates meet in slot 7 of `red`, separated from its next use by a
+// barrier of the surrounding loop.
+template <int NW>
+__device__ __forceinline__ int block_first(bool p, float* red) {
+  const unsigned long long b = __ballot(p);
+  const int w = threadIdx.x >> 6;
+  const int mine = b ? 64 * w + __builtin_ctzll(b) : 64 * NW;
+  if constexpr (NW == 1) {
+    return mine;
+  } else {
+    if ((threadIdx.x & 63) == 0) red[7 * NW + w] = __int_as_float(mine);
+    __syncthreads();
+    int best = __float_as_int(red[7 * NW]);
+#pragma unroll
+    for (int i = 1; i < NW; ++i) best = min(best, __float_as_int(red[7 * NW + i]));
+    return best;
   }
 }
 
@@ -178,7 +205,8 @@ struct Lay {
   // columns of the rows of RB (never read or written otherwise) when they
   // hold 128 entries, else in a region of its own
   static constexpr bool GS_PAD = !NO_RB && 4 * NMAX >= 128;
-  static constexpr int GS = STA + RMAX;
+  static constexpr int PIV = STA + RMAX;           // [NMAX] column of each Cholesky step (int)
+  static constexpr int GS = PIV + NMAX;
   static constexpr int RED = GS + (GS_PAD ? 0 : 128);   // [8][NW] cross-wave partials
   static constexpr int MISC = RED + 8 * NW + (8 * NW) % 4;
   static constexpr int TOTAL = MISC + 4;
@@ -348,35 +376,6 @@ __device__ __forceinline__ bool live_row(int i, int j) {
   else return (i | 7) > j;
 }
 
-// B, one column: thread t owns column t of the Schur complement in g, gj is
-// its entry j (= G~[j][t]) and piv the pivot G~[j][j].  Writes row j of R~
-// (RB[t LDN + j] = R~[j][t]) and 1/R~[j][j], then removes the rank-one term.
-template <int NMAX, bool STATIC>
-__device__ __forceinline__ void chol_step(float (&g)[NMAX], int j, float gj, float piv, int t,
-                                          bool act, float* RB, float* WB, float* IRD) {
-  constexpr int LDN = NMAX + 4;
-  const bool ok = piv > kPivTol;
-  const float rp = ok ? frsq(piv) : 0.f;
-  const float r = (t > j) ? gj * rp : 0.f;
-  if (act) {
-    RB[t * LDN + j] = (t == j) ? piv * rp : r;
-    WB[t] = r;
-  }
-  if (t == j) IRD[j] = rp;
-  __syncthreads();
-  // every read is issued before the first use
-  float wr[NMAX];
-  load_row<NMAX>(WB, wr);
-#pragma unroll
-  for (int b = 0; b < NMAX / 8; ++b) {
-    if (live_row<STATIC>(8 * b + 7, j)) {
-#pragma unroll
-      for (int i = 8 * b; i < 8 * b + 8; ++i)
-        if (live_row<STATIC>(i, j)) g[i] = fmaf(-wr[i], r, g[i]);
-    }
-  }
-}
-
 // D, one Householder step k: thread t owns column t of H in h, hk is
 // H[t][k], alpha = H[k+1][k], dkk = H[k][k].  Records T's row k and the
 // reflector (row k of G), then H <- H - v w^T - w v^T on the rows > k (rows
@@ -510,6 +509,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   float* const LAM = sm + L::LAM;
   int* const RNK = reinterpret_cast<int*>(sm + L::RNK);
   int* const STA = reinterpret_cast<int*>(sm + L::STA);
+  int* const PIV = reinterpret_cast<int*>(sm + L::PIV);
   float* const RED = sm + L::RED;
   // entry i of the staged decay product
   auto gs_at = [=](int i) -> float* {
@@ -606,52 +606,81 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     gram<NMAX, NW, DK, false, FMT, KR>(ucol, Ukh, n, G, nullptr, gamh, gam_per_row);
     __syncthreads();
     if (act) {
+      // a column whose squared norm is below the normal fp32 range (norm
+      // under 1.1e-19: decayed to nothing) is taken as dependent; its
+      // reciprocal square root would read the subnormal as zero
       const float gtt = G[t * LDN + t];
-      const bool pos = t < n && gtt > 0.f;
+      const bool pos = t < n && gtt >= kMinNormal;
       DVs[t] = pos ? fsqrt(gtt) : 0.f;
       IDV[t] = pos ? frsq(gtt) : 0.f;
     }
     __syncthreads();
     float g[NMAX];
+    float dg;   // this column's own diagonal entry of the Schur complement
     {
       const float it = act ? IDV[t] : 0.f;
       // the scale d_t^-1 d_i^-1 is one product for both (i, t) and (t, i), so
       // the columns stay exactly symmetric through the Cholesky
   #pragma unroll
       for (int i = 0; i < NMAX; ++i) g[i] = act ? G[i * LDN + t] * (it * IDV[i]) : 0.f;
+      dg = (act && t < n) ? G[t * LDN + t] * (it * it) : 0.f;
     }
     __syncthreads();
     // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
     gram<NMAX, NW, DV_, true, FMT, KR>(vcol, Vkh, n, G, DVs, nullptr, false);
 
-    // @phase B: Cholesky of the equilibrated U^T U, thread t owning column t
-    if constexpr (NW == 1) {
-      // one wave: fully unrolled, so g[j] is a fixed register; the Schur
-      // complement is symmetric, so it is this column's copy of G~[j][t]
-  #pragma clang loop unroll(full)
-      for (int j = 0; j < NMAX; ++j) {
-        if (j < n) {
-          const float gj = g[j];
-          const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gj), j));
-          chol_step<NMAX, true>(g, j, gj, piv, t, act, RB, WB, IRD);
-        }
-      }
-    } else {
-      for (int j = 0; j < n; ++j) {
-        if (t == j) {
+    // @phase B: Cholesky with diagonal pivoting of the equilibrated U^T U,
+    // thread t owning column t (g) and its own diagonal entry (dg).  Step j
+    // takes the unprocessed column p with the largest remaining diagonal
+    // (the lowest such t): every multiplier is then at most 1 in size, so
+    // a near-dependent column cannot blow the factor up however badly the
+    // columns are conditioned.  It stops when that diagonal is at most
+    // kPivTol.  Row j of R~ is kept by original column,
+    // RB[t LDN + j] = R~[j][t] (0 for the columns taken before), with
+    // IRD[j] = 1 / R~[j][p] and PIV[j] = p; rows from `kept` on are zero.
+    bool taken = !(act && t < n && IDV[t] > 0.f);
+    int kept = 0;
+    for (int j = 0; j < n; ++j) {
+      const float cand = taken ? -1.f : dg;
+      const float mx = block_reduce<NW>(cand, MaxOp(), RED, 6);
+      if (!(mx > kPivTol)) break;
+      const int p = block_first<NW>(!taken && cand == mx, RED);
+      if (t == p) {
+        taken = true;
   #pragma unroll
-          for (int i = 0; i < NMAX; i += 4)
-            *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
-        }
-        __syncthreads();
-        chol_step<NMAX, false>(g, j, CB[t], CB[j], t, act, RB, WB, IRD);
+        for (int i = 0; i < NMAX; i += 4)
+          *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
       }
+      __syncthreads();
+      const float piv = CB[p];    // = mx: the same arithmetic kept both
+      const float rp = frsq(piv);
+      const float r = (act && !taken) ? CB[t] * rp : 0.f;
+      if (act) {
+        RB[t * LDN + j] = (t == p) ? piv * rp : r;
+        WB[t] = r;
+      }
+      if (t == 0) {
+        IRD[j] = rp;
+        PIV[j] = p;
+      }
+      __syncthreads();
+      float wr[NMAX];
+      load_row<NMAX>(WB, wr);
+  #pragma unroll
+      for (int i = 0; i < NMAX; ++i) g[i] = fmaf(-wr[i], r, g[i]);
+      dg = fmaf(-r, r, dg);
+      kept = j + 1;
     }
-    for (int j = n + t; j < NMAX; j += NTH) IRD[j] = 0.f;
+    for (int j = kept + t; j < NMAX; j += NTH) {
+      IRD[j] = 0.f;
+      PIV[j] = 0;
+    }
+    if (t == 0) MISC[1] = __int_as_float(kept);
     __syncthreads();
 
     // @phase C: Z = R~ G~ in place by column tiles, then H = Z R~^T in place
-    // by row tiles (R~[i][m] = 0 for m < i, so those k-steps are skipped)
+    // by row tiles (R~ is triangular only in pivot order, so no k-step is
+    // skipped)
     {
       constexpr int NT = NMAX / 16;
       const int l = t & 63, w = t >> 6;
@@ -668,7 +697,6 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           const float bv = G[m * LDN + 16 * J + ci];          // G~[m][j]
   #pragma unroll
           for (int I = 0; I < NT; ++I) {
-            if (4 * K + 3 < 16 * I) continue;
             const float av = RB[m * LDN + 16 * I + ci];        // R~[i][m]
             acc[I] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[I], 0, 0, 0);
           }
@@ -691,7 +719,6 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           const float av = G[(16 * I + ci) * LDN + m];        // Z[i][m]
   #pragma unroll
           for (int J = 0; J < NT; ++J) {
-            if (4 * K + 3 < 16 * J) continue;
             const float bv = RB[m * LDN + 16 * J + ci];        // R~[j][m]
             acc[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[J], 0, 0, 0);
           }
@@ -803,15 +830,18 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     // quarter-rate instruction) chains busy without adding passes' work.
     // A shift seeds inverse iteration, whose vector for lam_c picks up
     // lam_{c+1}'s in the ratio (shift error) / (lam_c - lam_{c+1}) per
-    // solve.  The conversion's n = d_k spectrum is graded over many decades
-    // and its gap at the rank-R cut can be far below eps |T|, so there the
-    // stop is relative to the eigenvalue (floored at the noise level of
-    // |T|).  A compression's gaps at the cut sit well above eps |T|, and
-    // the absolute stop saves the passes a small eigenvalue would take.
+    // solve.  The spectrum is graded (pivoted R~ puts the large rows first),
+    // and its leading R eigenvalues can reach far below eps |T|: a dense
+    // state's n = d_k Gram, or a window whose keys decay to nothing in some
+    // channels, where lam_R is 1e-9 |T|.  The stop is therefore relative to
+    // the eigenvalue, floored at kEigFloor eps |T| (a direction of content
+    // below sqrt(kEigFloor eps) of the largest one).  An absolute stop at a
+    // few eps |T| put such a shift above its eigenvalue by orders of
+    // magnitude, and lost about sqrt(eps) of the content.
     constexpr int NP = 2;
     const float frac = 1.f / (float)(NP * m + 1);
-    const float tol_rel = CONV ? 2.f * kEps : 0.f;
-    const float tol_floor = (CONV ? kEigFloor * kEps : 4.f * kEps) * tnorm + pivmin;
+    const float tol_rel = 2.f * kEps;
+    const float tol_floor = kEigFloor * kEps * tnorm + pivmin;
     // up to 64 rows, T sits in registers (padded rows never count)
     constexpr bool TREG = NMAX <= 64;
     float dr[TREG ? NMAX : 4], er[TREG ? NMAX : 4];
@@ -1084,7 +1114,6 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           f4v acc = f4v{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
           for (int K = 0; K < NMAX / 4; ++K) {
-            if (4 * K > 16 * J + 15) continue;                 // R~[i][j] = 0 for i > j
             const float av = RB[(16 * J + ci) * LDN + 4 * K + kk];   // R~[i][j]
             const float bv = XR[(4 * K + kk) * RMAX + 16 * C + ci];  // X_R[i][c]
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
@@ -1098,27 +1127,32 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       }
     }
     __syncthreads();
+    // the rows of T' that no step reaches (dropped columns) stay zero; y
+    // holds X_R in registers
+    for (int i = 4 * t; i < NMAX * RMAX; i += 4 * NTH)
+      *reinterpret_cast<float4*>(XR + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
     if (w0) {
-      // R~ t = y from the last row up; the lane owning row i broadcasts t_i
-      // to its group and stores t_i / d_i as row i of T'.  The reciprocal
-      // pivots of the lane's own rows are read before the serial chain.
-      float ird[CH], idv[CH];
+      // R11 y = X_R with R11[m][l] = R~[m][PIV[l]], upper triangular in step
+      // order, from the last kept step up: the lane owning row i broadcasts
+      // t_i to its group and stores t_i / d_p as row p = PIV[i] of T'.  The
+      // reciprocal pivots of the lane's own rows are read before the serial
+      // chain, and column PIV[i] of R~ one step ahead.
+      const int kept = __float_as_int(MISC[1]);
+      float ird[CH];
   #pragma unroll
-      for (int s = 0; s < CH; ++s) {
-        ird[s] = IRD[part * CH + s];
-        idv[s] = IDV[part * CH + s];
-      }
-      // column i of R~ (this lane's rows) is read one step ahead
+      for (int s = 0; s < CH; ++s) ird[s] = IRD[part * CH + s];
       float rc[CH], rn[CH];
   #pragma unroll
-      for (int s = 0; s < CH; ++s) rc[s] = RB[(NMAX - 1) * LDN + part * CH + s];
+      for (int s = 0; s < CH; ++s) rc[s] = RB[PIV[NMAX - 1] * LDN + part * CH + s];
   #pragma unroll
       for (int i = NMAX - 1; i >= 0; --i) {
         if (i > 0) {
+          const int pn = PIV[i - 1];
   #pragma unroll
-          for (int s = 0; s < CH; ++s) rn[s] = RB[(i - 1) * LDN + part * CH + s];   // R~[m][i-1]
+          for (int s = 0; s < CH; ++s) rn[s] = RB[pn * LDN + part * CH + s];   // R~[m][PIV[i-1]]
         }
-        if (i < n) {
+        if (i < kept) {
           const int own = i / CH, si = i - (i / CH) * CH;
           const float yi = y[si] * ird[si];
           float ti = (part == own) ? yi : 0.f;
@@ -1128,7 +1162,8 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
             case 2: if constexpr (PARTS > 2) ti = group_bcast<PARTS, 2>(ti); break;
             default: if constexpr (PARTS > 3) ti = group_bcast<PARTS, 3>(ti); break;
           }
-          if (part == own && c < R) XR[i * RMAX + c] = ti * idv[si];
+          const int pi = PIV[i];
+          if (part == own && c < R) XR[pi * RMAX + c] = ti * IDV[pi];
   #pragma unroll
           for (int s = 0; s < CH; ++s) y[s] = fmaf(-rc[s], ti, y[s]);
         }

@@ -12,8 +12,9 @@
 // key channel, d_v floats) is spread over d_v/4 lanes with one 16-byte
 // access each; the workgroup covers 256/(d_v/4) rows at a time and each
 // thread keeps d_k/(256/(d_v/4)) rows in registers, so S is read once and
-// written once.  The two column sums (S^T k, then S'^T q) are combined
-// across row groups through LDS.
+// written once, both non-temporally (a state is not reused before the other
+// layers' states have streamed through).  The two column sums (S^T k, then
+// S'^T q) are combined across row groups through LDS.
 #include "seed_device.h"
 #include "seed_launch.h"
 
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(256) void dense_step_kernel(
 
   float s[RPT][4];
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) load_vec<4>(Sh + (size_t)(rg + RG * m) * DV + lc * 4, s[m]);
+  for (int m = 0; m < RPT; ++m) load_vec_nt<4>(Sh + (size_t)(rg + RG * m) * DV + lc * 4, s[m]);
   float kr[RPT], qr[RPT], gr[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void dense_step_kernel(
   }
 
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) store_vec<4>(Sh + (size_t)(rg + RG * m) * DV + lc * 4, s[m]);
+  for (int m = 0; m < RPT; ++m) store_vec_nt<4>(Sh + (size_t)(rg + RG * m) * DV + lc * 4, s[m]);
 
   // o = S'^T q
   float po[4] = {0.f, 0.f, 0.f, 0.f};

@@ -46,6 +46,34 @@ __device__ __forceinline__ void load_vec(const bf16_t* __restrict__ p, float (&x
   }
 }
 
+// Non-temporal forms of load_vec / store_vec for data that is streamed once
+// per launch (factor columns, dense states): the same 8- or 16-byte
+// accesses, marked so the caches do not keep them for reuse that never
+// comes (a layer's state is not touched again before every other layer's
+// has streamed through).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int N>
+__device__ __forceinline__ void load_vec_nt(const float* __restrict__ p, float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "vector width");
+  if constexpr (N == 4) {
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+  } else {
+    const f32x2 t = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+    x[0] = t.x; x[1] = t.y;
+  }
+}
+template <int N>
+__device__ __forceinline__ void store_vec_nt(float* __restrict__ p, const float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "vector width");
+  if constexpr (N == 4) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+  } else {
+    __builtin_nontemporal_store(f32x2{x[0], x[1]}, reinterpret_cast<f32x2*>(p));
+  }
+}
+
 __device__ __forceinline__ float load_scalar(const float* p) { return *p; }
 __device__ __forceinline__ float load_scalar(const bf16_t* p) { return bf16_bits_to_f32(*p); }
 
@@ -109,6 +137,21 @@ __device__ __forceinline__ void load_vec16(const uint16_t* __restrict__ p, float
   }
 }
 
+// load_vec16 with a non-temporal access (see load_vec_nt).
+template <int FMT, int N>
+__device__ __forceinline__ void load_vec16_nt(const uint16_t* __restrict__ p, float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "vector width");
+  if constexpr (N == 4) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    x[0] = widen16<FMT>(t.x & 0xffffu); x[1] = widen16<FMT>(t.x >> 16);
+    x[2] = widen16<FMT>(t.y & 0xffffu); x[3] = widen16<FMT>(t.y >> 16);
+  } else {
+    const uint32_t t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    x[0] = widen16<FMT>(t & 0xffffu); x[1] = widen16<FMT>(t >> 16);
+  }
+}
+
 // Round to nearest, ties to the even pattern.  bf16: the carry of
 // 0x7fff + (bit 16) into the kept half does exactly that, overflow included;
 // NaN stays a (quiet) NaN.  fp16: the hardware conversion, which rounds to
@@ -122,6 +165,19 @@ __host__ __device__ __forceinline__ uint32_t round_nearest16(float x) {
     return b >> 16;
   } else {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+}
+
+// Store N (2 or 4) floats as consecutive 16-bit patterns, rounded to nearest.
+template <int FMT, int N>
+__device__ __forceinline__ void store_vec16_nearest(uint16_t* __restrict__ p, const float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "vector width");
+  if constexpr (N == 4) {
+    *reinterpret_cast<uint2*>(p) =
+        make_uint2(round_nearest16<FMT>(x[0]) | (round_nearest16<FMT>(x[1]) << 16),
+                   round_nearest16<FMT>(x[2]) | (round_nearest16<FMT>(x[3]) << 16));
+  } else {
+    *reinterpret_cast<uint32_t*>(p) = round_nearest16<FMT>(x[0]) | (round_nearest16<FMT>(x[1]) << 16);
   }
 }
 

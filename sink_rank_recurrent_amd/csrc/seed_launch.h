@@ -48,7 +48,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 // schedule.
 hipError_t launch_step(int rule, bool in_bf16, int store_fmt, int batch, int heads, int d_k,
                        int d_v, int cap, int r, int kR, float* a, float* U, float* V,
-                       const uint16_t* Uk, const uint16_t* Vk, float* gam, const float* vbar,
+                       uint16_t* Uk, const uint16_t* Vk, float* gam, const float* vbar,
                        const void* q, const void* k, const void* v, const float* g,
                        const float* beta, float* o, hipStream_t stream,
                        const RingArgs* ring = nullptr);
@@ -142,6 +142,13 @@ hipError_t launch_round_factors(int store_fmt, int units, int R, int d_k, int d_
 hipError_t launch_handoff(bool pack, int batch, int heads, int d_k, int d_v, int cap, int R,
                           int factor_bytes, int n_sel, const int* idx, float* a, void* U, void* V,
                           void* buf, hipStream_t stream);
+
+// Unpack of fp32 rank-R states into batch slots slot[0..n_sel) of a batch
+// that holds r >= R columns: a and columns 0..R-1 from buf, columns R..r-1
+// zeroed, and gam (gam_len floats per unit, 0: none) set to 1.
+hipError_t launch_join(int batch, int heads, int d_k, int d_v, int cap, int R, int r, int gam_len,
+                       int n_sel, const int* slot, const void* buf, float* a, float* U, float* V,
+                       float* gam, hipStream_t stream);
 
 // Statistics of dense states (seed_stats.hip): stat_fields() floats per
 // unit in rec; the sorted eigenvalues of S S^T and C C^T in specS, specC

@@ -9,18 +9,23 @@
 //   V+ = [V, beta (eps - V (G U)^T k)]            (Mamba-2: [V, eps])
 //   o  = vbar (a+.q) + V+ (U+^T q)               (read-out after the update)
 //
-// Mapping on gfx950: one 256-thread workgroup (4 wave64s) per (request,
-// head).  The workgroup is 8 column groups of 32 lanes (half-waves).  Group
-// c owns factor columns j = c, c+8, c+16, ...; inside a column each lane
-// holds d_k/32 consecutive entries of the U column and d_v/32 of the V
+// Mapping on gfx950: one 512-thread workgroup (8 wave64s) per (request,
+// head).  The workgroup is NG = 16 column groups of 32 lanes (half-waves).
+// Group c owns factor columns j = c, c+16, c+32, ...; inside a column each
+// lane holds d_k/32 consecutive entries of the U column and d_v/32 of the V
 // column, so every load and store is a coalesced 8- or 16-byte access per
 // lane.  All U and V columns are loaded into registers at the start (the
 // state is read exactly once), so the only dependent step is the reduction
 // of c_k = (G U)^T k and c_q = (G U)^T q inside each half-wave, which then
-// feeds that half-wave's own V columns without any exchange.  The 8 partial
-// V-sums are combined through LDS.  Every half-wave recomputes the scalars
-// (omega, k.Ga, k.q, a+.q) from its own copy of the small vectors, which
-// avoids a barrier; only group 0 writes a, the new V column and o.
+// feeds that half-wave's own V columns without any exchange.  The 16
+// partial V-sums are combined through LDS.  Every half-wave recomputes the
+// scalars (omega, k.Ga, k.q, a+.q) from its own copy of the small vectors,
+// which avoids a barrier; only group 0 writes a, the new V column and o.
+// With 16 groups a thread holds at most ceil(r/16) <= 3 columns below 48
+// held columns (<= 64 VGPRs), so 8 waves fit a SIMD: 1024 units run at once
+// and a launch of 8192 units is exactly 8 rounds.  The factor columns are
+// loaded and stored non-temporally: in a model every other layer's state
+// streams through before this one is touched again.
 //
 // LAZY: the decay of U is kept as a running product gam per unit (per key
 // channel for Kimi Delta Attention) instead of being applied in place: the
@@ -29,20 +34,35 @@
 // and appends U~_r = k / gam.  The arithmetic is Lemma 2's; only the U
 // write-back disappears.
 //
+// The running product must stay a normal fp32 number (k / gam is appended).
+// When a channel's product after this step falls below kFoldBelow = 2^-64,
+// the step applies it to that row of every held column -- the in-place
+// decay, for that channel -- and restarts the product at 1.  In the
+// per-request schedule's interval between a snapshot and its merge the
+// held columns may still be read by the snapshot's compression, so there
+// is no fold; a product below kPoisonBelow = 2^-110 in that interval makes
+// the unit's decay product NaN, which every later read-out carries.
+//
 // FMT != kStoreF32 (16-bit kept factors, always with LAZY): columns j < kR
 // are the 16-bit patterns the last compression rounded (SEED figures and
 // tables, Table 4 and Table 9: factors rounded at every compression) and are
 // widened exactly on load; columns j >= kR, appended since, are fp32 at
-// index j - kR of U and V.  A step never writes the 16-bit columns.
+// index j - kR of U and V.  A step writes a 16-bit column only to fold a
+// vanishing decay product into it (rounded to nearest).
 #include "seed_device.h"
 #include "seed_launch.h"
 
 namespace seed {
 
+constexpr float kFoldBelow = 0x1p-64f;
+constexpr float kPoisonBelow = 0x1p-110f;
+
+constexpr int kGroups = 16;   // column groups (half-waves) per workgroup
+
 template <int RULE, int DK, int DV, typename IN_T, int SLOTS, bool LAZY, int FMT>
-__global__ __launch_bounds__(256) void seed_step_kernel(
+__global__ __launch_bounds__(32 * kGroups) void seed_step_kernel(
     float* __restrict__ a, float* __restrict__ U, float* __restrict__ V,
-    const uint16_t* __restrict__ Uk, const uint16_t* __restrict__ Vk, float* __restrict__ gam,
+    uint16_t* __restrict__ Uk, const uint16_t* __restrict__ Vk, float* __restrict__ gam,
     const float* __restrict__ vbar, const IN_T* __restrict__ q, const IN_T* __restrict__ k,
     const IN_T* __restrict__ v, const float* __restrict__ g, const float* __restrict__ beta,
     float* __restrict__ o, int heads, int cap, int r_arg, int kR_arg, RingArgs rg) {
@@ -65,7 +85,7 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
   // the ring layout's per-request schedule (RingArgs in seed_launch.h)
   int r = r_arg;
   int win0 = 0;
-  bool merge = false, snap = false;
+  bool merge = false, snap = false, pending = false;
   float* keptU = nullptr;
   float* keptV = nullptr;
   if constexpr (RING) {
@@ -80,6 +100,9 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
     r = kR_arg + A - win0;
     merge = c >= 1 && A == win0 + rg.D;
     snap = (A + 1) % rg.W == 0;
+    // a snapshot taken and not yet merged: its compression may read the
+    // held columns
+    pending = A >= rg.W && A % rg.W < rg.D;
     const size_t kb = ((size_t)(c & 1) * gridDim.x + ub) * kR_arg;
     keptU = rg.KU + kb * DK;
     keptV = rg.KV + kb * DV;
@@ -103,13 +126,13 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
   float w[SLOTS][EV];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
-    const int j = grp + 8 * s;
+    const int j = grp + kGroups * s;
     if (H16 && j < r && j < kR) {
-      load_vec16<FMT, EK>(Uk + (ub * kR + j) * DK + lane * EK, u[s]);
-      load_vec16<FMT, EV>(Vk + (ub * kR + j) * DV + lane * EV, w[s]);
+      load_vec16_nt<FMT, EK>(Uk + (ub * kR + j) * DK + lane * EK, u[s]);
+      load_vec16_nt<FMT, EV>(Vk + (ub * kR + j) * DV + lane * EV, w[s]);
     } else if (j < r) {
-      load_vec<EK>(ucol(j) + lane * EK, u[s]);
-      load_vec<EV>(vcol(j) + lane * EV, w[s]);
+      load_vec_nt<EK>(ucol(j) + lane * EK, u[s]);
+      load_vec_nt<EV>(vcol(j) + lane * EV, w[s]);
     } else {
 #pragma unroll
       for (int e = 0; e < EK; ++e) u[s][e] = 0.f;
@@ -153,7 +176,7 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
         // fold the decay product into every held column, then restart it
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
-          const int j = grp + 8 * s;
+          const int j = grp + kGroups * s;
           if (j < r) {
 #pragma unroll
             for (int e = 0; e < EK; ++e) u[s][e] *= gn[e];
@@ -165,8 +188,39 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
       }
     }
 #pragma unroll
+    for (int e = 0; e < EK; ++e) gn[e] *= gk[e];
+    // a vanishing product: fold it into this row of every held column
+    bool fold[EK];
+    bool any = false;
+#pragma unroll
     for (int e = 0; e < EK; ++e) {
-      gn[e] *= gk[e];
+      fold[e] = gn[e] < kFoldBelow;
+      any = any || fold[e];
+    }
+    if (pending) {
+#pragma unroll
+      for (int e = 0; e < EK; ++e)
+        if (gn[e] < kPoisonBelow) gn[e] = __builtin_nanf("");
+    } else if (any) {
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const int j = grp + kGroups * s;
+        if (j < r) {
+#pragma unroll
+          for (int e = 0; e < EK; ++e)
+            if (fold[e]) u[s][e] *= gn[e];
+          if (H16 && j < kR)
+            store_vec16_nearest<FMT, EK>(Uk + (ub * kR + j) * DK + lane * EK, u[s]);
+          else
+            store_vec<EK>(ucol(j) + lane * EK, u[s]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EK; ++e)
+        if (fold[e]) gn[e] = 1.f;
+    }
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
       kx[e] = gn[e] * kk[e];
       qx[e] = gn[e] * qq[e];
     }
@@ -231,20 +285,20 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
         pk += x * kk[e];
         pq += x * qq[e];
       }
-      const int j = grp + 8 * s;
-      if (j < r) store_vec<EK>(ucol(j) + lane * EK, u[s]);
+      const int j = grp + kGroups * s;
+      if (j < r) store_vec_nt<EK>(ucol(j) + lane * EK, u[s]);
     }
     ck[s] = pk;
     cq[s] = pq;
   }
-  if (grp == (r & 7)) {
+  if (grp == r % kGroups) {
     if constexpr (LAZY) {
       float kd[EK];
 #pragma unroll
       for (int e = 0; e < EK; ++e) kd[e] = kk[e] / gn[e];
-      store_vec<EK>(ucol(r) + lane * EK, kd);
+      store_vec_nt<EK>(ucol(r) + lane * EK, kd);
     } else {
-      store_vec<EK>(ucol(r) + lane * EK, kk);
+      store_vec_nt<EK>(ucol(r) + lane * EK, kk);
     }
   }
 #pragma unroll
@@ -269,9 +323,9 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
     }
   }
 
-  // 7. combine the 8 column groups through LDS: thread e < d_v finishes
-  // value entry e (a short tail: 16 partial sums per thread)
-  __shared__ float red[2][8][DV];
+  // 7. combine the column groups through LDS: thread e < d_v finishes
+  // value entry e (a short tail: 2 kGroups partial sums per thread)
+  __shared__ float red[2][kGroups][DV];
   __shared__ float eps_s[DV], sink_s[DV];
 #pragma unroll
   for (int e = 0; e < EV; ++e) {
@@ -300,13 +354,13 @@ __global__ __launch_bounds__(256) void seed_step_kernel(
   if (tid < DV) {
     float tk = 0.f, tq = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < kGroups; ++c) {
       tk += red[0][c][tid];
       tq += red[1][c][tid];
     }
     const float eps = eps_s[tid];
     const float vn = (RULE == kMAMBA2) ? eps : bt * (eps - tk);
-    vcol(r)[tid] = vn;
+    __builtin_nontemporal_store(vn, vcol(r) + tid);
     o[ub * DV + tid] = sink_s[tid] + tq + vn * kq;
   }
 }
@@ -319,7 +373,7 @@ struct StepArgs {
   float* a;
   float* U;
   float* V;
-  const uint16_t* Uk;
+  uint16_t* Uk;
   const uint16_t* Vk;
   float* gam;
   const float* vbar;
@@ -334,7 +388,7 @@ struct StepArgs {
 template <int RULE, int DK, int DV, typename IN_T, int SLOTS, bool LAZY, int FMT>
 void step_launch(const StepArgs& p, hipStream_t s) {
   hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS, LAZY, FMT>), dim3(p.units),
-                     dim3(256), 0, s, p.a, p.U, p.V, p.Uk, p.Vk, p.gam, p.vbar,
+                     dim3(32 * kGroups), 0, s, p.a, p.U, p.V, p.Uk, p.Vk, p.gam, p.vbar,
                      static_cast<const IN_T*>(p.q), static_cast<const IN_T*>(p.k),
                      static_cast<const IN_T*>(p.v), p.g, p.beta, p.o, p.heads, p.cap, p.r, p.kR,
                      p.ring);
@@ -358,7 +412,8 @@ hipError_t step_go(int fmt, const StepArgs& p, hipStream_t s) {
 
 template <int RULE, int DK, int DV, typename IN_T>
 hipError_t step_slots(int fmt, const StepArgs& p, hipStream_t s) {
-  const int need = (p.r + 7) / 8;
+  const int need = (p.r + kGroups - 1) / kGroups;
+  static_assert(6 * kGroups >= kMaxCap, "slot instances cover the capacity");
 #define SEED_STEP_SLOTS(N) \
   if (need <= N) return step_go<RULE, DK, DV, IN_T, N>(fmt, p, s);
   SEED_STEP_SLOTS(1)
@@ -367,9 +422,6 @@ hipError_t step_slots(int fmt, const StepArgs& p, hipStream_t s) {
   SEED_STEP_SLOTS(4)
   SEED_STEP_SLOTS(5)
   SEED_STEP_SLOTS(6)
-  SEED_STEP_SLOTS(8)
-  SEED_STEP_SLOTS(10)
-  SEED_STEP_SLOTS(12)
 #undef SEED_STEP_SLOTS
   return hipErrorInvalidValue;
 }
@@ -392,7 +444,7 @@ hipError_t step_dtype(bool bf16, int d_k, int d_v, int fmt, const StepArgs& p, h
 
 hipError_t launch_step(int rule, bool in_bf16, int store_fmt, int batch, int heads, int d_k,
                        int d_v, int cap, int r, int kR, float* a, float* U, float* V,
-                       const uint16_t* Uk, const uint16_t* Vk, float* gam, const float* vbar,
+                       uint16_t* Uk, const uint16_t* Vk, float* gam, const float* vbar,
                        const void* q, const void* k, const void* v, const float* g,
                        const float* beta, float* o, hipStream_t stream, const RingArgs* ring) {
   if (store_fmt != kStoreF32 && gam == nullptr) return hipErrorInvalidValue;

@@ -21,10 +21,10 @@ def test_exports_every_declared_function():
                           "seed_state_stats", "seed_stat_fields",
                           "seed_decode_step_sched", "seed_compress_sched", "seed_stream_copy",
                           "seed_status_string", "seed_last_error", "seed_abi_version",
-                          "seed_workspace_bytes"}
+                          "seed_workspace_bytes", "seed_join_states"}
     for n in names:
         assert hasattr(L, n), n
-    assert L.seed_abi_version() == 107
+    assert L.seed_abi_version() == 109
 
 
 def test_status_strings():
@@ -234,3 +234,18 @@ def test_workspace_bytes():
         assert L.seed_workspace_bytes(*args) == reject, args
     with pytest.raises(ValueError):
         binding.workspace_bytes(1, 1, 128, 100, 48, 16)
+
+
+def test_join_validation():
+    """Joining needs R <= r < cap; nothing selected is a no-op; the lazy
+    form's gam is checked only when given.  (No call here passes every
+    check: the pointers are not real device memory.)"""
+    p = ALIGNED
+    fj = L.seed_join_states
+    assert fj(0, 4, 2, 128, 128, 48, 16, 15, 1, p, p, p, p, p, None, None) == 2   # r < R
+    assert fj(0, 4, 2, 128, 128, 48, 16, 48, 1, p, p, p, p, p, None, None) == 2   # r = cap
+    assert fj(5, 4, 2, 128, 128, 48, 16, 20, 1, p, p, p, p, p, None, None) == 1   # rule
+    assert fj(0, 4, 2, 128, 128, 48, 16, 20, 1, None, p, p, p, p, None, None) == 1
+    assert fj(1, 4, 2, 128, 128, 48, 16, 20, 1, p, p, p, p, p, MISALIGNED, None) == 1
+    assert b"gam" in L.seed_last_error()
+    assert fj(0, 4, 2, 128, 128, 48, 16, 20, 0, None, None, None, None, None, None, None) == 0

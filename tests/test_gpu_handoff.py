@@ -110,3 +110,88 @@ def test_handed_over_state_decodes_identically(form):
         xp = {k: (None if v is None else v[inv].contiguous()) for k, v in x.items()}
         dst.step_and_maybe_compress(xp["q"], xp["k"], xp["v"], xp["g"], xp["beta"], o2)
         assert torch.equal(o2, o1[inv]), t
+
+
+@pytest.mark.parametrize("lazy", [False, True])
+@pytest.mark.parametrize("rule,dims", [("gdn", (128, 128)), ("kda", (128, 128)),
+                                       ("mamba2", (128, 64))])
+def test_join_mid_window(rule, dims, lazy):
+    """Requests handed over while the batch is k steps into its window join
+    it (seed_join_states): each joined slot then follows the oracle started
+    from the handed-over state -- its own Lemma 2 steps, then the
+    compression of its R + (steps since the join) columns at the batch's
+    compression -- and every other slot is bit-identical to a batch that
+    saw no join."""
+    import numpy as np
+
+    import oracle
+    from gpu_util import (TOL_READOUT, TOL_STATE_COMPRESS, TOL_STATE_STEP, f64, inputs_np,
+                          rel_err, state_rel_err, true_U)
+
+    d_k, d_v = dims
+    B, H, R, W, k_join = 5, 3, 16, 16, 6
+    vbar = wl.make_vbar(H, d_v, 61, 0, "cuda")
+
+    def prefilled(seed):
+        S = torch.zeros(B, H, d_k, d_v, device="cuda")
+        o = torch.empty(B, H, d_v, device="cuda")
+        for t in range(-40, 0):
+            x = wl.make_step(rule, B, H, d_k, d_v, vbar, seed, t, 0, torch.bfloat16, "cuda")
+            binding.dense_decode_step(rule, S, x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        return S
+
+    def state():
+        return binding.ShallowState(rule, B, H, d_k, d_v, R, W, vbar, device="cuda", lazy=lazy)
+
+    S_batch, S_new = prefilled(62), prefilled(63)
+    batch, ref = state(), state()
+    batch.from_dense(S_batch)
+    ref.from_dense(S_batch)
+    arrivals = state()
+    arrivals.from_dense(S_new)
+    src = torch.tensor([1, 3], dtype=torch.int32, device="cuda")     # arriving requests
+    slots = torch.tensor([4, 0], dtype=torch.int32, device="cuda")   # their slots in the batch
+    buf = arrivals.pack(src)
+    o, o_ref = torch.empty(B, H, d_v, device="cuda"), torch.empty(B, H, d_v, device="cuda")
+    xs = [wl.make_step(rule, B, H, d_k, d_v, vbar, 64, t, 0, torch.bfloat16, "cuda")
+          for t in range(W + 8)]
+    for t in range(k_join):
+        for st, out in ((batch, o), (ref, o_ref)):
+            st.step_and_maybe_compress(xs[t]["q"], xs[t]["k"], xs[t]["v"], xs[t]["g"],
+                                       xs[t]["beta"], out)
+    batch.join(buf, slots)
+    torch.cuda.synchronize()
+    assert batch.r == R + k_join
+    # the oracle's copy of the joined requests: the handed-over state itself
+    units = [int(s) * H + h for s in slots.tolist() for h in range(H)]
+    srcu = [int(s) * H + h for s in src.tolist() for h in range(H)]
+    vb = np.broadcast_to(f64(vbar)[None], (B, H, d_v)).reshape(-1, d_v)[units]
+    a = f64(arrivals.a).reshape(B * H, d_k)[srcu]
+    U = f64(arrivals.U).reshape(B * H, -1, d_k)[srcu, :R].transpose(0, 2, 1)
+    V = f64(arrivals.V).reshape(B * H, -1, d_v)[srcu, :R].transpose(0, 2, 1)
+    others = [u for u in range(B * H) if u not in units]
+    compressed = False
+    for t in range(k_join, len(xs)):
+        x = xs[t]
+        c1 = batch.step_and_maybe_compress(x["q"], x["k"], x["v"], x["g"], x["beta"], o)
+        c2 = ref.step_and_maybe_compress(x["q"], x["k"], x["v"], x["g"], x["beta"], o_ref)
+        assert c1 == c2
+        xi = {key: (None if val is None else val[units]) for key, val in inputs_np(x).items()}
+        a, U, V, o_or = oracle.seed_step(rule, a, U, V, vb, **xi)
+        if c1:
+            U, V = oracle.compress(U, V, R)
+            compressed = True
+        og = f64(o).reshape(B * H, d_v)
+        assert rel_err(og[units], o_or, -1).max() < TOL_READOUT, t
+        assert torch.equal(o.reshape(B * H, d_v)[others], o_ref.reshape(B * H, d_v)[others]), t
+        ga = f64(batch.a).reshape(B * H, d_k)[units]
+        # the joined slots hold r columns, the first r - (steps since the
+        # join) - R of them zero before the compression
+        gU = f64(true_U(batch)).reshape(B * H, -1, d_k)[units, :batch.r].transpose(0, 2, 1)
+        gV = f64(batch.V).reshape(B * H, -1, d_v)[units, :batch.r].transpose(0, 2, 1)
+        tol = TOL_STATE_COMPRESS if compressed else TOL_STATE_STEP
+        assert state_rel_err(ga, gU, gV, a, U, V, vb).max() < tol, t
+    assert compressed
+    for name in ("a", "U", "V") + (("gam",) if lazy else ()):
+        x, y = getattr(batch, name), getattr(ref, name)
+        assert torch.equal(x.reshape(B * H, -1)[others], y.reshape(B * H, -1)[others]), name

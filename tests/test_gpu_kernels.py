@@ -269,7 +269,7 @@ def test_nan_stays_in_its_unit():
     assert torch.isnan(st.a[1, 2]).any() and torch.isnan(st.a).any(dim=-1).sum() == 1
 
 
-@pytest.mark.parametrize("case", ["dup_keys", "zero_v_cols", "all_zero_v", "zero_u_cols"])
+@pytest.mark.parametrize("case", ["dup_keys", "near_dup_keys", "zero_v_cols", "all_zero_v", "zero_u_cols"])
 def test_compress_degenerate(case):
     d_k = d_v = 128
     R, W = 16, 32
@@ -281,6 +281,16 @@ def test_compress_degenerate(case):
     if case == "dup_keys":
         U[:, :, 30] = 0.7 * U[:, :, 5]
         U[:, :, 41] = U[:, :, 40]
+    elif case == "near_dup_keys":
+        # keys at angles with sines 1e-3 .. 1e-2 from earlier ones (unit by
+        # unit), the rest of the column orthogonal noise of that size
+        for j, i in ((30, 5), (41, 40), (47, 17)):
+            sines = np.geomspace(1e-3, 1e-2, units)[rng.permutation(units)]
+            base = U[:, :, i] / np.linalg.norm(U[:, :, i], axis=-1, keepdims=True)
+            noise = rng.standard_normal((units, d_k))
+            noise -= np.sum(noise * base, axis=-1, keepdims=True) * base
+            noise /= np.linalg.norm(noise, axis=-1, keepdims=True)
+            U[:, :, j] = np.sqrt(1 - sines[:, None] ** 2) * base + sines[:, None] * noise
     elif case == "zero_v_cols":
         V[:, :, 16:] = 0.0
     elif case == "all_zero_v":
