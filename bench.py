@@ -253,97 +253,169 @@ def warm_compress_instances(w, form: str, rs, dev: str) -> None:
     torch.cuda.synchronize()
 
 
-def _segments(pl, lo: int, hi: int):
-    """The bench steps lo .. hi-1 of a plan as alternating runs: ("steps",
-    [(t, l, r), ...]) for every maximal run of step launches with no
-    compression between them, ("compress", [(l, r), ...]) for the
-    compressions that follow it."""
-    segs, cur = [], []
+def _ops(pl, lo: int, hi: int, overlap: bool, pending):
+    """The bench steps lo .. hi-1 of a plan as a list of operations:
+    ("steps", [(t, l, r), ...]) for every maximal run of step launches that
+    nothing has to come between, and then
+      * overlap: ("fork", l, r) right after layer l's step launch whose
+        window ends there (its compression, on the side stream), and
+        ("wait", l) right before layer l's next step launch (the launch
+        stream waits for that compression);
+      * otherwise: ("compress", [(l, r), ...]) after the L step launches of
+        the bench step, on the launch stream.
+    `pending` (a set of layers whose compression is in flight) is updated."""
+    ops, cur = [], []
+
+    def flush():
+        if cur:
+            ops.append(("steps", list(cur)))
+            cur.clear()
+
     for t in range(lo, hi):
         steps, comps = pl[t]
-        cur += [(t, l, r) for l, r in steps]
-        if comps:
-            segs.append(("steps", cur))
-            segs.append(("compress", comps))
-            cur = []
-    if cur:
-        segs.append(("steps", cur))
-    return segs
+        comp_of = dict(comps)
+        for l, r in steps:
+            if overlap and l in pending:
+                flush()
+                ops.append(("wait", l))
+                pending.discard(l)
+            cur.append((t, l, r))
+            if overlap and l in comp_of:
+                flush()
+                ops.append(("fork", l, comp_of[l]))
+                pending.add(l)
+        if not overlap and comps:
+            flush()
+            ops.append(("compress", comps))
+    flush()
+    return ops
 
 
 def run_stack(w, states, inputs, outs, n_pre: int, n_settle: int, n_timed: int, form: str,
-              dev: str, joins=None, join_bufs=None):
-    """Capture n_pre + n_settle + n_timed bench steps as HIP graphs -- one
-    per run of step launches between compressions, one per run of
-    compressions -- replay the pre-roll's and the settle steps' graphs (the
-    settle pass), then the timed ones with an event on the launch stream
-    before each graph and after the last.  joins: {bench step: int32 slots}
-    -- before its step launch at that bench step, each layer takes the
-    requests of join_bufs[layer] into those slots (seed_join_states, at the
-    column count the plan gives it)."""
+              dev: str, joins=None, join_bufs=None, overlap: bool = True):
+    """Run n_pre + n_settle + n_timed bench steps of the layer stack: each
+    run of step launches is one HIP graph, replayed on the launch stream.
+    With overlap, a layer's compression runs on a side stream (default
+    priority), forked right after the step launch that ends its window and
+    joined right before that layer's next step launch, so it overlaps the
+    other layers' steps; without, the compressions of a bench step follow
+    its L step launches on the launch stream.  The pre-roll and the settle
+    steps run first; in the timed steps an event pair on the launch stream
+    brackets every graph (the step launches' time), one on the side stream
+    every compression, and the timed region starts with no compression in
+    flight and ends when the last compression it started has finished.  joins: {bench step: int32 slots} -- before its
+    step launch at that bench step, each layer takes the requests of
+    join_bufs[layer] into those slots (seed_join_states, at the column count
+    the plan gives it)."""
     import torch
     from sink_rank_recurrent_amd import binding
 
-    t0 = 0
     pl, r_end, lim_end = plan(states, n_pre + n_settle + n_timed)
     warm_compress_instances(w, form, [r for _, comps in pl for _, r in comps], dev)
     fns = [st.bind_step(outs[l]) for l, st in enumerate(states)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    pending = set()
+    phases = [_ops(pl, 0, n_pre, overlap, pending),
+              _ops(pl, n_pre, n_pre + n_settle, overlap, pending)]
+    pending.clear()   # joined before the timed region (below)
+    phases.append(_ops(pl, n_pre + n_settle, n_pre + n_settle + n_timed, overlap, pending))
 
-    def capture(segs):
-        out = []
-        for kind, items in segs:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                if kind == "steps":
-                    for t, l, r in items:
-                        if joins is not None and t in joins:
-                            st = states[l]
-                            binding.seed_join_states(st.rule, join_bufs[l], st.a, st.U, st.V,
-                                                     st.gam, st.R, r, joins[t])
-                        x = inputs[l][t0 + t]
-                        fns[l](x["q"], x["k"], x["v"], x["g"], x["beta"], r)
-                else:
-                    for l, r in items:
-                        states[l].launch_compress(r)
-            out.append((kind, len(items), g))
-        return out
+    def capture(items):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t, l, r in items:
+                if joins is not None and t in joins:
+                    st = states[l]
+                    binding.seed_join_states(st.rule, join_bufs[l], st.a, st.U, st.V, st.gam,
+                                             st.R, r, joins[t])
+                x = inputs[l][t]
+                fns[l](x["q"], x["k"], x["v"], x["g"], x["beta"], r)
+        return g
 
-    pre = capture(_segments(pl, 0, n_pre))
-    settle = capture(_segments(pl, n_pre, n_pre + n_settle))
-    timed = capture(_segments(pl, n_pre + n_settle, n_pre + n_settle + n_timed))
+    graphs = [[capture(op[1]) if op[0] == "steps" else None for op in ops] for ops in phases]
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    for _, _, g in pre:
-        g.replay()
+    done = {}
+    rec = {"step": [], "comp": [], "all_comp": []}
+
+    def execute(ops, gs, timed):
+        for op, g in zip(ops, gs):
+            if op[0] == "steps":
+                if timed:
+                    a, b = ev(), ev()
+                    a.record(main)
+                    g.replay()
+                    b.record(main)
+                    rec["step"].append((a, b, [r for _, _, r in op[1]]))
+                else:
+                    g.replay()
+            elif op[0] == "wait":
+                main.wait_event(done.pop(op[1]))
+            elif op[0] == "fork":
+                l, r = op[1], op[2]
+                f = torch.cuda.Event()
+                f.record(main)
+                side.wait_event(f)
+                a, b = ev(), ev()
+                a.record(side)
+                states[l].launch_compress(r, stream=side)
+                b.record(side)
+                done[l] = b
+                rec["all_comp"].append((a, b))
+                if timed:
+                    rec["comp"].append((a, b, r))
+            else:
+                for l, r in op[1]:
+                    a, b = ev(), ev()
+                    a.record(main)
+                    states[l].launch_compress(r)
+                    b.record(main)
+                    if timed:
+                        rec["comp"].append((a, b, r))
+
+    execute(phases[0], graphs[0], False)
     s0, s1 = ev(), ev()
-    s0.record()
-    for _, _, g in settle:
-        g.replay()
-    s1.record()
-    marks = [ev() for _ in range(len(timed) + 1)]
-    for i, (_, _, g) in enumerate(timed):
-        marks[i].record()
-        g.replay()
-    marks[-1].record()
+    s0.record(main)
+    execute(phases[1], graphs[1], False)
+    # the timed region starts with no compression in flight (and ends after
+    # the last one it started): none of the settle pass's work is counted
+    for l in list(done):
+        main.wait_event(done.pop(l))
+    s1.record(main)
+    t0, t1 = ev(), ev()
+    t0.record(main)
+    n_fork0 = len(rec["comp"])
+    execute(phases[2], graphs[2], True)
+    # the region ends when the compressions it started have finished
+    for l in list(done):
+        main.wait_event(done.pop(l))
+    t1.record(main)
     torch.cuda.synchronize()
     for l, st in enumerate(states):
         st.r, st.limit = r_end[l], lim_end[l]
-    step_ms = comp_ms = 0.0
-    for i, (kind, _, _) in enumerate(timed):
-        ms = marks[i].elapsed_time(marks[i + 1])
-        if kind == "steps":
-            step_ms += ms
-        else:
-            comp_ms += ms
+    step_ms = sum(a.elapsed_time(b) for a, b, _ in rec["step"])
+    comp_ms = sum(a.elapsed_time(b) for a, b, _ in rec["comp"])
     timed_pl = pl[n_pre + n_settle:]
     step_r = [r for steps, _ in timed_pl for _, r in steps]
-    comp_r = [r for _, comps in timed_pl for _, r in comps]
-    return {"elapsed_ms": marks[0].elapsed_time(marks[-1]), "step_ms": step_ms,
-            "compress_ms": comp_ms, "compressions": len(comp_r), "step_r": step_r,
-            "compress_r": comp_r, "settle_ms": s0.elapsed_time(s1), "settle_steps": n_settle,
-            "timed_steps": n_timed, "graphs": len(timed), "pre_roll_steps": n_pre,
-            "compress_columns": sorted(set(comp_r))}
+    comp_r = [r for _, _, r in rec["comp"]]
+    assert n_fork0 == 0 and step_r == [r for _, _, rs in rec["step"] for r in rs]
+    # the graphs of step launches during which no compression ran (events of
+    # both streams on the one device clock, from the timed region's start)
+    comp_iv = [(t0.elapsed_time(a), t0.elapsed_time(b)) for a, b in rec["all_comp"]]
+    clear_ms, clear_r = 0.0, []
+    for a, b, rs in rec["step"]:
+        sa, sb = t0.elapsed_time(a), t0.elapsed_time(b)
+        if all(cb <= sa or ca >= sb for ca, cb in comp_iv):
+            clear_ms += sb - sa
+            clear_r += rs
+    return {"elapsed_ms": t0.elapsed_time(t1), "step_ms": step_ms, "compress_ms": comp_ms,
+            "compressions": len(comp_r), "step_r": step_r, "compress_r": comp_r,
+            "settle_ms": s0.elapsed_time(s1), "settle_steps": n_settle, "timed_steps": n_timed,
+            "graphs": sum(1 for op in phases[2] if op[0] == "steps"),
+            "pre_roll_steps": n_pre, "compress_columns": sorted(set(comp_r)),
+            "overlap": overlap, "clear_step_ms": clear_ms, "clear_step_r": clear_r}
 
 
 def summarise(spec, res, form: str, L: int) -> dict:
@@ -366,9 +438,22 @@ def summarise(spec, res, form: str, L: int) -> dict:
         "step_achieved_GBs": achieved,
         "step_frac_of_peak": achieved / HBM_PEAK_GBS,
         "step_only_head_steps_per_s": units * n_launch / (res["step_ms"] / 1e3),
+        # the same over the graphs of step launches with no compression
+        # running beside them
+        "step_clear_launches": len(res["clear_step_r"]),
+        "step_clear_avg_us": (res["clear_step_ms"] * 1e3 / len(res["clear_step_r"])
+                              if res["clear_step_r"] else None),
+        "step_clear_achieved_GBs": (sum(step_bytes_per_unit(spec, r, form)
+                                        for r in res["clear_step_r"]) * units
+                                    / (res["clear_step_ms"] / 1e3) / 1e9
+                                    if res["clear_step_r"] else None),
         "compressions": n_comp,
         "compress_avg_us": res["compress_ms"] * 1e3 / n_comp if n_comp else None,
-        "compress_share_of_time": res["compress_ms"] / res["elapsed_ms"],
+        # on the launch stream the compressions' time is a share of the
+        # elapsed time; overlapped on the side stream it is not
+        "compress_share_of_time": (None if res["overlap"]
+                                   else res["compress_ms"] / res["elapsed_ms"]),
+        "compressions_overlapped": res["overlap"],
         "compressions_per_layer_step": n_comp / (L * res["timed_steps"]),
         "graphs_replayed": res["graphs"],
         "pre_roll_steps": res["pre_roll_steps"],
@@ -633,7 +718,7 @@ def stats_of(w, S, vbar, dev: str) -> dict:
 
 
 def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, timed, dev,
-                         aligned):
+                         aligned, overlap: bool = True):
     """Requests that arrive at different times, on the stack, against the
     aligned lazily decayed form (`aligned`):
       * one global phase: an arriving request joins mid-window
@@ -642,7 +727,9 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
       * per-request schedules (seed_decode_step_sched): request b starts at
         phase b mod W and compresses on its own schedule, the snapshots of
         D consecutive steps compressed by one launch, D the smallest delay
-        whose launch gives every SIMD of the GPU a unit."""
+        whose launch gives every SIMD of the GPU a unit.
+    Both overlap their compressions with the steps on a side stream as the
+    aligned run does (overlap), or run them on the launch stream."""
     import torch
     from sink_rank_recurrent_amd import binding
 
@@ -652,7 +739,8 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
     bufs = [st.pack(torch.zeros(1, dtype=torch.int32, device=dev)) for st in states]
     joins = {t: torch.tensor([(t // 8) % w.batch], dtype=torch.int32, device=dev)
              for t in range(pre, pre + settle + timed) if t % 8 == 0}
-    res = run_stack(spec, states, inputs, outs, pre, settle, timed, "lazy", dev, joins, bufs)
+    res = run_stack(spec, states, inputs, outs, pre, settle, timed, "lazy", dev, joins, bufs,
+                    overlap=overlap)
     r = summarise(spec, res, "lazy", len(states))
     n_join = sum(1 for t in joins if t >= pre + settle)
     out.append({"kind": "one global phase: arriving requests join mid-window "
@@ -673,7 +761,7 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
     scheds = []
     for l, (vbar, S) in enumerate(zip(vbars, Ss)):
         st = binding.ScheduledState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, D, vbar,
-                                    t_start, device=dev)
+                                    t_start, device=dev, side_streams=1 if overlap else 0)
         st.from_dense(S)
         scheds.append(st)
     for t in range(pre + settle):
@@ -714,10 +802,14 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
 
 
 def run_workload(w, layers: int, settle: int, timed: int, dev: str, forms, with_dense: bool,
-                 keep_layer0: bool = False, no_stagger: bool = True):
+                 keep_layer0: bool = False, no_stagger: bool = True, overlap: bool = True,
+                 sequential_too: bool = False):
     """Prefill, convert and time `layers` layers of workload w in every form
-    of `forms`, then the dense baseline.  Returns (results by form, dense,
-    conversion ms, layer-0 objects for the CPU snapshot / handoff / stats)."""
+    of `forms` (compressions overlapped on a side stream, or not), then the
+    dense baseline; sequential_too adds the first form with the compressions
+    on the launch stream (results["sequential"]).  Returns (results by form,
+    dense, conversion ms, layer-0 objects for the CPU snapshot / handoff /
+    stats)."""
     import torch
 
     spec = Spec(w)
@@ -731,25 +823,37 @@ def run_workload(w, layers: int, settle: int, timed: int, dev: str, forms, with_
     outs = [torch.empty(w.batch, w.heads, w.d_v, device=dev) for _ in range(layers)]
     results, conv_ms, layer0 = {}, None, None
     for form in forms:
-        states, cm = make_states(w, form, vbars, Ss, phases, dev, timed_conversion=(form == "in_place"))
+        states, cm = make_states(w, form, vbars, Ss, phases, dev,
+                                 timed_conversion=(form == forms[0]))
         if cm is not None:
             conv_ms = cm
-        if keep_layer0 and form == "in_place":
+        if keep_layer0 and form == forms[0]:
             # layer 0's converted and dense states as they are before any
             # timed step (copies: the runs below move the originals on)
             st0 = copy.copy(states[0])
             st0.a, st0.U, st0.V = states[0].a.clone(), states[0].U.clone(), states[0].V.clone()
             layer0 = {"state": st0, "S": Ss[0].clone(), "vbar": vbars[0],
                       "inputs": inputs[0][:min(pre + settle + timed, 64)]}
-        res = run_stack(spec, states, inputs, outs, pre, settle, timed, form, dev)
+        res = run_stack(spec, states, inputs, outs, pre, settle, timed, form, dev,
+                        overlap=overlap)
         results[form] = summarise(spec, res, form, layers)
         log(f"{w.name} [{form}]: {results[form]['ms_per_step']:.3f} ms per step, "
             f"{results[form]['compressions']} compressions in {timed} timed steps")
         del states
         torch.cuda.empty_cache()
+    if sequential_too and overlap:
+        form = forms[0]
+        states, _ = make_states(w, form, vbars, Ss, phases, dev)
+        res = run_stack(spec, states, inputs, outs, pre, settle, timed, form, dev, overlap=False)
+        results["sequential"] = summarise(spec, res, form, layers)
+        log(f"{w.name} [{form}, compressions on the launch stream]: "
+            f"{results['sequential']['ms_per_step']:.3f} ms per step")
+        del states
+        torch.cuda.empty_cache()
     if "lazy" in forms and layers > 1 and not no_stagger:
         results["stagger"] = run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre,
-                                                  settle, timed, dev, results.get("lazy"))
+                                                  settle, timed, dev, results.get("lazy"),
+                                                  overlap=overlap)
     dense = None
     if with_dense:
         d = run_dense(w, Ss, inputs, outs, pre, settle, timed)
@@ -781,6 +885,9 @@ def main() -> int:
                     help="skip the lazily decayed and 16-bit forms")
     ap.add_argument("--no-sub", action="store_true",
                     help="skip the other workloads' entries")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run every compression on the launch stream after its bench step "
+                         "(default: on a side stream, overlapping the other layers' steps)")
     ap.add_argument("--cpu-worker", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
@@ -815,11 +922,15 @@ def main() -> int:
     steps, warmup = args.steps, args.warmup
     log(f"workload {w.name}: {L} layer(s) x {spec.units} units, {steps} timed steps after "
         f"{warmup} settle steps")
-    forms = ["in_place"] if args.no_variant else ["in_place", "lazy", "h16"]
+    # the reported form first: U decayed lazily (fp32 factors); the in-place
+    # decay and the 16-bit kept factors are variants
+    forms = ["lazy"] if args.no_variant else ["lazy", "in_place", "h16"]
+    overlap = not args.no_overlap
     results, dense, conv_ms, layer0 = run_workload(w, L, warmup, steps, dev, forms,
                                                    not args.no_dense, keep_layer0=True,
-                                                   no_stagger=args.no_variant)
-    head = results["in_place"]
+                                                   no_stagger=args.no_variant, overlap=overlap,
+                                                   sequential_too=not args.no_variant)
+    head = results[forms[0]]
 
     handoff = stats = None
     if not args.no_variant:
@@ -847,16 +958,18 @@ def main() -> int:
             ws = wl.WORKLOADS[num]
             sp = Spec(ws)
             n_timed = ws.W * max(1, math.ceil(steps / ws.W))
-            rs, ds, cms, _ = run_workload(ws, 1, ws.W, n_timed, dev, forms, not args.no_dense)
-            e = dict(rs["in_place"])
+            rs, ds, cms, _ = run_workload(ws, 1, ws.W, n_timed, dev, forms, not args.no_dense,
+                                          overlap=overlap)
+            e = dict(rs[forms[0]])
             e["rule"] = "timed over whole windows: one settle window, then " \
                         f"{n_timed // ws.W} window(s) of {ws.W} steps and their compressions"
             e["us_per_step"] = e["ms_per_step"] * 1e3
             e["conversion_ms"] = cms
             e["dense_baseline"] = ds
             e["speedup_over_dense"] = e["value"] / ds["value"] if ds else None
-            for form, key in (("lazy", "lazy_decay_variant"), ("h16", "fp16_factor_variant")):
-                if form in rs:
+            for form, key in (("in_place", "in_place_decay_variant"),
+                              ("h16", "fp16_factor_variant")):
+                if form in rs and form != forms[0]:
                     e[key] = {"value": rs[form]["value"], "step_frac_of_peak":
                               rs[form]["step_frac_of_peak"],
                               "compress_avg_us": rs[form]["compress_avg_us"]}
@@ -890,10 +1003,17 @@ def main() -> int:
                    "heads": w.heads, "heads_per_launch": spec.units,
                    "heads_total": L * spec.units, "d_k": w.d_k, "d_v": w.d_v, "R": w.R,
                    "W": w.W, "inputs": "bf16 q/k/v, fp32 gates" if spec.in_dtype_name == "bf16"
-                   else "fp32", "prefill": w.prefill, "decay_of_U": "in place",
+                   else "fp32", "prefill": w.prefill,
+                   "decay_of_U": "lazy: U = Diag(gam) U~ with a running decay product per "
+                                 "head, folded in below 2^-64 (fp32 factors)",
                    "schedule": "layer l compresses every W steps, first window W - floor(l W / L)",
-                   "launch": "one HIP graph per bench step (the layers' step launches) and one "
-                             "for its compressions, replayed after a settle pass",
+                   "launch": ("one HIP graph per run of step launches; each layer's "
+                              "compression on a side stream, forked after the step that ends "
+                              "its window and joined before that layer's next step"
+                              if overlap else
+                              "one HIP graph per run of step launches, the compressions of a "
+                              "bench step after its step launches on the same stream") +
+                             "; pre-roll and settle pass first",
                    "resident_factor_bytes": L * spec.units * 4 * (w.d_k + w.d_v) * (w.R + w.W)
                    + L * spec.units * 4 * w.d_k},
         "roofline": {"bound": "hbm", "kernel": "seed_step_kernel", "achieved": achieved,
@@ -902,18 +1022,32 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": head["step_algorithmic_bytes_per_launch"],
                      "avg_launch_us": head["step_kernel_avg_us"],
                      "launches": head["step_launches"],
+                     "without_concurrent_compression": {
+                         "launches": head["step_clear_launches"],
+                         "avg_launch_us": head["step_clear_avg_us"],
+                         "achieved": head["step_clear_achieved_GBs"],
+                         "frac": (head["step_clear_achieved_GBs"] / HBM_PEAK_GBS
+                                  if head["step_clear_achieved_GBs"] else None)},
                      "achievable_copy_GBs": copy_gbs,
                      "frac_of_achievable": achieved / copy_gbs if copy_gbs else None},
         "cpu_baseline": cpu,
         "breakdown": {k: head[k] for k in ("step_kernel_avg_us", "step_bytes_per_head_step",
                                            "step_only_head_steps_per_s", "compressions",
                                            "compress_avg_us", "compress_share_of_time",
+                                           "compressions_overlapped",
                                            "compressions_per_layer_step", "compress_columns",
                                            "pre_roll_steps")},
+        "compressions_on_launch_stream": ({"value": results["sequential"]["value"],
+                                           "ms_per_step": results["sequential"]["ms_per_step"],
+                                           "compress_avg_us":
+                                           results["sequential"]["compress_avg_us"],
+                                           "compress_share_of_time":
+                                           results["sequential"]["compress_share_of_time"]}
+                                          if "sequential" in results else None),
         "settle": head["settle"],
         "dense_baseline": dense,
         "speedup_over_dense": head["value"] / dense["value"] if dense else None,
-        "lazy_decay_variant": results.get("lazy"),
+        "in_place_decay_variant": results.get("in_place"),
         "fp16_factor_variant": results.get("h16"),
         "staggered_schedule_variants": results.get("stagger"),
         "conversion": {"kernel": "compress_wave_kernel (conversion instance)", "ms": conv_ms,

@@ -638,13 +638,21 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     // kPivTol.  Row j of R~ is kept by original column,
     // RB[t LDN + j] = R~[j][t] (0 for the columns taken before), with
     // IRD[j] = 1 / R~[j][p] and PIV[j] = p; rows from `kept` on are zero.
+    // The pivot value is the reduction's maximum (the pivot's own dg, equal
+    // to its column's entry p up to rounding), and row j of R~ is the
+    // published column times its reciprocal square root, so a step takes one
+    // LDS round trip.  Every thread updates its column with the whole
+    // column p: the pivot's own row comes out as zero up to rounding, and
+    // the rows of earlier pivots are never read again.
+    // (The largest diagonal is reduced at the end of the previous step, so
+    // the loop has one exit and its columns are updated in place.)
     bool taken = !(act && t < n && IDV[t] > 0.f);
     int kept = 0;
-    for (int j = 0; j < n; ++j) {
+    float mx = block_reduce<NW>(taken ? -1.f : dg, MaxOp(), RED, 6);
+    for (int j = 0; j < n && mx > kPivTol; ++j) {
       const float cand = taken ? -1.f : dg;
-      const float mx = block_reduce<NW>(cand, MaxOp(), RED, 6);
-      if (!(mx > kPivTol)) break;
       const int p = block_first<NW>(!taken && cand == mx, RED);
+      const float rp = frsq(mx);
       if (t == p) {
         taken = true;
   #pragma unroll
@@ -652,24 +660,23 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
       }
       __syncthreads();
-      const float piv = CB[p];    // = mx: the same arithmetic kept both
-      const float rp = frsq(piv);
-      const float r = (act && !taken) ? CB[t] * rp : 0.f;
-      if (act) {
-        RB[t * LDN + j] = (t == p) ? piv * rp : r;
-        WB[t] = r;
-      }
+      float wr[NMAX];
+      load_row<NMAX>(CB, wr);
+      const float ct = CB[t];
+      const float r = (act && !taken) ? ct * rp : 0.f;
+      if (act) RB[t * LDN + j] = (t == p) ? mx * rp : r;
       if (t == 0) {
         IRD[j] = rp;
         PIV[j] = p;
       }
-      __syncthreads();
-      float wr[NMAX];
-      load_row<NMAX>(WB, wr);
+      const float rr = r * rp;
   #pragma unroll
-      for (int i = 0; i < NMAX; ++i) g[i] = fmaf(-wr[i], r, g[i]);
+      for (int i = 0; i < NMAX; ++i) g[i] = fmaf(-wr[i], rr, g[i]);
       dg = fmaf(-r, r, dg);
       kept = j + 1;
+      // the next pivot rewrites CB (one wave reads it in order before that)
+      if constexpr (NW > 1) __syncthreads();
+      mx = block_reduce<NW>(taken ? -1.f : dg, MaxOp(), RED, 6);
     }
     for (int j = kept + t; j < NMAX; j += NTH) {
       IRD[j] = 0.f;

@@ -4,8 +4,9 @@
 #   sink_rank_recurrent_amd/profile_bench.sh OUT_DIR [bench.py arguments]
 #
 # 1. rocprofv3 --kernel-trace --stats of `bench.py ARGS --no-cpu` -> OUT_DIR/
-#    kernel_trace.md, with the average of the in-place step kernel over the
-#    headline's timed launches.  The CPU oracle leg launches no kernel; it is
+#    kernel_trace.md, with the average of the reported form's step kernel
+#    (lazy decay) over the headline's timed launches, which follow its
+#    pre-roll and settle steps.  The CPU oracle leg launches no kernel; it is
 #    left out so that no oracle process runs under the profiler.
 # 2. Two --pmc passes over the same headline (FETCH_SIZE, then WRITE_SIZE,
 #    counted on the step kernel only; the other forms, workloads and the
@@ -52,11 +53,13 @@ L=$(json_field "$out/trace_bench.json" "d['config']['layers']")
 warm=$(json_field "$out/trace_bench.json" "d['warmup']")
 steps=$(json_field "$out/trace_bench.json" "d['steps']")
 name=$(json_field "$out/trace_bench.json" "d['config']['workload']")
+pre=$(json_field "$out/trace_bench.json" "d['breakdown']['pre_roll_steps']")
 python3 -m sink_rank_recurrent_amd.profile_summary trace \
   "$(find_csv "$work/trace" kernel_stats.csv)" "$(find_csv "$work/trace" kernel_trace.csv)" \
   --command "sink_rank_recurrent_amd/profile_bench.sh $out $args   # runs: rocprofv3 --kernel-trace --stats -d <tmp> -o trace --output-format csv -- python3 bench.py $args --no-cpu" \
   --title "Kernel trace: bench.py $args (workload $name, CPU leg left out)" \
-  --window "$((warm * L)):$((steps * L))" --out "$out/kernel_trace.md" > "$out/kernel_trace.json"
+  --window "$(((pre + warm) * L)):$((steps * L))" --group "seed_step_kernel (lazy decay)" \
+  --out "$out/kernel_trace.md" > "$out/kernel_trace.json"
 
 pmc_args="$args --no-cpu --no-sub --no-variant --no-dense"
 for c in FETCH_SIZE WRITE_SIZE; do

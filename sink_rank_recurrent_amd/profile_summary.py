@@ -45,7 +45,7 @@ def short(name: str) -> str:
 
 
 def trace_summary(stats_csv: str, trace_csv: str, command: str, title: str,
-                  window=None, window_group: str = "seed_step_kernel (U decayed in place)"):
+                  window=None, window_group: str = "seed_step_kernel (lazy decay)"):
     rows = list(csv.DictReader(open(stats_csv)))
     top = 25
     lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
@@ -120,22 +120,24 @@ def main() -> int:
     t.add_argument("--title", default="rocprofv3 kernel trace")
     t.add_argument("--out", required=True)
     t.add_argument("--window", default=None,
-                   help="START:COUNT -- also average the in-place step kernel over these "
+                   help="START:COUNT -- also average one kernel group (--group) over these "
                         "dispatches in launch order")
+    t.add_argument("--group", default="seed_step_kernel (lazy decay)", choices=sorted(GROUPS),
+                   help="the kernel group --window counts")
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True, help="counter_collection.csv of the FETCH_SIZE run")
     c.add_argument("--write", required=True, help="counter_collection.csv of the WRITE_SIZE run")
     c.add_argument("--copy-fetch", required=True)
     c.add_argument("--copy-write", required=True)
     c.add_argument("--copy-bytes", type=float, default=float(1 << 30))
-    c.add_argument("--kernel", default=GROUPS["seed_step_kernel (U decayed in place)"])
+    c.add_argument("--kernel", default=GROUPS["seed_step_kernel (lazy decay)"])
     c.add_argument("--source", required=True, help="kernel source whose hash is recorded")
     c.add_argument("--bench-json", required=True,
                    help="the JSON line bench.py printed in the profiled run: its algorithmic "
                         "bytes per launch, steps, warm-up steps and layers")
     c.add_argument("--window", default=None,
                    help="START:COUNT of the kernel's dispatches to average (default: the "
-                        "bench line's timed launches)")
+                        "bench line's timed launches, after its pre-roll and settle steps)")
     c.add_argument("--commands", required=True)
     c.add_argument("--out", required=True)
     m = sub.add_parser("pmc")
@@ -169,7 +171,7 @@ def main() -> int:
 
     if args.cmd == "trace":
         text, merged = trace_summary(args.stats, args.trace, args.command, args.title,
-                                     _window(args.window))
+                                     _window(args.window), args.group)
         with open(args.out, "w") as f:
             f.write(text)
         print(json.dumps(merged))
@@ -187,7 +189,8 @@ def main() -> int:
     if line is None:
         raise SystemExit(f"no JSON line in {args.bench_json}")
     L = line["config"]["layers"]
-    window = _window(args.window) or (line["warmup"] * L, line["steps"] * L)
+    pre = line["breakdown"]["pre_roll_steps"]
+    window = _window(args.window) or ((pre + line["warmup"]) * L, line["steps"] * L)
     fetch, nf = mean_kib(args.fetch, args.kernel, "FETCH_SIZE", window)
     write, nw = mean_kib(args.write, args.kernel, "WRITE_SIZE", window)
     algorithmic = line["roofline"]["algorithmic_bytes_per_launch"]

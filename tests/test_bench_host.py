@@ -124,20 +124,47 @@ def test_cpu_worker_and_no_leftover_process(tmp_path):
     assert res["host_cpus_usable"] >= 1
 
 
-def test_segments_group_step_runs():
-    """Consecutive step launches with no compression between them form one
-    graph; each run of compressions another; every launch appears once, in
-    order."""
+def test_ops_group_step_runs():
+    """Sequential: consecutive step launches with no compression between
+    them form one graph, the compressions of a bench step follow its L
+    launches.  Overlapped: a layer's compression is forked right after the
+    step launch that ends its window and waited for right before that
+    layer's next step launch, with the other L - 1 layers' launches between.
+    Every launch appears once, in order, in both."""
     L, W, R = 36, 32, 16
     ph = bench.layer_phases(L, W)
     pl, _, _ = bench.plan([_St(R, W, W - p) for p in ph], 40)
-    segs = bench._segments(pl, 5, 25)
-    launches = [(t, l) for kind, items in segs if kind == "steps" for t, l, _ in items]
+    ops = bench._ops(pl, 5, 25, False, set())
+    launches = [(t, l) for op in ops if op[0] == "steps" for t, l, _ in op[1]]
     assert launches == [(t, l) for t in range(5, 25) for l in range(L)]
-    comps = [c for kind, items in segs if kind == "compress" for c in items]
+    comps = [c for op in ops if op[0] == "compress" for c in op[1]]
     assert comps == [c for t in range(5, 25) for c in pl[t][1]]
-    assert all(a[0] != b[0] for a, b in zip(segs, segs[1:]))
+    assert all(a[0] != b[0] for a, b in zip(ops, ops[1:]))
     # one layer: a whole window of W steps is one run
     pl1, _, _ = bench.plan([_St(R, W, W)], 3 * W)
-    segs1 = bench._segments(pl1, W, 3 * W)
-    assert [(k, len(i)) for k, i in segs1] == [("steps", W), ("compress", 1)] * 2
+    ops1 = bench._ops(pl1, W, 3 * W, False, set())
+    assert [(op[0], len(op[1])) for op in ops1] == [("steps", W), ("compress", 1)] * 2
+
+    pending = set()
+    ops = bench._ops(pl, 5, 25, True, pending)
+    seq = []
+    for op in ops:
+        if op[0] == "steps":
+            seq += [("step", t, l) for t, l, _ in op[1]]
+        else:
+            seq.append(op)
+    assert [(x[1], x[2]) for x in seq if x[0] == "step"] == \
+        [(t, l) for t in range(5, 25) for l in range(L)]
+    forks = [(i, x) for i, x in enumerate(seq) if x[0] == "fork"]
+    assert [(x[1], x[2]) for _, x in forks] == [c for t in range(5, 25) for c in pl[t][1]]
+    for i, (_, l, r) in forks:
+        # right after the step of layer l that ends its window
+        assert seq[i - 1][0] == "step" and seq[i - 1][2] == l
+        nxt = [j for j in range(i + 1, len(seq)) if seq[j][0] == "step" and seq[j][2] == l]
+        if nxt:
+            j = nxt[0]
+            assert seq[j - 1] == ("wait", l)
+            assert sum(1 for x in seq[i:j] if x[0] == "step") == L - 1
+        else:
+            assert l in pending
+    assert sum(1 for x in seq if x[0] == "wait") + len(pending) == len(forks)

@@ -175,3 +175,11 @@ def test_workload_parity_lazy_decay(num):
     seed_compress_lazy), its state read at true scale, U = Diag(gam) U~."""
     stats = run_workload(num, n_sample=1 if num == 1 else 6, lazy=True)
     print(f"workload {num}, lazy decay: {stats}")
+
+
+def test_workload5_layer_parity_lazy_decay():
+    """The lazily decayed form on the 36-layer workload's middle layer over
+    all 16384 steps (the form bench.py reports first)."""
+    stats = run_workload(5, n_sample=6, layer=17, lazy=True)
+    assert stats["compressions"] == 1 + (16384 - first_window(wl.WORKLOADS[5], 17)) // 32
+    print(f"workload 5, layer 17, lazy decay: {stats}")
