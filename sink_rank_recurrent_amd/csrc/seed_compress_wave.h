@@ -179,41 +179,63 @@ struct Lay {
   static constexpr int PARTS = NTH / RMAX < 4 ? NTH / RMAX : 4;   // lanes per eigenvector
   static constexpr int NACT = RMAX * PARTS;        // threads holding eigenvector rows
   static constexpr int CH = NMAX / PARTS;          // rows per lane
-  static constexpr int G = 0;                      // [NMAX][LDN] Grams, Z, H, then reflectors (row k)
-  static constexpr int RB = G + NMAX * LDN;        // [NMAX][LDN] R~ by columns: RB[m*LDN + i] = R~[i][m]
-  static constexpr int XR = RB + (NO_RB ? 0 : NMAX * LDN);   // [NMAX][RMAX] eigenvectors, Y, then T'
-  static constexpr int FA = XR + NMAX * RMAX;      // [NMAX][RMAX] x 3: solve factors; FA then holds P2
-  static constexpr int FB = FA + NMAX * RMAX;
-  static constexpr int FC = FB + NMAX * RMAX;
-  static constexpr int CB = FC + NMAX * RMAX;      // [NTH] published column
-  static constexpr int VB = CB + NTH;              // [NTH] Householder vector
-  static constexpr int WB = VB + NTH;              // [NTH] rank-2 update vector / Cholesky row
-  static constexpr int CB2 = WB + NTH;             // [2][NMAX] Gram-Schmidt pivot (double buffer)
-  static constexpr int TD = CB2 + 2 * NMAX;        // [NMAX] diagonal of T
+  // one wave keeps two of the three solve factors of phase F in registers
+  static constexpr bool FREG = NW == 1;
+  static constexpr int G = 0;                      // [NMAX][LDN] Grams, Z, H (the conversion: then reflectors)
+  // [NMAX][LDN] R~ in pivot order, RB[p LDN + i] = R~[i][PIV[p]] (i <= p),
+  // and reflector k in row k at entries > k
+  static constexpr int RB = G + NMAX * LDN;
+  // The regions used from phase D on ("late") go into G, which is free once
+  // H is in registers, when they fit (the compression); else after RB.
+  static constexpr int LATE = 2 * NMAX * RMAX + (FREG ? 0 : 2 * NMAX * RMAX) + 6 * NMAX + 3 * RMAX;
+  static constexpr bool COMPACT = !NO_RB && LATE <= NMAX * LDN;
+  static constexpr int L0 = COMPACT ? G : RB + (NO_RB ? 0 : NMAX * LDN);
+  static constexpr int XR = L0;                    // [NMAX][RMAX] eigenvectors, Y, then T'
+  static constexpr int FA = XR + NMAX * RMAX;      // [NMAX][RMAX] reciprocal pivots of phase F, then P2
+  static constexpr int FB = FA + NMAX * RMAX;      // [NMAX][RMAX] x 2 (not with FREG): the superdiagonals
+  static constexpr int FC = FB + (FREG ? 0 : NMAX * RMAX);
+  static constexpr int TD = FC + (FREG ? 0 : NMAX * RMAX);   // [NMAX] diagonal of T
   static constexpr int TE = TD + NMAX;             // [NMAX] off-diagonal of T
   static constexpr int E2 = TE + NMAX;             // [NMAX] E2[i] = TE[i-1]^2
   static constexpr int TAU = E2 + NMAX;            // [NMAX]
-  static constexpr int DV = TAU + NMAX;            // [NMAX] column norms d of U
-  static constexpr int IDV = DV + NMAX;            // [NMAX] 1/d
-  static constexpr int IRD = IDV + NMAX;           // [NMAX] 1/R~[i][i]
-  static constexpr int BPT = FA;                   // [4 NTH] bisection points (FA is free then)
-  static constexpr int BFL = FA + 4 * NTH;         // [4 NTH] their flags (int)
-  static constexpr int LAM = IRD + NMAX;           // [RMAX] eigenvalues (descending)
+  static constexpr int CB2 = TAU + NMAX;           // [2][NMAX] Gram-Schmidt pivot (double buffer)
+  static constexpr int LAM = CB2 + 2 * NMAX;       // [RMAX] eigenvalues (descending)
   static constexpr int RNK = LAM + RMAX;           // [RMAX] round of each vector (int)
   static constexpr int STA = RNK + RMAX;           // [RMAX] first index of its run (int)
+  static constexpr int LEND = STA + RMAX;
+  static constexpr int BPT = XR;                   // [4 NTH] bisection points (XR, FA free then)
+  static constexpr int BFL = XR + 4 * NTH;         // [4 NTH] their flags (int)
+  // the regions used before phase D or throughout ("early")
+  static constexpr int E0 = COMPACT ? RB + NMAX * LDN : LEND;
+  static constexpr int CB = E0;                    // [NTH] published column
+  static constexpr int VB = CB + NTH;              // [NTH] Householder vector
+  static constexpr int WB = VB + NTH;              // [NTH] rank-2 update vector
+  static constexpr int DV = WB + NTH;              // [NMAX] column norms d of U
+  static constexpr int IDV = DV + NMAX;            // [NMAX] 1/d
+  static constexpr int IRD = IDV + NMAX;           // [NMAX] 1/R~[i][i]
+  static constexpr int PIV = IRD + NMAX;           // [NMAX] column at each pivot position (int)
   // decay product per key row (lazy form), 128 entries: in the 4 padding
   // columns of the rows of RB (never read or written otherwise) when they
   // hold 128 entries, else in a region of its own
   static constexpr bool GS_PAD = !NO_RB && 4 * NMAX >= 128;
-  static constexpr int PIV = STA + RMAX;           // [NMAX] column of each Cholesky step (int)
   static constexpr int GS = PIV + NMAX;
   static constexpr int RED = GS + (GS_PAD ? 0 : 128);   // [8][NW] cross-wave partials
   static constexpr int MISC = RED + 8 * NW + (8 * NW) % 4;
   static constexpr int TOTAL = MISC + 4;
   static_assert(NMAX % 16 == 0 && NMAX <= 128, "NMAX");
-  static_assert(8 * NTH <= 3 * NMAX * RMAX, "bisection points fit in the solve factors");
+  static_assert(8 * NTH <= 2 * NMAX * RMAX, "bisection points fit in XR and FA");
   static_assert(RMAX == 16 || RMAX == 32, "RMAX");
+  static_assert(!COMPACT || LEND <= G + NMAX * LDN, "late regions fit in G");
 };
+
+// Waves per SIMD the compiler plans registers for: two where a
+// compression's LDS lets more than four units share a CU, one otherwise
+// (the conversion, at n = d_k, keeps the whole register file).
+template <int NMAX, int RMAX, bool NO_RB>
+constexpr int wave_min_waves() {
+  return (!NO_RB && Lay<NMAX, RMAX, NO_RB>::NW == 1 &&
+          4 * Lay<NMAX, RMAX, NO_RB>::TOTAL <= 32 * 1024) ? 2 : 1;
+}
 
 // ---------------------------------------------------------------------------
 // A: G[i][j] = s_ij sum_e X[e][i] X[e][j] for i, j < NMAX (zero beyond n),
@@ -225,14 +247,17 @@ struct Lay {
 // meet in LDS (wave 1 stores, wave 0 adds and stores the total).  If rs is
 // not NULL, row e of X is first multiplied by rs[e] (rs_per_row) or by rs[0].
 // With CORR, column j is first replaced by X_j - ca[j] cb (the content of a
-// dense state: a row of S less its sink).
+// dense state: a row of S less its sink).  With PERM, entry (i, j) is that of
+// columns perm[i] and perm[j] (perm a permutation of 0 .. NMAX-1 that keeps
+// 0 .. n-1 among themselves), scaled by dv[perm[i]] dv[perm[j]].
 template <int NMAX, int NW, int D, bool SCALE, int FMT, int KR, typename ColF,
-          bool CORR = false>
+          bool CORR = false, bool PERM = false>
 __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
                                      int n, float* __restrict__ G,
                                      const float* __restrict__ dv, const float* __restrict__ rs,
                                      bool rs_per_row, const float* __restrict__ ca = nullptr,
-                                     const float* __restrict__ cb = nullptr) {
+                                     const float* __restrict__ cb = nullptr,
+                                     const int* __restrict__ perm = nullptr) {
   constexpr int LDN = NMAX + 4;
   constexpr int NT = NMAX / 16;
   constexpr int NP = NT * (NT + 1) / 2;
@@ -251,7 +276,8 @@ __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
     float x[NT][KC];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int col = t * 16 + ci;
+      const int pos = t * 16 + ci;
+      const int col = PERM ? perm[pos] : pos;
       const int off = (w * 4 + kk) * KPL + s0;
       if ((FMT == kStoreBF16 || FMT == kStoreF16) && col < n && col < KR) {
         const uint16_t* src = Xk + (size_t)col * D + off;
@@ -357,7 +383,7 @@ __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
         for (int r = 0; r < 4; ++r) {
           const int i = I * 16 + 4 * kk + r, j = J * 16 + ci;
           float v = acc[p][r];
-          if constexpr (SCALE) v *= dv[i] * dv[j];
+          if constexpr (SCALE) v *= dv[PERM ? perm[i] : i] * dv[PERM ? perm[j] : j];
           G[i * LDN + j] = v;
           G[j * LDN + i] = v;
         }
@@ -378,11 +404,11 @@ __device__ __forceinline__ bool live_row(int i, int j) {
 
 // D, one Householder step k: thread t owns column t of H in h, hk is
 // H[t][k], alpha = H[k+1][k], dkk = H[k][k].  Records T's row k and the
-// reflector (row k of G), then H <- H - v w^T - w v^T on the rows > k (rows
-// <= k of a column are never read again).
+// reflector (row k of RS, entries > k), then H <- H - v w^T - w v^T on the
+// rows > k (rows <= k of a column are never read again).
 template <int NMAX, int NW, bool STATIC>
 __device__ __forceinline__ void tri_step(float (&h)[NMAX], int k, float hk, float alpha, float dkk,
-                                         int t, bool act, float* VB, float* WB, float* G,
+                                         int t, bool act, float* VB, float* WB, float* RS,
                                          float* TD, float* TE, float* TAU, float* RED) {
   constexpr int LDN = NMAX + 4;
   const float xn2 = block_reduce<NW>(t > k + 1 ? hk * hk : 0.f, AddOp(), RED, 0);
@@ -401,10 +427,10 @@ __device__ __forceinline__ void tri_step(float (&h)[NMAX], int k, float hk, floa
     TE[k] = beta;
     TAU[k] = tau;
   }
-  if (act) {
-    VB[t] = vl;
-    G[k * LDN + t] = vl;                     // reflector k, zero at rows <= k
-  }
+  if (act) VB[t] = vl;
+  // reflector k in row k of RS at entries t > k (its zeros at t <= k are
+  // not stored: readers take them as zero)
+  if (act && t > k) RS[k * LDN + t] = vl;
   __syncthreads();
   // v is read whole before the first use (it stays live for the update)
   float vv[NMAX];
@@ -466,7 +492,9 @@ __device__ __forceinline__ void tri_step(float (&h)[NMAX], int k, float hk, floa
 // ---------------------------------------------------------------------------
 
 template <int NMAX, int RMAX, int DK, int DV_, int FMT>
-__global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(CompressArgs args) {
+__global__ __launch_bounds__(64 * ((NMAX + 63) / 64))
+__attribute__((amdgpu_waves_per_eu(wave_min_waves<NMAX, RMAX, FMT == kConvert>())))
+void compress_wave_kernel(CompressArgs args) {
   const int cap = args.cap, n = args.n, R = args.R;
   float* const __restrict__ U = args.U;
   float* const __restrict__ V = args.V;
@@ -517,6 +545,9 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     else return sm + L::GS + i;
   };
   float* const MISC = sm + L::MISC;
+  // the Householder reflectors: in the strict upper triangle of R~ (pivot
+  // order), or of G for the conversion, which has no R~
+  float* const RS = CONV ? G : RB;
 
   const int t = threadIdx.x;
   const bool act = t < NMAX;
@@ -561,8 +592,6 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     for (int i = 4 * t; i < NMAX * LDN; i += 4 * NTH)
       *reinterpret_cast<float4*>(RB + i) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int i = 4 * t; i < NMAX * RMAX; i += 4 * NTH)
-    *reinterpret_cast<float4*>(XR + i) = make_float4(0.f, 0.f, 0.f, 0.f);
   CB[t] = 0.f;
   VB[t] = 0.f;
   WB[t] = 0.f;
@@ -626,8 +655,6 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       dg = (act && t < n) ? G[t * LDN + t] * (it * it) : 0.f;
     }
     __syncthreads();
-    // Gram of V, scaled to D V^T V D, while the Cholesky runs on registers
-    gram<NMAX, NW, DV_, true, FMT, KR>(vcol, Vkh, n, G, DVs, nullptr, false);
 
     // @phase B: Cholesky with diagonal pivoting of the equilibrated U^T U,
     // thread t owning column t (g) and its own diagonal entry (dg).  Step j
@@ -648,6 +675,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     // the loop has one exit and its columns are updated in place.)
     bool taken = !(act && t < n && IDV[t] > 0.f);
     int kept = 0;
+    int mypos = -1;   // the step that takes this column as its pivot
     float mx = block_reduce<NW>(taken ? -1.f : dg, MaxOp(), RED, 6);
     for (int j = 0; j < n && mx > kPivTol; ++j) {
       const float cand = taken ? -1.f : dg;
@@ -655,6 +683,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       const float rp = frsq(mx);
       if (t == p) {
         taken = true;
+        mypos = j;
   #pragma unroll
         for (int i = 0; i < NMAX; i += 4)
           *reinterpret_cast<float4*>(CB + i) = make_float4(g[i], g[i + 1], g[i + 2], g[i + 3]);
@@ -678,11 +707,43 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       if constexpr (NW > 1) __syncthreads();
       mx = block_reduce<NW>(taken ? -1.f : dg, MaxOp(), RED, 6);
     }
-    for (int j = kept + t; j < NMAX; j += NTH) {
-      IRD[j] = 0.f;
-      PIV[j] = 0;
-    }
+    for (int j = kept + t; j < NMAX; j += NTH) IRD[j] = 0.f;
     if (t == 0) MISC[1] = __int_as_float(kept);
+
+    // The pivot order: position j < kept is step j's pivot, the columns
+    // never taken follow in column order (0 .. n-1 stay among the first n
+    // positions).  PIV[j] is the column at position j, and R~ moves to rows
+    // in that order: RB[j LDN + i] = R~[i][PIV[j]], zero for i > j, so R~
+    // is lower trapezoidal and the Householder reflectors fit in the strict
+    // upper triangle.  The V Gram is formed in the same order, so phases C
+    // and H read both as they are.
+    {
+      const bool rest = act && mypos < 0;
+      const unsigned long long b = __ballot(rest);
+      int before = __popcll(b & ((1ull << (t & 63)) - 1ull));
+      if constexpr (NW > 1) {
+        if (t == 0) MISC[2] = __int_as_float(__popcll(b));
+        __syncthreads();
+        if (t >= 64) before += __float_as_int(MISC[2]);
+      }
+      if (rest) mypos = kept + before;
+    }
+    if (act) PIV[mypos] = t;
+    __syncthreads();
+    {
+      float row[NMAX];
+      if (act) load_row<NMAX>(RB + t * LDN, row);
+      __syncthreads();
+      if (act) {
+  #pragma unroll
+        for (int i = 0; i < NMAX; i += 4)
+          *reinterpret_cast<float4*>(RB + mypos * LDN + i) =
+              make_float4(row[i], row[i + 1], row[i + 2], row[i + 3]);
+      }
+    }
+    // Gram of V in pivot order, scaled to D V^T V D
+    gram<NMAX, NW, DV_, true, FMT, KR, decltype(vcol), false, true>(
+        vcol, Vkh, n, G, DVs, nullptr, false, nullptr, nullptr, PIV);
     __syncthreads();
 
     // @phase C: Z = R~ G~ in place by column tiles, then H = Z R~^T in place
@@ -769,7 +830,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
         const float hk = h[k];
         const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hk), k + 1));
         const float dkk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hk), k));
-        tri_step<NMAX, NW, true>(h, k, hk, alpha, dkk, t, act, VB, WB, G, TD, TE, TAU, RED);
+        tri_step<NMAX, NW, true>(h, k, hk, alpha, dkk, t, act, VB, WB, RS, TD, TE, TAU, RED);
       }
     }
   } else {
@@ -780,7 +841,7 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           *reinterpret_cast<float4*>(CB + i) = make_float4(h[i], h[i + 1], h[i + 2], h[i + 3]);
       }
       __syncthreads();
-      tri_step<NMAX, NW, false>(h, k, CB[t], CB[k + 1], CB[k], t, act, VB, WB, G, TD, TE, TAU,
+      tri_step<NMAX, NW, false>(h, k, CB[t], CB[k + 1], CB[k], t, act, VB, WB, RS, TD, TE, TAU,
                                 RED);
     }
   }
@@ -916,7 +977,10 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   }
   __syncthreads();
 
-  // @phase F: eigenvectors of T by inverse iteration
+  // @phase F: eigenvectors of T by inverse iteration (the eigenvector block
+  // starts at zero; it shares LDS with G, or the bisection points, before)
+  for (int i = 4 * t; i < NMAX * RMAX; i += 4 * NTH)
+    *reinterpret_cast<float4*>(XR + i) = make_float4(0.f, 0.f, 0.f, 0.f);
   if (t < 64) {
     // separate equal shifts: lam'_c = min_{j <= c} (lam_j - (c - j) sep_j),
     // sep_j = 10 eps |lam_j| (floored as the bisection's stop).  A
@@ -949,16 +1013,10 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     const int maxr = (int)MISC[0];
     const float tiny = kEps * tnorm + 1e-30f;
     const int c = t;
-    // up to 64 rows, T sits in registers: the factor stores below would
-    // otherwise hold back every read of T on the serial chain
-    constexpr bool TREG = NMAX <= 64;
-    float tdr[TREG ? NMAX : 4], ter[TREG ? NMAX : 4];
-    if constexpr (TREG) {
-      load_row<NMAX>(TD, tdr);
-      load_row<NMAX>(TE, ter);
-    }
-    auto tdv = [&](int i) { if constexpr (TREG) return tdr[i]; else return TD[i]; };
-    auto tev = [&](int i) { if constexpr (TREG) return ter[i]; else return TE[i]; };
+    // T is read from LDS (the same entry in every lane, independent of the
+    // serial chain, so the unrolled loops issue the reads early); one wave
+    // keeps the two superdiagonals of U in registers, two waves in LDS
+    constexpr bool FREG = L::FREG;
     for (int rnd = 0; rnd <= maxr; ++rnd) {
       if (c < R && RNK[c] == rnd) {
         const float lc = LAM[c];
@@ -967,21 +1025,28 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
         for (int i = 0; i < NMAX; ++i) x[i] = (i < n) ? start_entry(i, c) : 0.f;
         for (int it = 0; it < kInvIters; ++it) {
           // factor T - lc I with partial pivoting while eliminating x; the
-          // reciprocal pivots and the two superdiagonals of U go to LDS, the
-          // eliminated right-hand side stays in x
-          float a = tdv(0) - lc, b1 = tev(0), b2 = 0.f, rr = x[0];
+          // reciprocal pivots go to LDS, the two superdiagonals of U to
+          // registers (one wave) or LDS, the eliminated right-hand side
+          // stays in x
+          float fb[FREG ? NMAX : 1], fc[FREG ? NMAX : 1];
+          float a = TD[0] - lc, b1 = TE[0], b2 = 0.f, rr = x[0];
 #pragma unroll
           for (int i = 0; i + 1 < NMAX; ++i) {
-            const float lw = tev(i);
-            const float ap = tdv(i + 1) - lc;
-            const float b1p = (i + 2 < NMAX) ? tev(i + 1) : 0.f;
+            const float lw = TE[i];
+            const float ap = TD[i + 1] - lc;
+            const float b1p = (i + 2 < NMAX) ? TE[i + 1] : 0.f;
             const float rp = x[i + 1];
             const bool sw = fabsf(lw) > fabsf(a);
             const float pa = sw ? lw : ((a != 0.f) ? a : tiny);
             const float ipa = frcp(pa);
             FA[i * RMAX + c] = ipa;
-            FB[i * RMAX + c] = sw ? ap : b1;
-            FC[i * RMAX + c] = sw ? b1p : b2;
+            if constexpr (FREG) {
+              fb[i] = sw ? ap : b1;
+              fc[i] = sw ? b1p : b2;
+            } else {
+              FB[i * RMAX + c] = sw ? ap : b1;
+              FC[i * RMAX + c] = sw ? b1p : b2;
+            }
             x[i] = sw ? rp : rr;
             const float mm = (sw ? a : lw) * ipa;
             const float na = fmaf(-mm, sw ? ap : b1, sw ? b1 : ap);
@@ -990,8 +1055,13 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
             a = na; b1 = nb1; b2 = 0.f; rr = nr;
           }
           FA[(NMAX - 1) * RMAX + c] = frcp((a != 0.f) ? a : tiny);
-          FB[(NMAX - 1) * RMAX + c] = 0.f;
-          FC[(NMAX - 1) * RMAX + c] = 0.f;
+          if constexpr (FREG) {
+            fb[NMAX - 1] = 0.f;
+            fc[NMAX - 1] = 0.f;
+          } else {
+            FB[(NMAX - 1) * RMAX + c] = 0.f;
+            FC[(NMAX - 1) * RMAX + c] = 0.f;
+          }
           x[NMAX - 1] = rr;
           // mx is the largest |x_i|; fmaxf drops NaN, so an overflow that
           // turned into inf - inf or 0 inf is caught by fin
@@ -999,7 +1069,15 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           bool fin = true;
 #pragma unroll
           for (int i = NMAX - 1; i >= 0; --i) {
-            const float xi = (x[i] - FB[i * RMAX + c] * x1 - FC[i * RMAX + c] * x2) * FA[i * RMAX + c];
+            float ub1, ub2;
+            if constexpr (FREG) {
+              ub1 = fb[i];
+              ub2 = fc[i];
+            } else {
+              ub1 = FB[i * RMAX + c];
+              ub2 = FC[i * RMAX + c];
+            }
+            const float xi = (x[i] - ub1 * x1 - ub2 * x2) * FA[i * RMAX + c];
             x[i] = xi;
             mx = fmaxf(mx, fabsf(xi));
             fin = fin && fabsf(xi) < 3.0e38f;
@@ -1073,20 +1151,23 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
     }
   }
 
-  // @phase G: back-transform Y -> Q Y through the reflectors (rows of G)
+  // @phase G: back-transform Y -> Q Y through the reflectors (rows of RS,
+  // entries > k; the entries <= k of row k hold R~ and read as zero)
   if (w0) {
     // reflector k (this lane's rows) and tau_k are read one step ahead; the
     // loop runs over every k < NMAX - 2 so that it unrolls, and skips
     // k > n - 3
     float vk[CH], vn[CH];
-    load_row<CH>(G + (NMAX - 3) * LDN + part * CH, vk);
+    load_row<CH>(RS + (NMAX - 3) * LDN + part * CH, vk);
     float tk = TAU[NMAX - 3], tn = 0.f;
 #pragma unroll
     for (int k = NMAX - 3; k >= 0; --k) {
       if (k > 0) {
-        load_row<CH>(G + (k - 1) * LDN + part * CH, vn);
+        load_row<CH>(RS + (k - 1) * LDN + part * CH, vn);
         tn = TAU[k - 1];
       }
+#pragma unroll
+      for (int s = 0; s < CH; ++s) vk[s] = (part * CH + s > k) ? vk[s] : 0.f;
       if (k <= n - 3) {
         float pd0 = 0.f, pd1 = 0.f;
 #pragma unroll
@@ -1108,7 +1189,8 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
   __syncthreads();
 
   if constexpr (!CONV) {
-    // @phase H: P2 = D R~^T X_R (MFMA, into FA), then T' = D^-1 R~^-1 X_R
+    // @phase H: P2 = D R~^T X_R (MFMA, into FA), then T' = D^-1 R~^-1 X_R;
+    // both by original column (row PIV[p] for R~'s row p in pivot order)
     {
       constexpr int NT = NMAX / 16;
       const int l = t & 63, w = t >> 6;
@@ -1121,13 +1203,16 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
           f4v acc = f4v{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
           for (int K = 0; K < NMAX / 4; ++K) {
-            const float av = RB[(16 * J + ci) * LDN + 4 * K + kk];   // R~[i][j]
+            // R~[i][PIV[p]] for p = 16 J + ci, i = 4 K + kk; beyond i = p the
+            // row holds a reflector
+            const float av = (4 * K + kk <= 16 * J + ci) ? RB[(16 * J + ci) * LDN + 4 * K + kk]
+                                                         : 0.f;
             const float bv = XR[(4 * K + kk) * RMAX + 16 * C + ci];  // X_R[i][c]
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
           }
   #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int j = 16 * J + 4 * kk + r;
+            const int j = PIV[16 * J + 4 * kk + r];
             FA[j * RMAX + 16 * C + ci] = DVs[j] * acc[r];
           }
         }
@@ -1140,24 +1225,24 @@ __global__ __launch_bounds__(64 * ((NMAX + 63) / 64)) void compress_wave_kernel(
       *reinterpret_cast<float4*>(XR + i) = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
     if (w0) {
-      // R11 y = X_R with R11[m][l] = R~[m][PIV[l]], upper triangular in step
-      // order, from the last kept step up: the lane owning row i broadcasts
-      // t_i to its group and stores t_i / d_p as row p = PIV[i] of T'.  The
-      // reciprocal pivots of the lane's own rows are read before the serial
-      // chain, and column PIV[i] of R~ one step ahead.
+      // R11 y = X_R with R11[m][l] = R~[m][PIV[l]] = RB[l LDN + m], upper
+      // triangular, from the last kept step up: the lane owning row i
+      // broadcasts t_i to its group and stores t_i / d_p as row p = PIV[i]
+      // of T'.  The reciprocal pivots of the lane's own rows are read before
+      // the serial chain, and row i of RB one step ahead.  Its entries
+      // m > i (a reflector) only reach rows of y already solved.
       const int kept = __float_as_int(MISC[1]);
       float ird[CH];
   #pragma unroll
       for (int s = 0; s < CH; ++s) ird[s] = IRD[part * CH + s];
       float rc[CH], rn[CH];
   #pragma unroll
-      for (int s = 0; s < CH; ++s) rc[s] = RB[PIV[NMAX - 1] * LDN + part * CH + s];
+      for (int s = 0; s < CH; ++s) rc[s] = RB[(NMAX - 1) * LDN + part * CH + s];
   #pragma unroll
       for (int i = NMAX - 1; i >= 0; --i) {
         if (i > 0) {
-          const int pn = PIV[i - 1];
   #pragma unroll
-          for (int s = 0; s < CH; ++s) rn[s] = RB[pn * LDN + part * CH + s];   // R~[m][PIV[i-1]]
+          for (int s = 0; s < CH; ++s) rn[s] = RB[(i - 1) * LDN + part * CH + s];   // R~[m][PIV[i-1]]
         }
         if (i < kept) {
           const int own = i / CH, si = i - (i / CH) * CH;

@@ -202,11 +202,11 @@ __device__ __forceinline__ void top_vector(float lam, float tn, const float* G, 
     }
   }
   __syncthreads();
-  // x <- Q x, Q = H_0 H_1 ... H_{n-3} (reflector k in row k of G)
+  // x <- Q x, Q = H_0 H_1 ... H_{n-3} (reflector k in row k of G, entries > k)
   float xt = X1[t];
   __syncthreads();
   for (int k = NMAX - 3; k >= 0; --k) {
-    const float vk = G[k * LDN + t];
+    const float vk = (t > k) ? G[k * LDN + t] : 0.f;   // reflector k: entries > k
     const float d = block_reduce<NW>(vk * xt, AddOp(), RED, (k & 1) ? 7 : 4);
     xt = fmaf(-TAU[k] * d, vk, xt);
   }
