@@ -151,18 +151,35 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.cmd == "pmc":
+        # only the dispatches of the stated size (a warm-up launch of one
+        # unit is left out); the SQ counters may see part of the GPU, so the
+        # per-wave figures divide by SQ_WAVES of the same dispatches
+        grid = args.units * args.waves_per_unit * 64
         means = {}
         for path in args.csvs:
-            per = counter_totals(path, args.kernel)
+            rows = [r for r in csv.DictReader(open(path)) if re.search(args.kernel, r["Kernel_Name"])]
+            if rows and "Grid_Size" in rows[0]:
+                rows = [r for r in rows if int(float(r["Grid_Size"])) == grid]
+            per = defaultdict(lambda: defaultdict(float))
+            for r in rows:
+                per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
             names = sorted({k for d in per.values() for k in d})
             for name in names:
                 vals = [d[name] for d in per.values() if name in d]
                 means[name] = (sum(vals) / len(vals), len(vals))
+        waves = means.get("SQ_WAVES", (None, 0))[0]
         lines = [f"# {args.title}", "", "Commands:", "", "```", args.command, "```", "",
-                 f"Kernel: `{args.kernel}`, {args.units} units per dispatch.", "",
-                 "| counter | dispatches | mean per dispatch | per unit |", "|---|---|---|---|"]
+                 f"Kernel: `{args.kernel}`, dispatches of {args.units} units "
+                 f"({args.waves_per_unit} wave(s) per unit) only."]
+        if waves:
+            lines += ["", f"SQ_WAVES counts {waves:.0f} of the {args.units * args.waves_per_unit} "
+                      f"waves of a dispatch ({waves / (args.units * args.waves_per_unit):.3f}): "
+                      "the SQ counters see that share of the GPU, so the per-wave column "
+                      "divides by SQ_WAVES."]
+        lines += ["", "| counter | dispatches | mean per dispatch | per wave |", "|---|---|---|---|"]
         for name, (v, nd) in sorted(means.items()):
-            lines.append(f"| {name} | {nd} | {v:.4g} | {v / args.units:.4g} |")
+            pw = f"{v / waves:.4g}" if waves else "-"
+            lines.append(f"| {name} | {nd} | {v:.4g} | {pw} |")
         lines.append("")
         with open(args.out, "w") as f:
             f.write("\n".join(lines))
