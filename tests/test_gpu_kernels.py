@@ -126,6 +126,9 @@ def _oracle_precompress_states(rule, d_k, d_v, R, n, seed, units=4):
     ("gdn", (128, 128), 16, 32, 33),     # compress before the ring is full, odd n
     ("kda", (128, 128), 16, 64, 80),
     ("kda", (128, 128), 32, 64, 96),     # largest capacity
+    ("gdn", (128, 128), 16, 48, 64),     # one wave holding 64 columns
+    ("kda", (128, 128), 16, 48, 57),     # 49 .. 64 columns, odd n
+    ("gdn", (128, 128), 24, 24, 48),     # R above 16: the layout with separate late regions
     ("mamba2", (128, 64), 16, 32, 48),
     ("mamba2", (128, 64), 16, 32, 47),
     ("gdn", (64, 64), 8, 24, 32),
