@@ -8,8 +8,11 @@
 #        R = 16, W = 32: every compression of n = 48 columns);
 #   n80: workload 4 (64 requests x 32 KDA heads, 2048 units, R = 16, W = 64:
 #        n = 80, two waves per unit),
-# counted on the fp32 compression instance only, then summarised per
-# dispatch and per unit -> OUT_DIR/counters_compress_wave_<case>.md.
+# counted on the fp32 compression instance only, and
+#   conv: the end-of-prefill conversion of workload 2 (1024 dense 128 x 128
+#        states to rank 16, two waves per unit, the conversion instance),
+# then summarised per dispatch and per wave ->
+# OUT_DIR/counters_compress_wave_<case>.md.
 # Raw profiler output stays in a temporary directory under /tmp.
 set -eu -o pipefail
 if [ $# -ne 1 ]; then
@@ -24,9 +27,14 @@ export TMPDIR=/tmp
 work=$(mktemp -d /tmp/seedcprof.XXXXXX)
 p1="SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_WAVE_CYCLES SQ_BUSY_CYCLES"
 p2="SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_LDS_BANK_CONFLICT"
-regex='compress_wave_kernel<[0-9]+, [0-9]+, [0-9]+, [0-9]+, 0>'
-for case in n48 n80; do
-  if [ "$case" = n48 ]; then
+for case in n48 n80 conv; do
+  regex='compress_wave_kernel<[0-9]+, [0-9]+, [0-9]+, [0-9]+, 0>'
+  if [ "$case" = conv ]; then
+    args="--workload 2 --no-cpu --no-dense --no-variant --no-sub --steps 32 --warmup 0"
+    units=1024
+    wpu=2
+    regex='compress_wave_kernel<128, 16, 128, 128, 4>'
+  elif [ "$case" = n48 ]; then
     args="--workload 5 --layers 1 --no-cpu --no-dense --no-variant --no-sub --steps 64 --warmup 0"
     units=8192
     wpu=1
@@ -50,4 +58,4 @@ for case in n48 n80; do
     --out "$out/counters_compress_wave_$case.md" > /dev/null
 done
 rm -rf "$work"
-echo "[profile] done: $out/counters_compress_wave_n48.md $out/counters_compress_wave_n80.md" >&2
+echo "[profile] done: $out/counters_compress_wave_{n48,n80,conv}.md" >&2
