@@ -489,6 +489,87 @@ __device__ __forceinline__ void tri_step(float (&h)[NMAX], int k, float hk, floa
   }
 }
 
+// D with two waves and k a compile-time constant (fully unrolled), step k in
+// three barriers.  Thread t's own entry k stands for H[t][k] (H is
+// symmetric); the owners of rows k and k + 1 store d_kk and alpha into ad
+// before the barrier of the norm's reduction.  v goes through VB, and p
+// through WB together with the per-wave partial sums of v^T p (slot 1 of
+// red).  Live rows are the aligned 4-row groups past row k, as in tri_step.
+// Each slot is rewritten one step later, past a barrier that all its reads
+// precede.
+template <int NMAX, int NW>
+__device__ __forceinline__ void tri_step_static2(float (&h)[NMAX], int k, int t, bool act, float* VB,
+                                                 float* WB, float* RS, float* TD, float* TE,
+                                                 float* TAU, float* red, float* ad) {
+  constexpr int LDN = NMAX + 4;
+  const float hk = h[k];
+  if (t == k) ad[0] = hk;
+  if (t == k + 1) ad[1] = hk;
+  const float xn2 = block_reduce<NW>(t > k + 1 ? hk * hk : 0.f, AddOp(), red, 0);
+  const float dkk = ad[0], alpha = ad[1];
+  float tau = 0.f, beta = alpha, sc = 0.f;
+  // a column whose sub-subdiagonal part squares to a subnormal is taken as
+  // already reduced (as in tri_step)
+  if (xn2 >= kMinNormal) {
+    const float nrm = fsqrt(fmaf(alpha, alpha, xn2));
+    beta = alpha >= 0.f ? -nrm : nrm;
+    tau = (beta - alpha) * frcp(beta);
+    sc = frcp(alpha - beta);
+  }
+  const float vl = (t > k + 1) ? hk * sc : (t == k + 1 ? 1.f : 0.f);
+  if (t == 0) {
+    TD[k] = dkk;
+    TE[k] = beta;
+    TAU[k] = tau;
+  }
+  if (act) VB[t] = vl;
+  if (act && t > k) RS[k * LDN + t] = vl;
+  __syncthreads();
+  float vv[NMAX];
+#pragma unroll
+  for (int i = 0; i < NMAX; i += 4) {
+    if (live_row<true>(i + 3, k)) {
+      const float4 x4 = *reinterpret_cast<const float4*>(VB + i);
+      vv[i] = x4.x; vv[i + 1] = x4.y; vv[i + 2] = x4.z; vv[i + 3] = x4.w;
+    } else {
+      vv[i] = vv[i + 1] = vv[i + 2] = vv[i + 3] = 0.f;
+    }
+  }
+  float pa = 0.f, pb = 0.f;
+#pragma unroll
+  for (int i = 0; i < NMAX; i += 2) {
+    if (live_row<true>(i, k)) {
+      pa = fmaf(h[i], vv[i], pa);
+      pb = fmaf(h[i + 1], vv[i + 1], pb);
+    }
+  }
+  const float pl = (pa + pb) * tau;
+  if (act) WB[t] = pl;
+  const float part = wave_reduce(pl * vl, AddOp());
+  if ((t & 63) == 0) red[NW + (t >> 6)] = part;
+  __syncthreads();
+  float vp = red[NW];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) vp += red[NW + w];
+  // w = p + K v with K = -tau/2 v^T p; H <- H - v w^T - w v^T, on this
+  // column h - v (w_t + K v_t) - p v_t
+  const float K = -0.5f * tau * vp;
+  const float wl = fmaf(K, vl, pl);
+  const float a = fmaf(K, vl, wl);
+#pragma unroll
+  for (int i = 0; i < NMAX; i += 4) {
+    if (live_row<true>(i + 3, k)) {
+      const float4 p4 = *reinterpret_cast<const float4*>(WB + i);
+      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        h[i + s] = fmaf(-vv[i + s], a, h[i + s]);
+        h[i + s] = fmaf(-pv[s], vl, h[i + s]);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 
 template <int NMAX, int RMAX, int DK, int DV_, int FMT>
@@ -832,6 +913,13 @@ void compress_wave_kernel(CompressArgs args) {
         const float dkk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hk), k));
         tri_step<NMAX, NW, true>(h, k, hk, alpha, dkk, t, act, VB, WB, RS, TD, TE, TAU, RED);
       }
+    }
+  } else if constexpr (NW == 2 && NMAX <= 96) {
+    // two waves (compressions at 64 < n <= 96): fully unrolled as well
+#pragma clang loop unroll(full)
+    for (int k = 0; k < NMAX - 2; ++k) {
+      if (k + 2 < n)
+        tri_step_static2<NMAX, NW>(h, k, t, act, VB, WB, RS, TD, TE, TAU, RED, CB);
     }
   } else {
     for (int k = 0; k + 2 < n; ++k) {

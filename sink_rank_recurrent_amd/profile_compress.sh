@@ -1,7 +1,7 @@
 #!/bin/bash
 # Instruction and cycle counters of the compression kernel on one MI355X.
 #
-#   sink_rank_recurrent_amd/profile_compress.sh OUT_DIR
+#   sink_rank_recurrent_amd/profile_compress.sh OUT_DIR [CASE ...]
 #
 # Two rocprofv3 --pmc passes (at most 8 SQ counters each) over each of:
 #   n48: one layer of workload 5 (256 requests x 32 GDN heads, 8192 units,
@@ -12,14 +12,23 @@
 #   conv: the end-of-prefill conversion of workload 2 (1024 dense 128 x 128
 #        states to rank 16, two waves per unit, the conversion instance),
 # then summarised per dispatch and per wave ->
-# OUT_DIR/counters_compress_wave_<case>.md.
+# OUT_DIR/counters_compress_wave_<case>.md.  CASE limits the run to the
+# cases named (default: all three).
 # Raw profiler output stays in a temporary directory under /tmp.
 set -eu -o pipefail
-if [ $# -ne 1 ]; then
-  echo "usage: $0 OUT_DIR" >&2
+if [ $# -lt 1 ]; then
+  echo "usage: $0 OUT_DIR [n48|n80|conv ...]" >&2
   exit 2
 fi
 out=$1
+shift
+cases=${*:-n48 n80 conv}
+for case in $cases; do
+  case $case in
+    n48|n80|conv) ;;
+    *) echo "unknown case $case (n48, n80 or conv)" >&2; exit 2 ;;
+  esac
+done
 root=$(cd "$(dirname "$0")/.." && pwd)
 cd "$root"
 mkdir -p "$out"
@@ -27,7 +36,7 @@ export TMPDIR=/tmp
 work=$(mktemp -d /tmp/seedcprof.XXXXXX)
 p1="SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_WAVE_CYCLES SQ_BUSY_CYCLES"
 p2="SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_LDS_BANK_CONFLICT"
-for case in n48 n80 conv; do
+for case in $cases; do
   regex='compress_wave_kernel<[0-9]+, [0-9]+, [0-9]+, [0-9]+, 0>'
   if [ "$case" = conv ]; then
     args="--workload 2 --no-cpu --no-dense --no-variant --no-sub --steps 32 --warmup 0"
@@ -54,8 +63,8 @@ for case in n48 n80 conv; do
   done
   python3 -m sink_rank_recurrent_amd.profile_summary pmc $csvs --kernel "$regex" --units $units --waves-per-unit $wpu \
     --title "Counters of the compression kernel ($case): bench.py $args" \
-    --command "sink_rank_recurrent_amd/profile_compress.sh $out   # runs, for the two counter sets: rocprofv3 --pmc <set> --kernel-include-regex '$regex' -d <tmp> -o p<k> --output-format csv -- python3 bench.py $args; set 1: $p1; set 2: $p2" \
+    --command "sink_rank_recurrent_amd/profile_compress.sh $out $case   # runs, for the two counter sets: rocprofv3 --pmc <set> --kernel-include-regex '$regex' -d <tmp> -o p<k> --output-format csv -- python3 bench.py $args; set 1: $p1; set 2: $p2" \
     --out "$out/counters_compress_wave_$case.md" > /dev/null
 done
 rm -rf "$work"
-echo "[profile] done: $out/counters_compress_wave_{n48,n80,conv}.md" >&2
+echo "[profile] done: $(for c in $cases; do printf "%s " "$out/counters_compress_wave_$c.md"; done)" >&2

@@ -272,18 +272,22 @@ def test_nan_stays_in_its_unit():
     assert torch.isnan(st.a[1, 2]).any() and torch.isnan(st.a).any(dim=-1).sum() == 1
 
 
+@pytest.mark.parametrize("W", [32, 64])   # one wave (n = 48), two waves (n = 80)
 @pytest.mark.parametrize("case", ["dup_keys", "near_dup_keys", "zero_v_cols", "all_zero_v", "zero_u_cols"])
-def test_compress_degenerate(case):
+def test_compress_degenerate(case, W):
     d_k = d_v = 128
-    R, W = 16, 32
+    R = 16
     n = R + W
-    rng = np.random.default_rng(73)
+    rng = np.random.default_rng(73 + W)
     units = B * H
     U = rng.standard_normal((units, d_k, n)) / np.sqrt(d_k)
     V = rng.standard_normal((units, d_v, n))
     if case == "dup_keys":
         U[:, :, 30] = 0.7 * U[:, :, 5]
         U[:, :, 41] = U[:, :, 40]
+        if n > 64:
+            # a column of the second wave repeats one of the first
+            U[:, :, 70] = -U[:, :, 10]
     elif case == "near_dup_keys":
         # keys at angles with sines 1e-3 .. 1e-2 from earlier ones (unit by
         # unit), the rest of the column orthogonal noise of that size
