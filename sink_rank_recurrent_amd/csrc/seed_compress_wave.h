@@ -207,13 +207,22 @@ struct Lay {
   static constexpr int BFL = XR + 4 * NTH;         // [4 NTH] their flags (int)
   // the regions used before phase D or throughout ("early")
   static constexpr int E0 = COMPACT ? RB + NMAX * LDN : LEND;
-  static constexpr int CB = E0;                    // [NTH] published column
+  // The published vectors and the two scales of phase H go into the tail of
+  // G past the late regions when they fit there: G holds nothing during
+  // phase B (each thread has its Gram column in registers) and nothing
+  // there from phase D on, and the scales are kept in registers until D
+  // stores them.  That keeps a unit at n = 48, R = 16 within 20 KB, so
+  // eight units share a CU.
+  static constexpr int TAILN = 3 * NTH + 2 * NMAX;
+  static constexpr bool TAIL = COMPACT && LEND + TAILN <= G + NMAX * LDN;
+  static constexpr int T0 = TAIL ? LEND : E0;
+  static constexpr int CB = T0;                    // [NTH] published column
   static constexpr int VB = CB + NTH;              // [NTH] Householder vector
   static constexpr int WB = VB + NTH;              // [NTH] rank-2 update vector
-  static constexpr int DV = WB + NTH;              // [NMAX] column norms d of U
-  static constexpr int IDV = DV + NMAX;            // [NMAX] 1/d
-  static constexpr int IRD = IDV + NMAX;           // [NMAX] 1/R~[i][i]
-  static constexpr int PIV = IRD + NMAX;           // [NMAX] column at each pivot position (int)
+  static constexpr int IDV = WB + NTH;             // [NMAX] 1/d (stored in phase D)
+  static constexpr int IRD = IDV + NMAX;           // [NMAX] 1/R~[i][i] (stored in phase D)
+  static constexpr int DV = TAIL ? E0 : IRD + NMAX;   // [NMAX] column norms d of U
+  static constexpr int PIV = DV + NMAX;            // [NMAX] column at each pivot position (int)
   // decay product per key row (lazy form), 128 entries: in the 4 padding
   // columns of the rows of RB (never read or written otherwise) when they
   // hold 128 entries, else in a region of its own
@@ -673,9 +682,15 @@ void compress_wave_kernel(CompressArgs args) {
     for (int i = 4 * t; i < NMAX * LDN; i += 4 * NTH)
       *reinterpret_cast<float4*>(RB + i) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  CB[t] = 0.f;
-  VB[t] = 0.f;
-  WB[t] = 0.f;
+  if constexpr (!L::TAIL) {
+    // (in G's tail they are written before every read)
+    CB[t] = 0.f;
+    VB[t] = 0.f;
+    WB[t] = 0.f;
+  }
+  // this column's 1/d and the reciprocal pivot of step t (phase B), kept in
+  // registers until phase D stores them for phase H
+  float idv_own = 0.f, ird_own = 0.f;
   if (gamh != nullptr) {
     // the decay product of every key row, staged once
     __syncthreads();   // after the zeroing of RB
@@ -722,17 +737,21 @@ void compress_wave_kernel(CompressArgs args) {
       const float gtt = G[t * LDN + t];
       const bool pos = t < n && gtt >= kMinNormal;
       DVs[t] = pos ? fsqrt(gtt) : 0.f;
-      IDV[t] = pos ? frsq(gtt) : 0.f;
+      idv_own = pos ? frsq(gtt) : 0.f;
     }
-    __syncthreads();
     float g[NMAX];
     float dg;   // this column's own diagonal entry of the Schur complement
     {
-      const float it = act ? IDV[t] : 0.f;
+      const float it = idv_own;
       // the scale d_t^-1 d_i^-1 is one product for both (i, t) and (t, i), so
-      // the columns stay exactly symmetric through the Cholesky
+      // the columns stay exactly symmetric through the Cholesky; 1/d_i is
+      // formed from the diagonal as thread i forms its own
   #pragma unroll
-      for (int i = 0; i < NMAX; ++i) g[i] = act ? G[i * LDN + t] * (it * IDV[i]) : 0.f;
+      for (int i = 0; i < NMAX; ++i) {
+        const float gii = G[i * LDN + i];
+        const float di = (i < n && gii >= kMinNormal) ? frsq(gii) : 0.f;
+        g[i] = act ? G[i * LDN + t] * (it * di) : 0.f;
+      }
       dg = (act && t < n) ? G[t * LDN + t] * (it * it) : 0.f;
     }
     __syncthreads();
@@ -745,7 +764,8 @@ void compress_wave_kernel(CompressArgs args) {
     // columns are conditioned.  It stops when that diagonal is at most
     // kPivTol.  Row j of R~ is kept by original column,
     // RB[t LDN + j] = R~[j][t] (0 for the columns taken before), with
-    // IRD[j] = 1 / R~[j][p] and PIV[j] = p; rows from `kept` on are zero.
+    // 1 / R~[j][p] kept by thread j and PIV[j] = p; rows from `kept` on are
+    // zero.
     // The pivot value is the reduction's maximum (the pivot's own dg, equal
     // to its column's entry p up to rounding), and row j of R~ is the
     // published column times its reciprocal square root, so a step takes one
@@ -754,7 +774,7 @@ void compress_wave_kernel(CompressArgs args) {
     // the rows of earlier pivots are never read again.
     // (The largest diagonal is reduced at the end of the previous step, so
     // the loop has one exit and its columns are updated in place.)
-    bool taken = !(act && t < n && IDV[t] > 0.f);
+    bool taken = !(act && t < n && idv_own > 0.f);
     int kept = 0;
     int mypos = -1;   // the step that takes this column as its pivot
     float mx = block_reduce<NW>(taken ? -1.f : dg, MaxOp(), RED, 6);
@@ -775,10 +795,8 @@ void compress_wave_kernel(CompressArgs args) {
       const float ct = CB[t];
       const float r = (act && !taken) ? ct * rp : 0.f;
       if (act) RB[t * LDN + j] = (t == p) ? mx * rp : r;
-      if (t == 0) {
-        IRD[j] = rp;
-        PIV[j] = p;
-      }
+      if (t == j) ird_own = rp;
+      if (t == 0) PIV[j] = p;
       const float rr = r * rp;
   #pragma unroll
       for (int i = 0; i < NMAX; ++i) g[i] = fmaf(-wr[i], rr, g[i]);
@@ -788,7 +806,6 @@ void compress_wave_kernel(CompressArgs args) {
       if constexpr (NW > 1) __syncthreads();
       mx = block_reduce<NW>(taken ? -1.f : dg, MaxOp(), RED, 6);
     }
-    for (int j = kept + t; j < NMAX; j += NTH) IRD[j] = 0.f;
     if (t == 0) MISC[1] = __int_as_float(kept);
 
     // The pivot order: position j < kept is step j's pivot, the columns
@@ -902,6 +919,14 @@ void compress_wave_kernel(CompressArgs args) {
 #pragma unroll
   for (int i = 0; i < NMAX; ++i) h[i] = act ? G[i * LDN + t] * hs : 0.f;
   __syncthreads();
+  if constexpr (!CONV) {
+    // the scales phase H reads: IDV[i] = 1/d_i, IRD[j] = 1/R~[j][PIV[j]]
+    // (zero from `kept` on)
+    if (act) {
+      IDV[t] = idv_own;
+      IRD[t] = ird_own;
+    }
+  }
   if constexpr (NW == 1) {
     // one wave: fully unrolled, so h[k] is a fixed register; H is
     // symmetric, so entry k of this thread's column stands for H[t][k]
