@@ -718,7 +718,7 @@ def stats_of(w, S, vbar, dev: str) -> dict:
 
 
 def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, timed, dev,
-                         aligned, overlap: bool = True):
+                         aligned, overlap: bool = True, delays=None):
     """Requests that arrive at different times, on the stack, against the
     aligned lazily decayed form (`aligned`):
       * one global phase: an arriving request joins mid-window
@@ -727,7 +727,8 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
       * per-request schedules (seed_decode_step_sched): request b starts at
         phase b mod W and compresses on its own schedule, the snapshots of
         D consecutive steps compressed by one launch, D the smallest delay
-        whose launch gives every SIMD of the GPU a unit.
+        whose launch gives every SIMD of the GPU two units (the compression
+        at n <= 64 is built for two waves per SIMD), or each of `delays`.
     The global phase runs its compressions as the aligned run does (on a
     side stream with overlap, else on the launch stream); the per-request
     schedules' smaller launches always run on a side stream."""
@@ -757,13 +758,23 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
     units = spec.units
     simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
     cap_d = min(w.W - 1, 96 - w.R - w.W)
-    D = min(cap_d, -(-simds // (units // w.W)))
+    for D in (delays or [min(cap_d, -(-2 * simds // (units // w.W)))]):
+        out.append(_per_request_run(w, spec, vbars, Ss, inputs, outs, pre, settle, timed, dev,
+                                    aligned, min(D, cap_d)))
+    return out
+
+
+def _per_request_run(w, spec, vbars, Ss, inputs, outs, pre, settle, timed, dev, aligned, D):
+    import torch
+    from sink_rank_recurrent_amd import binding
+
+    units = spec.units
     t_start = [-(b % w.W) - (w.W + D) for b in range(w.batch)]
     scheds = []
     for l, (vbar, S) in enumerate(zip(vbars, Ss)):
-        # a launch holds the units of D phases only (1024 of 8192 at D = 4),
-        # so it leaves most CUs to the steps: on a side stream it runs beside
-        # them (4.10 against 4.40 ms per step on the launch stream)
+        # a launch holds the units of D phases only (2048 of 8192 at D = 8),
+        # so it leaves CUs to the steps: on a side stream it runs beside them
+        # (at D = 4, 4.10 against 4.40 ms per step on the launch stream)
         st = binding.ScheduledState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, D, vbar,
                                     t_start, device=dev, side_streams=1)
         st.from_dense(S)
@@ -794,19 +805,20 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
     value = len(scheds) * units * timed / el
     cols = [scheds[0].held_columns(b, t) for t in range(pre + settle, pre + settle + timed)
             for b in range(w.batch)]
-    out.append({"kind": "per-request schedules (seed_decode_step_sched): request b starts at "
-                        "phase b mod W, the snapshots of D consecutive steps share one "
-                        "compression launch", "D": D, "value": value, "unit": "head-steps/s",
-                "ms_per_step": el * 1e3 / timed, "mean_columns": sum(cols) / len(cols),
-                "vs_aligned_lazy": value / aligned["value"] if aligned else None})
+    res = {"kind": "per-request schedules (seed_decode_step_sched): request b starts at "
+                   "phase b mod W, the snapshots of D consecutive steps share one "
+                   "compression launch", "D": D, "value": value, "unit": "head-steps/s",
+           "ms_per_step": el * 1e3 / timed, "mean_columns": sum(cols) / len(cols),
+           "vs_aligned_lazy": value / aligned["value"] if aligned else None}
     log(f"{w.name} [per-request schedules, D = {D}]: {el * 1e3 / timed:.3f} ms per step")
     del g, scheds
     torch.cuda.empty_cache()
-    return out
+    return res
 
 
 def run_workload(w, layers: int, settle: int, timed: int, dev: str, forms, with_dense: bool,
                  keep_layer0: bool = False, no_stagger: bool = True, overlap: bool = False,
+                 delays=None,
                  other_schedule: bool = False):
     """Prefill, convert and time `layers` layers of workload w in every form
     of `forms` (compressions overlapped on a side stream, or not), then the
@@ -858,7 +870,7 @@ def run_workload(w, layers: int, settle: int, timed: int, dev: str, forms, with_
     if "lazy" in forms and layers > 1 and not no_stagger:
         results["stagger"] = run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre,
                                                   settle, timed, dev, results.get("lazy"),
-                                                  overlap=overlap)
+                                                  overlap=overlap, delays=delays)
     dense = None
     if with_dense:
         d = run_dense(w, Ss, inputs, outs, pre, settle, timed)
@@ -890,6 +902,9 @@ def main() -> int:
                     help="skip the lazily decayed and 16-bit forms")
     ap.add_argument("--no-sub", action="store_true",
                     help="skip the other workloads' entries")
+    ap.add_argument("--stagger-d", type=lambda x: [int(v) for v in x.split(",")], default=None,
+                    help="merge delays D of the per-request schedule variant (comma list; "
+                         "default: the smallest that gives every SIMD a unit per launch)")
     ap.add_argument("--overlap", action="store_true",
                     help="run each layer's compression on a side stream, beside the other "
                          "layers' steps (default: on the launch stream after its bench step; "
@@ -935,7 +950,8 @@ def main() -> int:
     results, dense, conv_ms, layer0 = run_workload(w, L, warmup, steps, dev, forms,
                                                    not args.no_dense, keep_layer0=True,
                                                    no_stagger=args.no_variant, overlap=overlap,
-                                                   other_schedule=not args.no_variant)
+                                                   other_schedule=not args.no_variant,
+                                                   delays=args.stagger_d)
     head = results[forms[0]]
 
     handoff = stats = None

@@ -56,11 +56,15 @@ namespace seed {
 
 constexpr float kFoldBelow = 0x1p-64f;
 constexpr float kPoisonBelow = 0x1p-110f;
+// Lazily decayed launches (fp32, 16-bit or ring layout) of at least this
+// many units and at most 48 held columns use 8 column groups (256 threads)
+// per workgroup: 5 to 8 units share a CU instead of 4.  The form decayed in
+// place keeps 16 groups (its U write-back fills the combine phase), as do
+// small batches, which 16 groups spread over more of the GPU.
+constexpr int kHalfGroupUnits = 4096;
 
-constexpr int kGroups = 16;   // column groups (half-waves) per workgroup
-
-template <int RULE, int DK, int DV, typename IN_T, int SLOTS, bool LAZY, int FMT>
-__global__ __launch_bounds__(32 * kGroups) void seed_step_kernel(
+template <int RULE, int DK, int DV, typename IN_T, int NG, int SLOTS, bool LAZY, int FMT>
+__global__ __launch_bounds__(32 * NG) void seed_step_kernel(
     float* __restrict__ a, float* __restrict__ U, float* __restrict__ V,
     uint16_t* __restrict__ Uk, const uint16_t* __restrict__ Vk, float* __restrict__ gam,
     const float* __restrict__ vbar, const IN_T* __restrict__ q, const IN_T* __restrict__ k,
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(32 * kGroups) void seed_step_kernel(
   float w[SLOTS][EV];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
-    const int j = grp + kGroups * s;
+    const int j = grp + NG * s;
     if (H16 && j < r && j < kR) {
       load_vec16_nt<FMT, EK>(Uk + (ub * kR + j) * DK + lane * EK, u[s]);
       load_vec16_nt<FMT, EV>(Vk + (ub * kR + j) * DV + lane * EV, w[s]);
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(32 * kGroups) void seed_step_kernel(
         // fold the decay product into every held column, then restart it
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) {
-          const int j = grp + kGroups * s;
+          const int j = grp + NG * s;
           if (j < r) {
 #pragma unroll
             for (int e = 0; e < EK; ++e) u[s][e] *= gn[e];
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(32 * kGroups) void seed_step_kernel(
     } else if (any) {
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
-        const int j = grp + kGroups * s;
+        const int j = grp + NG * s;
         if (j < r) {
 #pragma unroll
           for (int e = 0; e < EK; ++e)
@@ -285,13 +289,13 @@ __global__ __launch_bounds__(32 * kGroups) void seed_step_kernel(
         pk += x * kk[e];
         pq += x * qq[e];
       }
-      const int j = grp + kGroups * s;
+      const int j = grp + NG * s;
       if (j < r) store_vec_nt<EK>(ucol(j) + lane * EK, u[s]);
     }
     ck[s] = pk;
     cq[s] = pq;
   }
-  if (grp == r % kGroups) {
+  if (grp == r % NG) {
     if constexpr (LAZY) {
       float kd[EK];
 #pragma unroll
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(32 * kGroups) void seed_step_kernel(
 
   // 7. combine the column groups through LDS: thread e < d_v finishes
   // value entry e (a short tail: 2 kGroups partial sums per thread)
-  __shared__ float red[2][kGroups][DV];
+  __shared__ float red[2][NG][DV];
   __shared__ float eps_s[DV], sink_s[DV];
 #pragma unroll
   for (int e = 0; e < EV; ++e) {
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(32 * kGroups) void seed_step_kernel(
   if (tid < DV) {
     float tk = 0.f, tq = 0.f;
 #pragma unroll
-    for (int c = 0; c < kGroups; ++c) {
+    for (int c = 0; c < NG; ++c) {
       tk += red[0][c][tid];
       tq += red[1][c][tid];
     }
@@ -385,37 +389,49 @@ struct StepArgs {
   float* o;
 };
 
-template <int RULE, int DK, int DV, typename IN_T, int SLOTS, bool LAZY, int FMT>
+template <int RULE, int DK, int DV, typename IN_T, int NG, int SLOTS, bool LAZY, int FMT>
 void step_launch(const StepArgs& p, hipStream_t s) {
-  hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, SLOTS, LAZY, FMT>), dim3(p.units),
-                     dim3(32 * kGroups), 0, s, p.a, p.U, p.V, p.Uk, p.Vk, p.gam, p.vbar,
+  hipLaunchKernelGGL((seed_step_kernel<RULE, DK, DV, IN_T, NG, SLOTS, LAZY, FMT>), dim3(p.units),
+                     dim3(32 * NG), 0, s, p.a, p.U, p.V, p.Uk, p.Vk, p.gam, p.vbar,
                      static_cast<const IN_T*>(p.q), static_cast<const IN_T*>(p.k),
                      static_cast<const IN_T*>(p.v), p.g, p.beta, p.o, p.heads, p.cap, p.r, p.kR,
                      p.ring);
 }
 
-template <int RULE, int DK, int DV, typename IN_T, int SLOTS>
+template <int RULE, int DK, int DV, typename IN_T, int NG, int SLOTS>
 hipError_t step_go(int fmt, const StepArgs& p, hipStream_t s) {
   if (fmt == kStoreRing) {
-    step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreRing>(p, s);
+    step_launch<RULE, DK, DV, IN_T, NG, SLOTS, true, kStoreRing>(p, s);
   } else if (fmt == kStoreBF16) {
-    step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreBF16>(p, s);
+    step_launch<RULE, DK, DV, IN_T, NG, SLOTS, true, kStoreBF16>(p, s);
   } else if (fmt == kStoreF16) {
-    step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreF16>(p, s);
+    step_launch<RULE, DK, DV, IN_T, NG, SLOTS, true, kStoreF16>(p, s);
   } else if (p.gam != nullptr) {
-    step_launch<RULE, DK, DV, IN_T, SLOTS, true, kStoreF32>(p, s);
+    step_launch<RULE, DK, DV, IN_T, NG, SLOTS, true, kStoreF32>(p, s);
   } else {
-    step_launch<RULE, DK, DV, IN_T, SLOTS, false, kStoreF32>(p, s);
+    step_launch<RULE, DK, DV, IN_T, NG, SLOTS, false, kStoreF32>(p, s);
   }
   return hipGetLastError();
 }
 
 template <int RULE, int DK, int DV, typename IN_T>
 hipError_t step_slots(int fmt, const StepArgs& p, hipStream_t s) {
-  const int need = (p.r + kGroups - 1) / kGroups;
-  static_assert(6 * kGroups >= kMaxCap, "slot instances cover the capacity");
+  static_assert(6 * 16 >= kMaxCap, "slot instances cover the capacity");
+  if (p.gam != nullptr && p.units >= kHalfGroupUnits && p.r <= 6 * 8) {
+    const int need = (p.r + 7) / 8;
 #define SEED_STEP_SLOTS(N) \
-  if (need <= N) return step_go<RULE, DK, DV, IN_T, N>(fmt, p, s);
+    if (need <= N) return step_go<RULE, DK, DV, IN_T, 8, N>(fmt, p, s);
+    SEED_STEP_SLOTS(1)
+    SEED_STEP_SLOTS(2)
+    SEED_STEP_SLOTS(3)
+    SEED_STEP_SLOTS(4)
+    SEED_STEP_SLOTS(5)
+    SEED_STEP_SLOTS(6)
+#undef SEED_STEP_SLOTS
+  }
+  const int need = (p.r + 15) / 16;
+#define SEED_STEP_SLOTS(N) \
+  if (need <= N) return step_go<RULE, DK, DV, IN_T, 16, N>(fmt, p, s);
   SEED_STEP_SLOTS(1)
   SEED_STEP_SLOTS(2)
   SEED_STEP_SLOTS(3)

@@ -95,25 +95,39 @@ def dense_prefill(rule, batch, heads, d_k, d_v, vbar, seed, steps, in_dtype, lay
 # Read-back of the lazily decayed forms at true scale.  The stored columns
 # are U~ with U = Diag(gam) U~ (gam one float per unit, or one per key
 # channel for Kimi Delta Attention); the library only marshals them, so the
-# tests apply the scale themselves, in torch on the device.
+# tests apply the scale themselves.  The device only gathers the units asked
+# for (a copy); the scale is applied on the host in float64, so no device
+# arithmetic outside the library enters a check.
 
 def _gam_rows(st, gam):
     return gam if st.rule == "kda" else gam[..., None]
 
 
-def true_U(st: binding.ShallowState) -> torch.Tensor:
-    """U [B, H, cap, d_k] at true scale: st.U itself when decayed in place."""
+def _host(x, idx):
+    """x [B, H, ...] as float64 on the host: every unit, or the flat unit
+    indices idx ([len(idx), ...])."""
+    if idx is not None:
+        x = x.reshape((-1,) + tuple(x.shape[2:]))[idx]
+    return x.detach().to("cpu", torch.float64)
+
+
+def true_U(st: binding.ShallowState, idx=None) -> torch.Tensor:
+    """U at true scale, float64 on the host: [B, H, cap, d_k], or
+    [len(idx), cap, d_k] for the flat unit indices idx (st.U itself when
+    decayed in place)."""
+    U = _host(st.U, idx)
     if not st.lazy:
-        return st.U
-    return st.U * _gam_rows(st, st.gam)[:, :, None, :]
+        return U
+    return U * _gam_rows(st, _host(st.gam, idx))[..., None, :]
 
 
-def true_factors16(st: binding.ShallowState16):
-    """(U, V) of the 16-bit form over the r columns held, fp32, U at true scale."""
+def true_factors16(st: binding.ShallowState16, idx=None):
+    """(U, V) of the 16-bit form over the r columns held, U at true scale,
+    float64 on the host ([B, H, r, .], or [len(idx), r, .])."""
     w = st.r - st.R
-    U = torch.cat([st.Uk.float(), st.Uw[:, :, :w]], dim=2)
-    V = torch.cat([st.Vk.float(), st.Vw[:, :, :w]], dim=2)
-    return U * _gam_rows(st, st.gam)[:, :, None, :], V
+    U = torch.cat([_host(st.Uk, idx), _host(st.Uw, idx)[..., :w, :]], dim=-2)
+    V = torch.cat([_host(st.Vk, idx), _host(st.Vw, idx)[..., :w, :]], dim=-2)
+    return U * _gam_rows(st, _host(st.gam, idx))[..., None, :], V
 
 
 def sched_true_factors(st: binding.ScheduledState, b: int, h: int):
@@ -131,7 +145,7 @@ def sched_true_factors(st: binding.ScheduledState, b: int, h: int):
         slots = [(c * W + i) % (W + D) for i in range(w)]
         cols_u.append(st.Uw[b, h, slots])
         cols_v.append(st.Vw[b, h, slots])
-    U = torch.cat(cols_u, 0)
-    V = torch.cat(cols_v, 0)
-    gs = st.gam[b, h] if st.rule == "kda" else st.gam[b, h].reshape(1)
+    U = torch.cat(cols_u, 0).to("cpu", torch.float64)
+    V = torch.cat(cols_v, 0).to("cpu", torch.float64)
+    gs = (st.gam[b, h] if st.rule == "kda" else st.gam[b, h].reshape(1)).to("cpu", torch.float64)
     return (U * gs[None, :]).T, V.T

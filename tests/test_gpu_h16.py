@@ -461,9 +461,9 @@ def test_h16_workload_launch_size(num):
         worst = max(worst, float(e.max()) if e.size else 0.0)
         assert e.size == 0 or e.max() < tol, (t, e)
     ga = f64(st.a.reshape(units, w.d_k)[idx])
-    Ut, Vt = true_factors16(st)
-    gU = f64(Ut.reshape(units, st.r, w.d_k)[idx]).transpose(0, 2, 1)
-    gV = f64(Vt.reshape(units, st.r, w.d_v)[idx]).transpose(0, 2, 1)
+    Ut, Vt = true_factors16(st, torch.as_tensor(idx, device="cuda"))
+    gU = f64(Ut).transpose(0, 2, 1)
+    gV = f64(Vt).transpose(0, 2, 1)
     assert state_rel_err(ga, gU, gV, a, U, V, vb)[ok].max() < tol
     assert ok.sum() >= len(idx) - 1
     print(f"workload {num} fp16: worst read-out error {worst:.2e} (bar {tol:.2e})")

@@ -56,7 +56,7 @@ def _units_state(st, idx_t, r):
     """(a, U at true scale, V) of the sampled units, float64, math orientation."""
     cap = st.cap
     a = f64(st.a.reshape(-1, st.d_k)[idx_t])
-    U = f64(true_U(st).reshape(-1, cap, st.d_k)[idx_t, :r]).transpose(0, 2, 1)
+    U = f64(true_U(st, idx_t)[:, :r]).transpose(0, 2, 1)
     V = f64(st.V.reshape(-1, cap, st.d_v)[idx_t, :r]).transpose(0, 2, 1)
     return a, U, V
 
