@@ -61,6 +61,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix rate, vendor figure
 DEFAULT_WORKLOAD = 5
 STEP_SOURCE = os.path.join(ROOT, "sink_rank_recurrent_amd", "csrc", "seed_step.hip")
 METRIC = ("decode head-steps/s + achieved HBM GB/s (% peak), sink+rank-R state update "
@@ -132,6 +133,64 @@ def load_traffic(w, steps: int, warmup: int):
     if t.get("bench_steps") != steps or t.get("bench_warmup") != warmup:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def counters_file(w) -> str:
+    return os.path.join(ROOT, "profiles",
+                        f"counters_compress_wave_{w.rule}_{w.batch}x{w.heads}_n{w.R + w.W}.md")
+
+
+def load_compress_counters(w):
+    """Per-unit instruction counts of the fp32 compression kernel from the
+    committed rocprofv3 summary of this workload's compressions
+    (profile_compress.sh), or None if there is none.  MFMA work does not
+    depend on the data: it is fixed by n, R and the head shape."""
+    import re
+    path = counters_file(w)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"dispatches of (\d+) units \((\d+) wave", text)
+    if not m:
+        return None
+    units, wpu = int(m.group(1)), int(m.group(2))
+    rows = {}
+    for name, per_dispatch, per_wave in re.findall(
+            r"^\| (SQ_\w+) \| \d+ \| ([0-9.e+-]+) \| ([0-9.e+-]+) \|$", text, re.M):
+        rows[name] = (float(per_dispatch), float(per_wave))
+    if "SQ_INSTS_VALU_MFMA_MOPS_F32" not in rows or "SQ_INSTS_VALU" not in rows:
+        return None
+    return {"file": os.path.relpath(path, ROOT),
+            # one MOP of this counter is 512 fp32 flops
+            "mfma_flops_per_unit": rows["SQ_INSTS_VALU_MFMA_MOPS_F32"][0] * 512 / units,
+            "valu_insts_per_unit": rows["SQ_INSTS_VALU"][1] * wpu,
+            "mfma_insts_per_unit": rows["SQ_INSTS_MFMA"][1] * wpu if "SQ_INSTS_MFMA" in rows
+            else None}
+
+
+def compression_roofline(w, units: int, avg_us):
+    """The compression kernel against both of its ceilings: HBM (it reads
+    n = R + W columns of U and V and writes R) and fp32 MFMA (its dense
+    products, counted by rocprofv3).  It is bound by neither: its serial
+    Cholesky, Householder and eigen-solver chains bound it."""
+    if not avg_us:
+        return None
+    n = w.R + w.W
+    bytes_unit = 4 * (w.d_k + w.d_v) * (n + w.R)
+    s = avg_us * 1e-6
+    rec = {"kernel": "compress_wave_kernel", "columns": n, "units_per_launch": units,
+           "avg_launch_us": avg_us, "bytes_per_unit": bytes_unit,
+           "achieved_GBs": bytes_unit * units / s / 1e9,
+           "hbm_frac": bytes_unit * units / s / 1e9 / HBM_PEAK_GBS}
+    c = load_compress_counters(w)
+    if c:
+        tf = c["mfma_flops_per_unit"] * units / s / 1e12
+        rec.update({"mfma_flops_per_unit": c["mfma_flops_per_unit"],
+                    "mfma_achieved_TFLOPs": tf, "mfma_peak_TFLOPs": MFMA_F32_PEAK_TFLOPS,
+                    "mfma_frac": tf / MFMA_F32_PEAK_TFLOPS,
+                    "valu_insts_per_unit": c["valu_insts_per_unit"],
+                    "mfma_insts_per_unit": c["mfma_insts_per_unit"], "counters": c["file"]})
+    return rec
 
 
 # ---------------------------------------------------------------------------
@@ -989,6 +1048,7 @@ def main() -> int:
             e["conversion_ms"] = cms
             e["dense_baseline"] = ds
             e["speedup_over_dense"] = e["value"] / ds["value"] if ds else None
+            e["compression"] = compression_roofline(ws, sp.units, e["compress_avg_us"])
             for form, key in (("in_place", "in_place_decay_variant"),
                               ("h16", "fp16_factor_variant")):
                 if form in rs and form != forms[0]:
@@ -1059,6 +1119,7 @@ def main() -> int:
                                            "compressions_overlapped",
                                            "compressions_per_layer_step", "compress_columns",
                                            "pre_roll_steps")},
+        "compression": compression_roofline(w, spec.units, head["compress_avg_us"]),
         "other_compression_schedule": (
             {k: results["other_schedule"][k]
              for k in ("value", "ms_per_step", "compressions_overlapped", "step_kernel_avg_us",

@@ -168,3 +168,21 @@ def test_ops_group_step_runs():
         else:
             assert l in pending
     assert sum(1 for x in seq if x[0] == "wait") + len(pending) == len(forks)
+
+
+@pytest.mark.parametrize("num, cols", [(5, 48), (4, 80)])
+def test_compression_counters_parse(num, cols):
+    """The committed compression counters give the MFMA work per unit that
+    the compression roofline divides: MOPS x 512 agrees with the MFMA
+    instruction count x 2048 flops of v_mfma_f32_16x16x4f32 (each summary
+    rounds to four digits), and the bytes per unit are those of n = R + W
+    columns read and R written."""
+    w = wl.WORKLOADS[num]
+    c = bench.load_compress_counters(w)
+    assert c is not None, bench.counters_file(w)
+    assert abs(c["mfma_flops_per_unit"] / (c["mfma_insts_per_unit"] * 2048) - 1) < 1e-3
+    rec = bench.compression_roofline(w, 1000, 100.0)
+    assert rec["columns"] == cols
+    assert rec["bytes_per_unit"] == 4 * (w.d_k + w.d_v) * (cols + w.R)
+    assert abs(rec["mfma_achieved_TFLOPs"] - c["mfma_flops_per_unit"] * 1000 / 1e-4 / 1e12) < 1e-9
+    assert bench.compression_roofline(w, 1000, None) is None
