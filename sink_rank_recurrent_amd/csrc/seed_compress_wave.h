@@ -181,14 +181,23 @@ struct Lay {
   static constexpr int CH = NMAX / PARTS;          // rows per lane
   // one wave keeps two of the three solve factors of phase F in registers
   static constexpr bool FREG = NW == 1;
-  static constexpr int G = 0;                      // [NMAX][LDN] Grams, Z, H (the conversion: then reflectors)
-  // [NMAX][LDN] R~ in pivot order, RB[p LDN + i] = R~[i][PIV[p]] (i <= p),
-  // and reflector k in row k at entries > k
-  static constexpr int RB = G + NMAX * LDN;
   // The regions used from phase D on ("late") go into G, which is free once
   // H is in registers, when they fit (the compression); else after RB.
   static constexpr int LATE = 2 * NMAX * RMAX + (FREG ? 0 : 2 * NMAX * RMAX) + 6 * NMAX + 3 * RMAX;
-  static constexpr bool COMPACT = !NO_RB && LATE <= NMAX * LDN;
+  // the published vectors and the two scales of phase H (see T0 below)
+  static constexpr int TAILN = 3 * NTH + 2 * NMAX;
+  // Two-wave compressions keep G unpadded (row stride NMAX) when the late
+  // regions and that tail still fit: at n = 80 that brings a unit to 53.2
+  // KB, so three units share a CU.  The padding only spreads the banks of
+  // G's transposed stores and tile reads (phases A and C, once per
+  // compression).
+  static constexpr bool GPACK = !NO_RB && NW == 2 && LATE + TAILN <= NMAX * NMAX;
+  static constexpr int LDG = GPACK ? NMAX : LDN;   // row stride of G
+  static constexpr int G = 0;                      // [NMAX][LDG] Grams, Z, H (the conversion: then reflectors)
+  // [NMAX][LDN] R~ in pivot order, RB[p LDN + i] = R~[i][PIV[p]] (i <= p),
+  // and reflector k in row k at entries > k
+  static constexpr int RB = G + NMAX * LDG;
+  static constexpr bool COMPACT = !NO_RB && LATE <= NMAX * LDG;
   static constexpr int L0 = COMPACT ? G : RB + (NO_RB ? 0 : NMAX * LDN);
   static constexpr int XR = L0;                    // [NMAX][RMAX] eigenvectors, Y, then T'
   static constexpr int FA = XR + NMAX * RMAX;      // [NMAX][RMAX] reciprocal pivots of phase F, then P2
@@ -213,8 +222,7 @@ struct Lay {
   // there from phase D on, and the scales are kept in registers until D
   // stores them.  That keeps a unit at n = 48, R = 16 within 20 KB, so
   // eight units share a CU.
-  static constexpr int TAILN = 3 * NTH + 2 * NMAX;
-  static constexpr bool TAIL = COMPACT && LEND + TAILN <= G + NMAX * LDN;
+  static constexpr bool TAIL = COMPACT && LEND + TAILN <= G + NMAX * LDG;
   static constexpr int T0 = TAIL ? LEND : E0;
   static constexpr int CB = T0;                    // [NTH] published column
   static constexpr int VB = CB + NTH;              // [NTH] Householder vector
@@ -234,16 +242,19 @@ struct Lay {
   static_assert(NMAX % 16 == 0 && NMAX <= 128, "NMAX");
   static_assert(8 * NTH <= 2 * NMAX * RMAX, "bisection points fit in XR and FA");
   static_assert(RMAX == 16 || RMAX == 32, "RMAX");
-  static_assert(!COMPACT || LEND <= G + NMAX * LDN, "late regions fit in G");
+  static_assert(!COMPACT || LEND <= G + NMAX * LDG, "late regions fit in G");
 };
 
 // Waves per SIMD the compiler plans registers for: two where a
-// compression's LDS lets more than four units share a CU, one otherwise
-// (the conversion, at n = d_k, keeps the whole register file).
+// compression's LDS lets more than four one-wave units, or three two-wave
+// units (in 512-byte allocation granules), share a CU; one otherwise (the
+// conversion, at n = d_k, keeps the whole register file).
 template <int NMAX, int RMAX, bool NO_RB>
 constexpr int wave_min_waves() {
-  return (!NO_RB && Lay<NMAX, RMAX, NO_RB>::NW == 1 &&
-          4 * Lay<NMAX, RMAX, NO_RB>::TOTAL <= 32 * 1024) ? 2 : 1;
+  using L = Lay<NMAX, RMAX, NO_RB>;
+  constexpr size_t granules = (4 * (size_t)L::TOTAL + 511) / 512;
+  return (!NO_RB && ((L::NW == 1 && 4 * L::TOTAL <= 32 * 1024) ||
+                     (L::NW == 2 && 3 * 512 * granules <= 160 * 1024))) ? 2 : 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -260,14 +271,13 @@ constexpr int wave_min_waves() {
 // columns perm[i] and perm[j] (perm a permutation of 0 .. NMAX-1 that keeps
 // 0 .. n-1 among themselves), scaled by dv[perm[i]] dv[perm[j]].
 template <int NMAX, int NW, int D, bool SCALE, int FMT, int KR, typename ColF,
-          bool CORR = false, bool PERM = false>
+          bool CORR = false, bool PERM = false, int LDG = NMAX + 4>
 __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
                                      int n, float* __restrict__ G,
                                      const float* __restrict__ dv, const float* __restrict__ rs,
                                      bool rs_per_row, const float* __restrict__ ca = nullptr,
                                      const float* __restrict__ cb = nullptr,
                                      const int* __restrict__ perm = nullptr) {
-  constexpr int LDN = NMAX + 4;
   constexpr int NT = NMAX / 16;
   constexpr int NP = NT * (NT + 1) / 2;
   constexpr int KPL = D / (4 * NW);
@@ -363,7 +373,7 @@ __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
 #pragma unroll
         for (int J = I; J < NT; ++J) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) G[(I * 16 + 4 * kk + r) * LDN + J * 16 + ci] = acc[p][r];
+          for (int r = 0; r < 4; ++r) G[(I * 16 + 4 * kk + r) * LDG + J * 16 + ci] = acc[p][r];
           ++p;
         }
     }
@@ -377,7 +387,7 @@ __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
 #pragma unroll
         for (int J = I; J < NT; ++J) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[p][r] += G[(I * 16 + 4 * kk + r) * LDN + J * 16 + ci];
+          for (int r = 0; r < 4; ++r) acc[p][r] += G[(I * 16 + 4 * kk + r) * LDG + J * 16 + ci];
           ++p;
         }
     }
@@ -393,8 +403,8 @@ __device__ __forceinline__ void gram(ColF colf, const uint16_t* __restrict__ Xk,
           const int i = I * 16 + 4 * kk + r, j = J * 16 + ci;
           float v = acc[p][r];
           if constexpr (SCALE) v *= dv[PERM ? perm[i] : i] * dv[PERM ? perm[j] : j];
-          G[i * LDN + j] = v;
-          G[j * LDN + i] = v;
+          G[i * LDG + j] = v;
+          G[j * LDG + i] = v;
         }
         ++p;
       }
@@ -601,7 +611,7 @@ void compress_wave_kernel(CompressArgs args) {
   constexpr bool CONV = FMT == kConvert;
   constexpr int KR = H16 ? RMAX : 0;
   using L = Lay<NMAX, RMAX, CONV>;
-  constexpr int NW = L::NW, NTH = L::NTH, LDN = L::LDN;
+  constexpr int NW = L::NW, NTH = L::NTH, LDN = L::LDN, LDG = L::LDG;
   constexpr int PARTS = L::PARTS, CH = L::CH, NACT = L::NACT;
   extern __shared__ float4 smem4[];
   float* const sm = reinterpret_cast<float*>(smem4);
@@ -728,13 +738,14 @@ void compress_wave_kernel(CompressArgs args) {
     __syncthreads();
   } else {
     // @phase A: Gram of U and column norms
-    gram<NMAX, NW, DK, false, FMT, KR>(ucol, Ukh, n, G, nullptr, gamh, gam_per_row);
+    gram<NMAX, NW, DK, false, FMT, KR, decltype(ucol), false, false, LDG>(ucol, Ukh, n, G, nullptr,
+                                                                         gamh, gam_per_row);
     __syncthreads();
     if (act) {
       // a column whose squared norm is below the normal fp32 range (norm
       // under 1.1e-19: decayed to nothing) is taken as dependent; its
       // reciprocal square root would read the subnormal as zero
-      const float gtt = G[t * LDN + t];
+      const float gtt = G[t * LDG + t];
       const bool pos = t < n && gtt >= kMinNormal;
       DVs[t] = pos ? fsqrt(gtt) : 0.f;
       idv_own = pos ? frsq(gtt) : 0.f;
@@ -748,11 +759,11 @@ void compress_wave_kernel(CompressArgs args) {
       // formed from the diagonal as thread i forms its own
   #pragma unroll
       for (int i = 0; i < NMAX; ++i) {
-        const float gii = G[i * LDN + i];
+        const float gii = G[i * LDG + i];
         const float di = (i < n && gii >= kMinNormal) ? frsq(gii) : 0.f;
-        g[i] = act ? G[i * LDN + t] * (it * di) : 0.f;
+        g[i] = act ? G[i * LDG + t] * (it * di) : 0.f;
       }
-      dg = (act && t < n) ? G[t * LDN + t] * (it * it) : 0.f;
+      dg = (act && t < n) ? G[t * LDG + t] * (it * it) : 0.f;
     }
     __syncthreads();
 
@@ -840,7 +851,7 @@ void compress_wave_kernel(CompressArgs args) {
       }
     }
     // Gram of V in pivot order, scaled to D V^T V D
-    gram<NMAX, NW, DV_, true, FMT, KR, decltype(vcol), false, true>(
+    gram<NMAX, NW, DV_, true, FMT, KR, decltype(vcol), false, true, LDG>(
         vcol, Vkh, n, G, DVs, nullptr, false, nullptr, nullptr, PIV);
     __syncthreads();
 
@@ -860,7 +871,7 @@ void compress_wave_kernel(CompressArgs args) {
   #pragma unroll
         for (int K = 0; K < NMAX / 4; ++K) {
           const int m = 4 * K + kk;
-          const float bv = G[m * LDN + 16 * J + ci];          // G~[m][j]
+          const float bv = G[m * LDG + 16 * J + ci];          // G~[m][j]
   #pragma unroll
           for (int I = 0; I < NT; ++I) {
             const float av = RB[m * LDN + 16 * I + ci];        // R~[i][m]
@@ -870,7 +881,7 @@ void compress_wave_kernel(CompressArgs args) {
   #pragma unroll
         for (int I = 0; I < NT; ++I)
   #pragma unroll
-          for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDN + 16 * J + ci] = acc[I][r];
+          for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDG + 16 * J + ci] = acc[I][r];
       }
       __syncthreads();
   #pragma unroll
@@ -882,7 +893,7 @@ void compress_wave_kernel(CompressArgs args) {
   #pragma unroll
         for (int K = 0; K < NMAX / 4; ++K) {
           const int m = 4 * K + kk;
-          const float av = G[(16 * I + ci) * LDN + m];        // Z[i][m]
+          const float av = G[(16 * I + ci) * LDG + m];        // Z[i][m]
   #pragma unroll
           for (int J = 0; J < NT; ++J) {
             const float bv = RB[m * LDN + 16 * J + ci];        // R~[j][m]
@@ -892,7 +903,7 @@ void compress_wave_kernel(CompressArgs args) {
   #pragma unroll
         for (int J = 0; J < NT; ++J)
   #pragma unroll
-          for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDN + 16 * J + ci] = acc[J][r];
+          for (int r = 0; r < 4; ++r) G[(16 * I + 4 * kk + r) * LDG + 16 * J + ci] = acc[J][r];
       }
       __syncthreads();
     }
@@ -907,7 +918,7 @@ void compress_wave_kernel(CompressArgs args) {
   // puts H near 1e-12 and its small entries' squares below 1e-38).
   float hs = 1.f;
   {
-    const float dg = (act && t < n) ? G[t * LDN + t] : 0.f;
+    const float dg = (act && t < n) ? G[t * LDG + t] : 0.f;
     const float mxd = block_reduce<NW>(dg, MaxOp(), RED, 5);
     if (mxd > 0.f && mxd < 3.0e38f) {
       int ex;
@@ -917,7 +928,7 @@ void compress_wave_kernel(CompressArgs args) {
   }
   float h[NMAX];
 #pragma unroll
-  for (int i = 0; i < NMAX; ++i) h[i] = act ? G[i * LDN + t] * hs : 0.f;
+  for (int i = 0; i < NMAX; ++i) h[i] = act ? G[i * LDG + t] * hs : 0.f;
   __syncthreads();
   if constexpr (!CONV) {
     // the scales phase H reads: IDV[i] = 1/d_i, IRD[j] = 1/R~[j][PIV[j]]
