@@ -107,16 +107,19 @@ def test_scheduled_run_matches_oracle(rule, dims, W, D, K, NS, R):
     assert skipped <= B * H // 4, skipped
 
 
-def test_scheduled_launch_size_sampled():
-    """Workload 2's launch (64 requests x 16 GDN heads, R = 16, W = 32) with
-    starts spread over the W phases and D = 16, as bench.py times it;
-    sampled heads against the oracle's schedule from the oracle's own
-    conversion of its own prefill."""
-    w = wl.WORKLOADS[2]
-    B, H, R, W, D = w.batch, w.heads, w.R, w.W, 16
+@pytest.mark.parametrize("num,D", [(2, 16), (5, 8)])
+def test_scheduled_launch_size_sampled(num, D):
+    """Launch-size per-request schedules with starts spread over the W
+    phases, sampled heads against the oracle's schedule from the oracle's
+    own conversion of its own prefill: workload 2 (64 requests x 16 GDN
+    heads, R = 16, W = 32) at D = 16, and one layer of the 36-layer
+    workload (256 requests x 32 heads, 8192 units) at D = 8, as bench.py
+    times it (up to 55 held columns, the 256-thread step workgroup)."""
+    w = wl.WORKLOADS[num]
+    B, H, R, W = w.batch, w.heads, w.R, w.W
     units = B * H
     t_start = [b % W for b in range(B)]
-    idx = np.array([0, 17, 330, 700, units - 1])
+    idx = np.array([0, 17, 330, 700, units - 1] if num == 2 else [0, 17, 2731, 5466, units - 1])
     vbar = wl.make_vbar(H, w.d_v, w.seed, 0, "cuda")
     vb = f64(vbar)[idx % H]
     S = torch.zeros(B, H, w.d_k, w.d_v, device="cuda")
