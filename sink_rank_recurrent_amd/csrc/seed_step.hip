@@ -57,7 +57,7 @@ namespace seed {
 constexpr float kFoldBelow = 0x1p-64f;
 constexpr float kPoisonBelow = 0x1p-110f;
 // Lazily decayed launches (fp32, 16-bit or ring layout) of at least this
-// many units and at most 64 held columns use 8 column groups (256 threads)
+// many units and at most 80 held columns use 8 column groups (256 threads)
 // per workgroup: 4 to 8 units share a CU instead of 3 or 4.  The form decayed in
 // place keeps 16 groups (its U write-back fills the combine phase), as do
 // small batches, which 16 groups spread over more of the GPU.
@@ -434,7 +434,7 @@ hipError_t step_go(int fmt, const StepArgs& p, hipStream_t s) {
 template <int RULE, int DK, int DV, typename IN_T>
 hipError_t step_slots(int fmt, const StepArgs& p, hipStream_t s) {
   static_assert(6 * 16 >= kMaxCap, "slot instances cover the capacity");
-  if (p.gam != nullptr && p.units >= kHalfGroupUnits && p.r <= 8 * 8) {
+  if (p.gam != nullptr && p.units >= kHalfGroupUnits && p.r <= 10 * 8) {
     const int need = (p.r + 7) / 8;
 #define SEED_STEP_SLOTS(N) \
     if (need <= N) return step_go<RULE, DK, DV, IN_T, 8, N>(fmt, p, s);
@@ -446,6 +446,8 @@ hipError_t step_slots(int fmt, const StepArgs& p, hipStream_t s) {
     SEED_STEP_SLOTS(6)
     SEED_STEP_SLOTS(7)
     SEED_STEP_SLOTS(8)
+    SEED_STEP_SLOTS(9)
+    SEED_STEP_SLOTS(10)
 #undef SEED_STEP_SLOTS
   }
   const int need = (p.r + 15) / 16;
