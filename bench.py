@@ -62,6 +62,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix rate, vendor figure
+# Merge delay of the per-request schedule variant: on the 36 resident layers
+# D = 2 measured fastest of 1..12 (3.41 ms per bench step; 3.97 at D = 1,
+# where every step launches a compression per layer, and 3.46-3.78 from 3
+# to 12, where each step of delay holds one more column).
+PER_REQUEST_DELAY = 2
 DEFAULT_WORKLOAD = 5
 STEP_SOURCE = os.path.join(ROOT, "sink_rank_recurrent_amd", "csrc", "seed_step.hip")
 METRIC = ("decode head-steps/s + achieved HBM GB/s (% peak), sink+rank-R state update "
@@ -785,9 +790,8 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
         every 8 bench steps, joining every layer;
       * per-request schedules (seed_decode_step_sched): request b starts at
         phase b mod W and compresses on its own schedule, the snapshots of
-        D consecutive steps compressed by one launch, D the smallest delay
-        whose launch gives every SIMD of the GPU two units (the compression
-        at n <= 64 is built for two waves per SIMD), or each of `delays`.
+        D consecutive steps compressed by one launch, D = PER_REQUEST_DELAY
+        (or each of `delays`).
     The global phase runs its compressions as the aligned run does (on a
     side stream with overlap, else on the launch stream); the per-request
     schedules' smaller launches always run on a side stream."""
@@ -814,10 +818,8 @@ def run_stagger_variants(w, spec, vbars, Ss, phases, inputs, outs, pre, settle, 
     torch.cuda.empty_cache()
 
     # per-request schedules
-    units = spec.units
-    simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
     cap_d = min(w.W - 1, 96 - w.R - w.W)
-    for D in (delays or [min(cap_d, -(-2 * simds // (units // w.W)))]):
+    for D in (delays or [PER_REQUEST_DELAY]):
         out.append(_per_request_run(w, spec, vbars, Ss, inputs, outs, pre, settle, timed, dev,
                                     aligned, min(D, cap_d)))
     return out
@@ -831,7 +833,7 @@ def _per_request_run(w, spec, vbars, Ss, inputs, outs, pre, settle, timed, dev, 
     t_start = [-(b % w.W) - (w.W + D) for b in range(w.batch)]
     scheds = []
     for l, (vbar, S) in enumerate(zip(vbars, Ss)):
-        # a launch holds the units of D phases only (2048 of 8192 at D = 8),
+        # a launch holds the units of D phases only (512 of 8192 at D = 2),
         # so it leaves CUs to the steps: on a side stream it runs beside them
         # (at D = 4, 4.10 against 4.40 ms per step on the launch stream)
         st = binding.ScheduledState(w.rule, w.batch, w.heads, w.d_k, w.d_v, w.R, w.W, D, vbar,
@@ -963,7 +965,7 @@ def main() -> int:
                     help="skip the other workloads' entries")
     ap.add_argument("--stagger-d", type=lambda x: [int(v) for v in x.split(",")], default=None,
                     help="merge delays D of the per-request schedule variant (comma list; "
-                         "default: the smallest that gives every SIMD a unit per launch)")
+                         "default: PER_REQUEST_DELAY)")
     ap.add_argument("--overlap", action="store_true",
                     help="run each layer's compression on a side stream, beside the other "
                          "layers' steps (default: on the launch stream after its bench step; "
