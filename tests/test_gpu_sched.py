@@ -107,14 +107,15 @@ def test_scheduled_run_matches_oracle(rule, dims, W, D, K, NS, R):
     assert skipped <= B * H // 4, skipped
 
 
-@pytest.mark.parametrize("num,D", [(2, 16), (5, 8)])
+@pytest.mark.parametrize("num,D", [(2, 16), (5, 8), (5, 2)])
 def test_scheduled_launch_size_sampled(num, D):
     """Launch-size per-request schedules with starts spread over the W
     phases, sampled heads against the oracle's schedule from the oracle's
     own conversion of its own prefill: workload 2 (64 requests x 16 GDN
     heads, R = 16, W = 32) at D = 16, and one layer of the 36-layer
-    workload (256 requests x 32 heads, 8192 units) at D = 8, as bench.py
-    times it (up to 55 held columns, the 256-thread step workgroup)."""
+    workload (256 requests x 32 heads, 8192 units, the 256-thread step
+    workgroup) at D = 8 (up to 55 held columns) and at D = 2, as bench.py
+    times it."""
     w = wl.WORKLOADS[num]
     B, H, R, W = w.batch, w.heads, w.R, w.W
     units = B * H
